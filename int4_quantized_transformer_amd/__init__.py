@@ -1,0 +1,19 @@
+"""zq: the fused quantized linear layer of ZeroQuant, native on MI355X.
+
+The compute lives in ``libzq.so`` (hand-written HIP kernels for gfx950 behind a
+C ABI declared in ``include/zq.h``).  This package is a thin ctypes binding
+over it plus the seeded synthetic workloads.  Nothing here falls back to a CPU
+or PyTorch implementation: if the library is missing, every call raises.
+"""
+__all__ = ["quantize_weights", "ln_quant_act", "quant_act", "gemm_w8a8",
+           "gemm_w4a8", "gemm_w8a8_i32", "gemm_w4a8_i32", "ZQError",
+           "library_path"]
+
+
+def __getattr__(name):
+    # The binding is imported on first use so that importing the workloads
+    # module alone never needs the shared library.
+    if name in __all__:
+        from . import _lib
+        return getattr(_lib, name)
+    raise AttributeError(name)

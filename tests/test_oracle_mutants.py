@@ -1,0 +1,63 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of ``oracle/zq_oracle.c`` (on the CPU,
+in a temporary directory), builds it, and runs the pin suite against it with
+``ZQ_ORACLE_LIB``; the suite must fail.  The committed oracle is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "zq_oracle.c")
+
+MUTANTS = {
+    # Eq. (2) read literally: S = max|x| (codes collapse to -1, 0, 1)
+    "scale_without_qmax": ("s = amax / (float)qmax;", "s = amax;"),
+    # ties away from zero instead of to even
+    "round_half_away": ("r = rintf(x);", "r = roundf(x);"),
+    # truncation instead of rounding
+    "truncate": ("r = rintf(x);", "r = truncf(x);"),
+    # unbiased variance in LayerNorm
+    "ln_unbiased_var": ("var /= K;", "var /= (K - 1);"),
+    # eps dropped from LayerNorm
+    "ln_no_eps": ("sqrt(var + (double)eps)", "sqrt(var)"),
+    # wrong operand index in the GEMM
+    "gemm_shifted_k": ("s += (int64_t)a[k] * (int64_t)b[k];",
+                       "s += (int64_t)a[k] * (int64_t)b[(k + 1) % K];"),
+    # weight scale looked up by token instead of by output group
+    "epilogue_scale_by_token": ("(double)sw[n / G]", "(double)sw[t % (N / G)]"),
+    # bias dropped
+    "epilogue_no_bias": ("v += zqo_half_to_double(bias[n]);", "v += 0.0;"),
+    # GeLU with erf(x) instead of erf(x / sqrt 2)
+    "gelu_wrong_arg": ("erf(v / sqrt(2.0))", "erf(v)"),
+    # W4 nibbles not sign-extended
+    "w4_no_sign_extend": ("if (lo >= 8)\n                lo -= 16;", ""),
+    # W4 nibble order swapped
+    "w4_nibble_order": ("(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
+    # binary16 rounding by truncation
+    "half_truncates": ("n = rint(a / quantum);", "n = floor(a / quantum);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    c = tmp_path / "mut.c"
+    c.write_text(mutated)
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
+                    "-o", str(so), str(c), "-lm"], check=True)
+    env = dict(os.environ, ZQ_ORACLE_LIB=str(so))
+    r = subprocess.run(
+        [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, (
+        f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}")

@@ -1,0 +1,358 @@
+"""Pins for the CPU oracle, none of which is the oracle itself.
+
+Each check comes from something the pages or mathematics fix: hand-derived
+worked examples (tests/golden, each with its derivation), closed forms,
+invariants of the quantizer (Eq. (2) of the ZeroQuant summary page, Sec. 3.4
+"Group-wise Weight Quantization"), brute force with Python integers, and
+library routines (numpy's binary16 conversion, torch's layer_norm, numpy's
+int64 matmul, math.erf-free textbook values of the normal CDF).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int4_quantized_transformer_amd import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _f16(a):
+    return np.asarray(a, dtype=np.float16)
+
+
+# ---------------------------------------------------------------- binary16 --
+def test_half_to_double_all_bit_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = bits.view(np.float16)
+    ours = oracle.half_to_double(h)
+    ref = h.astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_double_to_half_matches_numpy_rounding():
+    rng = np.random.default_rng(1)
+    # random magnitudes over the whole binary16 range, plus exact ties
+    v = np.concatenate([
+        rng.standard_normal(200_000) * 10.0 ** rng.integers(-9, 5, 200_000),
+        rng.uniform(-70000, 70000, 20_000),
+        # exact midpoints between neighbouring fp16 values (ties)
+        (np.arange(1, 4096, dtype=np.float64) + 0.5) * 2.0 ** -24,
+        (np.arange(1024, 2048, dtype=np.float64) + 0.5) * 2.0 ** -10,
+        np.array([65504.0, 65519.99, 65520.0, 1e9, -1e9, 0.0, -0.0,
+                  2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26, np.inf,
+                  -np.inf]),
+    ])
+    ours = oracle.double_to_half(v).view(np.uint16)
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# --------------------------------------------------------------- quantizer --
+def test_quantizer_worked_token_rows():
+    g = _gold("quantizer_worked.json")
+    for case in g["token_rows"]:
+        q, sx = oracle.quant_tokens(_f16([case["x"]]))
+        assert q[0].tolist() == case["codes"], case["why"]
+        assert float(sx[0]) == case["scale"], case["why"]
+
+
+def test_quantizer_worked_weight_groups():
+    g = _gold("quantizer_worked.json")
+    for case in g["weight_groups"]:
+        q, sw = oracle.quantize_weights(_f16(case["w"]), case["G"],
+                                        case["bits"])
+        assert q.tolist() == case["codes"], case["why"]
+        if "scales" in case:
+            assert sw.tolist() == case["scales"]
+        else:
+            exp = [np.float32(127.0) / np.float32(127.0),
+                   np.float32(1.0) / np.float32(127.0)]
+            assert sw.tolist() == [float(e) for e in exp]
+        if "packed" in case:
+            assert oracle.pack_w4(q).tolist() == case["packed"]
+
+
+@pytest.mark.parametrize("bits,qmax", [(8, 127), (4, 7)])
+def test_quantizer_invariants_weights(bits, qmax):
+    w = W.randn_fp16((96, 80), seed=3, std=0.02).numpy()
+    w[:32] *= 50.0  # group 0 has a much larger range than the others
+    G = 32
+    q, sw = oracle.quantize_weights(w, G, bits)
+    wf = w.astype(np.float64)
+    assert q.min() >= -qmax and q.max() <= qmax
+    for g in range(w.shape[0] // G):
+        blk = wf[g * G:(g + 1) * G]
+        amax = np.abs(blk).max()
+        # scale is amax/qmax in fp32
+        assert sw[g] == np.float32(np.float32(amax) / np.float32(qmax))
+        # the amax element(s) map to +-qmax exactly
+        qb = q[g * G:(g + 1) * G]
+        at = np.abs(blk) == amax
+        assert np.all(np.abs(qb[at]) == qmax)
+        assert np.all(np.sign(qb[at]) == np.sign(blk[at]))
+        # every element is reconstructed within half a step (+ fp32 slack)
+        s = float(sw[g])
+        err = np.abs(blk - qb.astype(np.float64) * s)
+        assert np.all(err <= s / 2 + 2.0 ** -22 * np.abs(blk) + 1e-30)
+        # each group uses its own range: the small groups still reach qmax
+        assert np.abs(qb).max() == qmax
+
+
+def test_quantizer_invariants_tokens():
+    x = W.randn_fp16((64, 200), seed=5).numpy()
+    x[::3] *= 30.0          # tokens with ranges far apart
+    x[7] = 0.0              # an all-zero token
+    q, sx = oracle.quant_tokens(x)
+    xf = x.astype(np.float64)
+    for t in range(x.shape[0]):
+        amax = np.abs(xf[t]).max()
+        if amax == 0:
+            assert sx[t] == 0 and np.all(q[t] == 0)
+            continue
+        assert sx[t] == np.float32(np.float32(amax) / np.float32(127))
+        at = np.abs(xf[t]) == amax
+        assert np.all(np.abs(q[t][at]) == 127)
+        err = np.abs(xf[t] - q[t].astype(np.float64) * float(sx[t]))
+        assert np.all(err <= float(sx[t]) / 2 + 2.0 ** -22 * np.abs(xf[t]))
+    assert q.min() >= -127 and q.max() <= 127
+
+
+def test_quantizer_ties_go_to_even():
+    # S = 1 exactly (amax 127): x = k + 0.5 must give the even neighbour
+    ks = np.arange(-60, 60) + 0.5
+    row = np.concatenate([[127.0], ks])
+    q, sx = oracle.quant_tokens(_f16([row]))
+    assert sx[0] == 1.0
+    exp = [127] + [int(2 * round(k / 2)) for k in ks]  # even neighbour
+    for k, got in zip(ks, q[0][1:]):
+        lo, hi = math.floor(k), math.ceil(k)
+        assert got == (lo if lo % 2 == 0 else hi)
+    assert q[0].tolist() == exp
+
+
+def test_quantizer_constant_magnitude_group():
+    w = np.full((4, 6), 0.75, np.float16)
+    w[1, ::2] = -0.75
+    q, sw = oracle.quantize_weights(w, 4, 8)
+    assert np.all(np.abs(q) == 127)
+    q4, _ = oracle.quantize_weights(w, 2, 4)
+    assert np.all(np.abs(q4) == 7)
+
+
+def test_quantizer_zero_group():
+    w = np.zeros((4, 8), np.float16)
+    w[2:] = 1.0
+    q, sw = oracle.quantize_weights(w, 2, 8)
+    assert sw[0] == 0 and np.all(q[:2] == 0)
+    assert np.all(q[2:] == 127)
+
+
+def test_quantizer_rejects_bad_groups():
+    w = np.zeros((6, 8), np.float16)
+    with pytest.raises(ValueError):
+        oracle.quantize_weights(w, 4, 8)   # N % G != 0
+    with pytest.raises(ValueError):
+        oracle.quantize_weights(w, 3, 5)   # bits not 4/8
+
+
+# ---------------------------------------------------------------- W4 packing --
+def test_w4_pack_roundtrip_and_nibble_order():
+    rng = np.random.default_rng(7)
+    q = rng.integers(-8, 8, size=(5, 18)).astype(np.int8)
+    p = oracle.pack_w4(q)
+    assert p.shape == (5, 9)
+    assert np.array_equal(oracle.unpack_w4(p), q)
+    # low nibble is the even k, two's complement
+    assert oracle.pack_w4(np.array([[1, -1]], np.int8)).tolist() == [[0xF1]]
+    assert oracle.pack_w4(np.array([[-8, 7]], np.int8)).tolist() == [[0x78]]
+    assert oracle.unpack_w4(np.array([[0x9E]], np.uint8)).tolist() == [[-2, -7]]
+
+
+# ----------------------------------------------------------------- LayerNorm --
+def test_layernorm_worked():
+    for case in _gold("layernorm_worked.json")["cases"]:
+        beta = _f16(case["beta"]) if "beta" in case else None
+        h = oracle.layernorm(_f16([case["x"]]), None, beta, case["eps"])
+        assert h[0].astype(np.float64).tolist() == case["h"], case["why"]
+
+
+def test_layernorm_matches_torch_fp64():
+    x = W.randn_fp16((37, 300), seed=11, std=3.0, mean=0.7).numpy()
+    x[:, 5] *= 20
+    gamma = W.randn_fp16((300,), seed=12, std=0.5, mean=1.0).numpy()
+    beta = W.randn_fp16((300,), seed=13, std=0.1).numpy()
+    h = oracle.layernorm(x, gamma, beta, 1e-5)
+    ref = torch.nn.functional.layer_norm(
+        torch.from_numpy(x.astype(np.float64)), (300,),
+        torch.from_numpy(gamma.astype(np.float64)),
+        torch.from_numpy(beta.astype(np.float64)),
+        eps=float(np.float32(1e-5))).numpy()
+    ref16 = ref.astype(np.float16)
+    # both are fp64 computations rounded once; allow 1 fp16 ulp for
+    # reduction-order differences that land on a rounding boundary
+    ulp = np.spacing(np.abs(ref16).astype(np.float16)).astype(np.float64)
+    d = np.abs(h.astype(np.float64) - ref16.astype(np.float64))
+    assert np.all(d <= ulp)
+    assert np.mean(d == 0) > 0.999
+
+
+def test_layernorm_invariants():
+    x = W.randn_fp16((16, 1024), seed=17, std=4.0, mean=-2.0).numpy()
+    h = oracle.layernorm(x).astype(np.float64)
+    assert np.all(np.abs(h.mean(1)) < 2e-3)
+    var_x = x.astype(np.float64).var(1)
+    exp = var_x / (var_x + float(np.float32(1e-5)))
+    assert np.allclose(h.var(1), exp, rtol=2e-3)
+
+
+# ---------------------------------------------------------------------- GEMM --
+def _brute(qx, qw):
+    M, K = qx.shape
+    N = qw.shape[0]
+    out = [[0] * N for _ in range(M)]
+    for t in range(M):
+        for n in range(N):
+            s = 0
+            for k in range(K):
+                s += int(qx[t][k]) * int(qw[n][k])
+            out[t][n] = s
+    return out
+
+
+def test_gemm_brute_force_tiny():
+    rng = np.random.default_rng(19)
+    for (M, N, K) in [(1, 1, 1), (3, 5, 7), (8, 8, 8), (2, 7, 64)]:
+        qx = rng.integers(-127, 128, (M, K)).astype(np.int8)
+        qw = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        qx.flat[0] = -127
+        qw.flat[-1] = 127
+        assert oracle.gemm_i32(qx, qw).tolist() == _brute(qx, qw)
+        qw4 = rng.integers(-7, 8, (N, K)).astype(np.int8)
+        assert oracle.gemm_i32(qx, qw4).tolist() == _brute(qx, qw4)
+
+
+def test_gemm_matches_numpy_int64():
+    rng = np.random.default_rng(23)
+    qx = rng.integers(-127, 128, (67, 320)).astype(np.int8)
+    qw = rng.integers(-127, 128, (45, 320)).astype(np.int8)
+    ref = qx.astype(np.int64) @ qw.astype(np.int64).T
+    assert np.array_equal(oracle.gemm_i32(qx, qw).astype(np.int64), ref)
+
+
+def test_gemm_one_hot_closed_form():
+    # a token a*e_j quantizes to +-127*e_j, so acc[t,n] = +-127*qw[n,j]
+    K = 64
+    x = np.zeros((3, K), np.float16)
+    x[0, 5] = 3.0
+    x[1, 0] = -0.5
+    x[2, 63] = 1000.0
+    qx, sx = oracle.quant_tokens(x)
+    rng = np.random.default_rng(29)
+    qw = rng.integers(-127, 128, (10, K)).astype(np.int8)
+    acc = oracle.gemm_i32(qx, qw)
+    assert np.array_equal(acc[0], 127 * qw[:, 5].astype(np.int32))
+    assert np.array_equal(acc[1], -127 * qw[:, 0].astype(np.int32))
+    assert np.array_equal(acc[2], 127 * qw[:, 63].astype(np.int32))
+    assert sx.tolist() == [float(np.float32(3) / np.float32(127)),
+                           float(np.float32(0.5) / np.float32(127)),
+                           float(np.float32(1000) / np.float32(127))]
+
+
+def test_gemm_overflow_is_reported():
+    # 127*127*K > 2^31 - 1 once K >= 133_145
+    K = 133_200
+    qx = np.full((1, K), 127, np.int8)
+    qw = np.full((1, K), 127, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_i32(qx, qw)
+    acc = oracle.gemm_i32(qx[:, :133_000], qw[:, :133_000])
+    assert int(acc[0, 0]) == 127 * 127 * 133_000
+
+
+def test_no_workload_can_overflow_int32():
+    # |acc| <= K * 127 * qmax for every linear of every workload
+    for wl in W.WORKLOADS:
+        for L in wl.linears:
+            qmax = 127 if L.bits == 8 else 7
+            assert L.K * 127 * qmax < 2 ** 31 - 1
+
+
+# ------------------------------------------------------------------ epilogue --
+def test_epilogue_worked():
+    for c in _gold("epilogue_worked.json")["cases"]:
+        z, y = oracle.epilogue(np.array([[c["acc"]]], np.int32),
+                               np.array([c["sx"]], np.float32),
+                               np.array([c["sw"]], np.float32), 1,
+                               _f16([c["bias"]]), c["act"])
+        assert abs(z[0, 0] - c["z"]) <= 1e-15 * max(1.0, abs(c["z"])), c["why"]
+        assert y[0, 0] == np.float16(c["z"])
+
+
+def test_epilogue_gelu_odd_part_identity():
+    # GeLU(x) - GeLU(-x) = x * (Phi(x) + Phi(-x)) = x
+    v = np.linspace(-6, 6, 97)
+    acc = np.round(v * 1000).astype(np.int32).reshape(1, -1)
+    sx = np.array([1e-3], np.float32)
+    sw = np.array([1.0], np.float32)
+    zp, _ = oracle.epilogue(acc, sx, sw, acc.shape[1], None, 1)
+    zm, _ = oracle.epilogue(-acc, sx, sw, acc.shape[1], None, 1)
+    zl, _ = oracle.epilogue(acc, sx, sw, acc.shape[1], None, 0)
+    assert np.allclose(zp - zm, zl, rtol=0, atol=1e-12)
+    assert np.all(zp >= np.minimum(zl, 0) - 1e-12)  # GeLU(x) >= min(x,0)
+
+
+def test_epilogue_group_and_token_indexing():
+    # acc = 1 everywhere: z[t,n] = sx[t] * sw[n // G] (+ bias[n])
+    M, N, G = 3, 8, 4
+    acc = np.ones((M, N), np.int32)
+    sx = np.array([1.0, 2.0, 4.0], np.float32)
+    sw = np.array([0.5, 0.25], np.float32)
+    bias = _f16(np.arange(N) * 0.125)
+    z, _ = oracle.epilogue(acc, sx, sw, G, bias, 0)
+    for t in range(M):
+        for n in range(N):
+            assert z[t, n] == sx[t] * sw[n // G] + n * 0.125
+
+
+# ------------------------------------------------------------- end to end ----
+def test_linear_reconstructs_float_product():
+    # with token-wise A8 and group-wise W8 the dequantized output is close to
+    # the fp64 product LN(x) W^T + b (error bounded by the two rounding steps)
+    wl = W.workload("single")
+    w, b = W.gen_weights(wl, 0)
+    x = W.gen_activations(wl, 0)
+    qw, sw = oracle.quantize_weights(w.numpy(), wl.G, 8)
+    out = oracle.linear(x.numpy(), qw, sw, wl.G, b.numpy(), 0, ln=True)
+    h = out["h"].astype(np.float64)
+    ref = h @ w.numpy().astype(np.float64).T + b.numpy().astype(np.float64)
+    # per element: |sum_k h*w - sum_k (qx*sx)(qw*sw)| <= sum_k (|h| sw/2 + |w| sx/2 + sx sw/4)
+    sx = out["sx"].astype(np.float64)[:, None]
+    swn = np.repeat(sw.astype(np.float64), wl.G)[None, :]
+    bound = (np.abs(h).sum(1, keepdims=True) * swn / 2
+             + sx / 2 * np.abs(w.numpy().astype(np.float64)).sum(1)[None, :]
+             + sx * swn / 4 * h.shape[1])
+    assert np.all(np.abs(out["z"] - ref) <= bound + 1e-9)
+    # and the typical error is far inside the bound
+    assert np.median(np.abs(out["z"] - ref)) < 0.1 * np.median(bound)
+
+
+def test_w48_memory_is_one_third_of_fp16():
+    # INT4 FFN + INT8 attention weights vs fp16, for FFN = 4H: exactly 3x
+    for wl in (W.workload("bert-large"), W.workload("neox-20b")):
+        fp16 = sum(L.N * L.K * 2 for L in wl.linears)
+        q = sum(L.N * L.K * L.bits // 8 for L in wl.linears)
+        assert fp16 == 3 * q
