@@ -1,0 +1,175 @@
+/*
+ * zq.h -- C ABI of libzq, the fused quantized linear layer of ZeroQuant
+ * (arXiv 2206.01861) as hand-written HIP kernels for MI355X (gfx950).
+ *
+ * Source pages: "ZeroQuant: Efficient and Affordable Post-Training
+ * Quantization for Large-Scale Transformers", long-form summary
+ * (paper-graph-ui), Sec. 3.4 "Group-wise Weight Quantization" (paper
+ * Sec. 4.1, Eq. (2)), "Token-wise Activation Quantization" (paper Sec. 4.1)
+ * and "Quantization-Optimized Transformer Kernels" (paper Sec. 4.3, App. D,
+ * Fig. 2).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronizes; each call enqueues its
+ *    kernels on `stream` (a hipStream_t; NULL means the null stream) and
+ *    returns at once.  Results are ready when the stream reaches them.
+ *  - All matrices are row-major and dense.  Activations are [M][K] (one
+ *    row per token = batch*seqlen entry), weights [N][K] (one row per output
+ *    feature, K contiguous), outputs [M][N].
+ *  - fp16 means IEEE binary16.  Scales are fp32.
+ *  - Arguments are checked before anything is launched.  A failed check
+ *    returns a non-zero zq_status and launches nothing; the reason is kept
+ *    in a thread-local string returned by zq_last_error().  M == 0 is a
+ *    valid empty call (ZQ_OK, nothing launched).
+ *  - Base pointers of int8/uint8/fp16 tensors must be 16-byte aligned
+ *    (PyTorch allocations are); fp32 scale arrays 4-byte aligned.
+ *  - Calls on one stream run in order; calls on different streams that
+ *    write the same memory race, as with any kernel.
+ */
+#ifndef ZQ_H
+#define ZQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZQ_OK = 0,
+    ZQ_EINVAL = 1,       /* null or misaligned pointer, bad bits or act   */
+    ZQ_ESHAPE = 2,       /* negative/zero sizes, N % G != 0, odd K for W4 */
+    ZQ_EHIP = 3,         /* the HIP runtime refused a launch              */
+    ZQ_EUNSUPPORTED = 4  /* valid but outside the implemented range       */
+} zq_status;
+
+typedef enum { ZQ_ACT_NONE = 0, ZQ_ACT_GELU = 1 } zq_act;
+
+/* Largest K accepted by zq_ln_quant_act / zq_quant_act (a token row is held
+ * in registers).  Larger K returns ZQ_EUNSUPPORTED. */
+#define ZQ_MAX_ROW_K 65536
+/* Largest K accepted by the GEMMs: the int32 accumulator of an 8-bit
+ * product cannot overflow while K * 127 * 127 < 2^31 (W8) and, for the
+ * W4 path which accumulates 16 * acc, K * 127 * 7 * 16 < 2^31. */
+#define ZQ_MAX_GEMM_K_W8 133144
+#define ZQ_MAX_GEMM_K_W4 150976
+
+/*
+ * zq_quantize_weights -- group-wise symmetric weight quantization
+ * (Sec. 3.4 "Group-wise Weight Quantization", paper Sec. 4.1, Eq. (2)).
+ *
+ * W[N][K] fp16 is split into N/G groups of G contiguous rows (output
+ * features).  Group g has scale S_g = max|W[gG:(g+1)G, :]| / qmax with
+ * qmax = 127 (bits = 8) or 7 (bits = 4), and codes
+ *     q = rint(clamp(W / S_g, -qmax, qmax))   (fp32 IEEE division,
+ *                                              round half to even)
+ * An all-zero group gets S_g = 0 and zero codes.
+ *   bits = 8: qw is int8 [N][K].
+ *   bits = 4: qw is uint8 [N][K/2]; byte j of a row holds k = 2j in its low
+ *             nibble and k = 2j+1 in its high nibble, two's complement.
+ *   sw: fp32 [N/G].
+ * Errors: ZQ_EINVAL (null pointer, bits not 4/8), ZQ_ESHAPE (N, K or G <= 0,
+ * N % G != 0, odd K with bits = 4).  One workgroup per group; an offline
+ * step, not on the per-token path.
+ */
+zq_status zq_quantize_weights(const void *w_fp16, int N, int K, int G,
+                              int bits, void *qw, float *sw, void *stream);
+
+/*
+ * zq_ln_quant_act -- LayerNorm fused with dynamic token-wise INT8
+ * quantization (Sec. 3.4 "Quantization-Optimized Transformer Kernels",
+ * paper App. D, Fig. 2; token-wise scale from "Token-wise Activation
+ * Quantization", paper Sec. 4.1).
+ *
+ * Per token row t of x fp16 [M][K]:
+ *     mean, biased variance over K (fp32),
+ *     h = fp16((x - mean) / sqrt(var + eps) * gamma + beta),
+ *     sx[t] = max_k |h| / 127,
+ *     qx[t][k] = rint(clamp(h / sx[t], -127, 127))   (0 if sx[t] == 0).
+ * Only int8 codes and one fp32 scale per token leave the kernel; h stays in
+ * registers unless ln_out is given.
+ *   gamma, beta: fp16 [K], each may be NULL (1 and 0).
+ *   qx: int8 [M][K]; sx: fp32 [M]; ln_out: fp16 [M][K] or NULL.
+ * Errors: ZQ_EINVAL (null x/qx/sx), ZQ_ESHAPE (M < 0, K <= 0),
+ * ZQ_EUNSUPPORTED (K > ZQ_MAX_ROW_K).
+ */
+zq_status zq_ln_quant_act(const void *x_fp16, const void *gamma_fp16,
+                          const void *beta_fp16, float eps, int M, int K,
+                          int8_t *qx, float *sx, void *ln_out_fp16,
+                          void *stream);
+
+/*
+ * zq_quant_act -- token-wise INT8 quantization without LayerNorm, for the
+ * GEMM inputs that follow a bias-add or GeLU rather than a LayerNorm
+ * (Sec. 3.4 "Quantization-Optimized Transformer Kernels", paper App. D).
+ * Same quantizer as zq_ln_quant_act applied to x itself.
+ *   x: fp16 [M][K]; qx: int8 [M][K]; sx: fp32 [M].
+ * Errors as zq_ln_quant_act.
+ */
+zq_status zq_quant_act(const void *x_fp16, int M, int K, int8_t *qx,
+                       float *sx, void *stream);
+
+/*
+ * zq_gemm_w8a8 -- INT8 x INT8 GEMM with the dequantization fused into the
+ * epilogue (Sec. 3.4 "Quantization-Optimized Transformer Kernels", paper
+ * Sec. 4.3 and App. D):
+ *     acc[t][n] = sum_k qx[t][k] * qw[n][k]           (exact, int32)
+ *     y[t][n]   = fp16(act(acc * (sx[t] * sw[n / G]) + bias[n]))
+ * act: ZQ_ACT_NONE or ZQ_ACT_GELU (exact erf form).  The fp32 epilogue is
+ * computed in registers; only fp16 y is written.
+ *   qx int8 [M][K], sx fp32 [M], qw int8 [N][K], sw fp32 [N/G],
+ *   bias fp16 [N] or NULL, y fp16 [M][N].
+ * Errors: ZQ_EINVAL (null/misaligned pointer, act not 0/1), ZQ_ESHAPE
+ * (M < 0, N or K <= 0, G <= 0, N % G != 0), ZQ_EUNSUPPORTED (K % 64 != 0,
+ * K > ZQ_MAX_GEMM_K_W8).
+ */
+zq_status zq_gemm_w8a8(const int8_t *qx, const float *sx, const int8_t *qw,
+                       const float *sw, int G, const void *bias_fp16, int act,
+                       int M, int N, int K, void *y_fp16, void *stream);
+
+/*
+ * zq_gemm_w4a8 -- as zq_gemm_w8a8 with nibble-packed INT4 weights (the
+ * mixed W4/8 scheme puts INT4 on the feed-forward weights, Sec. 3.4
+ * "Group-wise Weight Quantization", paper Sec. 5).  qw4 is uint8 [N][K/2]
+ * in the zq_quantize_weights(bits = 4) layout; nibbles are expanded to int8
+ * in registers and fed to the same INT8 matrix instructions.
+ * Errors as zq_gemm_w8a8, with K limited to ZQ_MAX_GEMM_K_W4.
+ */
+zq_status zq_gemm_w4a8(const int8_t *qx, const float *sx, const uint8_t *qw4,
+                       const float *sw, int G, const void *bias_fp16, int act,
+                       int M, int N, int K, void *y_fp16, void *stream);
+
+/*
+ * zq_gemm_w8a8_i32 / zq_gemm_w4a8_i32 -- the same main loops with a raw
+ * epilogue: acc int32 [M][N] = sum_k qx[t][k] * qw[n][k].  These expose the
+ * integer accumulator (paper App. D: the INT32 result before
+ * dequantization) so that it can be compared exactly.
+ * Errors as the fused calls (no G/bias/act arguments).
+ */
+zq_status zq_gemm_w8a8_i32(const int8_t *qx, const int8_t *qw, int M, int N,
+                           int K, int32_t *acc, void *stream);
+zq_status zq_gemm_w4a8_i32(const int8_t *qx, const uint8_t *qw4, int M, int N,
+                           int K, int32_t *acc, void *stream);
+
+/*
+ * zq_gemm_plan -- which kernel and tile shape the GEMM calls pick for a
+ * problem (the schedule chosen by token count, paper App. D), written as a
+ * NUL-terminated string into buf (at most buflen bytes).  No launch.
+ * Errors: ZQ_EINVAL (null buf, buflen <= 0), as zq_gemm_w8a8 for shapes.
+ */
+zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *zq_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int zq_version(void);
+#define ZQ_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZQ_H */

@@ -1,0 +1,213 @@
+"""ctypes binding of libzq (include/zq.h): argument marshalling only.
+
+Each function checks dtypes/devices/shapes of the torch tensors it is given,
+allocates outputs with torch when the caller passes none (PyTorch is the
+device-memory and stream plumbing), and calls the C entry point of the same
+name on the current HIP stream.  Every computation happens in libzq's
+kernels; there is no fallback: if the library is missing or a call fails,
+an exception is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["ZQError", "library_path", "lib", "quantize_weights",
+           "ln_quant_act", "quant_act", "gemm_w8a8", "gemm_w4a8",
+           "gemm_w8a8_i32", "gemm_w4a8_i32", "gemm_plan", "ACT_NONE",
+           "ACT_GELU"]
+
+ACT_NONE = 0
+ACT_GELU = 1
+_STATUS = {0: "ZQ_OK", 1: "ZQ_EINVAL", 2: "ZQ_ESHAPE", 3: "ZQ_EHIP",
+           4: "ZQ_EUNSUPPORTED"}
+
+
+class ZQError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get(
+        "ZQ_LIBRARY",
+        os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzq.so"))
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built; run "
+                "`python -m int4_quantized_transformer_amd.build` first")
+        L = ctypes.CDLL(path)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        sigs = {
+            "zq_quantize_weights": [P, I, I, I, I, P, P, P],
+            "zq_ln_quant_act": [P, P, P, F, I, I, P, P, P, P],
+            "zq_quant_act": [P, I, I, P, P, P],
+            "zq_gemm_w8a8": [P, P, P, P, I, P, I, I, I, I, P, P],
+            "zq_gemm_w4a8": [P, P, P, P, I, P, I, I, I, I, P, P],
+            "zq_gemm_w8a8_i32": [P, P, I, I, I, P, P],
+            "zq_gemm_w4a8_i32": [P, P, I, I, I, P, P],
+            "zq_gemm_plan": [I, I, I, I, ctypes.c_char_p, I],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = I
+        L.zq_last_error.argtypes = []
+        L.zq_last_error.restype = ctypes.c_char_p
+        L.zq_version.argtypes = []
+        L.zq_version.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise ZQError(status, lib().zq_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, dev=None, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_weights(w, G, bits, qw=None, sw=None, stream=None):
+    """Group-wise W8 (int8 [N,K]) or nibble-packed W4 (uint8 [N,K/2]) codes
+    and fp32 scales [N/G] of fp16 weights W[N,K]."""
+    _need(w, "w", torch.float16, dim=2)
+    N, K = w.shape
+    if qw is None:
+        qw = (torch.empty(N, K, dtype=torch.int8, device=w.device) if bits == 8
+              else torch.empty(N, K // 2, dtype=torch.uint8, device=w.device))
+    if sw is None:
+        sw = torch.empty(max(N // G, 1) if G > 0 else 1, dtype=torch.float32,
+                         device=w.device)
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, w.device)
+    _need(sw, "sw", torch.float32, w.device)
+    _check(lib().zq_quantize_weights(_p(w), N, K, G, bits, _p(qw), _p(sw),
+                                     _stream(w, stream)))
+    return qw, sw
+
+
+def ln_quant_act(x, gamma=None, beta=None, eps=1e-5, qx=None, sx=None,
+                 ln_out=None, stream=None):
+    """LayerNorm + token-wise INT8 quantization: returns (qx, sx), or
+    (qx, sx, ln_out) when ``ln_out`` is True or a tensor."""
+    _need(x, "x", torch.float16, dim=2)
+    M, K = x.shape
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None:
+            _need(t, name, torch.float16, x.device)
+            if t.numel() != K:
+                raise ValueError(f"{name} must have K={K} elements")
+    qx = torch.empty(M, K, dtype=torch.int8, device=x.device) if qx is None else qx
+    sx = torch.empty(M, dtype=torch.float32, device=x.device) if sx is None else sx
+    _need(qx, "qx", torch.int8, x.device)
+    _need(sx, "sx", torch.float32, x.device)
+    want_ln = ln_out is not None and ln_out is not False
+    if ln_out is True:
+        ln_out = torch.empty_like(x)
+    if want_ln:
+        _need(ln_out, "ln_out", torch.float16, x.device)
+    _check(lib().zq_ln_quant_act(_p(x), _p(gamma), _p(beta),
+                                 ctypes.c_float(eps), M, K, _p(qx), _p(sx),
+                                 _p(ln_out) if want_ln else None,
+                                 _stream(x, stream)))
+    return (qx, sx, ln_out) if want_ln else (qx, sx)
+
+
+def quant_act(x, qx=None, sx=None, stream=None):
+    """Token-wise INT8 quantization of fp16 x[M,K] -> (qx, sx)."""
+    _need(x, "x", torch.float16, dim=2)
+    M, K = x.shape
+    qx = torch.empty(M, K, dtype=torch.int8, device=x.device) if qx is None else qx
+    sx = torch.empty(M, dtype=torch.float32, device=x.device) if sx is None else sx
+    _need(qx, "qx", torch.int8, x.device)
+    _need(sx, "sx", torch.float32, x.device)
+    _check(lib().zq_quant_act(_p(x), M, K, _p(qx), _p(sx), _stream(x, stream)))
+    return qx, sx
+
+
+def _gemm(fn, bits, qx, sx, qw, sw, G, bias, act, y, stream):
+    _need(qx, "qx", torch.int8, dim=2)
+    M, K = qx.shape
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, qx.device, 2)
+    N = qw.shape[0]
+    if qw.shape[1] != (K if bits == 8 else K // 2):
+        raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+    _need(sx, "sx", torch.float32, qx.device)
+    _need(sw, "sw", torch.float32, qx.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, qx.device)
+    y = torch.empty(M, N, dtype=torch.float16, device=qx.device) if y is None else y
+    _need(y, "y", torch.float16, qx.device)
+    _check(fn(_p(qx), _p(sx), _p(qw), _p(sw), G, _p(bias), int(act), M, N, K,
+              _p(y), _stream(qx, stream)))
+    return y
+
+
+def gemm_w8a8(qx, sx, qw, sw, G, bias=None, act=ACT_NONE, y=None, stream=None):
+    """y[M,N] fp16 = act(sx[t]*sw[n//G]*sum_k qx*qw + bias)."""
+    return _gemm(lib().zq_gemm_w8a8, 8, qx, sx, qw, sw, G, bias, act, y, stream)
+
+
+def gemm_w4a8(qx, sx, qw4, sw, G, bias=None, act=ACT_NONE, y=None, stream=None):
+    """As gemm_w8a8 with nibble-packed W4 weights uint8 [N, K/2]."""
+    return _gemm(lib().zq_gemm_w4a8, 4, qx, sx, qw4, sw, G, bias, act, y, stream)
+
+
+def _gemm_i32(fn, bits, qx, qw, acc, stream):
+    _need(qx, "qx", torch.int8, dim=2)
+    M, K = qx.shape
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, qx.device, 2)
+    N = qw.shape[0]
+    if qw.shape[1] != (K if bits == 8 else K // 2):
+        raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+    acc = torch.empty(M, N, dtype=torch.int32, device=qx.device) if acc is None else acc
+    _need(acc, "acc", torch.int32, qx.device)
+    _check(fn(_p(qx), _p(qw), M, N, K, _p(acc), _stream(qx, stream)))
+    return acc
+
+
+def gemm_w8a8_i32(qx, qw, acc=None, stream=None):
+    """Raw int32 accumulator acc[M,N] = sum_k qx[t,k]*qw[n,k]."""
+    return _gemm_i32(lib().zq_gemm_w8a8_i32, 8, qx, qw, acc, stream)
+
+
+def gemm_w4a8_i32(qx, qw4, acc=None, stream=None):
+    return _gemm_i32(lib().zq_gemm_w4a8_i32, 4, qx, qw4, acc, stream)
+
+
+def gemm_plan(M, N, K, bits) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().zq_gemm_plan(M, N, K, bits, buf, 256))
+    return buf.value.decode()

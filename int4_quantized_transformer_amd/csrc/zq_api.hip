@@ -1,0 +1,194 @@
+// zq_api.hip -- the extern "C" entry points declared in include/zq.h:
+// argument checks, error reporting and dispatch to the kernels.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "zq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+zq_status fail(zq_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+zq_status ok() {
+  g_err[0] = '\0';
+  return ZQ_OK;
+}
+
+zq_status hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess)
+    return fail(ZQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+zq_status check_gemm(const int8_t *qx, const void *qw, int M, int N, int K,
+                     int bits, const char *fn) {
+  if (!qx || !qw) return fail(ZQ_EINVAL, "%s: null qx/qw", fn);
+  if (!aligned(qx, 16) || !aligned(qw, 16))
+    return fail(ZQ_EINVAL, "%s: qx/qw must be 16-byte aligned", fn);
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d N=%d K=%d", fn, M, N, K);
+  if (K % 64 != 0)
+    return fail(ZQ_EUNSUPPORTED, "%s: K=%d is not a multiple of 64", fn, K);
+  const int kmax = bits == 4 ? ZQ_MAX_GEMM_K_W4 : ZQ_MAX_GEMM_K_W8;
+  if (K > kmax)
+    return fail(ZQ_EUNSUPPORTED,
+                "%s: K=%d exceeds %d (int32 accumulator bound)", fn, K, kmax);
+  return ZQ_OK;
+}
+
+zq_status gemm_fused(const int8_t *qx, const float *sx, const void *qw,
+                     const float *sw, int G, const void *bias, int act, int M,
+                     int N, int K, void *y, void *stream, int bits,
+                     const char *fn) {
+  zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (!sx || !sw || !y) return fail(ZQ_EINVAL, "%s: null sx/sw/y", fn);
+  if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 8) ||
+      (bias && !aligned(bias, 2)))
+    return fail(ZQ_EINVAL, "%s: misaligned sx/sw/y/bias", fn);
+  if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+    return fail(ZQ_EINVAL, "%s: act=%d", fn, act);
+  if (G <= 0 || N % G != 0)
+    return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  if (M == 0) return ok();
+  zq::GemmArgs a{};
+  a.qx = qx;
+  a.sx = sx;
+  a.qw = qw;
+  a.sw = sw;
+  a.bias = static_cast<const zq::half_t *>(bias);
+  a.out = y;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.act = act;
+  a.bits = bits;
+  a.raw_i32 = false;
+  return hip_status(zq::launch_gemm(a, (hipStream_t)stream), fn);
+}
+
+zq_status gemm_raw(const int8_t *qx, const void *qw, int M, int N, int K,
+                   int32_t *acc, void *stream, int bits, const char *fn) {
+  zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (!acc) return fail(ZQ_EINVAL, "%s: null acc", fn);
+  if (!aligned(acc, 16)) return fail(ZQ_EINVAL, "%s: acc must be 16-byte aligned", fn);
+  if (M == 0) return ok();
+  zq::GemmArgs a{};
+  a.qx = qx;
+  a.qw = qw;
+  a.out = acc;
+  a.G = 1;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.bits = bits;
+  a.raw_i32 = true;
+  return hip_status(zq::launch_gemm(a, (hipStream_t)stream), fn);
+}
+
+zq_status row_quant(const void *x, const void *gamma, const void *beta,
+                    float eps, int M, int K, bool ln, int8_t *qx, float *sx,
+                    void *ln_out, void *stream, const char *fn) {
+  if (!x || !qx || !sx) return fail(ZQ_EINVAL, "%s: null x/qx/sx", fn);
+  if (!aligned(x, 2) || !aligned(sx, 4) || (gamma && !aligned(gamma, 2)) ||
+      (beta && !aligned(beta, 2)) || (ln_out && !aligned(ln_out, 2)))
+    return fail(ZQ_EINVAL, "%s: misaligned pointer", fn);
+  if (M < 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d K=%d", fn, M, K);
+  if (K > ZQ_MAX_ROW_K)
+    return fail(ZQ_EUNSUPPORTED, "%s: K=%d exceeds %d", fn, K, ZQ_MAX_ROW_K);
+  if (ln && !(eps >= 0.0f))
+    return fail(ZQ_EINVAL, "%s: eps must be >= 0", fn);
+  if (M == 0) return ok();
+  return hip_status(zq::launch_row_quant(x, gamma, beta, eps, M, K, ln, qx,
+                                         sx, ln_out, (hipStream_t)stream),
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+zq_status zq_quantize_weights(const void *w_fp16, int N, int K, int G,
+                              int bits, void *qw, float *sw, void *stream) {
+  const char *fn = "zq_quantize_weights";
+  if (!w_fp16 || !qw || !sw) return fail(ZQ_EINVAL, "%s: null pointer", fn);
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  if (!aligned(w_fp16, 2) || !aligned(sw, 4))
+    return fail(ZQ_EINVAL, "%s: misaligned pointer", fn);
+  if (N <= 0 || K <= 0 || G <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape N=%d K=%d G=%d", fn, N, K, G);
+  if (N % G != 0)
+    return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  if (bits == 4 && K % 2 != 0)
+    return fail(ZQ_ESHAPE, "%s: W4 needs an even K (K=%d)", fn, K);
+  return hip_status(zq::launch_quantize_weights(w_fp16, N, K, G, bits, qw, sw,
+                                                (hipStream_t)stream),
+                    fn);
+}
+
+zq_status zq_ln_quant_act(const void *x_fp16, const void *gamma_fp16,
+                          const void *beta_fp16, float eps, int M, int K,
+                          int8_t *qx, float *sx, void *ln_out_fp16,
+                          void *stream) {
+  return row_quant(x_fp16, gamma_fp16, beta_fp16, eps, M, K, true, qx, sx,
+                   ln_out_fp16, stream, "zq_ln_quant_act");
+}
+
+zq_status zq_quant_act(const void *x_fp16, int M, int K, int8_t *qx,
+                       float *sx, void *stream) {
+  return row_quant(x_fp16, nullptr, nullptr, 0.0f, M, K, false, qx, sx,
+                   nullptr, stream, "zq_quant_act");
+}
+
+zq_status zq_gemm_w8a8(const int8_t *qx, const float *sx, const int8_t *qw,
+                       const float *sw, int G, const void *bias_fp16, int act,
+                       int M, int N, int K, void *y_fp16, void *stream) {
+  return gemm_fused(qx, sx, qw, sw, G, bias_fp16, act, M, N, K, y_fp16,
+                    stream, 8, "zq_gemm_w8a8");
+}
+
+zq_status zq_gemm_w4a8(const int8_t *qx, const float *sx, const uint8_t *qw4,
+                       const float *sw, int G, const void *bias_fp16, int act,
+                       int M, int N, int K, void *y_fp16, void *stream) {
+  return gemm_fused(qx, sx, qw4, sw, G, bias_fp16, act, M, N, K, y_fp16,
+                    stream, 4, "zq_gemm_w4a8");
+}
+
+zq_status zq_gemm_w8a8_i32(const int8_t *qx, const int8_t *qw, int M, int N,
+                           int K, int32_t *acc, void *stream) {
+  return gemm_raw(qx, qw, M, N, K, acc, stream, 8, "zq_gemm_w8a8_i32");
+}
+
+zq_status zq_gemm_w4a8_i32(const int8_t *qx, const uint8_t *qw4, int M, int N,
+                           int K, int32_t *acc, void *stream) {
+  return gemm_raw(qx, qw4, M, N, K, acc, stream, 4, "zq_gemm_w4a8_i32");
+}
+
+zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen) {
+  const char *fn = "zq_gemm_plan";
+  if (!buf || buflen <= 0) return fail(ZQ_EINVAL, "%s: null buffer", fn);
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d N=%d K=%d", fn, M, N, K);
+  zq::describe_gemm_plan(M, N, K, bits, buf, buflen);
+  return ok();
+}
+
+const char *zq_last_error(void) { return g_err; }
+
+int zq_version(void) { return ZQ_VERSION; }
+
+}  // extern "C"

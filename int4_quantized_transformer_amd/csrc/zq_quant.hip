@@ -1,0 +1,335 @@
+// zq_quant.hip -- quantization kernels of libzq for gfx950.
+//
+//  * row_quant_kernel: one token row per thread team; LayerNorm (optional)
+//    and the token-wise INT8 quantizer fused, the row held in registers
+//    (ZeroQuant summary page, Sec. 3.4 "Quantization-Optimized Transformer
+//    Kernels": one row per compute unit, scale computed from values already
+//    in registers, only INT8 written out; paper App. D, Fig. 2).
+//  * weight_quant_kernel: group-wise W8/W4 quantization (Sec. 3.4
+//    "Group-wise Weight Quantization", paper Sec. 4.1, Eq. (2)); one
+//    workgroup per group of G weight rows, an offline step.
+#include "zq_internal.h"
+
+namespace zq {
+
+// ===================================================================== rows
+// A team of TPR threads owns one row; each thread holds NCH chunks of 8
+// consecutive fp16 values (chunk c = lane + j*TPR covers k = 8c .. 8c+7),
+// so global reads are 16-byte per lane and fully coalesced across the team,
+// and the int8 writes are 8-byte per lane.  VEC = false is the same
+// algorithm with scalar, bounds-checked accesses for K % 8 != 0.
+template <int TPR>
+struct RowTeam {
+  static constexpr int kBlock = TPR < 256 ? 256 : TPR;
+  static constexpr int kRows = kBlock / TPR;
+  static constexpr int kWaves = TPR / kWave;
+};
+
+template <int TPR>
+__device__ __forceinline__ float team_sum(float v, float *lds) {
+  v = wave_sum(v);
+  if constexpr (TPR > kWave) {
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
+    __syncthreads();
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TPR / kWave; ++i) s += lds[i];
+    v = s;
+  }
+  return v;
+}
+
+template <int TPR>
+__device__ __forceinline__ float team_max(float v, float *lds) {
+  v = wave_max(v);
+  if constexpr (TPR > kWave) {
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
+    __syncthreads();
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TPR / kWave; ++i) m = fmaxf(m, lds[i]);
+    v = m;
+  }
+  return v;
+}
+
+template <int TPR, int NCH, bool LN, bool VEC>
+__global__ void __launch_bounds__(RowTeam<TPR>::kBlock)
+row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
+                 const half_t *__restrict__ beta, float eps, int M, int K,
+                 int8_t *__restrict__ qx, float *__restrict__ sx,
+                 half_t *__restrict__ ln_out) {
+  using T = RowTeam<TPR>;
+  __shared__ float red[TPR > kWave ? TPR / kWave : 1];
+  const int team = threadIdx.x / TPR;
+  const int tl = threadIdx.x % TPR;
+  const int row = blockIdx.x * T::kRows + team;
+  // Teams are whole waves (TPR >= 64); with TPR > 64 the block holds one
+  // team, so a row past the end retires the entire block together.
+  if (row >= M) return;
+
+  const half_t *xr = x + (size_t)row * K;
+  float v[NCH][8];
+
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tl + j * TPR;
+    if constexpr (VEC) {
+      if (c * 8 < K) {
+        half8 h = *reinterpret_cast<const half8 *>(xr + c * 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][i] = (float)h[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = c * 8 + i;
+        v[j][i] = (k < K) ? (float)xr[k] : 0.0f;
+      }
+    }
+  }
+
+  if constexpr (LN) {
+    // mean and biased variance (two passes over the registers, fp32)
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[j][i];  // out-of-range values are 0
+    const float mean = team_sum<TPR>(s, red) / (float)K;
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = (tl + j * TPR) * 8 + i;
+        const float d = v[j][i] - mean;
+        ss += (k < K) ? d * d : 0.0f;
+      }
+    const float var = team_sum<TPR>(ss, red) / (float)K;
+    const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = (tl + j * TPR) * 8 + i;
+        if (k < K) {
+          const float g = gamma ? (float)gamma[k] : 1.0f;
+          const float b = beta ? (float)beta[k] : 0.0f;
+          // round to the fp16 value that the unfused LayerNorm would emit
+          v[j][i] = (float)(half_t)((v[j][i] - mean) * rstd * g + b);
+        } else {
+          v[j][i] = 0.0f;
+        }
+      }
+    if (ln_out) {
+      half_t *lr = ln_out + (size_t)row * K;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tl + j * TPR;
+        if constexpr (VEC) {
+          if (c * 8 < K) {
+            half8 h;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = (half_t)v[j][i];
+            *reinterpret_cast<half8 *>(lr + c * 8) = h;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (c * 8 + i < K) lr[c * 8 + i] = (half_t)v[j][i];
+        }
+      }
+    }
+  }
+
+  // token-wise scale: max |h| / 127
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
+  const float amax = team_max<TPR>(m, red);
+  const float s = amax / 127.0f;
+  if (tl == 0) sx[row] = s;
+
+  int8_t *qr = qx + (size_t)row * K;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tl + j * TPR;
+    int q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quant_code(v[j][i], s, 127.0f);
+    if constexpr (VEC) {
+      if (c * 8 < K) {
+        v2i p;
+        p[0] = (int)pack4_i8(q[0], q[1], q[2], q[3]);
+        p[1] = (int)pack4_i8(q[4], q[5], q[6], q[7]);
+        *reinterpret_cast<v2i *>(qr + c * 8) = p;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (c * 8 + i < K) qr[c * 8 + i] = (int8_t)q[i];
+    }
+  }
+}
+
+template <int TPR, int NCH, bool LN, bool VEC>
+static hipError_t launch_rows(const half_t *x, const half_t *g,
+                              const half_t *b, float eps, int M, int K,
+                              int8_t *qx, float *sx, half_t *ln_out,
+                              hipStream_t s) {
+  using T = RowTeam<TPR>;
+  const int grid = (M + T::kRows - 1) / T::kRows;
+  hipLaunchKernelGGL((row_quant_kernel<TPR, NCH, LN, VEC>), dim3(grid),
+                     dim3(T::kBlock), 0, s, x, g, b, eps, M, K, qx, sx,
+                     ln_out);
+  return hipGetLastError();
+}
+
+template <int TPR, bool LN, bool VEC>
+static hipError_t dispatch_nch(int nch, const half_t *x, const half_t *g,
+                               const half_t *b, float eps, int M, int K,
+                               int8_t *qx, float *sx, half_t *ln_out,
+                               hipStream_t s) {
+  switch (nch) {
+    case 1: return launch_rows<TPR, 1, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
+    case 2: return launch_rows<TPR, 2, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
+    case 3: return launch_rows<TPR, 3, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
+    case 4: return launch_rows<TPR, 4, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
+    case 6: return launch_rows<TPR, 6, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
+    default: return launch_rows<TPR, 8, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
+  }
+}
+
+template <bool LN, bool VEC>
+static hipError_t dispatch_tpr(const half_t *x, const half_t *g,
+                               const half_t *b, float eps, int M, int K,
+                               int8_t *qx, float *sx, half_t *ln_out,
+                               hipStream_t s) {
+  const int chunks = (K + 7) / 8;
+  int tpr = chunks <= 8 * 64 ? 64 : (chunks <= 8 * 256 ? 256 : 1024);
+  const int per = (chunks + tpr - 1) / tpr;
+  const int nch = per <= 4 ? per : (per <= 6 ? 6 : 8);
+  if (tpr == 64) return dispatch_nch<64, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
+  if (tpr == 256) return dispatch_nch<256, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
+  return dispatch_nch<1024, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
+}
+
+hipError_t launch_row_quant(const void *x, const void *gamma, const void *beta,
+                            float eps, int M, int K, bool ln, int8_t *qx,
+                            float *sx, void *ln_out, hipStream_t s) {
+  const half_t *xh = static_cast<const half_t *>(x);
+  const half_t *g = static_cast<const half_t *>(gamma);
+  const half_t *b = static_cast<const half_t *>(beta);
+  half_t *lo = static_cast<half_t *>(ln_out);
+  const bool vec = (K % 8 == 0) && ((uintptr_t)x % 16 == 0) &&
+                   ((uintptr_t)qx % 8 == 0) &&
+                   (!lo || (uintptr_t)lo % 16 == 0);
+  if (ln)
+    return vec ? dispatch_tpr<true, true>(xh, g, b, eps, M, K, qx, sx, lo, s)
+               : dispatch_tpr<true, false>(xh, g, b, eps, M, K, qx, sx, lo, s);
+  return vec ? dispatch_tpr<false, true>(xh, g, b, eps, M, K, qx, sx, lo, s)
+             : dispatch_tpr<false, false>(xh, g, b, eps, M, K, qx, sx, lo, s);
+}
+
+// ================================================================= weights
+constexpr int kWQThreads = 1024;
+
+template <bool VEC>
+__global__ void __launch_bounds__(kWQThreads)
+weight_quant_kernel(const half_t *__restrict__ w, int K, int G, int bits,
+                    void *__restrict__ qw, float *__restrict__ sw) {
+  __shared__ float red[kWQThreads / kWave];
+  const int g = blockIdx.x;
+  const size_t n = (size_t)G * K;        // elements in the group
+  const half_t *src = w + (size_t)g * n;
+  const float qmax = bits == 8 ? 127.0f : 7.0f;
+
+  // pass 1: group amax
+  float m = 0.0f;
+  if constexpr (VEC) {
+    for (size_t i = (size_t)threadIdx.x * 8; i < n; i += (size_t)kWQThreads * 8) {
+      half8 h = *reinterpret_cast<const half8 *>(src + i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)h[e]));
+    }
+  } else {
+    for (size_t i = threadIdx.x; i < n; i += kWQThreads)
+      m = fmaxf(m, fabsf((float)src[i]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kWQThreads / kWave; ++i) amax = fmaxf(amax, red[i]);
+  const float s = amax / qmax;
+  if (threadIdx.x == 0) sw[g] = s;
+
+  // pass 2: codes
+  if (bits == 8) {
+    int8_t *dst = static_cast<int8_t *>(qw) + (size_t)g * n;
+    if constexpr (VEC) {
+      for (size_t i = (size_t)threadIdx.x * 8; i < n; i += (size_t)kWQThreads * 8) {
+        half8 h = *reinterpret_cast<const half8 *>(src + i);
+        int q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = quant_code((float)h[e], s, qmax);
+        v2i p;
+        p[0] = (int)pack4_i8(q[0], q[1], q[2], q[3]);
+        p[1] = (int)pack4_i8(q[4], q[5], q[6], q[7]);
+        *reinterpret_cast<v2i *>(dst + i) = p;
+      }
+    } else {
+      for (size_t i = threadIdx.x; i < n; i += kWQThreads)
+        dst[i] = (int8_t)quant_code((float)src[i], s, qmax);
+    }
+  } else {
+    // K is even, so element pairs (2j, 2j+1) of the flattened group are
+    // the (even k, odd k) pairs of one row: low nibble = even k.
+    uint8_t *dst = static_cast<uint8_t *>(qw) + (size_t)g * (n / 2);
+    if constexpr (VEC) {
+      for (size_t i = (size_t)threadIdx.x * 8; i < n; i += (size_t)kWQThreads * 8) {
+        half8 h = *reinterpret_cast<const half8 *>(src + i);
+        uint32_t p = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          p |= (uint32_t)(quant_code((float)h[e], s, qmax) & 0xF) << (4 * e);
+        *reinterpret_cast<uint32_t *>(dst + i / 2) = p;
+      }
+    } else {
+      for (size_t j = threadIdx.x; j < n / 2; j += kWQThreads) {
+        const int lo = quant_code((float)src[2 * j], s, qmax) & 0xF;
+        const int hi = quant_code((float)src[2 * j + 1], s, qmax) & 0xF;
+        dst[j] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_weights(const void *w, int N, int K, int G,
+                                   int bits, void *qw, float *sw,
+                                   hipStream_t s) {
+  const size_t n = (size_t)G * K;
+  const bool vec = (n % 8 == 0) && ((uintptr_t)w % 16 == 0) &&
+                   ((uintptr_t)qw % 8 == 0);
+  const half_t *wh = static_cast<const half_t *>(w);
+  if (vec)
+    hipLaunchKernelGGL(weight_quant_kernel<true>, dim3(N / G), dim3(kWQThreads),
+                       0, s, wh, K, G, bits, qw, sw);
+  else
+    hipLaunchKernelGGL(weight_quant_kernel<false>, dim3(N / G),
+                       dim3(kWQThreads), 0, s, wh, K, G, bits, qw, sw);
+  return hipGetLastError();
+}
+
+}  // namespace zq

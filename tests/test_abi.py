@@ -1,0 +1,103 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/zq.h declares, and its host-side argument checks return the
+documented statuses before anything is launched (no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from int4_quantized_transformer_amd import _lib as Z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zq.h")
+
+OK, EINVAL, ESHAPE, EHIP, EUNSUP = 0, 1, 2, 3, 4
+# Fake, 256-byte aligned "device" addresses: every call below fails its
+# argument check before any pointer is used.
+A, B, C, D, E = (ctypes.c_void_p(0x10000 * i) for i in range(1, 6))
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"\b(zq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = Z.lib()
+    names = declared_functions()
+    assert "zq_gemm_w8a8" in names and "zq_ln_quant_act" in names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in zq.h but not exported"
+    assert L.zq_version() == 100
+
+
+def test_last_error_starts_empty_and_is_set_on_failure():
+    L = Z.lib()
+    assert L.zq_quant_act(None, 4, 64, B, C, None) == EINVAL
+    assert b"null" in L.zq_last_error()
+    assert L.zq_quant_act(A, 0, 64, B, C, None) == OK   # M = 0: empty call
+    assert L.zq_last_error() == b""
+
+
+def test_quant_argument_checks():
+    L = Z.lib()
+    assert L.zq_quant_act(A, -1, 64, B, C, None) == ESHAPE
+    assert L.zq_quant_act(A, 4, 0, B, C, None) == ESHAPE
+    assert L.zq_quant_act(A, 4, 65537, B, C, None) == EUNSUP
+    assert L.zq_ln_quant_act(A, None, None, ctypes.c_float(-1.0), 4, 64, B, C,
+                             None, None) == EINVAL
+    assert L.zq_ln_quant_act(A, None, None, ctypes.c_float(1e-5), 4, 64, None,
+                             C, None, None) == EINVAL
+    assert L.zq_ln_quant_act(A, None, None, ctypes.c_float(1e-5), 0, 64, B, C,
+                             None, None) == OK
+
+
+def test_quantize_weights_argument_checks():
+    L = Z.lib()
+    assert L.zq_quantize_weights(A, 96, 64, 64, 8, B, C, None) == ESHAPE  # N % G
+    assert L.zq_quantize_weights(A, 128, 63, 64, 4, B, C, None) == ESHAPE  # odd K, W4
+    assert L.zq_quantize_weights(A, 128, 64, 64, 5, B, C, None) == EINVAL  # bits
+    assert L.zq_quantize_weights(A, 128, 64, 0, 8, B, C, None) == ESHAPE
+    assert L.zq_quantize_weights(None, 128, 64, 64, 8, B, C, None) == EINVAL
+
+
+@pytest.mark.parametrize("fn", ["zq_gemm_w8a8", "zq_gemm_w4a8"])
+def test_gemm_argument_checks(fn):
+    f = getattr(Z.lib(), fn)
+    # (qx, sx, qw, sw, G, bias, act, M, N, K, y, stream)
+    assert f(A, B, C, D, 64, None, 0, 16, 256, 100, E, None) == EUNSUP  # K % 64
+    assert f(A, B, C, D, 64, None, 0, 16, 96, 256, E, None) == ESHAPE   # N % G
+    assert f(A, B, C, D, 0, None, 0, 16, 256, 256, E, None) == ESHAPE   # G
+    assert f(A, B, C, D, 64, None, 2, 16, 256, 256, E, None) == EINVAL  # act
+    assert f(A, B, C, D, 64, None, 0, -1, 256, 256, E, None) == ESHAPE
+    assert f(A, B, C, D, 64, None, 0, 16, 0, 256, E, None) == ESHAPE
+    assert f(None, B, C, D, 64, None, 0, 16, 256, 256, E, None) == EINVAL
+    assert f(A, None, C, D, 64, None, 0, 16, 256, 256, E, None) == EINVAL
+    assert f(ctypes.c_void_p(0x10008), B, C, D, 64, None, 0, 16, 256, 256, E,
+             None) == EINVAL                                            # align
+    big = 133_184 if fn == "zq_gemm_w8a8" else 151_040
+    assert f(A, B, C, D, 64, None, 0, 16, 256, big, E, None) == EUNSUP   # int32 bound
+    assert f(A, B, C, D, 64, None, 0, 0, 256, 256, E, None) == OK       # empty
+
+
+def test_gemm_i32_argument_checks():
+    L = Z.lib()
+    assert L.zq_gemm_w8a8_i32(A, B, 4, 64, 96, C, None) == EUNSUP
+    assert L.zq_gemm_w4a8_i32(A, B, 4, 64, 128, None, None) == EINVAL
+    assert L.zq_gemm_w8a8_i32(A, B, 0, 64, 128, C, None) == OK
+
+
+def test_header_limits_match_int32_bound():
+    # K * 127 * 127 < 2^31 for W8 and K * 127 * 7 * 16 < 2^31 for the W4 path
+    assert 133_144 * 127 * 127 < 2 ** 31 <= 133_145 * 127 * 127
+    assert 150_976 * 127 * 7 * 16 < 2 ** 31 <= 150_977 * 127 * 7 * 16
+
+
+def test_gemm_plan_covers_both_regimes():
+    assert Z.gemm_plan(1, 4096, 4096, 8).startswith("skinny")
+    assert Z.gemm_plan(64, 4096, 4096, 4).startswith("skinny")
+    assert Z.gemm_plan(2048, 4096, 4096, 8).startswith("tiled")
+    with pytest.raises(Z.ZQError):
+        Z.gemm_plan(16, 256, 256, 3)

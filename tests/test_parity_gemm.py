@@ -1,0 +1,112 @@
+"""GPU parity of the INT8 GEMMs against the CPU oracle.
+
+* zq_gemm_{w8a8,w4a8}_i32 on the oracle's codes: int32 accumulators
+  bit-exact, over shapes that cover both kernels (skinny for M <= 64, tiled
+  above), ragged M/N tails, several k-tiles, K % 128 == 64, and extreme codes.
+* zq_gemm_{w8a8,w4a8}: fp16 outputs within 1 fp16 ulp + 1e-3 of the
+  oracle's fp64 epilogue, with and without bias and GeLU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import int4_quantized_transformer_amd as zq
+from int4_quantized_transformer_amd import workloads as W
+
+from _util import assert_fp16_close_to_oracle, dev, needs_gpu, to_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+SHAPES = [  # (M, N, K)
+    (1, 16, 64), (1, 200, 192), (16, 256, 256), (17, 320, 192),
+    (33, 48, 640), (63, 64, 64), (64, 4096, 128), (64, 100, 1024),
+    (65, 320, 576), (128, 128, 128), (200, 384, 1024), (257, 200, 64),
+    (300, 1000, 640), (512, 768, 3072), (1, 4096, 4096), (7, 64, 24576),
+]
+
+
+def _codes(shape, lo, hi, seed):
+    g = np.random.default_rng(seed)
+    return g.integers(lo, hi + 1, size=shape).astype(np.int8)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_i32_w8a8_bit_exact(M, N, K):
+    qx = _codes((M, K), -127, 127, M * 7 + K)
+    qw = _codes((N, K), -127, 127, N * 11 + K)
+    acc = zq.gemm_w8a8_i32(torch.from_numpy(qx).to(dev()),
+                           torch.from_numpy(qw).to(dev()))
+    ref = oracle.gemm_i32(qx, qw)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(acc), ref), zq.gemm_plan(M, N, K, 8)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_i32_w4a8_bit_exact(M, N, K):
+    qx = _codes((M, K), -127, 127, M * 5 + K)
+    q4 = _codes((N, K), -8, 7, N * 13 + K)     # full nibble range incl. -8
+    packed = oracle.pack_w4(q4)
+    acc = zq.gemm_w4a8_i32(torch.from_numpy(qx).to(dev()),
+                           torch.from_numpy(packed).to(dev()))
+    ref = oracle.gemm_i32(qx, q4)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(acc), ref), zq.gemm_plan(M, N, K, 4)
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 130])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_i32_extreme_codes(M, bits):
+    # every product at its maximum magnitude: |acc| = K*127*qmax
+    K, N = 24576, 64
+    qmax = 127 if bits == 8 else 7
+    qx = np.full((M, K), 127, np.int8)
+    qx[::2] = -127
+    q = np.full((N, K), qmax, np.int8)
+    q[1::2] = -qmax if bits == 8 else -8
+    qw = q if bits == 8 else oracle.pack_w4(q)
+    fn = zq.gemm_w8a8_i32 if bits == 8 else zq.gemm_w4a8_i32
+    acc = fn(torch.from_numpy(qx).to(dev()), torch.from_numpy(qw).to(dev()))
+    ref = oracle.gemm_i32(qx, q)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(acc), ref)
+
+
+@pytest.mark.parametrize("M,N,K,G", [
+    (16, 256, 256, 64), (1, 4096, 1024, 128), (5, 384, 768, 128),
+    (64, 512, 512, 64), (100, 320, 192, 64), (300, 768, 768, 64),
+    (257, 1000, 320, 8), (2048, 256, 512, 128), (3, 20, 64, 4)])
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bias,act", [(True, 0), (True, 1), (False, 1),
+                                      (False, 0)])
+def test_fused_epilogue_vs_oracle(M, N, K, G, bits, bias, act):
+    seed = M + 3 * N + 7 * K + G + bits
+    x = W.randn_fp16((M, K), seed=seed, std=1.0)
+    w = W.randn_fp16((N, K), seed=seed + 1, std=0.02)
+    b = W.randn_fp16((N,), seed=seed + 2, std=0.5) if bias else None
+    qx, sx = oracle.quant_tokens(x.numpy())
+    q, sw = oracle.quantize_weights(w.numpy(), G, bits)
+    qw = q if bits == 8 else oracle.pack_w4(q)
+    d = dev()
+    fn = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    y = fn(torch.from_numpy(qx).to(d), torch.from_numpy(sx).to(d),
+           torch.from_numpy(qw).to(d), torch.from_numpy(sw).to(d), G,
+           None if b is None else b.to(d), act)
+    acc = oracle.gemm_i32(qx, q)
+    z, _ = oracle.epilogue(acc, sx, sw, G, None if b is None else b.numpy(),
+                           act)
+    torch.cuda.synchronize()
+    assert_fp16_close_to_oracle(to_np(y), z, zq.gemm_plan(M, N, K, bits))
+
+
+def test_empty_m_is_a_no_op():
+    d = dev()
+    qx = torch.empty(0, 128, dtype=torch.int8, device=d)
+    qw = torch.zeros(64, 128, dtype=torch.int8, device=d)
+    acc = zq.gemm_w8a8_i32(qx, qw)
+    assert acc.shape == (0, 64)
+
+
+def test_plans_used_by_tests_cover_both_kernels():
+    plans = {zq.gemm_plan(M, N, K, 8).split()[0] for M, N, K in SHAPES}
+    assert plans == {"skinny", "tiled"}

@@ -1,0 +1,112 @@
+"""GPU parity of the quantization kernels against the CPU oracle.
+
+* zq_quantize_weights: codes, packed W4 bytes and scales bit-exact.
+* zq_quant_act on the oracle's own fp16 values ("identical quantizer
+  inputs"): codes and scales bit-exact.
+* zq_ln_quant_act (LayerNorm in fp32 on the GPU, fp64 in the oracle): LN
+  output within 2e-3 relative, codes within +-1 in <= 0.1% of elements,
+  scales within 2e-3 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import int4_quantized_transformer_amd as zq
+from int4_quantized_transformer_amd import workloads as W
+
+from _util import (assert_codes_within_one, assert_ln_close, dev, needs_gpu,
+                   to_np)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _x(M, K, seed, outliers=True):
+    x = W.randn_fp16((M, K), seed=seed).float()
+    if outliers and K >= 4:
+        g = torch.Generator().manual_seed(seed + 1)
+        ch = torch.randperm(K, generator=g)[: max(1, K // 100)]
+        x[:, ch] *= 20.0
+    return x.half()
+
+
+QUANT_SHAPES = [(1, 8), (16, 256), (17, 768), (63, 1024), (65, 3072),
+                (4, 1000), (3, 13), (33, 4096), (5, 6144), (7, 16384),
+                (3, 24576), (2, 65536), (1, 1)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+def test_quant_act_bit_exact(M, K):
+    x = _x(M, K, seed=M * 1000 + K)
+    x[0, :] = 0.0                      # an all-zero token
+    if M > 2 and K >= 8:
+        x[2, :8] = torch.tensor([127, 2.5, 3.5, -2.5, -127, .5, 1.5, -.5])
+        x[2, 8:] = 0.0                 # a row whose scale is exactly 1
+    qx, sx = zq.quant_act(x.to(dev()))
+    q_ref, s_ref = oracle.quant_tokens(x.numpy())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(sx), s_ref)
+    assert np.array_equal(to_np(qx), q_ref)
+
+
+@pytest.mark.parametrize("M,K", [(16, 256), (17, 768), (64, 1024), (3, 1000),
+                                 (9, 4096), (5, 6144), (2, 16384), (1, 24),
+                                 (130, 768)])
+@pytest.mark.parametrize("affine", [False, True])
+def test_ln_quant_act_vs_oracle(M, K, affine):
+    x = _x(M, K, seed=7 * M + K) * 3 + 0.5
+    x = x.half()
+    gamma = beta = None
+    if affine:
+        gamma = W.randn_fp16((K,), seed=K + 1, std=0.3, mean=1.0)
+        beta = W.randn_fp16((K,), seed=K + 2, std=0.2)
+    d = dev()
+    qx, sx, h = zq.ln_quant_act(x.to(d), None if gamma is None else gamma.to(d),
+                                None if beta is None else beta.to(d), 1e-5,
+                                ln_out=True)
+    h_ref = oracle.layernorm(x.numpy(), None if gamma is None else gamma.numpy(),
+                             None if beta is None else beta.numpy(), 1e-5)
+    q_ref, s_ref = oracle.quant_tokens(h_ref)
+    torch.cuda.synchronize()
+    assert_ln_close(to_np(h), h_ref, "ln_out")
+    assert np.allclose(to_np(sx), s_ref, rtol=2e-3, atol=0)
+    assert_codes_within_one(to_np(qx), q_ref, 1e-3, "qx")
+    # given its own LN output, the fused kernel's quantizer is bit-exact
+    q_own, s_own = oracle.quant_tokens(to_np(h))
+    assert np.array_equal(to_np(qx), q_own)
+    assert np.array_equal(to_np(sx), s_own)
+
+
+def test_ln_quant_act_without_ln_out_matches_with():
+    x = _x(40, 768, seed=3)
+    qa, sa = zq.ln_quant_act(x.to(dev()))
+    qb, sb, _ = zq.ln_quant_act(x.to(dev()), ln_out=True)
+    torch.cuda.synchronize()
+    assert torch.equal(qa, qb) and torch.equal(sa, sb)
+
+
+def test_ln_constant_rows():
+    x = torch.full((4, 512), 3.0, dtype=torch.float16)
+    qx, sx = zq.ln_quant_act(x.to(dev()))
+    torch.cuda.synchronize()
+    assert torch.all(sx == 0) and torch.all(qx == 0)
+
+
+@pytest.mark.parametrize("N,K,G,bits", [
+    (256, 256, 64, 8), (256, 256, 64, 4), (768, 768, 64, 8),
+    (4096, 1024, 64, 4), (4096, 4096, 128, 8), (384, 6144, 128, 4),
+    (96, 100, 32, 8), (96, 100, 32, 4), (15, 7, 5, 8), (8, 30, 8, 4),
+    (64, 64, 1, 8), (64, 64, 1, 4), (1, 64, 1, 8), (128, 512, 128, 4)])
+def test_quantize_weights_bit_exact(N, K, G, bits):
+    w = W.randn_fp16((N, K), seed=N + K + G + bits, std=0.02)
+    w[: min(G, N)] *= 30.0            # one group with a much larger range
+    if N >= 2 * G:
+        w[G:2 * G] = 0.0              # an all-zero group
+    qw, sw = zq.quantize_weights(w.to(dev()), G, bits)
+    q_ref, s_ref = oracle.quantize_weights(w.numpy(), G, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(sw), s_ref)
+    if bits == 8:
+        assert np.array_equal(to_np(qw), q_ref)
+    else:
+        assert np.array_equal(to_np(qw), oracle.pack_w4(q_ref))
