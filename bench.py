@@ -1,0 +1,450 @@
+"""Benchmark of the fused quantized linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch: for every linear of
+the workload, LayerNorm + token-wise INT8 quantization (QKV and FFN1 inputs)
+or plain token-wise quantization (attn-out and FFN2 inputs), then the INT8
+GEMM with the fused dequant/bias(/GeLU) epilogue.  Default workload: the
+BERT-base encoder linears at 4096 tokens (batch 32 x seq 128), hidden 768,
+W8A8 with 64-row weight groups.
+
+Memory: R rotating sets of weights, inputs, intermediates and outputs (each
+set one "layer") make the working set larger than twice the 256 MB Infinity
+Cache, so every step reads its inputs from HBM.  Steps are replayed from HIP
+graphs, one per set (the pages replay CUDA graphs for small models).
+
+Prints one JSON line (stdout).  Details go to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+METRIC = ("fused W8A8/W4A8 GEMM TOPS (% INT8 peak); decode GB/s (% HBM peak)")
+ROTATE_BYTES = 600 * 2 ** 20   # > 2 x 256 MB Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="bert-base")
+    ap.add_argument("--m-index", type=int, default=None,
+                    help="which token count of the workload (default: largest)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode (GPT-J-6B, M=1) secondary figure")
+    ap.add_argument("--no-fp16", action="store_true",
+                    help="skip the fp16 torch.matmul comparator")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
+                                                      "traffic.json"))
+    ap.add_argument("--only", default=None,
+                    help="(profiling) run only the step loop, no extras")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ setup --
+class LinearSet:
+    """Device buffers of one linear for one rotating set."""
+
+
+def gemm_bytes(M, N, K, bits, G):
+    return M * K + N * K * bits // 8 + 4 * (N // G) + 4 * M + 2 * N + 2 * M * N
+
+
+def quant_bytes(M, K):
+    return 2 * M * K + M * K + 4 * M
+
+
+def build_sets(wl, M, dev, rotate_bytes):
+    import torch
+    import int4_quantized_transformer_amd as zq
+    from int4_quantized_transformer_amd import workloads as W
+
+    base = []
+    for li, L in enumerate(wl.linears):
+        w, b = W.gen_weights(wl, li)
+        x = W.gen_activations(wl, li, M=M, m_index=list(wl.M).index(M))
+        wd = w.to(dev)
+        qw, sw = zq.quantize_weights(wd, wl.G, L.bits)
+        del wd
+        base.append(dict(L=L, x=x.to(dev), qw=qw, sw=sw, b=b.to(dev),
+                         w_cpu=w, b_cpu=b, x_cpu=x))
+    per_set = 0
+    for d in base:
+        L = d["L"]
+        per_set += (d["qw"].numel() + d["x"].numel() * 2 + M * L.K
+                    + 2 * M * L.N + 4 * M)
+    R = max(1, -(-rotate_bytes // per_set))
+    sets = []
+    for r in range(R):
+        lins = []
+        for d in base:
+            L = d["L"]
+            s = LinearSet()
+            s.L = L
+            s.x = d["x"] if r == 0 else d["x"].clone()
+            s.qw = d["qw"] if r == 0 else d["qw"].clone()
+            s.sw = d["sw"] if r == 0 else d["sw"].clone()
+            s.b = d["b"] if r == 0 else d["b"].clone()
+            s.qx = torch.empty(M, L.K, dtype=torch.int8, device=dev)
+            s.sx = torch.empty(M, dtype=torch.float32, device=dev)
+            s.y = torch.empty(M, L.N, dtype=torch.float16, device=dev)
+            lins.append(s)
+        sets.append(lins)
+    torch.cuda.synchronize()
+    return base, sets, R, per_set
+
+
+def make_step(zq, lins, wl, M, stream_ptr):
+    """Pre-marshalled launches of one step: a list of (name, fn, args)."""
+    import ctypes
+    L_ = zq.lib()
+    P = ctypes.c_void_p
+    st = P(stream_ptr)
+    calls = []
+    for s in lins:
+        L = s.L
+        if L.ln:
+            calls.append((f"{L.name}.ln_quant", L_.zq_ln_quant_act,
+                          (P(s.x.data_ptr()), None, None,
+                           ctypes.c_float(wl.ln_eps), M, L.K,
+                           P(s.qx.data_ptr()), P(s.sx.data_ptr()), None, st)))
+        else:
+            calls.append((f"{L.name}.quant", L_.zq_quant_act,
+                          (P(s.x.data_ptr()), M, L.K, P(s.qx.data_ptr()),
+                           P(s.sx.data_ptr()), st)))
+        fn = L_.zq_gemm_w8a8 if L.bits == 8 else L_.zq_gemm_w4a8
+        calls.append((f"{L.name}.gemm_w{L.bits}a8", fn,
+                      (P(s.qx.data_ptr()), P(s.sx.data_ptr()),
+                       P(s.qw.data_ptr()), P(s.sw.data_ptr()), wl.G,
+                       P(s.b.data_ptr()), int(L.gelu), M, L.N, L.K,
+                       P(s.y.data_ptr()), st)))
+    return calls
+
+
+def run_calls(calls):
+    for name, fn, args in calls:
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"{name} failed with status {rc}")
+
+
+def kernel_work(name, L, M, G):
+    """(ops, bytes, bound) of one launch."""
+    if ".gemm" in name:
+        return (2 * M * L.N * L.K, gemm_bytes(M, L.N, L.K, L.bits, G), "mfma")
+    return (0, quant_bytes(M, L.K), "hbm")
+
+
+# ------------------------------------------------------------- CPU oracle --
+def cpu_baseline(base, wl, M, target_s=12.0):
+    """The CPU oracle, untuned, on a bounded sample of the same step."""
+    import oracle
+    ops_per_token = sum(2 * d["L"].N * d["L"].K for d in base)
+    prepared = []
+    for d in base:
+        q, sw = oracle.quantize_weights(d["w_cpu"].numpy(), wl.G, d["L"].bits)
+        prepared.append((d, q, sw))
+
+    def run(S):
+        t0 = time.perf_counter()
+        for d, q, sw in prepared:
+            L = d["L"]
+            oracle.linear(d["x_cpu"].numpy()[:S], q, sw, wl.G,
+                          d["b_cpu"].numpy(), int(L.gelu), ln=L.ln,
+                          eps=wl.ln_eps)
+        return time.perf_counter() - t0
+
+    S = min(M, 64)
+    t = run(S)
+    S = int(min(M, max(S, S * target_s / max(t, 1e-3))))
+    t = run(S)
+    tops = ops_per_token * S / t / 1e12
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": (f"first {S} of {M} tokens through all {len(base)} "
+                       f"linears (LN/quant, int64 GEMM, fp64 epilogue); "
+                       f"{t:.1f} s")}
+
+
+# ----------------------------------------------------------------- timing --
+def timed_graphs(torch, graphs, steps, stream):
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def timed_eager(torch, step_calls, steps, stream):
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        run_calls(step_calls[i % len(step_calls)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def kernel_breakdown(torch, step_calls, steps, stream):
+    """Per-launch durations from events around every launch (eager)."""
+    names = [c[0] for c in step_calls[0]]
+    acc = {n: 0.0 for n in names}
+    n_it = max(1, steps)
+    evs = []
+    for i in range(n_it):
+        calls = step_calls[i % len(step_calls)]
+        es = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+        es[0].record(stream)
+        for j, (name, fn, args) in enumerate(calls):
+            fn(*args)
+            es[j + 1].record(stream)
+        evs.append(es)
+    torch.cuda.synchronize()
+    for es in evs:
+        for j, n in enumerate(names):
+            acc[n] += es[j].elapsed_time(es[j + 1])
+    return {n: acc[n] / n_it for n in names}
+
+
+def traffic_for(path, kernel_name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    if absent or taken on a different kernel source."""
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    src = os.path.join(ROOT, "int4_quantized_transformer_amd", "csrc",
+                       t.get("source", ""))
+    try:
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    e = t.get("kernels", {}).get(kernel_name)
+    if not e or sha != t.get("source_sha256"):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ decode --
+def decode_figure(torch, zq, dev, steps=100):
+    """GPT-J-6B decoder linears at M = 1 (W8A8): GEMM GB/s against HBM."""
+    from int4_quantized_transformer_amd import workloads as W
+    wl = W.workload("gptj-6b")
+    M = 1
+    lin = []
+    for li, L in enumerate(wl.linears):
+        w, b = W.gen_weights(wl, li)
+        x = W.gen_activations(wl, li, m_index=0)
+        qw, sw = zq.quantize_weights(w.to(dev), wl.G, L.bits)
+        qx, sx = zq.quant_act(x.to(dev))
+        lin.append((L, qx, sx, qw, sw, b.to(dev)))
+        del w
+    wbytes = sum(l[3].numel() for l in lin)
+    R = max(1, -(-ROTATE_BYTES // wbytes))
+    sets = [lin] + [[(L, qx, sx, qw.clone(), sw, b) for (L, qx, sx, qw, sw, b)
+                     in lin] for _ in range(R - 1)]
+    ys = [torch.empty(M, l[0].N, dtype=torch.float16, device=dev) for l in lin]
+
+    def step(s):
+        for (L, qx, sx, qw, sw, b), y in zip(s, ys):
+            zq.gemm_w8a8(qx, sx, qw, sw, wl.G, b, int(L.gelu), y=y)
+
+    stream = torch.cuda.current_stream()
+    for i in range(2 * R):
+        step(sets[i % R])
+    g = []
+    for s in sets:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step(s)
+        g.append(gr)
+    ms, _ = timed_graphs(torch, g, steps, stream)
+    nbytes = sum(gemm_bytes(M, L.N, L.K, L.bits, wl.G)
+                 for (L, *_r) in lin)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "gptj-6b decoder linears W8A8, M=1 (QKV, out, FFN1"
+                        "+GeLU, FFN2), 128-row groups, HIP-graph replay",
+            "GB_per_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs /
+                                                             HBM_PEAK_GBS, 1),
+            "us_per_step": round(ms * 1e3, 2), "bytes_per_step": nbytes,
+            "rotating_sets": R}
+
+
+# -------------------------------------------------------------------- main --
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the fused linear shards over tokens with "
+              "no communication, see the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_quantized_transformer_amd as zq
+    from int4_quantized_transformer_amd import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = W.workload(args.workload)
+    M = wl.M[-1] if args.m_index is None else wl.M[args.m_index]
+    zq.lib()
+
+    base, sets, R, per_set = build_sets(wl, M, dev, ROTATE_BYTES)
+    stream = torch.cuda.current_stream()
+    step_calls = [make_step(zq, s, wl, M, stream.cuda_stream) for s in sets]
+    log(f"workload {wl.name} M={M}: {R} rotating sets x "
+        f"{per_set / 2**20:.1f} MiB")
+
+    run_calls(step_calls[0])
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_calls(step_calls[i % R])
+    torch.cuda.synchronize()
+
+    graphs = []
+    if not args.no_graph:
+        for calls in step_calls:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            with torch.cuda.graph(g, stream=s):
+                run_calls(make_step(zq, [c for c in sets[len(graphs)]], wl, M,
+                                    s.cuda_stream))
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        ms, wall_ms = timed_graphs(torch, graphs, args.steps, stream)
+    else:
+        ms = timed_eager(torch, step_calls, args.steps, stream)
+        wall_ms = ms
+    if args.only:
+        print(json.dumps({"ms_per_step": ms}))
+        return
+
+    eager_ms = timed_eager(torch, step_calls, max(20, args.steps // 4), stream)
+    bd = kernel_breakdown(torch, step_calls, max(20, args.steps // 4), stream)
+
+    ops_step = sum(2 * M * d["L"].N * d["L"].K for d in base)
+    tops = ops_step / (ms * 1e-3) / 1e12
+    lin_by = {d["L"].name: d["L"] for d in base}
+    breakdown = {}
+    for n, t in bd.items():
+        L = lin_by[n.split(".")[0]]
+        ops, nbytes, bound = kernel_work(n, L, M, wl.G)
+        e = {"us": round(t * 1e3, 2)}
+        if ops:
+            e["TOPS"] = round(ops / (t * 1e-3) / 1e12, 1)
+            e["pct_int8_peak"] = round(100 * e["TOPS"] / INT8_PEAK_TOPS, 1)
+        e["GB_per_s"] = round(nbytes / (t * 1e-3) / 1e9, 1)
+        breakdown[n] = e
+    dom = max(bd, key=bd.get)
+    Ld = lin_by[dom.split(".")[0]]
+    ops, nbytes, bound = kernel_work(dom, Ld, M, wl.G)
+    t_dom = bd[dom] * 1e-3
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(ops / t_dom / 1e12, 1),
+                "peak": INT8_PEAK_TOPS, "unit": "TOPS"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nbytes / t_dom / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = round(bd[dom] * 1e3, 2)
+    roof["algorithmic"] = {"ops": ops, "bytes": nbytes}
+    roof["traffic"] = traffic_for(args.traffic, dom)
+
+    out = {
+        "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} encoder linears"
+                   if wl.name.startswith("bert") else f"{wl.name} linears",
+                   "tokens": M, "hidden": wl.linears[0].K, "group_rows": wl.G,
+                   "linears": {L.name: f"{L.N}x{L.K} W{L.bits}A8"
+                               + (" +LN" if L.ln else "")
+                               + (" +GeLU" if L.gelu else "")
+                               for L in wl.linears},
+                   "rotating_sets": R, "graph": not args.no_graph},
+        "roofline": roof,
+    }
+    extras = {"eager_ms_per_step": round(eager_ms, 5),
+              "host_wall_ms_per_step": round(wall_ms, 5),
+              "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+              "breakdown": breakdown}
+    if not args.no_fp16:
+        extras["fp16_matmul"] = fp16_comparator(torch, base, M, args.steps)
+    if not args.no_decode:
+        extras["decode"] = decode_figure(torch, zq, dev)
+    out["extras"] = extras
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(base, wl, M)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def fp16_comparator(torch, base, M, steps):
+    """torch fp16 matmul + bias (+GeLU) at the same shapes (library run)."""
+    mats = []
+    for d in base:
+        L = d["L"]
+        mats.append((d["x"], d["w_cpu"].to(d["x"].device), d["b"], L.gelu))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for x, w, b, gelu in mats:
+            y = torch.addmm(b, x, w.t())
+            if gelu:
+                y = torch.nn.functional.gelu(y)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n = max(10, steps // 4)
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    ops = sum(2 * M * d["L"].N * d["L"].K for d in base)
+    return {"ms_per_step": round(ms, 5),
+            "TFLOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+            "note": "torch.addmm fp16 (+gelu), eager, same shapes, no quant"}
+
+
+if __name__ == "__main__":
+    main()

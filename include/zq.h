@@ -22,7 +22,8 @@
  *  - Arguments are checked before anything is launched.  A failed check
  *    returns a non-zero zq_status and launches nothing; the reason is kept
  *    in a thread-local string returned by zq_last_error().  M == 0 is a
- *    valid empty call (ZQ_OK, nothing launched).
+ *    valid empty call (ZQ_OK, nothing launched); buffers sized by M may
+ *    then be NULL.
  *  - Base pointers of int8/uint8/fp16 tensors must be 16-byte aligned
  *    (PyTorch allocations are); fp32 scale arrays 4-byte aligned.
  *  - Calls on one stream run in order; calls on different streams that

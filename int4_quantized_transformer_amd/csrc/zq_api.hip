@@ -30,9 +30,10 @@ zq_status hip_status(hipError_t e, const char *what) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Buffers sized by M (qx, sx, y, acc) may be NULL when M == 0.
 zq_status check_gemm(const int8_t *qx, const void *qw, int M, int N, int K,
                      int bits, const char *fn) {
-  if (!qx || !qw) return fail(ZQ_EINVAL, "%s: null qx/qw", fn);
+  if ((!qx && M != 0) || !qw) return fail(ZQ_EINVAL, "%s: null qx/qw", fn);
   if (!aligned(qx, 16) || !aligned(qw, 16))
     return fail(ZQ_EINVAL, "%s: qx/qw must be 16-byte aligned", fn);
   if (M < 0 || N <= 0 || K <= 0)
@@ -52,7 +53,8 @@ zq_status gemm_fused(const int8_t *qx, const float *sx, const void *qw,
                      const char *fn) {
   zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
   if (st != ZQ_OK) return st;
-  if (!sx || !sw || !y) return fail(ZQ_EINVAL, "%s: null sx/sw/y", fn);
+  if (!sw || ((!sx || !y) && M != 0))
+    return fail(ZQ_EINVAL, "%s: null sx/sw/y", fn);
   if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 8) ||
       (bias && !aligned(bias, 2)))
     return fail(ZQ_EINVAL, "%s: misaligned sx/sw/y/bias", fn);
@@ -82,7 +84,7 @@ zq_status gemm_raw(const int8_t *qx, const void *qw, int M, int N, int K,
                    int32_t *acc, void *stream, int bits, const char *fn) {
   zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
   if (st != ZQ_OK) return st;
-  if (!acc) return fail(ZQ_EINVAL, "%s: null acc", fn);
+  if (!acc && M != 0) return fail(ZQ_EINVAL, "%s: null acc", fn);
   if (!aligned(acc, 16)) return fail(ZQ_EINVAL, "%s: acc must be 16-byte aligned", fn);
   if (M == 0) return ok();
   zq::GemmArgs a{};
@@ -101,7 +103,8 @@ zq_status gemm_raw(const int8_t *qx, const void *qw, int M, int N, int K,
 zq_status row_quant(const void *x, const void *gamma, const void *beta,
                     float eps, int M, int K, bool ln, int8_t *qx, float *sx,
                     void *ln_out, void *stream, const char *fn) {
-  if (!x || !qx || !sx) return fail(ZQ_EINVAL, "%s: null x/qx/sx", fn);
+  if ((!x || !qx || !sx) && M != 0)
+    return fail(ZQ_EINVAL, "%s: null x/qx/sx", fn);
   if (!aligned(x, 2) || !aligned(sx, 4) || (gamma && !aligned(gamma, 2)) ||
       (beta && !aligned(beta, 2)) || (ln_out && !aligned(ln_out, 2)))
     return fail(ZQ_EINVAL, "%s: misaligned pointer", fn);

@@ -17,7 +17,7 @@ from . import build as _build
 __all__ = [
     "lib", "half_to_double", "double_to_half", "quantize_weights", "pack_w4",
     "unpack_w4", "layernorm", "quant_tokens", "gemm_i32", "epilogue",
-    "linear",
+    "linear", "threads",
 ]
 
 _lib = None
@@ -46,6 +46,8 @@ def lib():
         L.zqo_gemm_i32.argtypes = [P, P, I, I, I, P]
         L.zqo_gemm_i32.restype = ctypes.c_long
         L.zqo_epilogue.argtypes = [P, P, P, I, P, I, I, I, P, P]
+        L.zqo_threads.argtypes = []
+        L.zqo_threads.restype = I
         _lib = L
     return _lib
 
@@ -167,3 +169,8 @@ def linear(x, qw, sw, G, bias=None, act=0, ln=False, gamma=None, beta=None,
     acc = gemm_i32(qx, qw)
     z, y = epilogue(acc, sx, sw, G, bias, act)
     return {"h": h, "qx": qx, "sx": sx, "acc": acc, "z": z, "y": y}
+
+
+def threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().zqo_threads())

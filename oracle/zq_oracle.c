@@ -23,6 +23,7 @@
  * invariants, brute force, library routines); none is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -299,4 +300,10 @@ void zqo_epilogue(const int32_t *acc, const float *sx, const float *sw, int G,
         if (y)
             y[idx] = zqo_double_to_half(v);
     }
+}
+
+/* Threads the OpenMP loops above use (reported with CPU timings). */
+int zqo_threads(void)
+{
+    return omp_get_max_threads();
 }

@@ -87,6 +87,12 @@ def test_gemm_i32_argument_checks():
     assert L.zq_gemm_w8a8_i32(A, B, 4, 64, 96, C, None) == EUNSUP
     assert L.zq_gemm_w4a8_i32(A, B, 4, 64, 128, None, None) == EINVAL
     assert L.zq_gemm_w8a8_i32(A, B, 0, 64, 128, C, None) == OK
+    # M == 0: the M-sized buffers may be NULL (an empty torch tensor's pointer)
+    assert L.zq_gemm_w8a8_i32(None, B, 0, 64, 128, None, None) == OK
+    assert L.zq_gemm_w8a8(None, None, B, C, 64, None, 0, 0, 64, 128, None,
+                          None) == OK
+    assert L.zq_quant_act(None, 0, 64, None, None, None) == OK
+    assert L.zq_gemm_w8a8_i32(None, B, 1, 64, 128, C, None) == EINVAL
 
 
 def test_header_limits_match_int32_bound():
