@@ -21,8 +21,12 @@
 // into the same (even, odd) order, the MFMA accumulates 16*acc, and the
 // result is shifted right by 4 (exact: every product is a multiple of 16).
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "zq_internal.h"
+
+#define ZQ_GPTR(p) ((__attribute__((address_space(1))) void *)(p))
+#define ZQ_LPTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 namespace zq {
 
@@ -55,20 +59,69 @@ __device__ __forceinline__ v4i ld16(const void *p) {
   return *reinterpret_cast<const v4i *>(p);
 }
 
+// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9
+// encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) |
+                             ((N >> 4) << 14));
+}
+
 // ---------------------------------------------------------------- epilogue
-// Lane holds acc for n = nb + r (r = 0..3) at token t.  Fused path:
-// y = fp16(act(float(acc) * (sx[t] * sw[n / G]) + bias[n])).
+// Output columns of one fragment row: n = nb .. nb+3.  The group scale and
+// the bias are fetched once per fragment, before the main loop (their
+// latency hides behind it), and reused for every token of the tile.  All
+// loads are unconditional with clamped indices so that no wait is needed
+// until the epilogue uses them.
+struct QuadCol {
+  float sw[4];
+  half_t b[4];
+};
+
+__device__ __forceinline__ QuadCol load_quad_col(const GemmArgs &p, int nb) {
+  QuadCol c;
+  const int n = nb < p.N ? nb : p.N - 1;
+  const int g0 = n / p.G;
+  const int rem = n - g0 * p.G;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    // group of column n + r: g0 + (rem + r) / G, which for G >= 4 is
+    // g0 or g0 + 1; clamp to the last column
+    int gi;
+    if (p.G >= 4) {
+      gi = g0 + (rem + r >= p.G ? 1 : 0);
+    } else {
+      gi = (n + r) / p.G;
+    }
+    const int last = (p.N - 1) / p.G;
+    c.sw[r] = p.sw[gi < last ? gi : last];
+  }
+  if (p.bias) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c.b[r] = p.bias[n + r < p.N ? n + r : p.N - 1];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c.b[r] = (half_t)0.0f;
+  }
+  return c;
+}
+
+// y = fp16(act(float(acc) * (sx[t] * sw[n / G]) + bias[n])), or the raw
+// int32 accumulator.  Lane holds n = nb .. nb+3 of token t.
 template <bool W4, bool RAW>
 __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
-                                           v4i acc, float sxt) {
+                                           v4i acc, float sxt,
+                                           const QuadCol &c) {
   if (t >= p.M || nb >= p.N) return;
   if constexpr (W4) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] >>= 4;
   }
+  const bool full = nb + 3 < p.N && (p.N & 3) == 0;
   if constexpr (RAW) {
     int32_t *o = static_cast<int32_t *>(p.out) + (size_t)t * p.N + nb;
-    if (nb + 3 < p.N && (p.N & 3) == 0) {
+    if (full) {
       *reinterpret_cast<v4i *>(o) = acc;
     } else {
 #pragma unroll
@@ -79,14 +132,12 @@ __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
     half4 h;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int n = nb + r < p.N ? nb + r : p.N - 1;
-      float z = (float)acc[r] * (sxt * p.sw[n / p.G]);
-      if (p.bias) z += (float)p.bias[n];
+      float z = fmaf((float)acc[r], sxt * c.sw[r], (float)c.b[r]);
       if (p.act == ZQ_ACT_GELU) z = gelu_erf(z);
       h[r] = (half_t)z;
     }
     half_t *o = static_cast<half_t *>(p.out) + (size_t)t * p.N + nb;
-    if (nb + 3 < p.N && (p.N & 3) == 0) {
+    if (full) {
       *reinterpret_cast<half4 *>(o) = h;
     } else {
 #pragma unroll
@@ -97,37 +148,220 @@ __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
 }
 
 // =================================================================== tiled
-// Block tile BN (n) x BM (t) x BK (k bytes of activation per stage),
-// waves arranged (BN/WN) x (BM/WM), each wave WN x WM with 16x16 MFMA
-// fragments.  Global -> registers -> LDS with double buffering: the loads
-// for stage k+1 are in flight while stage k is multiplied.  LDS rows are
-// padded by 16 bytes so that the 16-byte fragment reads of 8 consecutive
-// rows hit disjoint banks.
-template <int BN_, int BM_, int WN_, int WM_, bool W4_>
+// Prefill-sized M.  v_mfma_i32_32x32x32_i8 (on gfx950 it sustains twice the
+// integer rate of the 16x16x64 form): lane l holds row l%32 of a 32x32
+// operand block and 16 k-bytes chosen by its lane half h = l/32; the result
+// lane l holds token t = l%32 and outputs n = 8q + 4h + (0..3), q = 0..3.
+//
+// Block tile BN (n) x BM (t), k in stages of 128 activation bytes (64
+// packed W4 bytes).  Operands travel global -> LDS directly
+// (global_load_lds_dwordx4: each lane's 16 bytes land at a wave-contiguous
+// LDS address, no register staging) through an S-stage ring; while stage k
+// is multiplied, stages k+1 .. k+S-1 are in flight.  One barrier per stage:
+// a wave waits for its own copies of stage k (vmcnt), the barrier makes all
+// copies visible, and only then is stage k+S-1 issued into the slot that
+// stage k-1 used.
+//
+// LDS rows are unpadded (128 B, or 64 B for packed W4) and their 16-byte
+// chunks are XOR-swizzled so that the 16-byte fragment reads of 8
+// consecutive rows (one LDS cycle) hit 8 different bank groups:
+//   128-byte rows: slot = chunk ^ (row & 7)
+//    64-byte rows: slot = chunk ^ ((row >> 1) & 3)
+template <int BN_, int BM_, int WN_, int WM_, int S_, bool W4_>
 struct Tile {
-  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
+  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, S = S_;
   static constexpr bool W4 = W4_;
-  static constexpr int BK = 128;
   static constexpr int NWN = BN / WN, NWM = BM / WM;
   static constexpr int NWAVES = NWN * NWM, NT = NWAVES * kWave;
-  static constexpr int FN = WN / 16, FM = WM / 16;
-  static constexpr int WROW = W4 ? BK / 2 : BK;  // weight bytes per row/stage
-  static constexpr int WSTRIDE = WROW + 16;
-  static constexpr int XSTRIDE = BK + 16;
-  static constexpr int WCPR = WROW / 16, XCPR = BK / 16;  // chunks per row
-  static constexpr int WCH = BN * WCPR / NT, XCH = BM * XCPR / NT;
-  static constexpr int WBYTES = BN * WSTRIDE, XBYTES = BM * XSTRIDE;
+  static constexpr int FN = WN / 32, FM = WM / 32;
+  static constexpr int XROW = 128;                  // activation bytes/row/stage
+  static constexpr int WROW = W4 ? 64 : 128;        // weight bytes/row/stage
+  static constexpr int WCPR = WROW / 16, XCPR = XROW / 16;  // chunks per row
+  static constexpr int WRPI = 64 / WCPR, XRPI = 64 / XCPR;  // rows per wave copy
+  static constexpr int WINS = BN / WRPI, XINS = BM / XRPI;  // wave copies/stage
+  static constexpr int IW = WINS / NWAVES, IX = XINS / NWAVES;  // per wave
+  static constexpr int WBYTES = BN * WROW, XBYTES = BM * XROW;
   static constexpr int STAGE = WBYTES + XBYTES;
-  static_assert((BN * WCPR) % NT == 0 && (BM * XCPR) % NT == 0, "tile/threads");
-  static_assert(WN % 16 == 0 && WM % 16 == 0, "wave tile");
+  static constexpr int LDS = S * STAGE;
+  static_assert(WINS % NWAVES == 0 && XINS % NWAVES == 0, "copy split");
+  static_assert(WN % 32 == 0 && WM % 32 == 0 && S >= 2, "tile");
+  static_assert((IW + IX) * (S - 2) < 64, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
 
+__device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+template <int BYTES>
+__device__ __forceinline__ int wswz(int chunk, int row) {
+  if constexpr (BYTES == 128) return chunk ^ (row & 7);
+  else return chunk ^ ((row >> 1) & 3);
+}
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const GemmArgs &p, const char *W,
+                                            const char *X, int ldw, int n0,
+                                            int m0, int kt, char *stage,
+                                            int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < C::IW; ++j) {
+    const int q = wave * C::IW + j;
+    const int row = q * C::WRPI + lane / C::WCPR;
+    const int chunk = wswz<C::WROW>(lane % C::WCPR, row);
+    int n = n0 + row;
+    n = n < p.N ? n : p.N - 1;                 // rows past N: never stored
+    int kb = kt * C::WROW + chunk * 16;
+    if (kb >= ldw) kb -= C::WROW / 2;          // K % 128 == 64: unused half
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + (size_t)n * ldw + kb),
+                                     ZQ_LPTR(stage + q * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < C::IX; ++j) {
+    const int q = wave * C::IX + j;
+    const int row = q * C::XRPI + lane / C::XCPR;
+    const int chunk = wswz<C::XROW>(lane % C::XCPR, row);
+    int t = m0 + row;
+    t = t < p.M ? t : p.M - 1;
+    int kb = kt * C::XROW + chunk * 16;
+    if (kb >= p.K) kb -= C::XROW / 2;
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * p.K + kb),
+                                     ZQ_LPTR(stage + C::WBYTES + q * 1024), 16,
+                                     0, 0);
+  }
+}
+
+// Wait until at most `left` stages of this wave's copies are in flight.
+template <class C>
+__device__ __forceinline__ void wait_stages(int left) {
+  constexpr int P = C::IW + C::IX;
+  if constexpr (C::S >= 4) {
+    if (left >= 3) { wait_vmcnt<3 * P>(); return; }
+  }
+  if constexpr (C::S >= 3) {
+    if (left >= 2) { wait_vmcnt<2 * P>(); return; }
+  }
+  if (left >= 1) { wait_vmcnt<P>(); return; }
+  wait_vmcnt<0>();
+}
+
+// Operand fragments of one MFMA k-step (32 k): weights a[FN] (for W4 the
+// packed source, unpacked at use), activations b[FM].
+template <class C>
+struct Frag {
+  v4i a[C::FN];
+  v4i b[C::FM];
+};
+
+// Full 128-k stage, k-step s (0..3), lane half h.
+//   W8: weight and activation chunk 2s + h (k = 32s + 16h).
+//   W4: lane half h takes k = 64h + 16s: packed chunk 2h (s = 0, 1) or
+//       2h + 1 (s = 2, 3), read once per pair into raw0 / raw1, and
+//       activation chunk 4h + s.
+template <class C>
+__device__ __forceinline__ void fetch(const char *ws, const char *xs, int s,
+                                      int wn0, int wm0, int r32, int h,
+                                      Frag<C> &f, v4i (&raw)[2][C::FN]) {
+  const int x7 = r32 & 7;
+  if constexpr (!C::W4) {
+    const int c = 2 * s + h;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+      f.a[fn] = ld16(ws + (wn0 + fn * 32 + r32) * 128 + ((c ^ x7) << 4));
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+      f.b[fm] = ld16(xs + (wm0 + fm * 32 + r32) * 128 + ((c ^ x7) << 4));
+  } else {
+    const int w4 = (r32 >> 1) & 3;
+    if (s == 0 || s == 2) {
+      const int pc = 2 * h + (s >> 1);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        raw[s >> 1][fn] = ld16(ws + (wn0 + fn * 32 + r32) * 64 + ((pc ^ w4) << 4));
+    }
+    const int c = 4 * h + s;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+      f.b[fm] = ld16(xs + (wm0 + fm * 32 + r32) * 128 + ((c ^ x7) << 4));
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mma(const Frag<C> &f, int s,
+                                    const v4i (&raw)[2][C::FN],
+                                    v16i (&acc)[C::FN][C::FM]) {
+  v4i a[C::FN], b[C::FM];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    if constexpr (C::W4) {
+      const v4i &rw = raw[s >> 1][fn];
+      a[fn] = unpack_w4(rw[2 * (s & 1)], rw[2 * (s & 1) + 1]);
+    } else {
+      a[fn] = f.a[fn];
+    }
+  }
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+    b[fm] = C::W4 ? perm_even_odd(f.b[fm]) : f.b[fm];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+      acc[fn][fm] = mfma32_i8(a[fn], b[fm], acc[fn][fm]);
+}
+
+// 64-k tail stage, k-step s (0, 1): k = 32s + 16h.  W8: chunk 2s + h.
+// W4: packed bytes 16s + 8h .. +7 (chunk s, half h), activation chunk
+// 2s + h.  Fetched and multiplied without overlap (it happens once).
+template <class C>
+__device__ __forceinline__ void tail_stage(const char *ws, const char *xs,
+                                           int wn0, int wm0, int r32, int h,
+                                           v16i (&acc)[C::FN][C::FM]) {
+  const int x7 = r32 & 7;
+  const int w4 = (r32 >> 1) & 3;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v4i a[C::FN], b[C::FM];
+    const int c = 2 * s + h;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      if constexpr (C::W4) {
+        const v2i w = *reinterpret_cast<const v2i *>(
+            ws + (wn0 + fn * 32 + r32) * 64 + ((s ^ w4) << 4) + h * 8);
+        a[fn] = unpack_w4(w[0], w[1]);
+      } else {
+        a[fn] = ld16(ws + (wn0 + fn * 32 + r32) * 128 + ((c ^ x7) << 4));
+      }
+    }
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const v4i x = ld16(xs + (wm0 + fm * 32 + r32) * 128 + ((c ^ x7) << 4));
+      b[fm] = C::W4 ? perm_even_odd(x) : x;
+    }
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+        acc[fn][fm] = mfma32_i8(a[fn], b[fm], acc[fn][fm]);
+  }
+}
+
+// Main loop schedule (S LDS slots; stage j is copied into slot j % S):
+//   prologue: copy stages 0 .. S-1, wait for stage 0, barrier, read the
+//             fragments of (stage 0, k-step 0).
+//   stage kt, k-step s = 0, 1, 2: read fragments of k-step s+1 into the
+//             other register set, then issue the MFMAs of k-step s (the
+//             reads complete under the MFMAs).
+//   k-step 3: wait for stage kt+1's copies and for this wave's LDS reads,
+//             barrier (now every wave is done with slot kt % S and stage
+//             kt+1 is visible), copy stage kt+S into slot kt % S, read
+//             fragments of (stage kt+1, k-step 0), MFMAs of k-step 3.
 template <class C, bool RAW>
 __global__ void __launch_bounds__(C::NT)
 gemm_tiled_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
+  const int r32 = lane & 31, h = lane >> 5;
 
   // tile order: XCD-contiguous ranges, then groups of 8 token tiles that
   // share one weight tile
@@ -147,120 +381,167 @@ gemm_tiled_kernel(GemmArgs p) {
   const char *W = static_cast<const char *>(p.qw);
   const char *X = reinterpret_cast<const char *>(p.qx);
 
-  // token scales for this lane's columns, read before the main loop
+  // Epilogue operands, read before the main loop so that their latency
+  // hides behind it (branch-free, clamped indices: no wait until used).
+  // Token scales: one per fragment column.  When 32 | G every 32-row weight
+  // fragment lies in one group: one scale per fragment.  Bias: 16 values
+  // per fragment (n = 8q + 4h + r).
   float sxv[C::FM];
+  float swv[C::FN];
+  half4 bq[C::FN][4];
+  const bool g32 = (p.G & 31) == 0;
+  if constexpr (!RAW) {
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int t = m0 + wm0 + fm * 16 + r16;
-    sxv[fm] = (!RAW && t < p.M) ? p.sx[t] : 0.0f;
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int t = m0 + wm0 + fm * 32 + r32;
+      sxv[fm] = p.sx[t < p.M ? t : p.M - 1];
+    }
+    const int lastg = (p.N - 1) / p.G;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int gi = (n0 + wn0 + fn * 32) / p.G;
+      swv[fn] = g32 ? p.sw[gi < lastg ? gi : lastg] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nb = n0 + wn0 + fn * 32 + 8 * q + 4 * h;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          bq[fn][q][r] = p.bias ? p.bias[nb + r < p.N ? nb + r : p.N - 1]
+                                : (half_t)0.0f;
+      }
+    }
   }
 
-  v4i acc[C::FN][C::FM];
+  v16i acc[C::FN][C::FM];
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = v16i{};
 
-  v4i wreg[C::WCH], xreg[C::XCH];
-  const v4i zero = {0, 0, 0, 0};
+  const int KT = (p.K + C::XROW - 1) / C::XROW;
+  const bool half_tail = (p.K % C::XROW) != 0;  // last stage holds 64 k
+  const int KTF = KT - (half_tail ? 1 : 0);      // stages with 128 k
 
-  auto load_stage = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < C::WCH; ++i) {
-      const int c = tid + i * C::NT;
-      const int row = c / C::WCPR, col = c % C::WCPR;
-      const int n = n0 + row;
-      const int kb = kt * C::WROW + col * 16;
-      wreg[i] = (n < p.N && kb < ldw) ? ld16(W + (size_t)n * ldw + kb) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < C::XCH; ++i) {
-      const int c = tid + i * C::NT;
-      const int row = c / C::XCPR, col = c % C::XCPR;
-      const int t = m0 + row;
-      const int kb = kt * C::BK + col * 16;
-      v4i v = (t < p.M && kb < p.K) ? ld16(X + (size_t)t * p.K + kb) : zero;
-      if constexpr (C::W4) v = perm_even_odd(v);
-      xreg[i] = v;
-    }
-  };
-  auto store_stage = [&](int buf) {
-    char *ws = lds + buf * C::STAGE;
-    char *xs = ws + C::WBYTES;
-#pragma unroll
-    for (int i = 0; i < C::WCH; ++i) {
-      const int c = tid + i * C::NT;
-      *reinterpret_cast<v4i *>(ws + (c / C::WCPR) * C::WSTRIDE + (c % C::WCPR) * 16) = wreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::XCH; ++i) {
-      const int c = tid + i * C::NT;
-      *reinterpret_cast<v4i *>(xs + (c / C::XCPR) * C::XSTRIDE + (c % C::XCPR) * 16) = xreg[i];
-    }
-  };
-  auto compute = [&](int buf) {
-    const char *ws = lds + buf * C::STAGE;
+  const int npro = KT < C::S ? KT : C::S;
+  for (int j = 0; j < npro; ++j)
+    issue_stage<C>(p, W, X, ldw, n0, m0, j, lds + j * C::STAGE, wave, lane);
+  wait_stages<C>(npro - 1);
+  __builtin_amdgcn_s_barrier();
+
+  Frag<C> f0, f1;
+  v4i raw[2][C::FN];
+  if (KTF > 0) fetch<C>(lds, lds + C::WBYTES, 0, wn0, wm0, r32, h, f0, raw);
+
+  // sched_barrier(0) keeps the phases in this order (the scheduler would
+  // otherwise hoist the barrier above the MFMAs of k-step 2).
+  for (int kt = 0; kt < KTF; ++kt) {
+    char *ws = lds + (kt % C::S) * C::STAGE;
     const char *xs = ws + C::WBYTES;
-    if constexpr (!C::W4) {
-#pragma unroll
-      for (int s = 0; s < C::BK / 64; ++s) {
-        v4i a[C::FN], b[C::FM];
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          a[fn] = ld16(ws + (wn0 + fn * 16 + r16) * C::WSTRIDE + s * 64 + g * 16);
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-          b[fm] = ld16(xs + (wm0 + fm * 16 + r16) * C::XSTRIDE + s * 64 + g * 16);
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-          for (int fm = 0; fm < C::FM; ++fm)
-            acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
-      }
-    } else {
-      // one 16-byte packed read covers k = 32g .. 32g+31 of the stage:
-      // bytes 0-7 feed MFMA slot 0 and bytes 8-15 slot 1
-      v4i raw[C::FN];
+    fetch<C>(ws, xs, 1, wn0, wm0, r32, h, f1, raw);
+    mma<C>(f0, 0, raw, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch<C>(ws, xs, 2, wn0, wm0, r32, h, f0, raw);
+    mma<C>(f1, 1, raw, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch<C>(ws, xs, 3, wn0, wm0, r32, h, f1, raw);
+    mma<C>(f0, 2, raw, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 3: stage boundary
+    wait_stages<C>(max(0, min(C::S - 2, KT - 2 - kt)));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own LDS reads done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + C::S < KT)
+      issue_stage<C>(p, W, X, ldw, n0, m0, kt + C::S, ws, wave, lane);
+    if (kt + 1 < KTF) {
+      char *wn = lds + ((kt + 1) % C::S) * C::STAGE;
+      fetch<C>(wn, wn + C::WBYTES, 0, wn0, wm0, r32, h, f0, raw);
+    }
+    mma<C>(f1, 3, raw, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (half_tail) {
+    const char *ws = lds + ((KT - 1) % C::S) * C::STAGE;
+    tail_stage<C>(ws, ws + C::WBYTES, wn0, wm0, r32, h, acc);
+  }
+
+  if constexpr (!RAW && C::BM * C::BN * 2 <= C::LDS && C::BN >= 128) {
+    if (g32) {
+      // Stage the fp16 tile through LDS so that every global store writes
+      // whole 256-byte row segments with 16 bytes per lane.  Layout: row t
+      // of the tile holds BN halves; its 16-byte chunks are XOR-swizzled by
+      // (t & 15) so that the 8-byte writes of 32 consecutive rows spread
+      // over the banks.
+      __syncthreads();  // every wave is done reading the operand stages
+      constexpr int RB = C::BN * 2;  // bytes per tile row
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
-        raw[fn] = ld16(ws + (wn0 + fn * 16 + r16) * C::WSTRIDE + g * 16);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        v4i a[C::FN], b[C::FM];
+        for (int fm = 0; fm < C::FM; ++fm) {
+          const int tl = wm0 + fm * 32 + r32;
+          const float sc = sxv[fm] * swv[fn];
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          a[fn] = unpack_w4(raw[fn][2 * s], raw[fn][2 * s + 1]);
+          for (int q = 0; q < 4; ++q) {
+            half4 hv;
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-          b[fm] = ld16(xs + (wm0 + fm * 16 + r16) * C::XSTRIDE + g * 32 + s * 16);
+            for (int r = 0; r < 4; ++r) {
+              int a = acc[fn][fm][4 * q + r];
+              if constexpr (C::W4) a >>= 4;
+              float z = fmaf((float)a, sc, (float)bq[fn][q][r]);
+              if (p.act == ZQ_ACT_GELU) z = gelu_erf(z);
+              hv[r] = (half_t)z;
+            }
+            const int chunk = (wn0 + fn * 32) / 8 + q;
+            *reinterpret_cast<half4 *>(lds + tl * RB + ((chunk ^ (tl & 15)) << 4) + h * 8) = hv;
+          }
+        }
+      __syncthreads();
+      constexpr int CPR = C::BN / 8;  // 16-byte chunks per tile row
+      const bool vec = (p.N & 7) == 0 && (((uintptr_t)p.out) & 15) == 0;
+      half_t *Y = static_cast<half_t *>(p.out);
+      for (int i = tid; i < C::BM * CPR; i += C::NT) {
+        const int row = i / CPR, c = i % CPR;
+        const int t = m0 + row, n = n0 + c * 8;
+        if (t >= p.M || n >= p.N) continue;
+        const v4i v = ld16(lds + row * RB + ((c ^ (row & 15)) << 4));
+        half_t *o = Y + (size_t)t * p.N + n;
+        if (vec && n + 8 <= p.N) {
+          *reinterpret_cast<v4i *>(o) = v;
+        } else {
+          const half8 hv = __builtin_bit_cast(half8, v);
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-          for (int fm = 0; fm < C::FM; ++fm)
-            acc[fn][fm] = mfma_i8(a[fn], b[fm], acc[fn][fm]);
+          for (int e = 0; e < 8; ++e)
+            if (n + e < p.N) o[e] = hv[e];
+        }
       }
+      return;
     }
-  };
-
-  const int KT = (p.K + C::BK - 1) / C::BK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_stage(kt + 1);
-    compute(cur);
-    if (kt + 1 < KT) store_stage(cur ^ 1);
-    __syncthreads();
   }
 
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
-      const int t = m0 + wm0 + fm * 16 + r16;
-      const int nb = n0 + wn0 + fn * 16 + g * 4;
-      store_quad<C::W4, RAW>(p, t, nb, acc[fn][fm], sxv[fm]);
+      const int t = m0 + wm0 + fm * 32 + r32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nb = n0 + wn0 + fn * 32 + 8 * q + 4 * h;
+        const v4i a = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1],
+                       acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]};
+        QuadCol qc;
+        if constexpr (!RAW) {
+          if (g32) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              qc.sw[r] = swv[fn];
+              qc.b[r] = bq[fn][q][r];
+            }
+          } else {
+            qc = load_quad_col(p, nb);
+          }
+        }
+        store_quad<C::W4, RAW>(p, t, nb, a, RAW ? 0.0f : sxv[fm], qc);
+      }
     }
 }
 
@@ -392,8 +673,10 @@ gemm_skinny_kernel(GemmArgs p) {
     for (int r = 0; r < 4; ++r) a[r] = red[(pr * kWave + lane) * 4 + r];
     const int t = fm * 16 + r16;
     const int nb = n0 + fn * 16 + g * 4;
-    const float sxt = (!RAW && t < p.M) ? p.sx[t] : 0.0f;
-    store_quad<C::W4, RAW>(p, t, nb, a, sxt);
+    const float sxt = RAW ? 0.0f : p.sx[t < p.M ? t : p.M - 1];
+    QuadCol qc;
+    if constexpr (!RAW) qc = load_quad_col(p, nb);
+    store_quad<C::W4, RAW>(p, t, nb, a, sxt, qc);
   }
 }
 
@@ -414,15 +697,56 @@ static hipError_t run_skinny(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tiled configurations: {BN, BM, WN, WM, stages}.
+struct TileCfg {
+  int bn, bm, wn, wm, s;
+};
+static const TileCfg kTileCfgs[] = {
+    {128, 128, 64, 64, 2},    // 0: 4 waves
+    {256, 128, 128, 64, 2},   // 1: 4 waves
+    {128, 256, 64, 128, 2},   // 2: 4 waves
+    {256, 256, 128, 128, 2},  // 3: 4 waves
+    {128, 128, 64, 64, 3},    // 4: 4 waves
+    {256, 256, 128, 64, 2},   // 5: 8 waves
+    {256, 128, 128, 64, 3},   // 6: 4 waves
+};
+constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
+
+template <bool W4, bool RAW>
+static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
+  switch (id) {
+    case 0: return run_tiled<Tile<128, 128, 64, 64, 2, W4>, RAW>(a, s);
+    case 1: return run_tiled<Tile<256, 128, 128, 64, 2, W4>, RAW>(a, s);
+    case 2: return run_tiled<Tile<128, 256, 64, 128, 2, W4>, RAW>(a, s);
+    case 3: return run_tiled<Tile<256, 256, 128, 128, 2, W4>, RAW>(a, s);
+    case 4: return run_tiled<Tile<128, 128, 64, 64, 3, W4>, RAW>(a, s);
+    case 5: return run_tiled<Tile<256, 256, 128, 64, 2, W4>, RAW>(a, s);
+    default: return run_tiled<Tile<256, 128, 128, 64, 3, W4>, RAW>(a, s);
+  }
+}
+
 enum PlanKind { kSkinny = 0, kTiled = 1 };
 struct Plan {
   PlanKind kind;
-  int mf;  // skinny: 16-token fragments
+  int mf;   // skinny: 16-token fragments
+  int cfg;  // tiled: index into kTileCfgs
 };
 
+// ZQ_GEMM_TILE=<index> forces one tiled configuration (tuning aid).
+static int forced_tile() {
+  static int v = [] {
+    const char *e = getenv("ZQ_GEMM_TILE");
+    if (!e) return -1;
+    const int i = atoi(e);
+    return (i >= 0 && i < kNumTileCfgs) ? i : -1;
+  }();
+  return v;
+}
+
 static Plan choose(int M, int /*N*/, int /*K*/, int /*bits*/) {
-  if (M <= 64) return Plan{kSkinny, (M + 15) / 16};
-  return Plan{kTiled, 0};
+  if (M <= 64) return Plan{kSkinny, (M + 15) / 16, 0};
+  const int f = forced_tile();
+  return Plan{kTiled, 0, f >= 0 ? f : 0};
 }
 
 template <bool W4, bool RAW>
@@ -436,7 +760,7 @@ static hipError_t run(const GemmArgs &a, hipStream_t s) {
       default: return run_skinny<Skinny<16, 4, 8, 2, W4>, RAW>(a, s);
     }
   }
-  return run_tiled<Tile<128, 128, 64, 64, W4>, RAW>(a, s);
+  return run_tile_cfg<W4, RAW>(pl.cfg, a, s);
 }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
@@ -450,8 +774,11 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
   if (pl.kind == kSkinny)
     return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d",
                     pl.mf, pl.mf <= 2 ? 4 : 2, bits, (N + 15) / 16);
-  return snprintf(buf, len, "tiled BN=128 BM=128 WN=64 WM=64 BK=128 W%d tiles=%d",
-                  bits, ((N + 127) / 128) * ((M + 127) / 128));
+  const TileCfg &c = kTileCfgs[pl.cfg];
+  return snprintf(buf, len,
+                  "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d W%d tiles=%d",
+                  pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, bits,
+                  ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm));
 }
 
 }  // namespace zq

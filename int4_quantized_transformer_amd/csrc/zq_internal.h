@@ -13,6 +13,7 @@ namespace zq {
 typedef _Float16 half_t;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
@@ -49,8 +50,22 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 }
 
 // ------------------------------------------------------------------- GeLU
+// GeLU(z) = z * Phi(z), the exact (erf) form, evaluated as
+//   z * sigmoid(z * P(min(z^2, 36)))
+// where P is a degree-4 polynomial fitted (iteratively reweighted least
+// squares on |z| <= 6) so that z * P(z^2) = logit(Phi(z)).  In fp32 the
+// result is within 3.5e-6 of z * Phi(z) for all z (checked on |z| <= 60;
+// beyond |z| = 6 the sigmoid is saturated: Phi differs from 0 or 1 by less
+// than 1e-9).  Coefficients below are -log2(e) * P so that
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)) needs one exp2 and one rcp.
 __device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+  const float u = fminf(z * z, 36.0f);
+  float q = fmaf(u, -3.2104740057548042e-06f, 8.791135769570246e-05f);
+  q = fmaf(u, q, 0.0003620403294917196f);
+  q = fmaf(u, q, -0.10522996634244919f);
+  q = fmaf(u, q, -2.3020436763763428f);
+  const float e = __builtin_amdgcn_exp2f(z * q);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // ------------------------------------------------------------ XCD mapping
@@ -63,12 +78,6 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   const int x = pid % X, i = pid / X;
   return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
-
-// ------------------------------------------------------ host-side helpers
-struct LaunchError {
-  hipError_t err;
-  const char *what;
-};
 
 // Launchers (defined in the .hip files); they return hipSuccess or the
 // error of the launch.  Arguments are already validated.

@@ -110,3 +110,27 @@ def test_empty_m_is_a_no_op():
 def test_plans_used_by_tests_cover_both_kernels():
     plans = {zq.gemm_plan(M, N, K, 8).split()[0] for M, N, K in SHAPES}
     assert plans == {"skinny", "tiled"}
+
+
+@pytest.mark.parametrize("M", [40, 256])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gelu_epilogue_dense_range(M, bits):
+    # acc[t,n] = 127 * qw[n,0] (one-hot tokens); with sw = 1/127 and
+    # sx[t] = 0.002 (t+1) the epilogue input z covers about [-8, 8] densely
+    K, N, G = 128, 256, 64
+    qmax = 127 if bits == 8 else 7
+    qx = np.zeros((M, K), np.int8)
+    qx[:, 0] = 127
+    q = np.zeros((N, K), np.int8)
+    q[:, 0] = np.clip(np.round(np.linspace(-qmax, qmax, N)), -qmax, qmax)
+    qw = q if bits == 8 else oracle.pack_w4(q)
+    sx = (0.002 * (np.arange(M) + 1) * (127 / qmax) * (64 / M)).astype(np.float32)
+    sw = np.full(N // G, 1 / 127, np.float32)
+    d = dev()
+    fn = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    y = fn(torch.from_numpy(qx).to(d), torch.from_numpy(sx).to(d),
+           torch.from_numpy(qw).to(d), torch.from_numpy(sw).to(d), G, None, 1)
+    z, _ = oracle.epilogue(oracle.gemm_i32(qx, q), sx, sw, G, None, 1)
+    torch.cuda.synchronize()
+    assert np.abs(z).max() > 7.5
+    assert_fp16_close_to_oracle(to_np(y), z, zq.gemm_plan(M, N, K, bits))
