@@ -20,27 +20,83 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- reductions
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Wave-wide all-reduce with DPP lane permutes inside each row of 16 lanes
+// (quad_perm, half-row mirror, row mirror) and v_readlane for the four
+// rows, instead of LDS-routed shuffles.  The sum's association order is
+// fixed, so results are deterministic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float rows_of_16_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+__device__ __forceinline__ float rows_of_16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
   return v;
+}
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = rows_of_16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = rows_of_16_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)),
+               fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // --------------------------------------------------------------- quantizer
 // Eq. (2) of the group-wise/token-wise quantizer with S = amax / qmax:
-// fp32 IEEE division, clamp to +-qmax, round half to even.  The division
-// must stay correctly rounded (the library is built with
-// -fhip-fp32-correctly-rounded-divide-sqrt and without fast-math).
-__device__ __forceinline__ int quant_code(float v, float s, float qmax) {
-  if (s == 0.0f) return 0;
-  float x = v / s;
-  x = fminf(fmaxf(x, -qmax), qmax);
+// q = rint(clamp(v / S, -qmax, qmax)) with the fp32 IEEE quotient v / S
+// and round half to even.
+//
+// Fast evaluation with identical results: with r = fl(1 / S) (IEEE) and
+// q0 = fl(v * r), |q0 - v/S| <= |v/S| * 2^-23 (two roundings of relative
+// size 2^-24), and fl(v/S) is within |v/S| * 2^-24 of v/S, so
+// |q0 - fl(v/S)| <= 3 * 2^-24 * |v/S| < 2.3e-5 for |v/S| <= 128.  The
+// integer rint(clamp(.)) can only differ between q0 and fl(v/S) if a
+// half-integer lies between them, i.e. if q0 is within 2.3e-5 of k + 0.5;
+// in that case (rare: about 6e-5 of the values) the exact division is
+// evaluated.  The library is built with -fhip-fp32-correctly-rounded-
+// divide-sqrt and without fast-math, so both divisions are IEEE.
+struct Quantizer {
+  float s;    // scale S
+  float r;    // fl(1 / S)
+  float qmax;
+};
+
+__device__ __forceinline__ Quantizer make_quantizer(float amax, float qmax) {
+  Quantizer z;
+  z.qmax = qmax;
+  z.s = amax / qmax;
+  z.r = z.s == 0.0f ? 0.0f : 1.0f / z.s;
+  return z;
+}
+
+__device__ __forceinline__ int quant_code(float v, const Quantizer &z) {
+  if (z.s == 0.0f) return 0;
+  float x = v * z.r;
+  const float d = x - floorf(x);
+  if (fabsf(d - 0.5f) <= 3.0517578125e-05f) x = v / z.s;  // 2^-15 margin
+  x = fminf(fmaxf(x, -z.qmax), z.qmax);
   return (int)__builtin_rintf(x);
 }
 

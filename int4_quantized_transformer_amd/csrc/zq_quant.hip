@@ -157,8 +157,8 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
   const float amax = team_max<TPR>(m, red);
-  const float s = amax / 127.0f;
-  if (tl == 0) sx[row] = s;
+  const Quantizer qz = make_quantizer(amax, 127.0f);
+  if (tl == 0) sx[row] = qz.s;
 
   int8_t *qr = qx + (size_t)row * K;
 #pragma unroll
@@ -166,7 +166,7 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
     const int c = tl + j * TPR;
     int q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quant_code(v[j][i], s, 127.0f);
+    for (int i = 0; i < 8; ++i) q[i] = quant_code(v[j][i], qz);
     if constexpr (VEC) {
       if (c * 8 < K) {
         v2i p;
@@ -272,8 +272,8 @@ weight_quant_kernel(const half_t *__restrict__ w, int K, int G, int bits,
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kWQThreads / kWave; ++i) amax = fmaxf(amax, red[i]);
-  const float s = amax / qmax;
-  if (threadIdx.x == 0) sw[g] = s;
+  const Quantizer qz = make_quantizer(amax, qmax);
+  if (threadIdx.x == 0) sw[g] = qz.s;
 
   // pass 2: codes
   if (bits == 8) {
@@ -283,7 +283,7 @@ weight_quant_kernel(const half_t *__restrict__ w, int K, int G, int bits,
         half8 h = *reinterpret_cast<const half8 *>(src + i);
         int q[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = quant_code((float)h[e], s, qmax);
+        for (int e = 0; e < 8; ++e) q[e] = quant_code((float)h[e], qz);
         v2i p;
         p[0] = (int)pack4_i8(q[0], q[1], q[2], q[3]);
         p[1] = (int)pack4_i8(q[4], q[5], q[6], q[7]);
@@ -291,7 +291,7 @@ weight_quant_kernel(const half_t *__restrict__ w, int K, int G, int bits,
       }
     } else {
       for (size_t i = threadIdx.x; i < n; i += kWQThreads)
-        dst[i] = (int8_t)quant_code((float)src[i], s, qmax);
+        dst[i] = (int8_t)quant_code((float)src[i], qz);
     }
   } else {
     // K is even, so element pairs (2j, 2j+1) of the flattened group are
@@ -303,13 +303,13 @@ weight_quant_kernel(const half_t *__restrict__ w, int K, int G, int bits,
         uint32_t p = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          p |= (uint32_t)(quant_code((float)h[e], s, qmax) & 0xF) << (4 * e);
+          p |= (uint32_t)(quant_code((float)h[e], qz) & 0xF) << (4 * e);
         *reinterpret_cast<uint32_t *>(dst + i / 2) = p;
       }
     } else {
       for (size_t j = threadIdx.x; j < n / 2; j += kWQThreads) {
-        const int lo = quant_code((float)src[2 * j], s, qmax) & 0xF;
-        const int hi = quant_code((float)src[2 * j + 1], s, qmax) & 0xF;
+        const int lo = quant_code((float)src[2 * j], qz) & 0xF;
+        const int hi = quant_code((float)src[2 * j + 1], qz) & 0xF;
         dst[j] = (uint8_t)(lo | (hi << 4));
       }
     }
