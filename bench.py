@@ -55,6 +55,15 @@ def parse():
                                                       "traffic.json"))
     ap.add_argument("--only", default=None,
                     help="(profiling) run only the step loop, no extras")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="(profiling) first run a plain 256 MiB device copy "
+                         "3 times, the reference for the HBM byte counters")
+    ap.add_argument("--summarize", default=None, metavar="DIR",
+                    help="summarize rocprofv3 CSV output in DIR (kernel trace "
+                         "and/or --pmc FETCH_SIZE / WRITE_SIZE runs); no GPU")
+    ap.add_argument("--write-traffic", default=None, metavar="JSON",
+                    help="with --summarize: write the per-launch HBM traffic "
+                         "of the GEMM and quantization kernels to JSON")
     return ap.parse_args()
 
 
@@ -231,7 +240,19 @@ def kernel_breakdown(torch, step_calls, steps, stream):
     return {n: acc[n] / n_it for n in names}
 
 
-def traffic_for(path, kernel_name):
+def grid_threads(name, L, M, G, zq):
+    """Launch grid (threads) of the kernel behind a step entry, as the
+    kernel trace reports it (used to find that launch in rocprofv3 output)."""
+    plan = zq.gemm_plan(M, L.N, L.K, L.bits) if ".gemm" in name else ""
+    if plan.startswith("tiled"):
+        tiles = int(plan.split("tiles=")[1].split()[0])
+        nt = 64 * (int(plan.split("BN=")[1].split()[0]) // int(plan.split("WN=")[1].split()[0])) \
+            * (int(plan.split("BM=")[1].split()[0]) // int(plan.split("WM=")[1].split()[0]))
+        return tiles * nt
+    return None
+
+
+def traffic_for(path, kernel_name, grid):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None
     if absent or taken on a different kernel source."""
     try:
@@ -246,7 +267,7 @@ def traffic_for(path, kernel_name):
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    e = t.get("kernels", {}).get(kernel_name)
+    e = t.get("kernels", {}).get(f"gemm_tiled_kernel@{grid}")
     if not e or sha != t.get("source_sha256"):
         return None
     return e.get("hbm_bytes_per_launch")
@@ -298,8 +319,117 @@ def decode_figure(torch, zq, dev, steps=100):
 
 
 # -------------------------------------------------------------------- main --
+# -------------------------------------------------------- profile summary --
+COPY_BYTES = 256 * 2 ** 20
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    for key in ("gemm_tiled_kernel", "gemm_skinny_kernel", "row_quant_kernel",
+                "weight_quant_kernel"):
+        if key in name:
+            return key
+    if "neg_kernel" in name:
+        return "copy"
+    return name[:40]
+
+
+def summarize(d, traffic_out=None):
+    """Per (kernel, grid) durations from a kernel trace and, when present,
+    FETCH_SIZE / WRITE_SIZE per dispatch scaled by the same counters of the
+    plain copy of COPY_BYTES bytes."""
+    import glob
+    import statistics as st
+    lines = []
+    for tr in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"),
+                               recursive=True)):
+        groups = {}
+        for r in _read_csv(tr):
+            k = (_short(r["Kernel_Name"]),
+                 int(r.get("Grid_Size_X") or r.get("Grid_Size")),
+                 int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size")))
+            groups.setdefault(k, []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines.append(f"kernel trace {os.path.relpath(tr, d)}")
+        lines.append("| kernel | grid (threads) | block | calls | avg us | "
+                     "median us |")
+        lines.append("|---|---|---|---|---|---|")
+        for (k, g, w), v in sorted(groups.items(), key=lambda x: -sum(x[1])):
+            lines.append(f"| {k} | {g} | {w} | {len(v)} | "
+                         f"{st.mean(v) / 1e3:.2f} | {st.median(v) / 1e3:.2f} |")
+    pmc = {}
+    for cc in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                               recursive=True)):
+        for r in _read_csv(cc):
+            cname = r["Counter_Name"]
+            if cname not in ("FETCH_SIZE", "WRITE_SIZE"):
+                continue
+            k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            pmc.setdefault(cname, {}).setdefault(k, {}).setdefault(
+                r["Dispatch_Id"], 0.0)
+            pmc[cname][k][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    traffic = {}
+    if pmc:
+        lines.append("")
+        lines.append("HBM counters (KiB per dispatch; factor = counter / true "
+                     f"bytes of the {COPY_BYTES >> 20} MiB copy)")
+        factors = {}
+        for cname, per in pmc.items():
+            cp = [v for (k, g), dd in per.items() if k == "copy"
+                  for v in dd.values()]
+            if cp:
+                factors[cname] = st.median(cp) * 1024 / COPY_BYTES
+        lines.append(f"factors: {json.dumps(factors)}")
+        lines.append("| counter | kernel | grid | dispatches | median KiB | "
+                     "scaled bytes |")
+        lines.append("|---|---|---|---|---|---|")
+        for cname, per in pmc.items():
+            f = factors.get(cname)
+            for (k, g), dd in sorted(per.items()):
+                med = st.median(dd.values())
+                scaled = med * 1024 / f if f else None
+                lines.append(f"| {cname} | {k} | {g} | {len(dd)} | {med:.0f} | "
+                             f"{'' if scaled is None else f'{scaled:.0f}'} |")
+                if scaled is not None and k.startswith(("gemm", "row_quant")):
+                    traffic.setdefault(f"{k}@{g}", {})[cname] = scaled
+    print("\n".join(lines))
+    if traffic_out and traffic:
+        src = os.path.join(ROOT, "int4_quantized_transformer_amd", "csrc",
+                           "zq_gemm.hip")
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        out = {"source": "zq_gemm.hip", "source_sha256": sha, "kernels": {}}
+        for key, v in traffic.items():
+            if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+                out["kernels"][key] = {
+                    "hbm_bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
+                    "fetch_bytes": round(v["FETCH_SIZE"]),
+                    "write_bytes": round(v["WRITE_SIZE"])}
+        with open(traffic_out, "w") as f:
+            json.dump(out, f, indent=1)
+
+
+def copy_calibration(torch, dev):
+    """A plain elementwise kernel that reads COPY_BYTES and writes
+    COPY_BYTES (torch.neg), three times."""
+    a = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=dev).normal_()
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.write_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
@@ -317,6 +447,8 @@ def main():
     M = wl.M[-1] if args.m_index is None else wl.M[args.m_index]
     zq.lib()
 
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     base, sets, R, per_set = build_sets(wl, M, dev, ROTATE_BYTES)
     stream = torch.cuda.current_stream()
     step_calls = [make_step(zq, s, wl, M, stream.cuda_stream) for s in sets]
@@ -380,7 +512,8 @@ def main():
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(bd[dom] * 1e3, 2)
     roof["algorithmic"] = {"ops": ops, "bytes": nbytes}
-    roof["traffic"] = traffic_for(args.traffic, dom)
+    roof["grid_threads"] = grid_threads(dom, Ld, M, wl.G, zq)
+    roof["traffic"] = traffic_for(args.traffic, dom, roof["grid_threads"])
 
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
