@@ -182,7 +182,12 @@ struct Tile {
   static constexpr int IW = WINS / NWAVES, IX = XINS / NWAVES;  // per wave
   static constexpr int WBYTES = BN * WROW, XBYTES = BM * XROW;
   static constexpr int STAGE = WBYTES + XBYTES;
-  static constexpr int LDS = S * STAGE;
+  // epilogue operands copied into LDS with stage 0: bias of the tile's BN
+  // columns and scales of its BM tokens, each padded to whole 256-byte wave
+  // copies (64 lanes x 4 bytes)
+  static constexpr int AUX_BIAS = ((BN * 2 + 255) / 256) * 256;
+  static constexpr int AUX_SX = ((BM * 4 + 255) / 256) * 256;
+  static constexpr int LDS = S * STAGE + AUX_BIAS + AUX_SX;
   static_assert(WINS % NWAVES == 0 && XINS % NWAVES == 0, "copy split");
   static_assert(WN % 32 == 0 && WM % 32 == 0 && S >= 2, "tile");
   static_assert((IW + IX) * (S - 2) < 64, "vmcnt range");
@@ -381,36 +386,45 @@ gemm_tiled_kernel(GemmArgs p) {
   const char *W = static_cast<const char *>(p.qw);
   const char *X = reinterpret_cast<const char *>(p.qx);
 
-  // Epilogue operands, read before the main loop so that their latency
-  // hides behind it (branch-free, clamped indices: no wait until used).
-  // Token scales: one per fragment column.  When 32 | G every 32-row weight
-  // fragment lies in one group: one scale per fragment.  Bias: 16 values
-  // per fragment (n = 8q + 4h + r).
-  float sxv[C::FM];
-  float swv[C::FN];
-  half4 bq[C::FN][4];
+  // Epilogue operands are fetched before the main loop so that their
+  // latency hides behind it (scales read before the multiplication ends).
+  // The tile's bias (BN halves) and token scales (BM floats) are copied by
+  // wave 0 straight into LDS, ahead of its stage-0 copies, so the stage-0
+  // wait and barrier also cover them.  Group scale: when 32 | G every
+  // 32-row weight fragment lies in one group, so one register per fragment.
+  char *aux = lds + C::S * C::STAGE;
   const bool g32 = (p.G & 31) == 0;
+  const bool bias_lds = p.bias && (p.N % 2 == 0) && (((uintptr_t)p.bias & 3) == 0);
+  float swv[C::FN];
   if constexpr (!RAW) {
+    if (wave == 0) {
+      if (bias_lds) {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int t = m0 + wm0 + fm * 32 + r32;
-      sxv[fm] = p.sx[t < p.M ? t : p.M - 1];
+        for (int j = 0; j < C::AUX_BIAS / 256; ++j) {
+          int n = n0 + 2 * (lane + 64 * j);
+          n = n < p.N ? n : p.N - 2;
+          __builtin_amdgcn_global_load_lds(ZQ_GPTR(p.bias + n),
+                                           ZQ_LPTR(aux + j * 256), 4, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < C::AUX_SX / 256; ++j) {
+        int t = m0 + lane + 64 * j;
+        t = t < p.M ? t : p.M - 1;
+        __builtin_amdgcn_global_load_lds(ZQ_GPTR(p.sx + t),
+                                         ZQ_LPTR(aux + C::AUX_BIAS + j * 256),
+                                         4, 0, 0);
+      }
     }
     const int lastg = (p.N - 1) / p.G;
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       const int gi = (n0 + wn0 + fn * 32) / p.G;
       swv[fn] = g32 ? p.sw[gi < lastg ? gi : lastg] : 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nb = n0 + wn0 + fn * 32 + 8 * q + 4 * h;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          bq[fn][q][r] = p.bias ? p.bias[nb + r < p.N ? nb + r : p.N - 1]
-                                : (half_t)0.0f;
-      }
     }
   }
+  const half_t *bias_l = reinterpret_cast<const half_t *>(aux);
+  const float *sx_l = reinterpret_cast<const float *>(aux + C::AUX_BIAS);
 
   v16i acc[C::FN][C::FM];
 #pragma unroll
@@ -465,34 +479,41 @@ gemm_tiled_kernel(GemmArgs p) {
     tail_stage<C>(ws, ws + C::WBYTES, wn0, wm0, r32, h, acc);
   }
 
-  if constexpr (!RAW && C::BM * C::BN * 2 <= C::LDS && C::BN >= 128) {
-    if (g32) {
+  if constexpr (!RAW && C::BM * C::BN * 2 <= C::S * C::STAGE && C::BN >= 64) {
+    if (g32 && (bias_lds || !p.bias)) {
       // Stage the fp16 tile through LDS so that every global store writes
-      // whole 256-byte row segments with 16 bytes per lane.  Layout: row t
-      // of the tile holds BN halves; its 16-byte chunks are XOR-swizzled by
-      // (t & 15) so that the 8-byte writes of 32 consecutive rows spread
+      // whole row segments with 16 bytes per lane.  Layout: row t of the
+      // tile holds BN halves; its 16-byte chunks are XOR-swizzled by
+      // (t & (SW-1)), SW the largest power of two dividing the chunk count
+      // (at most 16), so that the 8-byte writes of consecutive rows spread
       // over the banks.
       __syncthreads();  // every wave is done reading the operand stages
       constexpr int RB = C::BN * 2;  // bytes per tile row
+      constexpr int CPR0 = C::BN / 8;
+      constexpr int SW = (CPR0 % 16 == 0) ? 16 : (CPR0 % 8 == 0) ? 8 : 4;
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
           const int tl = wm0 + fm * 32 + r32;
-          const float sc = sxv[fm] * swv[fn];
+          const float sc = sx_l[tl] * swv[fn];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             half4 hv;
+            const int cl = wn0 + fn * 32 + 8 * q + 4 * h;  // tile column
+            const half4 bb = bias_lds
+                ? *reinterpret_cast<const half4 *>(bias_l + cl)
+                : half4{(half_t)0.0f, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               int a = acc[fn][fm][4 * q + r];
               if constexpr (C::W4) a >>= 4;
-              float z = fmaf((float)a, sc, (float)bq[fn][q][r]);
+              float z = fmaf((float)a, sc, (float)bb[r]);
               if (p.act == ZQ_ACT_GELU) z = gelu_erf(z);
               hv[r] = (half_t)z;
             }
             const int chunk = (wn0 + fn * 32) / 8 + q;
-            *reinterpret_cast<half4 *>(lds + tl * RB + ((chunk ^ (tl & 15)) << 4) + h * 8) = hv;
+            *reinterpret_cast<half4 *>(lds + tl * RB + ((chunk ^ (tl & (SW - 1))) << 4) + h * 8) = hv;
           }
         }
       __syncthreads();
@@ -503,7 +524,7 @@ gemm_tiled_kernel(GemmArgs p) {
         const int row = i / CPR, c = i % CPR;
         const int t = m0 + row, n = n0 + c * 8;
         if (t >= p.M || n >= p.N) continue;
-        const v4i v = ld16(lds + row * RB + ((c ^ (row & 15)) << 4));
+        const v4i v = ld16(lds + row * RB + ((c ^ (row & (SW - 1))) << 4));
         half_t *o = Y + (size_t)t * p.N + n;
         if (vec && n + 8 <= p.N) {
           *reinterpret_cast<v4i *>(o) = v;
@@ -529,18 +550,12 @@ gemm_tiled_kernel(GemmArgs p) {
         const v4i a = {acc[fn][fm][4 * q], acc[fn][fm][4 * q + 1],
                        acc[fn][fm][4 * q + 2], acc[fn][fm][4 * q + 3]};
         QuadCol qc;
+        float sxt = 0.0f;
         if constexpr (!RAW) {
-          if (g32) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              qc.sw[r] = swv[fn];
-              qc.b[r] = bq[fn][q][r];
-            }
-          } else {
-            qc = load_quad_col(p, nb);
-          }
+          qc = load_quad_col(p, nb);
+          sxt = p.sx[t < p.M ? t : p.M - 1];
         }
-        store_quad<C::W4, RAW>(p, t, nb, a, RAW ? 0.0f : sxv[fm], qc);
+        store_quad<C::W4, RAW>(p, t, nb, a, sxt, qc);
       }
     }
 }
@@ -709,6 +724,9 @@ static const TileCfg kTileCfgs[] = {
     {128, 128, 64, 64, 3},    // 4: 4 waves
     {256, 256, 128, 64, 2},   // 5: 8 waves
     {256, 128, 128, 64, 3},   // 6: 4 waves
+    {192, 256, 96, 128, 2},   // 7: 4 waves
+    {192, 128, 96, 64, 2},    // 8: 4 waves
+    {128, 192, 64, 96, 2},    // 9: 4 waves
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 
@@ -721,7 +739,10 @@ static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
     case 3: return run_tiled<Tile<256, 256, 128, 128, 2, W4>, RAW>(a, s);
     case 4: return run_tiled<Tile<128, 128, 64, 64, 3, W4>, RAW>(a, s);
     case 5: return run_tiled<Tile<256, 256, 128, 64, 2, W4>, RAW>(a, s);
-    default: return run_tiled<Tile<256, 128, 128, 64, 3, W4>, RAW>(a, s);
+    case 6: return run_tiled<Tile<256, 128, 128, 64, 3, W4>, RAW>(a, s);
+    case 7: return run_tiled<Tile<192, 256, 96, 128, 2, W4>, RAW>(a, s);
+    case 8: return run_tiled<Tile<192, 128, 96, 64, 2, W4>, RAW>(a, s);
+    default: return run_tiled<Tile<128, 192, 64, 96, 2, W4>, RAW>(a, s);
   }
 }
 
