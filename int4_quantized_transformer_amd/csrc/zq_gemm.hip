@@ -727,6 +727,9 @@ static const TileCfg kTileCfgs[] = {
     {192, 256, 96, 128, 2},   // 7: 4 waves
     {192, 128, 96, 64, 2},    // 8: 4 waves
     {128, 192, 64, 96, 2},    // 9: 4 waves
+    {256, 128, 64, 64, 3},    // 10: 8 waves
+    {128, 256, 64, 64, 3},    // 11: 8 waves
+    {256, 256, 64, 64, 2},    // 12: 16 waves
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 
@@ -742,7 +745,10 @@ static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
     case 6: return run_tiled<Tile<256, 128, 128, 64, 3, W4>, RAW>(a, s);
     case 7: return run_tiled<Tile<192, 256, 96, 128, 2, W4>, RAW>(a, s);
     case 8: return run_tiled<Tile<192, 128, 96, 64, 2, W4>, RAW>(a, s);
-    default: return run_tiled<Tile<128, 192, 64, 96, 2, W4>, RAW>(a, s);
+    case 9: return run_tiled<Tile<128, 192, 64, 96, 2, W4>, RAW>(a, s);
+    case 10: return run_tiled<Tile<256, 128, 64, 64, 3, W4>, RAW>(a, s);
+    case 11: return run_tiled<Tile<128, 256, 64, 64, 3, W4>, RAW>(a, s);
+    default: return run_tiled<Tile<256, 256, 64, 64, 2, W4>, RAW>(a, s);
   }
 }
 
@@ -764,21 +770,53 @@ static int forced_tile() {
   return v;
 }
 
-static Plan choose(int M, int /*N*/, int /*K*/, int /*bits*/) {
+// Schedule selection by problem shape (the pages pick, per batch x seqlen,
+// the tiling with the least waste): decode-sized M streams the weights
+// with the skinny kernel; otherwise 256x256 tiles (16 waves, half the
+// operand traffic per MFMA of 128x128 tiles) when W8 and there are enough
+// of them to occupy most of the 256 compute units, else 128x128 tiles with
+// two blocks per CU.  Chosen from measured sweeps over the five workloads.
+static Plan choose(int M, int N, int /*K*/, int bits) {
   if (M <= 64) return Plan{kSkinny, (M + 15) / 16, 0};
   const int f = forced_tile();
-  return Plan{kTiled, 0, f >= 0 ? f : 0};
+  if (f >= 0) return Plan{kTiled, 0, f};
+  const long tiles256 = (long)((N + 255) / 256) * ((M + 255) / 256);
+  if (bits == 8 && tiles256 >= 140) return Plan{kTiled, 0, 12};
+  return Plan{kTiled, 0, 0};
+}
+
+// Skinny configurations {BN, NW, U} per 16-token fragment count (tuning
+// aid: ZQ_SKINNY=<index> forces one).
+static int forced_skinny() {
+  static int v = [] {
+    const char *e = getenv("ZQ_SKINNY");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
+template <int MF, bool W4, bool RAW>
+static hipError_t run_skinny_mf(int id, const GemmArgs &a, hipStream_t s) {
+  switch (id) {
+    case 1: return run_skinny<Skinny<16, MF, 8, 8, W4>, RAW>(a, s);
+    case 2: return run_skinny<Skinny<16, MF, 16, 4, W4>, RAW>(a, s);
+    case 3: return run_skinny<Skinny<32, MF, 8, 4, W4>, RAW>(a, s);
+    case 4: return run_skinny<Skinny<16, MF, 4, 4, W4>, RAW>(a, s);
+    case 5: return run_skinny<Skinny<32, MF, 16, 2, W4>, RAW>(a, s);
+    default: return run_skinny<Skinny<16, MF, 8, (MF <= 2 ? 4 : 2), W4>, RAW>(a, s);
+  }
 }
 
 template <bool W4, bool RAW>
 static hipError_t run(const GemmArgs &a, hipStream_t s) {
   const Plan pl = choose(a.M, a.N, a.K, a.bits);
   if (pl.kind == kSkinny) {
+    const int id = forced_skinny();
     switch (pl.mf) {
-      case 1: return run_skinny<Skinny<16, 1, 8, 4, W4>, RAW>(a, s);
-      case 2: return run_skinny<Skinny<16, 2, 8, 4, W4>, RAW>(a, s);
-      case 3: return run_skinny<Skinny<16, 3, 8, 2, W4>, RAW>(a, s);
-      default: return run_skinny<Skinny<16, 4, 8, 2, W4>, RAW>(a, s);
+      case 1: return run_skinny_mf<1, W4, RAW>(id, a, s);
+      case 2: return run_skinny_mf<2, W4, RAW>(id, a, s);
+      case 3: return run_skinny_mf<3, W4, RAW>(id, a, s);
+      default: return run_skinny_mf<4, W4, RAW>(id, a, s);
     }
   }
   return run_tile_cfg<W4, RAW>(pl.cfg, a, s);
