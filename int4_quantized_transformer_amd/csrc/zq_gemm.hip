@@ -695,6 +695,472 @@ gemm_skinny_kernel(GemmArgs p) {
   }
 }
 
+// =============================================================== streaming
+// Decode-sized M (at most 64 tokens): the weight matrix is nearly all of the
+// bytes and must stream from HBM at full rate, which takes many bytes in
+// flight per compute unit.  Register-staged loads cannot hold enough of
+// them, so every wave runs its own ring of D LDS slots fed by
+// global_load_lds and waits on its own vmcnt only (no barrier per chunk).
+//
+// A row block is BN = 16*FN consecutive weight rows over all of K.  Blocks
+// are persistent: block b takes row blocks b, b + grid, ...  The bytes of
+// each weight row are cut into chunks of CK bytes and wave w of the block
+// takes chunks w, w + NW, ... of every row block, one after the other, so
+// its copies run on across row-block boundaries.  One copy instruction
+// moves 1 KB: 64 lanes x 16 consecutive bytes of 1024/CK rows, i.e. whole
+// 128-byte lines.  A slot holds, for one chunk:
+//   weights      [BN][CK] bytes (16-byte columns XOR-swizzled by row),
+//   activations  [MX][XCK] bytes, the chunk's k range of MX token rows
+//                (XCK = CK, or 2*CK for packed W4),
+//   epilogue aux 64*IA dwords: sx of the MX tokens, sw of the BN columns
+//                and bias pairs, gathered by 4-byte copies.
+// The aux copy rides in every chunk so that the copy count per chunk, and
+// with it every vmcnt wait, is a compile-time constant; at the end of a row
+// block the wave's last slot holds what the epilogue needs.
+//
+// K tails: copies past the end of a row read clamped (valid) addresses,
+// and the activation operand of every k past K is replaced by zero, so
+// those products vanish.  Tokens past M read row M-1 and are never stored.
+//
+// At the end of a row block each wave adds its int32 partial fragments into
+// an LDS buffer (exact, order-free), a barrier that waits on LDS only lets
+// the copies stay in flight, and the fragments are finished by the waves in
+// turn.  The buffer alternates between two halves by row-block parity, so
+// a half is cleared by its reader one barrier before it is used again.
+template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_>
+struct Stream {
+  static constexpr int FN = FN_, MX = MX_, NW = NW_, CK = CK_, D = D_;
+  static constexpr bool W4 = W4_;
+  static constexpr int BN = 16 * FN;
+  static constexpr int MF = (MX + 15) / 16;
+  static constexpr int NT = NW * kWave;
+  static constexpr int XCK = W4 ? 2 * CK : CK;
+  static constexpr int SPC = CK / 64;                // k-steps per chunk
+  static constexpr int IW = BN * CK / 1024;          // weight copies
+  static constexpr int IX = (MX * XCK + 1023) / 1024;  // activation copies
+  static constexpr int NAUX = MX + BN + BN / 2;      // aux dwords
+  static constexpr int IA = (NAUX + 63) / 64;        // aux copies
+  static constexpr int P = IW + IX + IA;             // copies per chunk
+  static constexpr int XOFF = IW * 1024, AOFF = (IW + IX) * 1024;
+  static constexpr int SLOT = AOFF + IA * 256;
+  static constexpr int RED = FN * MF * 1024;         // one half
+  static constexpr int LDS = NW * D * SLOT + 2 * RED;
+  static constexpr int WSW = (CK / 16 < 16 ? CK / 16 : 16) - 1;
+  static constexpr int XSW = (XCK / 16 < 16 ? XCK / 16 : 16) - 1;
+  static_assert(CK % 64 == 0 && (BN * CK) % 1024 == 0, "chunk");
+  static_assert(D >= 2 && (D - 1) * P < 64, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Workgroup barrier over LDS traffic that leaves the global->LDS copies in
+// flight: it waits for this wave's DS operations only (a release fence would
+// also wait for the copies, which are LDS writes too), and keeps the
+// compiler from moving memory accesses across it.  Correct only for LDS
+// data that no copy in flight writes.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no vmcnt wait
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS stores issued while global->LDS copies are in flight.  Written as
+// plain DS instructions because the compiler, unable to tell the
+// destinations apart, would otherwise wait for every copy in flight before
+// any LDS store.  The addresses never overlap a copy destination.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)ZQ_LPTR(p);
+}
+__device__ __forceinline__ void ds_add4(uint32_t addr, v4i v) {
+  asm volatile(
+      "ds_add_u32 %0, %1\n\t"
+      "ds_add_u32 %0, %2 offset:4\n\t"
+      "ds_add_u32 %0, %3 offset:8\n\t"
+      "ds_add_u32 %0, %4 offset:12"
+      :
+      : "v"(addr), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+      : "memory");
+}
+__device__ __forceinline__ void ds_zero16(uint32_t addr) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v4i{0, 0, 0, 0})
+               : "memory");
+}
+
+// Wait until at most `later` chunks of copies issued after the one needed
+// are still in flight.
+template <class C>
+__device__ __forceinline__ void wait_chunks(int later) {
+  if constexpr (C::D >= 4) {
+    if (later >= 3) { wait_vmcnt<3 * C::P>(); return; }
+  }
+  if constexpr (C::D >= 3) {
+    if (later >= 2) { wait_vmcnt<2 * C::P>(); return; }
+  }
+  if (later >= 1) { wait_vmcnt<C::P>(); return; }
+  wait_vmcnt<0>();
+}
+
+template <class C>
+__device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
+                                             const char *X, int ldw, int rb,
+                                             int c, char *slot, int lane) {
+  const int n0 = rb * C::BN;
+#pragma unroll
+  for (int q = 0; q < C::IW; ++q) {
+    const int o = q * 1024 + lane * 16;
+    const int row = o / C::CK;
+    const int col = ((o % C::CK) >> 4) ^ (row & C::WSW);
+    int n = n0 + row;
+    n = n < p.N ? n : p.N - 1;
+    int kb = c * C::CK + col * 16;
+    kb = kb < ldw ? kb : ldw - 16;
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + (size_t)n * ldw + kb),
+                                     ZQ_LPTR(slot + q * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < C::IX; ++q) {
+    const int o = q * 1024 + lane * 16;
+    int row = o / C::XCK;
+    row = row < C::MX ? row : C::MX - 1;       // padding lanes: duplicates
+    const int col = ((o % C::XCK) >> 4) ^ (row & C::XSW);
+    const int t = row < p.M ? row : p.M - 1;
+    int kb = c * C::XCK + col * 16;
+    kb = kb < p.K ? kb : p.K - 16;
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * p.K + kb),
+                                     ZQ_LPTR(slot + C::XOFF + q * 1024), 16,
+                                     0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < C::IA; ++q) {
+    const int e = q * 64 + lane;
+    const void *src = p.qw;                    // any valid dword
+    if (e < C::MX) {
+      if (p.sx) src = p.sx + (e < p.M ? e : p.M - 1);
+    } else if (e < C::MX + C::BN) {
+      int n = n0 + e - C::MX;
+      n = n < p.N ? n : p.N - 1;
+      if (p.sw) src = p.sw + n / p.G;
+    } else if (e < C::NAUX) {
+      int d = n0 / 2 + (e - C::MX - C::BN);    // bias dword: columns 2d, 2d+1
+      const int last = p.N / 2 - 1;            // N is even here
+      d = d < last ? d : last;
+      if (p.bias) src = reinterpret_cast<const int *>(p.bias) + d;
+    }
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(src),
+                                     ZQ_LPTR(slot + C::AOFF + q * 256), 4, 0,
+                                     0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void stream_compute(const GemmArgs &p,
+                                               const char *slot, int c,
+                                               int r16, int g,
+                                               v4i (&acc)[C::FN][C::MF]) {
+  const v4i zero = {0, 0, 0, 0};
+  const int k0 = c * (C::W4 ? 2 * C::CK : C::CK);
+#pragma unroll
+  for (int s = 0; s < C::SPC; ++s) {
+    v4i a[C::FN];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int row = fn * 16 + r16;
+      a[fn] = ld16(slot + row * C::CK + (((4 * s + g) ^ (row & C::WSW)) << 4));
+    }
+    if constexpr (!C::W4) {
+      const bool kok = k0 + 64 * s + 16 * g < p.K;
+#pragma unroll
+      for (int fm = 0; fm < C::MF; ++fm) {
+        int row = fm * 16 + r16;
+        row = row < p.M ? row : p.M - 1;
+        v4i b = ld16(slot + C::XOFF + row * C::XCK +
+                     (((4 * s + g) ^ (row & C::XSW)) << 4));
+        b = kok ? b : zero;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fn][fm] = mfma_i8(a[fn], b, acc[fn][fm]);
+      }
+    } else {
+      const bool kok = k0 + 128 * s + 32 * g < p.K;
+#pragma unroll
+      for (int fm = 0; fm < C::MF; ++fm) {
+        int row = fm * 16 + r16;
+        row = row < p.M ? row : p.M - 1;
+        const char *xr = slot + C::XOFF + row * C::XCK;
+        const int cx = 8 * s + 2 * g;
+        v4i b0 = ld16(xr + ((cx ^ (row & C::XSW)) << 4));
+        v4i b1 = ld16(xr + (((cx + 1) ^ (row & C::XSW)) << 4));
+        b0 = kok ? perm_even_odd(b0) : zero;
+        b1 = kok ? perm_even_odd(b1) : zero;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          acc[fn][fm] = mfma_i8(unpack_w4(a[fn][0], a[fn][1]), b0, acc[fn][fm]);
+          acc[fn][fm] = mfma_i8(unpack_w4(a[fn][2], a[fn][3]), b1, acc[fn][fm]);
+        }
+      }
+    }
+  }
+}
+
+template <class C, bool RAW>
+__global__ void __launch_bounds__(C::NT)
+gemm_stream_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int ldw = C::W4 ? p.K / 2 : p.K;
+  const char *W = static_cast<const char *>(p.qw);
+  const char *X = reinterpret_cast<const char *>(p.qx);
+  char *ring = lds + wave * (C::D * C::SLOT);
+  int *red = reinterpret_cast<int *>(lds + C::NW * C::D * C::SLOT);
+
+  const int NRB = (p.N + C::BN - 1) / C::BN;
+  const int NC = (ldw + C::CK - 1) / C::CK;            // chunks per row
+  const int ncw = NC > wave ? (NC - wave + C::NW - 1) / C::NW : 0;
+  const int nact = NC < C::NW ? NC : C::NW;            // waves with chunks
+  const int nrb = (NRB - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int total = ncw * nrb;
+
+  for (int i = threadIdx.x; i < 2 * C::RED / 4; i += C::NT) red[i] = 0;
+  lds_barrier();  // red[] cleared before any copy is issued
+
+  // copy cursor: chunk j_issue = (row block index ir, chunk index ic)
+  int j_issue = 0, ir = 0, ic = 0;
+  auto issue_next = [&]() {
+    stream_issue<C>(p, W, X, ldw, (int)blockIdx.x + ir * (int)gridDim.x,
+                    wave + ic * C::NW,
+                    ring + ((unsigned)j_issue % C::D) * C::SLOT, lane);
+    ++j_issue;
+    if (++ic == ncw) { ic = 0; ++ir; }
+  };
+#pragma unroll
+  for (int d = 0; d < C::D - 1; ++d)
+    if (j_issue < total) issue_next();
+
+  int j = 0;
+  for (int rbi = 0; rbi < nrb; ++rbi) {
+    const int rb = (int)blockIdx.x + rbi * (int)gridDim.x;
+    v4i acc[C::FN][C::MF];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < C::MF; ++fm) acc[fn][fm] = v4i{0, 0, 0, 0};
+
+    for (int ci = 0; ci < ncw; ++ci, ++j) {
+      if (j_issue < total) issue_next();
+      wait_chunks<C>(j_issue - 1 - j);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_compute<C>(p, ring + ((unsigned)j % C::D) * C::SLOT,
+                        wave + ci * C::NW, r16, g, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    int *rh = red + (rbi & 1) * (C::RED / 4);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < C::MF; ++fm)
+        ds_add4(lds_addr(&rh[((fn * C::MF + fm) * kWave + lane) * 4]),
+                acc[fn][fm]);
+    lds_barrier();
+
+    if (wave < nact) {
+      // the aux dwords of this row block sit in the slot of this wave's
+      // last chunk of it
+      const int *aux = reinterpret_cast<const int *>(
+          ring + ((unsigned)(j - 1) % C::D) * C::SLOT + C::AOFF);
+      for (int pr = wave; pr < C::FN * C::MF; pr += nact) {
+        const int fn = pr / C::MF, fm = pr % C::MF;
+        int *rp = &rh[(pr * kWave + lane) * 4];
+        const v4i a = *reinterpret_cast<const v4i *>(rp);
+        ds_zero16(lds_addr(rp));
+        const int t = fm * 16 + r16;
+        const int cb = fn * 16 + 4 * g;          // column within the row block
+        const int nb = rb * C::BN + cb;
+        QuadCol qc;
+        float sxt = 0.0f;
+        if constexpr (!RAW) {
+          sxt = __int_as_float(aux[t < p.M ? t : p.M - 1]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            qc.sw[r] = __int_as_float(aux[C::MX + cb + r]);
+            const int bw = aux[C::MX + C::BN + (cb + r) / 2];
+            const uint16_t hb = (uint16_t)(((cb + r) & 1) ? (bw >> 16) : bw);
+            qc.b[r] = p.bias ? __builtin_bit_cast(half_t, hb) : (half_t)0.0f;
+          }
+        }
+        store_quad<C::W4, RAW>(p, t, nb, a, sxt, qc);
+      }
+    }
+  }
+}
+
+// Number of compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <class C, bool RAW>
+static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
+  const int nrb = (a.N + C::BN - 1) / C::BN;
+  const int cus = device_cus();
+  const int grid = nrb < cus ? nrb : cus;
+  hipLaunchKernelGGL((gemm_stream_kernel<C, RAW>), dim3(grid), dim3(C::NT), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+// ==================================================================== gemv
+// One token (M = 1): y[n] = dot(W[n, :], x).  MFMA would waste 15/16 of its
+// work here, and the 16-row operand it needs makes every copy touch 16 rows;
+// reading each weight row front to back in long runs is what lets HBM
+// deliver its full rate.  So wave w of a block owns whole rows (the block's
+// rows r0 + w, r0 + w + NW, ...: the NW waves read NW consecutive rows, one
+// contiguous window), loads 1 KB pieces of its rows into registers (16
+// bytes per lane) with U pieces in flight, and multiplies them with
+// v_dot4_i32_i8 against the matching activation bytes, which are re-read
+// from the caches.  A row's 64 lane sums are added with DPP and kept in
+// LDS; the epilogue runs once at the end of the block, after the weight
+// stream, so that no scale or bias load waits behind weight loads.
+//
+// W4: the packed bytes are split as in the MFMA kernels into 16*q words
+// (even k / odd k), the activation bytes permuted to match, and the row sum
+// shifted right by 4 at the end.  Rows must be a whole number of 1 KB pieces
+// (K % 1024 == 0 for W8, K % 2048 == 0 for W4).
+template <int NW_, int U_, bool W4_>
+struct Gemv {
+  static constexpr int NW = NW_, U = U_;
+  static constexpr bool W4 = W4_;
+  static constexpr int NT = NW * kWave;
+  static constexpr int RMAX = 1024;  // rows per block
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_i<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_i<0x141>(v);  // row_half_mirror
+  v += dpp_i<0x140>(v);  // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ __forceinline__ int dot16(v4i w, v4i x, int acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_sdot4(w[i], x[i], acc, false);
+  return acc;
+}
+
+template <class C, bool RAW>
+__global__ void __launch_bounds__(C::NT)
+gemm_gemv_kernel(GemmArgs p, int rpb) {
+  __shared__ int rowsum[C::RMAX];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ldw = C::W4 ? p.K / 2 : p.K;
+  const int r0 = (int)blockIdx.x * rpb;
+  const int r1 = r0 + rpb < p.N ? r0 + rpb : p.N;
+  const int nrw = r1 - r0 > wave ? (r1 - r0 - wave + C::NW - 1) / C::NW : 0;
+  const int npieces = nrw * (ldw >> 10);
+  const char *W = static_cast<const char *>(p.qw);
+  const char *X = reinterpret_cast<const char *>(p.qx);
+
+  v4i wv[C::U];
+  v4i xv[C::U][C::W4 ? 2 : 1];
+  // load cursor: row lr, byte offset lk within it, pieces issued li
+  int lr = r0 + wave, lk = 0, li = 0;
+  auto load = [&](int u) {
+    // past the last piece: reload the last one (never used)
+    const int row = li < npieces ? lr : lr - C::NW;
+    const int kb = li < npieces ? lk : ldw - 1024;
+    const char *wp = W + (size_t)row * ldw + kb + lane * 16;
+    wv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wp));
+    if constexpr (C::W4) {
+      xv[u][0] = ld16(X + 2 * (kb + lane * 16));
+      xv[u][1] = ld16(X + 2 * (kb + lane * 16) + 16);
+    } else {
+      xv[u][0] = ld16(X + kb + lane * 16);
+    }
+    if (li < npieces) {
+      ++li;
+      lk += 1024;
+      if (lk == ldw) { lk = 0; lr += C::NW; }
+    }
+  };
+  if (npieces > 0) {
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) load(u);
+  }
+
+  int acc = 0, ck = 0, crow = wave;  // compute cursor (crow: row - r0)
+  for (int c0 = 0; c0 < npieces; c0 += C::U) {
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      if (c0 + u < npieces) {
+        if constexpr (C::W4) {
+          acc = dot16(unpack_w4(wv[u][0], wv[u][1]), perm_even_odd(xv[u][0]), acc);
+          acc = dot16(unpack_w4(wv[u][2], wv[u][3]), perm_even_odd(xv[u][1]), acc);
+        } else {
+          acc = dot16(wv[u], xv[u][0], acc);
+        }
+        ck += 1024;
+        if (ck == ldw) {
+          const int s = wave_sum_i(acc);
+          if (lane == 0) rowsum[crow] = C::W4 ? (s >> 4) : s;
+          acc = 0;
+          ck = 0;
+          crow += C::NW;
+        }
+      }
+      load(u);
+    }
+  }
+  __syncthreads();
+
+  // epilogue over the block's rows, consecutive threads on consecutive n
+  for (int i = threadIdx.x; i < r1 - r0; i += C::NT) {
+    const int n = r0 + i;
+    const int a = rowsum[i];
+    if constexpr (RAW) {
+      static_cast<int32_t *>(p.out)[n] = a;
+    } else {
+      const float b = p.bias ? (float)p.bias[n] : 0.0f;
+      float z = fmaf((float)a, p.sx[0] * p.sw[n / p.G], b);
+      if (p.act == ZQ_ACT_GELU) z = gelu_erf(z);
+      static_cast<half_t *>(p.out)[n] = (half_t)z;
+    }
+  }
+}
+
+template <class C, bool RAW>
+static hipError_t run_gemv(const GemmArgs &a, hipStream_t s) {
+  const int cus = device_cus();
+  int grid = 2 * cus;
+  if (grid > a.N) grid = a.N;
+  int rpb = (a.N + grid - 1) / grid;
+  if (rpb > C::RMAX) rpb = C::RMAX;
+  grid = (a.N + rpb - 1) / rpb;
+  hipLaunchKernelGGL((gemm_gemv_kernel<C, RAW>), dim3(grid), dim3(C::NT), 0,
+                     s, a, rpb);
+  return hipGetLastError();
+}
+
 // ================================================================ dispatch
 template <class C, bool RAW>
 static hipError_t run_tiled(const GemmArgs &a, hipStream_t s) {
@@ -752,7 +1218,7 @@ static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
   }
 }
 
-enum PlanKind { kSkinny = 0, kTiled = 1 };
+enum PlanKind { kSkinny = 0, kTiled = 1, kStream = 2, kGemv = 3 };
 struct Plan {
   PlanKind kind;
   int mf;   // skinny: 16-token fragments
@@ -776,8 +1242,28 @@ static int forced_tile() {
 // operand traffic per MFMA of 128x128 tiles) when W8 and there are enough
 // of them to occupy most of the 256 compute units, else 128x128 tiles with
 // two blocks per CU.  Chosen from measured sweeps over the five workloads.
-static Plan choose(int M, int N, int /*K*/, int bits) {
-  if (M <= 64) return Plan{kSkinny, (M + 15) / 16, 0};
+// ZQ_DECODE=<kind> forces the decode kernel (tuning aid): 0 skinny,
+// 2 stream, 3 gemv (each only where it applies).
+static int forced_decode() {
+  static int v = [] {
+    const char *e = getenv("ZQ_DECODE");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
+static Plan choose(int M, int N, int K, int bits) {
+  if (M <= 64) {
+    const int fd = forced_decode();
+    const int ldw = bits == 4 ? K / 2 : K;
+    const bool gemv_ok = M == 1 && ldw % 1024 == 0;
+    const bool stream_ok = M <= 16 && (N & 1) == 0;
+    if (fd == 0) return Plan{kSkinny, (M + 15) / 16, 0};
+    if (fd == 2 && stream_ok) return Plan{kStream, M == 1 ? 1 : 16, 0};
+    if (gemv_ok) return Plan{kGemv, 1, 0};
+    if (stream_ok) return Plan{kStream, M == 1 ? 1 : 16, 0};
+    return Plan{kSkinny, (M + 15) / 16, 0};
+  }
   const int f = forced_tile();
   if (f >= 0) return Plan{kTiled, 0, f};
   const long tiles256 = (long)((N + 255) / 256) * ((M + 255) / 256);
@@ -810,6 +1296,12 @@ static hipError_t run_skinny_mf(int id, const GemmArgs &a, hipStream_t s) {
 template <bool W4, bool RAW>
 static hipError_t run(const GemmArgs &a, hipStream_t s) {
   const Plan pl = choose(a.M, a.N, a.K, a.bits);
+  if (pl.kind == kGemv) return run_gemv<Gemv<4, 8, W4>, RAW>(a, s);
+  if (pl.kind == kStream) {
+    if (pl.mf == 1) return run_stream<Stream<1, 1, 4, 512, 4, W4>, RAW>(a, s);
+    if constexpr (W4) return run_stream<Stream<1, 16, 4, 256, 3, W4>, RAW>(a, s);
+    else return run_stream<Stream<1, 16, 4, 256, 4, W4>, RAW>(a, s);
+  }
   if (pl.kind == kSkinny) {
     const int id = forced_skinny();
     switch (pl.mf) {
@@ -830,6 +1322,11 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
 
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
   const Plan pl = choose(M, N, K, bits);
+  if (pl.kind == kGemv)
+    return snprintf(buf, len, "gemv NW=4 U=8 W%d rows=%d", bits, N);
+  if (pl.kind == kStream)
+    return snprintf(buf, len, "stream BN=16 MX=%d NW=4 W%d row_blocks=%d",
+                    pl.mf, bits, (N + 15) / 16);
   if (pl.kind == kSkinny)
     return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d",
                     pl.mf, pl.mf <= 2 ? 4 : 2, bits, (N + 15) / 16);

@@ -23,6 +23,7 @@ SHAPES = [  # (M, N, K)
     (33, 48, 640), (63, 64, 64), (64, 4096, 128), (64, 100, 1024),
     (65, 320, 576), (128, 128, 128), (200, 384, 1024), (257, 200, 64),
     (300, 1000, 640), (512, 768, 3072), (1, 4096, 4096), (7, 64, 24576),
+    (1, 1000, 1024), (1, 77, 2048), (1, 3000, 8192), (16, 24, 2048),
 ]
 
 
@@ -75,7 +76,8 @@ def test_i32_extreme_codes(M, bits):
 @pytest.mark.parametrize("M,N,K,G", [
     (16, 256, 256, 64), (1, 4096, 1024, 128), (5, 384, 768, 128),
     (64, 512, 512, 64), (100, 320, 192, 64), (300, 768, 768, 64),
-    (257, 1000, 320, 8), (2048, 256, 512, 128), (3, 20, 64, 4)])
+    (257, 1000, 320, 8), (2048, 256, 512, 128), (3, 20, 64, 4),
+    (1, 2048, 4096, 64), (1, 72, 2048, 8)])
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("bias,act", [(True, 0), (True, 1), (False, 1),
                                       (False, 0)])
@@ -107,9 +109,10 @@ def test_empty_m_is_a_no_op():
     assert acc.shape == (0, 64)
 
 
-def test_plans_used_by_tests_cover_both_kernels():
-    plans = {zq.gemm_plan(M, N, K, 8).split()[0] for M, N, K in SHAPES}
-    assert plans == {"skinny", "tiled"}
+def test_plans_used_by_tests_cover_every_kernel():
+    for bits in (8, 4):
+        plans = {zq.gemm_plan(M, N, K, bits).split()[0] for M, N, K in SHAPES}
+        assert plans == {"gemv", "stream", "skinny", "tiled"}, bits
 
 
 @pytest.mark.parametrize("M", [40, 256])
