@@ -1025,27 +1025,36 @@ static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
 
 // ==================================================================== gemv
 // One token (M = 1): y[n] = dot(W[n, :], x).  MFMA would waste 15/16 of its
-// work here, and the 16-row operand it needs makes every copy touch 16 rows;
-// reading each weight row front to back in long runs is what lets HBM
-// deliver its full rate.  So wave w of a block owns whole rows (the block's
-// rows r0 + w, r0 + w + NW, ...: the NW waves read NW consecutive rows, one
-// contiguous window), loads 1 KB pieces of its rows into registers (16
-// bytes per lane) with U pieces in flight, and multiplies them with
-// v_dot4_i32_i8 against the matching activation bytes, which are re-read
-// from the caches.  A row's 64 lane sums are added with DPP and kept in
-// LDS; the epilogue runs once at the end of the block, after the weight
-// stream, so that no scale or bias load waits behind weight loads.
+// work here, and the 16-row operand it needs makes every copy touch 16 rows
+// at once; HBM delivers its full rate only when reads run through long
+// contiguous windows.  So block b owns the rows [r0, r1), one contiguous
+// byte range of W, cut into 1 KB pieces; wave w takes pieces w, w + NW, ...
+// (the block's waves read one contiguous window), loads them into registers
+// (16 bytes per lane, non-temporal: read once) with U pieces in flight, and
+// multiplies them with v_dot4_i32_i8 against the matching activation bytes.
+// The activation row (K bytes) is copied into LDS once at the start when it
+// fits, else re-read from the caches.  A wave's
+// sum for a row (DPP across the wave) is added into an LDS row sum; the
+// epilogue runs once at the end of the block, with its scale and bias
+// operands loaded before the weight stream.
 //
 // W4: the packed bytes are split as in the MFMA kernels into 16*q words
 // (even k / odd k), the activation bytes permuted to match, and the row sum
 // shifted right by 4 at the end.  Rows must be a whole number of 1 KB pieces
 // (K % 1024 == 0 for W8, K % 2048 == 0 for W4).
-template <int NW_, int U_, bool W4_>
+template <int NW_, int U_, bool W4_, int XR_>
 struct Gemv {
   static constexpr int NW = NW_, U = U_;
   static constexpr bool W4 = W4_;
   static constexpr int NT = NW * kWave;
-  static constexpr int RMAX = 1024;  // rows per block
+  static constexpr int RMAX = 1024;   // rows per block
+  // XR > 0: the activation row (at most XMAX bytes) is held in LDS, loaded
+  // as XR 16-byte pieces per thread
+  static constexpr int XR = XR_;
+  static constexpr bool XL = XR > 0;
+  static constexpr int XMAX = XR * NT * 16;
+  static constexpr int L = XL ? 1 : (W4 ? 3 : 2);  // loads per piece
+  static_assert(U * L < 64, "vmcnt range");
 };
 
 template <int CTRL>
@@ -1067,97 +1076,188 @@ __device__ __forceinline__ int dot16(v4i w, v4i x, int acc) {
   return acc;
 }
 
+__device__ __forceinline__ void ds_add1(uint32_t addr, int v) {
+  asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 template <class C, bool RAW>
 __global__ void __launch_bounds__(C::NT)
-gemm_gemv_kernel(GemmArgs p, int rpb) {
+gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
   __shared__ int rowsum[C::RMAX];
+  __shared__ __attribute__((aligned(1024))) char xs[C::XL ? C::XMAX : 16];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ldw = C::W4 ? p.K / 2 : p.K;
+  const int ppr = ldw >> 10;                   // pieces per row
   const int r0 = (int)blockIdx.x * rpb;
   const int r1 = r0 + rpb < p.N ? r0 + rpb : p.N;
-  const int nrw = r1 - r0 > wave ? (r1 - r0 - wave + C::NW - 1) / C::NW : 0;
-  const int npieces = nrw * (ldw >> 10);
+  // piece order of a wave: interleaved (pieces wave, wave + NW, ... of the
+  // block's range: one contiguous window per block) or by rows (all pieces
+  // of rows wave, wave + NW, ...: one flush per row)
+  int npieces;
+  if (interleave) {
+    const int tot = (r1 - r0) * ppr;
+    npieces = tot > wave ? (tot - wave + C::NW - 1) / C::NW : 0;
+  } else {
+    const int nrw = r1 - r0 > wave ? (r1 - r0 - wave + C::NW - 1) / C::NW : 0;
+    npieces = nrw * ppr;
+  }
   const char *W = static_cast<const char *>(p.qw);
   const char *X = reinterpret_cast<const char *>(p.qx);
 
-  v4i wv[C::U];
-  v4i xv[C::U][C::W4 ? 2 : 1];
-  // load cursor: row lr, byte offset lk within it, pieces issued li
-  int lr = r0 + wave, lk = 0, li = 0;
-  auto load = [&](int u) {
-    // past the last piece: reload the last one (never used)
-    const int row = li < npieces ? lr : lr - C::NW;
-    const int kb = li < npieces ? lk : ldw - 1024;
-    const char *wp = W + (size_t)row * ldw + kb + lane * 16;
-    wv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wp));
-    if constexpr (C::W4) {
-      xv[u][0] = ld16(X + 2 * (kb + lane * 16));
-      xv[u][1] = ld16(X + 2 * (kb + lane * 16) + 16);
-    } else {
-      xv[u][0] = ld16(X + kb + lane * 16);
-    }
-    if (li < npieces) {
-      ++li;
-      lk += 1024;
-      if (lk == ldw) { lk = 0; lr += C::NW; }
-    }
-  };
-  if (npieces > 0) {
+  // row sums cleared before any copy into LDS is issued
+  for (int i = threadIdx.x; i < r1 - r0; i += C::NT) rowsum[i] = 0;
+
+  // epilogue operands of the rows this thread finishes (i = tid + e*NT)
+  // (kept as loaded bits, not converted, so that nothing waits for them
+  // here; without a bias a valid dummy is read and ignored)
+  constexpr int E = C::RMAX / C::NT;
+  float esw[E];
+  uint16_t ebits[E];
+  float esx = 0.0f;
+  if constexpr (!RAW) {
+    esx = p.sx[0];
 #pragma unroll
-    for (int u = 0; u < C::U; ++u) load(u);
+    for (int e = 0; e < E; ++e) {
+      int n = r0 + (int)threadIdx.x + e * C::NT;
+      n = n < r1 ? n : r1 - 1;
+      esw[e] = p.sw[n / p.G];
+      ebits[e] = *(p.bias ? reinterpret_cast<const uint16_t *>(p.bias) + n
+                          : reinterpret_cast<const uint16_t *>(p.sw));
+    }
   }
 
-  int acc = 0, ck = 0, crow = wave;  // compute cursor (crow: row - r0)
+  // activation row: loaded now (clamped, unconditional), stored into LDS
+  // after the first weight loads are in flight
+  constexpr int XR = C::XL ? C::XR : 1;
+  v4i xr[XR];
+  if constexpr (C::XL) {
+#pragma unroll
+    for (int e = 0; e < XR; ++e) {
+      const int off = (e * C::NT + (int)threadIdx.x) * 16;
+      xr[e] = ld16(X + (off < p.K ? off : p.K - 16));
+    }
+  }
+
+  v4i wv[C::U];
+  v4i xv[C::U][C::XL ? 1 : (C::W4 ? 2 : 1)];
+  // load cursor: piece wave + NW*li = row lr (relative to r0), piece lp of
+  // that row; it stays on the last piece once there (extra loads re-read
+  // it and are never used)
+  // cursor step: sp pieces and sr rows, plus wr rows when the piece index
+  // wraps past the row end
+  const int sp = interleave ? C::NW - (C::NW / ppr) * ppr : 1;
+  const int sr = interleave ? C::NW / ppr : 0;
+  const int wr = interleave ? 1 : C::NW;
+  const int lr0 = interleave ? wave / ppr : wave;
+  const int lp0 = interleave ? wave - (wave / ppr) * ppr : 0;
+  int li = 0, lr = lr0, lp = lp0;
+  auto load = [&](int u) {
+    const int kb = lp << 10;
+    const int row = r0 + lr < r1 ? r0 + lr : r1 - 1;  // (a wave without pieces)
+    const char *wp = W + (size_t)row * ldw + kb + lane * 16;
+    wv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wp));
+    if constexpr (!C::XL) {
+      if constexpr (C::W4) {
+        xv[u][0] = ld16(X + 2 * (kb + lane * 16));
+        xv[u][1] = ld16(X + 2 * (kb + lane * 16) + 16);
+      } else {
+        xv[u][0] = ld16(X + kb + lane * 16);
+      }
+    }
+    {
+      const bool adv = li < npieces - 1;
+      int np = lp + sp, nr = lr + sr;
+      const bool wrap = np >= ppr;
+      np = wrap ? np - ppr : np;
+      nr = wrap ? nr + wr : nr;
+      lp = adv ? np : lp;
+      lr = adv ? nr : lr;
+    }
+    ++li;
+  };
+#pragma unroll
+  for (int u = 0; u < C::U; ++u) load(u);
+  if constexpr (C::XL) {
+#pragma unroll
+    for (int e = 0; e < XR; ++e) {
+      const int off = (e * C::NT + (int)threadIdx.x) * 16;
+      if (off < p.K) *reinterpret_cast<v4i *>(xs + off) = xr[e];
+    }
+  }
+  lds_barrier();  // activation row and cleared row sums visible
+
+  int acc = 0, ci = 0, cr = lr0, cp = lp0;
   for (int c0 = 0; c0 < npieces; c0 += C::U) {
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       if (c0 + u < npieces) {
+        const int kb = cp << 10;
         if constexpr (C::W4) {
-          acc = dot16(unpack_w4(wv[u][0], wv[u][1]), perm_even_odd(xv[u][0]), acc);
-          acc = dot16(unpack_w4(wv[u][2], wv[u][3]), perm_even_odd(xv[u][1]), acc);
+          v4i x0, x1;
+          if constexpr (C::XL) {
+            x0 = ld16(xs + 2 * kb + lane * 32);
+            x1 = ld16(xs + 2 * kb + lane * 32 + 16);
+          } else {
+            x0 = xv[u][0];
+            x1 = xv[u][1];
+          }
+          acc = dot16(unpack_w4(wv[u][0], wv[u][1]), perm_even_odd(x0), acc);
+          acc = dot16(unpack_w4(wv[u][2], wv[u][3]), perm_even_odd(x1), acc);
         } else {
-          acc = dot16(wv[u], xv[u][0], acc);
+          const v4i x0 = C::XL ? ld16(xs + kb + lane * 16) : xv[u][0];
+          acc = dot16(wv[u], x0, acc);
         }
-        ck += 1024;
-        if (ck == ldw) {
-          const int s = wave_sum_i(acc);
-          if (lane == 0) rowsum[crow] = C::W4 ? (s >> 4) : s;
+        // next piece of this wave; flush the row sum when the row changes
+        const int row = cr;
+        cp += sp;
+        cr += sr;
+        const bool wrap = cp >= ppr;
+        cp = wrap ? cp - ppr : cp;
+        cr = wrap ? cr + wr : cr;
+        if (cr != row || ci == npieces - 1) {
+          const int sum = wave_sum_i(acc);
+          if (lane == 0) ds_add1(lds_addr(&rowsum[row]), C::W4 ? (sum >> 4) : sum);
           acc = 0;
-          ck = 0;
-          crow += C::NW;
         }
+        ++ci;
       }
       load(u);
     }
   }
-  __syncthreads();
+  lds_barrier();  // row sums complete (the trailing re-reads stay in flight)
 
   // epilogue over the block's rows, consecutive threads on consecutive n
-  for (int i = threadIdx.x; i < r1 - r0; i += C::NT) {
-    const int n = r0 + i;
-    const int a = rowsum[i];
-    if constexpr (RAW) {
-      static_cast<int32_t *>(p.out)[n] = a;
-    } else {
-      const float b = p.bias ? (float)p.bias[n] : 0.0f;
-      float z = fmaf((float)a, p.sx[0] * p.sw[n / p.G], b);
-      if (p.act == ZQ_ACT_GELU) z = gelu_erf(z);
-      static_cast<half_t *>(p.out)[n] = (half_t)z;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = (int)threadIdx.x + e * C::NT;
+    if (i < r1 - r0) {
+      const int n = r0 + i;
+      const int a = rowsum[i];
+      if constexpr (RAW) {
+        static_cast<int32_t *>(p.out)[n] = a;
+      } else {
+        const float b =
+            p.bias ? (float)__builtin_bit_cast(half_t, ebits[e]) : 0.0f;
+        float z = fmaf((float)a, esx * esw[e], b);
+        if (p.act == ZQ_ACT_GELU) z = gelu_erf(z);
+        static_cast<half_t *>(p.out)[n] = (half_t)z;
+      }
     }
   }
 }
 
 template <class C, bool RAW>
-static hipError_t run_gemv(const GemmArgs &a, hipStream_t s) {
+static hipError_t run_gemv(const GemmArgs &a, hipStream_t s, int bpc,
+                           int interleave) {
   const int cus = device_cus();
-  int grid = 2 * cus;
+  int grid = bpc * cus;
   if (grid > a.N) grid = a.N;
   int rpb = (a.N + grid - 1) / grid;
   if (rpb > C::RMAX) rpb = C::RMAX;
   grid = (a.N + rpb - 1) / rpb;
   hipLaunchKernelGGL((gemm_gemv_kernel<C, RAW>), dim3(grid), dim3(C::NT), 0,
-                     s, a, rpb);
+                     s, a, rpb, interleave);
   return hipGetLastError();
 }
 
@@ -1252,6 +1352,14 @@ static int forced_decode() {
   return v;
 }
 
+static int forced_gemv() {
+  static int v = [] {
+    const char *e = getenv("ZQ_GEMV");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
 static Plan choose(int M, int N, int K, int bits) {
   if (M <= 64) {
     const int fd = forced_decode();
@@ -1296,7 +1404,27 @@ static hipError_t run_skinny_mf(int id, const GemmArgs &a, hipStream_t s) {
 template <bool W4, bool RAW>
 static hipError_t run(const GemmArgs &a, hipStream_t s) {
   const Plan pl = choose(a.M, a.N, a.K, a.bits);
-  if (pl.kind == kGemv) return run_gemv<Gemv<4, 8, W4>, RAW>(a, s);
+  if (pl.kind == kGemv) {
+    // activation row in LDS when it fits in 8 KB (2 pieces per thread) or
+    // 32 KB (8 pieces)
+    const int xcls = a.K <= 8192 ? 1 : (a.K <= 32768 ? 2 : 0);
+    // default: pieces by rows, activation row in LDS, 6 pieces in flight
+    // (ZQ_GEMV=<bits> overrides: 1 interleave, 2 LDS activations, 4 U=6)
+    const int f = forced_gemv() >= 0 ? forced_gemv() : 6;
+    const int il = f & 1;
+    const int xsel = ((f >> 1) & 1) * xcls;
+    const int u6 = (f >> 2) & 1;
+    if (xsel == 1) {
+      if (u6) return run_gemv<Gemv<4, 6, W4, 2>, RAW>(a, s, 2, il);
+      return run_gemv<Gemv<4, 8, W4, 2>, RAW>(a, s, 2, il);
+    }
+    if (xsel == 2) {
+      if (u6) return run_gemv<Gemv<4, 6, W4, 8>, RAW>(a, s, 2, il);
+      return run_gemv<Gemv<4, 8, W4, 8>, RAW>(a, s, 2, il);
+    }
+    if (u6) return run_gemv<Gemv<4, 6, W4, 0>, RAW>(a, s, 2, il);
+    return run_gemv<Gemv<4, 8, W4, 0>, RAW>(a, s, 2, il);
+  }
   if (pl.kind == kStream) {
     if (pl.mf == 1) return run_stream<Stream<1, 1, 4, 512, 4, W4>, RAW>(a, s);
     if constexpr (W4) return run_stream<Stream<1, 16, 4, 256, 3, W4>, RAW>(a, s);
@@ -1323,7 +1451,8 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
   const Plan pl = choose(M, N, K, bits);
   if (pl.kind == kGemv)
-    return snprintf(buf, len, "gemv NW=4 U=8 W%d rows=%d", bits, N);
+    return snprintf(buf, len, "gemv NW=4 U=6 W%d rows=%d x_in_lds=%d", bits,
+                    N, K <= 32768 ? 1 : 0);
   if (pl.kind == kStream)
     return snprintf(buf, len, "stream BN=16 MX=%d NW=4 W%d row_blocks=%d",
                     pl.mf, bits, (N + 15) / 16);
