@@ -198,10 +198,13 @@ __device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ int sw128(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int sw64(int row) { return (row >> 2) & 3; }
+
 template <int BYTES>
 __device__ __forceinline__ int wswz(int chunk, int row) {
-  if constexpr (BYTES == 128) return chunk ^ (row & 7);
-  else return chunk ^ ((row >> 1) & 3);
+  if constexpr (BYTES == 128) return chunk ^ sw128(row);
+  else return chunk ^ sw64(row);
 }
 
 template <class C>
@@ -267,7 +270,7 @@ template <class C>
 __device__ __forceinline__ void fetch(const char *ws, const char *xs, int s,
                                       int wn0, int wm0, int r32, int h,
                                       Frag<C> &f, v4i (&raw)[2][C::FN]) {
-  const int x7 = r32 & 7;
+  const int x7 = sw128(r32);
   if constexpr (!C::W4) {
     const int c = 2 * s + h;
 #pragma unroll
@@ -277,7 +280,7 @@ __device__ __forceinline__ void fetch(const char *ws, const char *xs, int s,
     for (int fm = 0; fm < C::FM; ++fm)
       f.b[fm] = ld16(xs + (wm0 + fm * 32 + r32) * 128 + ((c ^ x7) << 4));
   } else {
-    const int w4 = (r32 >> 1) & 3;
+    const int w4 = sw64(r32);
     if (s == 0 || s == 2) {
       const int pc = 2 * h + (s >> 1);
 #pragma unroll
@@ -322,8 +325,8 @@ template <class C>
 __device__ __forceinline__ void tail_stage(const char *ws, const char *xs,
                                            int wn0, int wm0, int r32, int h,
                                            v16i (&acc)[C::FN][C::FM]) {
-  const int x7 = r32 & 7;
-  const int w4 = (r32 >> 1) & 3;
+  const int x7 = sw128(r32);
+  const int w4 = sw64(r32);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     v4i a[C::FN], b[C::FM];

@@ -100,6 +100,44 @@ __device__ __forceinline__ int quant_code(float v, const Quantizer &z) {
   return (int)__builtin_rintf(x);
 }
 
+// Eight values at once, with the same results as quant_code: q0 = rint(x)
+// for x = fl(v * r); x lies within 2^-15 of a half-integer exactly when
+// |x - q0| >= 0.5 - 2^-15 (x - q0 is exact), and then the eight are redone
+// with the IEEE division.  rint is monotonic and +-qmax are integers, so
+// clamping after rounding gives the same integers as clamping before.  The
+// codes are returned as two's-complement bytes, value i in byte i.
+__device__ __forceinline__ v2i quant8_pack(const float (&v)[8],
+                                           const Quantizer &z) {
+  float q[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = v[i] * z.r;  // S == 0: r == 0, every code 0
+    q[i] = __builtin_rintf(x);
+    near |= fabsf(x - q[i]) >= 0.499969482421875f;  // 0.5 - 2^-15
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_rintf(v[i] / z.s);
+  }
+  int c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    c[i] = (int)__builtin_amdgcn_fmed3f(q[i], -z.qmax, z.qmax);
+  // bytes: perm selector 0x0c yields zero, 0-3 bytes of the second
+  // operand, 4-7 bytes of the first
+  v2i r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c[4 * h + 1],
+                                              (uint32_t)c[4 * h], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c[4 * h + 3],
+                                              (uint32_t)c[4 * h + 2], 0x0c0c0400u);
+    r[h] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  return r;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) |
          ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);

@@ -74,12 +74,16 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
 
   const half_t *xr = x + (size_t)row * K;
   float v[NCH][8];
+  // VEC: chunk j of this lane is either wholly inside the row or wholly
+  // past its end (K % 8 == 0); such chunks hold zeros
+  bool ok[NCH];
 
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = tl + j * TPR;
+    ok[j] = c * 8 < K;
     if constexpr (VEC) {
-      if (c * 8 < K) {
+      if (ok[j]) {
         half8 h = *reinterpret_cast<const half8 *>(xr + c * 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[j][i] = (float)h[i];
@@ -106,36 +110,69 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
     const float mean = team_sum<TPR>(s, red) / (float)K;
     float ss = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j)
+    for (int j = 0; j < NCH; ++j) {
+      float cs = 0.0f;
+      if constexpr (VEC) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = (tl + j * TPR) * 8 + i;
-        const float d = v[j][i] - mean;
-        ss += (k < K) ? d * d : 0.0f;
+        for (int i = 0; i < 8; ++i) {
+          const float d = v[j][i] - mean;
+          cs = fmaf(d, d, cs);
+        }
+        ss += ok[j] ? cs : 0.0f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int k = (tl + j * TPR) * 8 + i;
+          const float d = v[j][i] - mean;
+          cs += (k < K) ? d * d : 0.0f;
+        }
+        ss += cs;
       }
+    }
     const float var = team_sum<TPR>(ss, red) / (float)K;
     const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
-    for (int j = 0; j < NCH; ++j)
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tl + j * TPR;
+      if (!ok[j]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = (tl + j * TPR) * 8 + i;
-        if (k < K) {
-          const float g = gamma ? (float)gamma[k] : 1.0f;
-          const float b = beta ? (float)beta[k] : 0.0f;
-          // round to the fp16 value that the unfused LayerNorm would emit
-          v[j][i] = (float)(half_t)((v[j][i] - mean) * rstd * g + b);
-        } else {
-          v[j][i] = 0.0f;
+        for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
+        continue;
+      }
+      float g[8], b[8];
+      if constexpr (VEC) {
+        const half8 hg = gamma ? *reinterpret_cast<const half8 *>(gamma + c * 8)
+                               : half8{1, 1, 1, 1, 1, 1, 1, 1};
+        const half8 hb = beta ? *reinterpret_cast<const half8 *>(beta + c * 8)
+                              : half8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          g[i] = (float)hg[i];
+          b[i] = (float)hb[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int k = c * 8 + i;
+          g[i] = (gamma && k < K) ? (float)gamma[k] : 1.0f;
+          b[i] = (beta && k < K) ? (float)beta[k] : 0.0f;
         }
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = c * 8 + i;
+        // round to the fp16 value that the unfused LayerNorm would emit
+        const float h = (float)(half_t)((v[j][i] - mean) * rstd * g[i] + b[i]);
+        v[j][i] = (VEC || k < K) ? h : 0.0f;
+      }
+    }
     if (ln_out) {
       half_t *lr = ln_out + (size_t)row * K;
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tl + j * TPR;
         if constexpr (VEC) {
-          if (c * 8 < K) {
+          if (ok[j]) {
             half8 h;
 #pragma unroll
             for (int i = 0; i < 8; ++i) h[i] = (half_t)v[j][i];
@@ -150,7 +187,7 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
     }
   }
 
-  // token-wise scale: max |h| / 127
+  // token-wise scale: max |h| / 127 (values past the row end are 0)
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j)
@@ -164,20 +201,13 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = tl + j * TPR;
-    int q[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quant_code(v[j][i], qz);
     if constexpr (VEC) {
-      if (c * 8 < K) {
-        v2i p;
-        p[0] = (int)pack4_i8(q[0], q[1], q[2], q[3]);
-        p[1] = (int)pack4_i8(q[4], q[5], q[6], q[7]);
-        *reinterpret_cast<v2i *>(qr + c * 8) = p;
-      }
+      const v2i p = quant8_pack(v[j], qz);
+      if (ok[j]) *reinterpret_cast<v2i *>(qr + c * 8) = p;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (c * 8 + i < K) qr[c * 8 + i] = (int8_t)q[i];
+        if (c * 8 + i < K) qr[c * 8 + i] = (int8_t)quant_code(v[j][i], qz);
     }
   }
 }
