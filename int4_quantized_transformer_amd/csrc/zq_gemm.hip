@@ -1340,11 +1340,13 @@ static int forced_tile() {
 }
 
 // Schedule selection by problem shape (the pages pick, per batch x seqlen,
-// the tiling with the least waste): decode-sized M streams the weights
-// with the skinny kernel; otherwise 256x256 tiles (16 waves, half the
-// operand traffic per MFMA of 128x128 tiles) when W8 and there are enough
-// of them to occupy most of the 256 compute units, else 128x128 tiles with
-// two blocks per CU.  Chosen from measured sweeps over the five workloads.
+// the tiling with the least waste).  Decode-sized M (<= 64) goes to the
+// weight-streaming kernels.  Otherwise, chosen from measured sweeps over the
+// five workloads: 256x256 tiles (16 waves, half the operand traffic per MFMA
+// of 128x128 tiles) when W8 and there are enough of them to occupy most of
+// the 256 compute units; else 128x128 tiles, with a third stage (one block
+// per CU, deeper prefetch) when all of them fit one per CU, and with two
+// stages (two blocks per CU) when they do not.
 // ZQ_DECODE=<kind> forces the decode kernel (tuning aid): 0 skinny,
 // 2 stream, 3 gemv (each only where it applies).
 static int forced_decode() {
@@ -1379,6 +1381,8 @@ static Plan choose(int M, int N, int K, int bits) {
   if (f >= 0) return Plan{kTiled, 0, f};
   const long tiles256 = (long)((N + 255) / 256) * ((M + 255) / 256);
   if (bits == 8 && tiles256 >= 140) return Plan{kTiled, 0, 12};
+  const long tiles128 = (long)((N + 127) / 128) * ((M + 127) / 128);
+  if (tiles128 <= device_cus()) return Plan{kTiled, 0, 4};
   return Plan{kTiled, 0, 0};
 }
 

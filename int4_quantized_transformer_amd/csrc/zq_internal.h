@@ -101,20 +101,24 @@ __device__ __forceinline__ int quant_code(float v, const Quantizer &z) {
 }
 
 // Eight values at once, with the same results as quant_code: q0 = rint(x)
-// for x = fl(v * r); x lies within 2^-15 of a half-integer exactly when
-// |x - q0| >= 0.5 - 2^-15 (x - q0 is exact), and then the eight are redone
-// with the IEEE division.  rint is monotonic and +-qmax are integers, so
-// clamping after rounding gives the same integers as clamping before.  The
-// codes are returned as two's-complement bytes, value i in byte i.
+// for x = fl(v * r), and the eight are redone with the IEEE division when
+// d = fma(v, r, -q0) (v*r - q0 rounded once) has |d| >= 0.5 - 2^-15.  d
+// differs from x - q0 by at most half an ulp of x plus half an ulp of d,
+// under 3.9e-6 for |x| <= 128, so every x within 2.3e-5 of a half-integer
+// (the only x whose code can differ from that of fl(v/S), see above) has
+// |d| > 0.5 - 2.7e-5 and is redone.  rint is monotonic and +-qmax are
+// integers, so clamping after rounding gives the same integers as clamping
+// before.  The codes are returned as two's-complement bytes, value i in
+// byte i.
 __device__ __forceinline__ v2i quant8_pack(const float (&v)[8],
                                            const Quantizer &z) {
   float q[8];
   bool near = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float x = v[i] * z.r;  // S == 0: r == 0, every code 0
-    q[i] = __builtin_rintf(x);
-    near |= fabsf(x - q[i]) >= 0.499969482421875f;  // 0.5 - 2^-15
+    q[i] = __builtin_rintf(v[i] * z.r);  // S == 0: r == 0, every code 0
+    const float d = __builtin_fmaf(v[i], z.r, -q[i]);
+    near |= fabsf(d) >= 0.499969482421875f;  // 0.5 - 2^-15
   }
   if (near) {
 #pragma unroll

@@ -78,19 +78,17 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
   // past its end (K % 8 == 0); such chunks hold zeros
   bool ok[NCH];
 
+  // every chunk is loaded (past the row end: the row's last chunk) so that
+  // all loads are in flight together, then masked
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = tl + j * TPR;
     ok[j] = c * 8 < K;
     if constexpr (VEC) {
-      if (ok[j]) {
-        half8 h = *reinterpret_cast<const half8 *>(xr + c * 8);
+      const int cc = ok[j] ? c : K / 8 - 1;
+      const half8 h = *reinterpret_cast<const half8 *>(xr + cc * 8);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[j][i] = (float)h[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
-      }
+      for (int i = 0; i < 8; ++i) v[j][i] = ok[j] ? (float)h[i] : 0.0f;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
