@@ -219,25 +219,28 @@ def timed_eager(torch, step_calls, steps, stream):
     return e0.elapsed_time(e1) / steps
 
 
-def kernel_breakdown(torch, step_calls, steps, stream):
-    """Per-launch durations from events around every launch (eager)."""
-    names = [c[0] for c in step_calls[0]]
-    acc = {n: 0.0 for n in names}
-    n_it = max(1, steps)
-    evs = []
-    for i in range(n_it):
-        calls = step_calls[i % len(step_calls)]
-        es = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-        es[0].record(stream)
-        for j, (name, fn, args) in enumerate(calls):
-            fn(*args)
-            es[j + 1].record(stream)
-        evs.append(es)
-    torch.cuda.synchronize()
-    for es in evs:
-        for j, n in enumerate(names):
-            acc[n] += es[j].elapsed_time(es[j + 1])
-    return {n: acc[n] / n_it for n in names}
+def entry_timings(torch, zq, sets, wl, M, steps):
+    """Average duration of each step entry's launch: one HIP graph per entry
+    holding that launch for every rotating set (so its inputs come from HBM
+    as in the step), replayed `steps` times and timed with events around
+    the replays.  Graph launches carry no host gaps, so this is the kernel's
+    own duration plus the small inter-kernel gap of a graph."""
+    names = [c[0] for c in make_step(zq, sets[0], wl, M, 0)]
+    out = {}
+    for j, name in enumerate(names):
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cs):
+            for s in sets:
+                call = make_step(zq, s, wl, M, cs.cuda_stream)[j]
+                run_calls([call])
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            g.replay()
+        ms, _ = timed_graphs(torch, [g], steps, stream)
+        out[name] = ms / len(sets)
+        del g
+    return out
 
 
 def grid_threads(name, L, M, G, zq):
@@ -252,25 +255,54 @@ def grid_threads(name, L, M, G, zq):
     return None
 
 
-def traffic_for(path, kernel_name, grid):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None
-    if absent or taken on a different kernel source."""
+KERNEL_SOURCES = ("zq_gemm.hip", "zq_quant.hip")
+
+
+def source_shas():
+    out = {}
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "int4_quantized_transformer_amd", "csrc",
+                               n), "rb") as f:
+            out[n] = hashlib.sha256(f.read()).hexdigest()
+    return out
+
+
+def traffic_for(path, entry, grid):
+    """HBM bytes per launch of one step entry from committed rocprofv3
+    counter runs, or None if absent, taken on other kernel sources, or on
+    another launch grid."""
     try:
         with open(path) as f:
             t = json.load(f)
+        shas = source_shas()
     except (OSError, ValueError):
         return None
-    src = os.path.join(ROOT, "int4_quantized_transformer_amd", "csrc",
-                       t.get("source", ""))
-    try:
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
-        return None
-    e = t.get("kernels", {}).get(f"gemm_tiled_kernel@{grid}")
-    if not e or sha != t.get("source_sha256"):
+    e = t.get("entries", {}).get(entry)
+    if not e or t.get("sources") != shas or e.get("grid") != grid:
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+def step_entries(zq, wl, M):
+    """The launches of one step, in order: name, kernel, grid (threads; GEMMs
+    only), algorithmic ops and bytes."""
+    out = []
+    for L in wl.linears:
+        qn = f"{L.name}.ln_quant" if L.ln else f"{L.name}.quant"
+        out.append({"name": qn, "kernel": "row_quant_kernel", "grid": None,
+                    "ops": 0, "bytes": quant_bytes(M, L.K)})
+        gn = f"{L.name}.gemm_w{L.bits}a8"
+        plan = zq.gemm_plan(M, L.N, L.K, L.bits)
+        kern = {"tiled": "gemm_tiled_kernel", "stream": "gemm_stream_kernel",
+                "gemv": "gemm_gemv_kernel", "skinny": "gemm_skinny_kernel"}[
+                    plan.split()[0]]
+        out.append({"name": gn, "kernel": kern,
+                    "grid": grid_threads(gn, L, M, wl.G, zq),
+                    "ops": 2 * M * L.N * L.K,
+                    "bytes": gemm_bytes(M, L.N, L.K, L.bits, wl.G),
+                    "read_bytes": gemm_bytes(M, L.N, L.K, L.bits, wl.G)
+                    - 2 * M * L.N})
+    return out
 
 
 # ------------------------------------------------------------------ decode --
@@ -330,8 +362,8 @@ def _read_csv(path):
 
 
 def _short(name):
-    for key in ("gemm_tiled_kernel", "gemm_skinny_kernel", "row_quant_kernel",
-                "weight_quant_kernel"):
+    for key in ("gemm_tiled_kernel", "gemm_skinny_kernel", "gemm_stream_kernel",
+                "gemm_gemv_kernel", "row_quant_kernel", "weight_quant_kernel"):
         if key in name:
             return key
     if "neg_kernel" in name:
@@ -339,13 +371,38 @@ def _short(name):
     return name[:40]
 
 
-def summarize(d, traffic_out=None):
-    """Per (kernel, grid) durations from a kernel trace and, when present,
+def _split(values, entries, key):
+    """Attribute the dispatches of one (kernel, grid) to the step entries that
+    launch it.  Every entry launches it equally often; sorted by the measured
+    value (duration, or fetched bytes), the i-th equal share goes to the entry
+    with the i-th smallest expected value `key` (entries with equal keys are
+    interchangeable).  Returns {entry name: [values]} or None if the count
+    does not divide."""
+    k = len(entries)
+    if k == 0 or len(values) % k:
+        return None
+    n = len(values) // k
+    vs = sorted(values)
+    es = sorted(entries, key=lambda e: e[key])
+    return {e["name"]: vs[i * n:(i + 1) * n] for i, e in enumerate(es)}
+
+
+def summarize(d, traffic_out=None, workload="bert-base", m_index=None):
+    """Per step entry: durations from the kernel trace and, when present,
     FETCH_SIZE / WRITE_SIZE per dispatch scaled by the same counters of the
-    plain copy of COPY_BYTES bytes."""
+    plain copy of COPY_BYTES bytes (GEMM entries; quantizer launches are
+    listed per kernel)."""
     import glob
     import statistics as st
-    lines = []
+    import int4_quantized_transformer_amd as zq
+    from int4_quantized_transformer_amd import workloads as W
+    wl = W.workload(workload)
+    M = wl.M[-1] if m_index is None else wl.M[m_index]
+    entries = step_entries(zq, wl, M)
+    gemm_e = [e for e in entries if e["grid"] is not None]
+    lines = [f"step entries ({wl.name}, M={M}): " + ", ".join(
+        f"{e['name']} -> {e['kernel']}@{e['grid']}" if e["grid"] else
+        f"{e['name']} -> {e['kernel']}" for e in entries), ""]
     for tr in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"),
                                recursive=True)):
         groups = {}
@@ -362,6 +419,19 @@ def summarize(d, traffic_out=None):
         for (k, g, w), v in sorted(groups.items(), key=lambda x: -sum(x[1])):
             lines.append(f"| {k} | {g} | {w} | {len(v)} | "
                          f"{st.mean(v) / 1e3:.2f} | {st.median(v) / 1e3:.2f} |")
+        lines.append("")
+        lines.append("GEMM step entries (dispatches of one kernel and grid "
+                     "split equally by sorted duration, matched to the "
+                     "entries' ops)")
+        lines.append("| entry | kernel@grid | calls | avg us | median us |")
+        lines.append("|---|---|---|---|---|")
+        for (k, g, w), v in sorted(groups.items()):
+            es = [e for e in gemm_e if e["kernel"] == k and e["grid"] == g]
+            sp = _split(v, es, "ops") if es else None
+            for name, vv in (sp or {}).items():
+                lines.append(f"| {name} | {k}@{g} | {len(vv)} | "
+                             f"{st.mean(vv) / 1e3:.2f} | "
+                             f"{st.median(vv) / 1e3:.2f} |")
     pmc = {}
     for cc in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
                                recursive=True)):
@@ -395,18 +465,37 @@ def summarize(d, traffic_out=None):
                 scaled = med * 1024 / f if f else None
                 lines.append(f"| {cname} | {k} | {g} | {len(dd)} | {med:.0f} | "
                              f"{'' if scaled is None else f'{scaled:.0f}'} |")
-                if scaled is not None and k.startswith(("gemm", "row_quant")):
-                    traffic.setdefault(f"{k}@{g}", {})[cname] = scaled
+        lines.append("")
+        lines.append("GEMM step entries (dispatches of one kernel and grid "
+                     "split equally by sorted counter value, matched to the "
+                     "entries' algorithmic read / write bytes)")
+        lines.append("| entry | counter | dispatches | median KiB | scaled "
+                     "bytes | algorithmic bytes |")
+        lines.append("|---|---|---|---|---|---|")
+        for cname, per in pmc.items():
+            f = factors.get(cname)
+            if not f:
+                continue
+            for (k, g), dd in sorted(per.items()):
+                es = [dict(e, write_bytes=e["bytes"] - e["read_bytes"])
+                      for e in gemm_e if e["kernel"] == k and e["grid"] == g]
+                key = "read_bytes" if cname == "FETCH_SIZE" else "write_bytes"
+                sp = _split(list(dd.values()), es, key) if es else None
+                for name, vv in (sp or {}).items():
+                    med = st.median(vv)
+                    scaled = med * 1024 / f
+                    alg = [e[key] for e in es if e["name"] == name][0]
+                    lines.append(f"| {name} | {cname} | {len(vv)} | {med:.0f} |"
+                                 f" {scaled:.0f} | {alg} |")
+                    traffic.setdefault(name, {"grid": g})[cname] = scaled
     print("\n".join(lines))
     if traffic_out and traffic:
-        src = os.path.join(ROOT, "int4_quantized_transformer_amd", "csrc",
-                           "zq_gemm.hip")
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        out = {"source": "zq_gemm.hip", "source_sha256": sha, "kernels": {}}
-        for key, v in traffic.items():
+        out = {"sources": source_shas(), "workload": wl.name, "tokens": M,
+               "entries": {}}
+        for name, v in traffic.items():
             if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
-                out["kernels"][key] = {
+                out["entries"][name] = {
+                    "grid": v["grid"],
                     "hbm_bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
                     "fetch_bytes": round(v["FETCH_SIZE"]),
                     "write_bytes": round(v["WRITE_SIZE"])}
@@ -428,7 +517,8 @@ def copy_calibration(torch, dev):
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize, args.write_traffic)
+        summarize(args.summarize, args.write_traffic, args.workload,
+                  args.m_index)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -483,7 +573,7 @@ def main():
         return
 
     eager_ms = timed_eager(torch, step_calls, max(20, args.steps // 4), stream)
-    bd = kernel_breakdown(torch, step_calls, max(20, args.steps // 4), stream)
+    bd = entry_timings(torch, zq, sets, wl, M, max(20, args.steps // 4))
 
     ops_step = sum(2 * M * d["L"].N * d["L"].K for d in base)
     tops = ops_step / (ms * 1e-3) / 1e12
@@ -514,6 +604,8 @@ def main():
     roof["algorithmic"] = {"ops": ops, "bytes": nbytes}
     roof["grid_threads"] = grid_threads(dom, Ld, M, wl.G, zq)
     roof["traffic"] = traffic_for(args.traffic, dom, roof["grid_threads"])
+    roof["timing"] = ("per-launch average from a HIP graph of this launch "
+                      "over the rotating sets, events around the replays")
 
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
