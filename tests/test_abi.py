@@ -101,9 +101,18 @@ def test_header_limits_match_int32_bound():
     assert 150_976 * 127 * 7 * 16 < 2 ** 31 <= 150_977 * 127 * 7 * 16
 
 
-def test_gemm_plan_covers_both_regimes():
-    assert Z.gemm_plan(1, 4096, 4096, 8).startswith("skinny")
+def test_gemm_plan_covers_every_regime():
+    # one token with whole 1 KB weight-row pieces: GEMV; other one-token or
+    # up-to-16-token problems with even N: streaming kernel; up to 64
+    # tokens otherwise: skinny kernel; above: tiled
+    assert Z.gemm_plan(1, 4096, 4096, 8).startswith("gemv")
+    assert Z.gemm_plan(1, 4096, 4096, 4).startswith("gemv")
+    assert Z.gemm_plan(1, 4096, 1024, 4).startswith("stream")
+    assert Z.gemm_plan(1, 77, 192, 8).startswith("skinny")
+    assert Z.gemm_plan(16, 4096, 4096, 8).startswith("stream")
+    assert Z.gemm_plan(17, 4096, 4096, 8).startswith("skinny")
     assert Z.gemm_plan(64, 4096, 4096, 4).startswith("skinny")
+    assert Z.gemm_plan(65, 4096, 4096, 8).startswith("tiled")
     assert Z.gemm_plan(2048, 4096, 4096, 8).startswith("tiled")
     with pytest.raises(Z.ZQError):
         Z.gemm_plan(16, 256, 256, 3)
