@@ -364,6 +364,76 @@ __device__ __forceinline__ void tail_stage(const char *ws, const char *xs,
 //             barrier (now every wave is done with slot kt % S and stage
 //             kt+1 is visible), copy stage kt+S into slot kt % S, read
 //             fragments of (stage kt+1, k-step 0), MFMAs of k-step 3.
+// Staged epilogue of the tiled kernel.  The fp16 tile goes through LDS so
+// that every global store writes whole row segments with 16 bytes per lane.
+// Layout: row t of the tile holds BN halves; its 16-byte chunks are
+// XOR-swizzled by (t & (SW-1)), SW the largest power of two dividing the
+// chunk count (at most 16), so that the 8-byte writes of consecutive rows
+// spread over the banks.
+template <class C>
+struct StageLayout {
+  static constexpr int RB = C::BN * 2;  // bytes per tile row
+  static constexpr int CPR = C::BN / 8;  // 16-byte chunks per tile row
+  static constexpr int SW = (CPR % 16 == 0) ? 16 : (CPR % 8 == 0) ? 8 : 4;
+};
+
+template <class C, bool GELU, bool BIAS>
+__device__ __forceinline__ void stage_epilogue(
+    const GemmArgs &p, char *lds, const v16i (&acc)[C::FN][C::FM],
+    const float *sx_l, const half_t *bias_l, const float (&swv)[C::FN],
+    int wn0, int wm0, int r32, int h) {
+  using S = StageLayout<C>;
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int tl = wm0 + fm * 32 + r32;
+      const float sc = sx_l[tl] * swv[fn];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cl = wn0 + fn * 32 + 8 * q + 4 * h;  // tile column
+        half4 bb = {(half_t)0.0f, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
+        if constexpr (BIAS) bb = *reinterpret_cast<const half4 *>(bias_l + cl);
+        half4 hv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int a = acc[fn][fm][4 * q + r];
+          if constexpr (C::W4) a >>= 4;
+          float z = fmaf((float)a, sc, (float)bb[r]);
+          if constexpr (GELU) z = gelu_erf(z);
+          hv[r] = (half_t)z;
+        }
+        const int chunk = (wn0 + fn * 32) / 8 + q;
+        *reinterpret_cast<half4 *>(lds + tl * S::RB +
+                                   ((chunk ^ (tl & (S::SW - 1))) << 4) + h * 8) = hv;
+      }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void store_staged_tile(const GemmArgs &p,
+                                                  const char *lds, int n0,
+                                                  int m0, int tid) {
+  using S = StageLayout<C>;
+  const bool vec = (p.N & 7) == 0 && (((uintptr_t)p.out) & 15) == 0;
+  half_t *Y = static_cast<half_t *>(p.out);
+  for (int i = tid; i < C::BM * S::CPR; i += C::NT) {
+    const int row = i / S::CPR, c = i % S::CPR;
+    const int t = m0 + row, n = n0 + c * 8;
+    if (t >= p.M || n >= p.N) continue;
+    const v4i v = ld16(lds + row * S::RB + ((c ^ (row & (S::SW - 1))) << 4));
+    half_t *o = Y + (size_t)t * p.N + n;
+    if (vec && n + 8 <= p.N) {
+      *reinterpret_cast<v4i *>(o) = v;
+    } else {
+      const half8 hv = __builtin_bit_cast(half8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < p.N) o[e] = hv[e];
+    }
+  }
+}
+
 template <class C, bool RAW>
 __global__ void __launch_bounds__(C::NT)
 gemm_tiled_kernel(GemmArgs p) {
@@ -484,60 +554,18 @@ gemm_tiled_kernel(GemmArgs p) {
 
   if constexpr (!RAW && C::BM * C::BN * 2 <= C::S * C::STAGE && C::BN >= 64) {
     if (g32 && (bias_lds || !p.bias)) {
-      // Stage the fp16 tile through LDS so that every global store writes
-      // whole row segments with 16 bytes per lane.  Layout: row t of the
-      // tile holds BN halves; its 16-byte chunks are XOR-swizzled by
-      // (t & (SW-1)), SW the largest power of two dividing the chunk count
-      // (at most 16), so that the 8-byte writes of consecutive rows spread
-      // over the banks.
       __syncthreads();  // every wave is done reading the operand stages
-      constexpr int RB = C::BN * 2;  // bytes per tile row
-      constexpr int CPR0 = C::BN / 8;
-      constexpr int SW = (CPR0 % 16 == 0) ? 16 : (CPR0 % 8 == 0) ? 8 : 4;
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-          const int tl = wm0 + fm * 32 + r32;
-          const float sc = sx_l[tl] * swv[fn];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            half4 hv;
-            const int cl = wn0 + fn * 32 + 8 * q + 4 * h;  // tile column
-            const half4 bb = bias_lds
-                ? *reinterpret_cast<const half4 *>(bias_l + cl)
-                : half4{(half_t)0.0f, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              int a = acc[fn][fm][4 * q + r];
-              if constexpr (C::W4) a >>= 4;
-              float z = fmaf((float)a, sc, (float)bb[r]);
-              if (p.act == ZQ_ACT_GELU) z = gelu_erf(z);
-              hv[r] = (half_t)z;
-            }
-            const int chunk = (wn0 + fn * 32) / 8 + q;
-            *reinterpret_cast<half4 *>(lds + tl * RB + ((chunk ^ (tl & (SW - 1))) << 4) + h * 8) = hv;
-          }
-        }
-      __syncthreads();
-      constexpr int CPR = C::BN / 8;  // 16-byte chunks per tile row
-      const bool vec = (p.N & 7) == 0 && (((uintptr_t)p.out) & 15) == 0;
-      half_t *Y = static_cast<half_t *>(p.out);
-      for (int i = tid; i < C::BM * CPR; i += C::NT) {
-        const int row = i / CPR, c = i % CPR;
-        const int t = m0 + row, n = n0 + c * 8;
-        if (t >= p.M || n >= p.N) continue;
-        const v4i v = ld16(lds + row * RB + ((c ^ (row & (SW - 1))) << 4));
-        half_t *o = Y + (size_t)t * p.N + n;
-        if (vec && n + 8 <= p.N) {
-          *reinterpret_cast<v4i *>(o) = v;
-        } else {
-          const half8 hv = __builtin_bit_cast(half8, v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (n + e < p.N) o[e] = hv[e];
-        }
+      // the activation and the bias are uniform: one straight-line variant
+      // each, so that independent elements interleave
+      if (p.act == ZQ_ACT_GELU) {
+        if (p.bias) stage_epilogue<C, true, true>(p, lds, acc, sx_l, bias_l, swv, wn0, wm0, r32, h);
+        else stage_epilogue<C, true, false>(p, lds, acc, sx_l, bias_l, swv, wn0, wm0, r32, h);
+      } else {
+        if (p.bias) stage_epilogue<C, false, true>(p, lds, acc, sx_l, bias_l, swv, wn0, wm0, r32, h);
+        else stage_epilogue<C, false, false>(p, lds, acc, sx_l, bias_l, swv, wn0, wm0, r32, h);
       }
+      __syncthreads();
+      store_staged_tile<C>(p, lds, n0, m0, tid);
       return;
     }
   }
