@@ -376,14 +376,18 @@ def _split(values, entries, key):
     launch it.  Every entry launches it equally often; sorted by the measured
     value (duration, or fetched bytes), the i-th equal share goes to the entry
     with the i-th smallest expected value `key` (entries with equal keys are
-    interchangeable).  Returns {entry name: [values]} or None if the count
-    does not divide."""
+    interchangeable).  Returns {entry name: [values]}, or None if the count
+    does not divide or two populations that should differ overlap."""
     k = len(entries)
     if k == 0 or len(values) % k:
         return None
     n = len(values) // k
     vs = sorted(values)
     es = sorted(entries, key=lambda e: e[key])
+    # entries with different expected values must form separate populations
+    for i in range(k - 1):
+        if es[i][key] != es[i + 1][key] and vs[(i + 1) * n - 1] >= vs[(i + 1) * n]:
+            return None
     return {e["name"]: vs[i * n:(i + 1) * n] for i, e in enumerate(es)}
 
 

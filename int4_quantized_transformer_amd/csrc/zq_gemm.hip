@@ -179,8 +179,13 @@ struct Tile {
   static constexpr int WCPR = WROW / 16, XCPR = XROW / 16;  // chunks per row
   static constexpr int WRPI = 64 / WCPR, XRPI = 64 / XCPR;  // rows per wave copy
   static constexpr int WINS = BN / WRPI, XINS = BM / XRPI;  // wave copies/stage
-  static constexpr int IW = WINS / NWAVES, IX = XINS / NWAVES;  // per wave
-  static constexpr int WBYTES = BN * WROW, XBYTES = BM * XROW;
+  // copies per wave (the same for every wave, so that every vmcnt wait is a
+  // constant); when the waves do not divide the copies evenly the last ones
+  // are padding that land in the padded tail of their region, never read
+  static constexpr int IW = (WINS + NWAVES - 1) / NWAVES;
+  static constexpr int IX = (XINS + NWAVES - 1) / NWAVES;
+  static constexpr int WBYTES = IW * NWAVES * 1024;  // weight region (padded)
+  static constexpr int XBYTES = IX * NWAVES * 1024;  // activation region
   static constexpr int STAGE = WBYTES + XBYTES;
   // epilogue operands copied into LDS with stage 0: bias of the tile's BN
   // columns and scales of its BM tokens, each padded to whole 256-byte wave
@@ -188,7 +193,7 @@ struct Tile {
   static constexpr int AUX_BIAS = ((BN * 2 + 255) / 256) * 256;
   static constexpr int AUX_SX = ((BM * 4 + 255) / 256) * 256;
   static constexpr int LDS = S * STAGE + AUX_BIAS + AUX_SX;
-  static_assert(WINS % NWAVES == 0 && XINS % NWAVES == 0, "copy split");
+  static_assert(BN % WRPI == 0 && BM % XRPI == 0, "copy split");
   static_assert(WN % 32 == 0 && WM % 32 == 0 && S >= 2, "tile");
   static_assert((IW + IX) * (S - 2) < 64, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -215,9 +220,9 @@ __device__ __forceinline__ void issue_stage(const GemmArgs &p, const char *W,
 #pragma unroll
   for (int j = 0; j < C::IW; ++j) {
     const int q = wave * C::IW + j;
-    const int row = q * C::WRPI + lane / C::WCPR;
+    const int row = q * C::WRPI + lane / C::WCPR;  // >= BN: padding copy
     const int chunk = wswz<C::WROW>(lane % C::WCPR, row);
-    int n = n0 + row;
+    int n = n0 + (row < C::BN ? row : C::BN - 1);
     n = n < p.N ? n : p.N - 1;                 // rows past N: never stored
     int kb = kt * C::WROW + chunk * 16;
     if (kb >= ldw) kb -= C::WROW / 2;          // K % 128 == 64: unused half
@@ -227,9 +232,9 @@ __device__ __forceinline__ void issue_stage(const GemmArgs &p, const char *W,
 #pragma unroll
   for (int j = 0; j < C::IX; ++j) {
     const int q = wave * C::IX + j;
-    const int row = q * C::XRPI + lane / C::XCPR;
+    const int row = q * C::XRPI + lane / C::XCPR;  // >= BM: padding copy
     const int chunk = wswz<C::XROW>(lane % C::XCPR, row);
-    int t = m0 + row;
+    int t = m0 + (row < C::BM ? row : C::BM - 1);
     t = t < p.M ? t : p.M - 1;
     int kb = kt * C::XROW + chunk * 16;
     if (kb >= p.K) kb -= C::XROW / 2;
@@ -1327,6 +1332,8 @@ static const TileCfg kTileCfgs[] = {
     {256, 128, 64, 64, 3},    // 10: 8 waves
     {128, 256, 64, 64, 3},    // 11: 8 waves
     {256, 256, 64, 64, 2},    // 12: 16 waves
+    {192, 256, 64, 64, 2},    // 13: 12 waves
+    {288, 128, 96, 32, 2},    // 14: 12 waves
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 
@@ -1345,6 +1352,8 @@ static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
     case 9: return run_tiled<Tile<128, 192, 64, 96, 2, W4>, RAW>(a, s);
     case 10: return run_tiled<Tile<256, 128, 64, 64, 3, W4>, RAW>(a, s);
     case 11: return run_tiled<Tile<128, 256, 64, 64, 3, W4>, RAW>(a, s);
+    case 13: return run_tiled<Tile<192, 256, 64, 64, 2, W4>, RAW>(a, s);
+    case 14: return run_tiled<Tile<288, 128, 96, 32, 2, W4>, RAW>(a, s);
     default: return run_tiled<Tile<256, 256, 64, 64, 2, W4>, RAW>(a, s);
   }
 }
@@ -1369,12 +1378,44 @@ static int forced_tile() {
 
 // Schedule selection by problem shape (the pages pick, per batch x seqlen,
 // the tiling with the least waste).  Decode-sized M (<= 64) goes to the
-// weight-streaming kernels.  Otherwise, chosen from measured sweeps over the
-// five workloads: 256x256 tiles (16 waves, half the operand traffic per MFMA
-// of 128x128 tiles) when W8 and there are enough of them to occupy most of
-// the 256 compute units; else 128x128 tiles, with a third stage (one block
-// per CU, deeper prefetch) when all of them fit one per CU, and with two
-// stages (two blocks per CU) when they do not.
+// weight-streaming kernels.  Otherwise, from measured sweeps of every
+// configuration on the five workloads:
+//  * when 128x128 tiles fit one per compute unit: 128x128 with a third stage
+//    (one block per CU, deeper prefetch);
+//  * W4: 128x128 with two stages (two blocks per CU);
+//  * W8: the candidate with the best score = fill x quality, where fill is
+//    the fraction of the CU slots that the rounds of tiles keep busy (tiles
+//    / (rounds x slots)) and quality the measured per-CU efficiency of the
+//    configuration relative to 256x256 with 16 waves.
+struct Candidate {
+  int cfg, slots_per_cu;
+  double quality;
+};
+static const Candidate kW8Candidates[] = {
+    {12, 1, 1.00},  // 256x256, 16 waves
+    {13, 1, 0.95},  // 192x256, 12 waves
+    {14, 1, 0.85},  // 288x128, 12 waves
+    {0, 2, 0.87},   // 128x128, 4 waves, two blocks per CU
+};
+
+static int pick_w8(int M, int N) {
+  const int cus = device_cus();
+  int best = 0;
+  double best_score = -1.0;
+  for (const Candidate &c : kW8Candidates) {
+    const TileCfg &t = kTileCfgs[c.cfg];
+    const long tiles = (long)((N + t.bn - 1) / t.bn) * ((M + t.bm - 1) / t.bm);
+    const long slots = (long)cus * c.slots_per_cu;
+    const long rounds = (tiles + slots - 1) / slots;
+    const double score = c.quality * (double)tiles / (double)(rounds * slots);
+    if (score > best_score) {
+      best_score = score;
+      best = c.cfg;
+    }
+  }
+  return best;
+}
+
 // ZQ_DECODE=<kind> forces the decode kernel (tuning aid): 0 skinny,
 // 2 stream, 3 gemv (each only where it applies).
 static int forced_decode() {
@@ -1407,11 +1448,10 @@ static Plan choose(int M, int N, int K, int bits) {
   }
   const int f = forced_tile();
   if (f >= 0) return Plan{kTiled, 0, f};
-  const long tiles256 = (long)((N + 255) / 256) * ((M + 255) / 256);
-  if (bits == 8 && tiles256 >= 140) return Plan{kTiled, 0, 12};
   const long tiles128 = (long)((N + 127) / 128) * ((M + 127) / 128);
   if (tiles128 <= device_cus()) return Plan{kTiled, 0, 4};
-  return Plan{kTiled, 0, 0};
+  if (bits == 4) return Plan{kTiled, 0, 0};
+  return Plan{kTiled, 0, pick_w8(M, N)};
 }
 
 // Skinny configurations {BN, NW, U} per 16-token fragment count (tuning
