@@ -1334,6 +1334,7 @@ static const TileCfg kTileCfgs[] = {
     {256, 256, 64, 64, 2},    // 12: 16 waves
     {192, 256, 64, 64, 2},    // 13: 12 waves
     {288, 128, 96, 32, 2},    // 14: 12 waves
+    {96, 128, 96, 32, 3},     // 15: 4 waves
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 
@@ -1354,6 +1355,7 @@ static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
     case 11: return run_tiled<Tile<128, 256, 64, 64, 3, W4>, RAW>(a, s);
     case 13: return run_tiled<Tile<192, 256, 64, 64, 2, W4>, RAW>(a, s);
     case 14: return run_tiled<Tile<288, 128, 96, 32, 2, W4>, RAW>(a, s);
+    case 15: return run_tiled<Tile<96, 128, 96, 32, 3, W4>, RAW>(a, s);
     default: return run_tiled<Tile<256, 256, 64, 64, 2, W4>, RAW>(a, s);
   }
 }
@@ -1380,8 +1382,8 @@ static int forced_tile() {
 // the tiling with the least waste).  Decode-sized M (<= 64) goes to the
 // weight-streaming kernels.  Otherwise, from measured sweeps of every
 // configuration on the five workloads:
-//  * when 128x128 tiles fit one per compute unit: 128x128 with a third stage
-//    (one block per CU, deeper prefetch);
+//  * when 128x128 tiles fit one per compute unit: three-stage tiles (one
+//    block per CU, deeper prefetch) of 128x128 or 96x128, by the score below;
 //  * W4: 128x128 with two stages (two blocks per CU);
 //  * W8: the candidate with the best score = fill x quality, where fill is
 //    the fraction of the CU slots that the rounds of tiles keep busy (tiles
@@ -1398,11 +1400,17 @@ static const Candidate kW8Candidates[] = {
     {0, 2, 0.87},   // 128x128, 4 waves, two blocks per CU
 };
 
-static int pick_w8(int M, int N) {
+static const Candidate kSmallCandidates[] = {
+    {4, 1, 1.00},   // 128x128, 3 stages
+    {15, 1, 0.81},  // 96x128, 3 stages
+};
+
+template <int NC>
+static int pick(const Candidate (&cands)[NC], int M, int N) {
   const int cus = device_cus();
-  int best = 0;
+  int best = cands[0].cfg;
   double best_score = -1.0;
-  for (const Candidate &c : kW8Candidates) {
+  for (const Candidate &c : cands) {
     const TileCfg &t = kTileCfgs[c.cfg];
     const long tiles = (long)((N + t.bn - 1) / t.bn) * ((M + t.bm - 1) / t.bm);
     const long slots = (long)cus * c.slots_per_cu;
@@ -1449,9 +1457,9 @@ static Plan choose(int M, int N, int K, int bits) {
   const int f = forced_tile();
   if (f >= 0) return Plan{kTiled, 0, f};
   const long tiles128 = (long)((N + 127) / 128) * ((M + 127) / 128);
-  if (tiles128 <= device_cus()) return Plan{kTiled, 0, 4};
+  if (tiles128 <= device_cus()) return Plan{kTiled, 0, pick(kSmallCandidates, M, N)};
   if (bits == 4) return Plan{kTiled, 0, 0};
-  return Plan{kTiled, 0, pick_w8(M, N)};
+  return Plan{kTiled, 0, pick(kW8Candidates, M, N)};
 }
 
 // Skinny configurations {BN, NW, U} per 16-token fragment count (tuning
