@@ -155,6 +155,38 @@ zq_status zq_gemm_w4a8_i32(const int8_t *qx, const uint8_t *qw4, int M, int N,
                            int K, int32_t *acc, void *stream);
 
 /*
+ * zq_gemm_w8a8_quant / zq_gemm_w4a8_quant -- the GEMM with its output
+ * quantized token-wise for the next linear (the inputs of attn-out and
+ * FFN2 follow a bias-add or GeLU, and the token quantization is fused into
+ * that producing step: Sec. 3.4 "Quantization-Optimized Transformer
+ * Kernels", paper App. D).  Arguments as zq_gemm_w8a8 / _w4a8, but instead
+ * of y the call writes
+ *   qy int8 [M][N] and sy fp32 [M]  (16- and 4-byte aligned)
+ * equal, bit for bit, to zq_gemm_w8a8 (fp16 y) followed by zq_quant_act(y):
+ * sy[t] = max_n |y[t][n]| / 127 over the fp16 outputs, qy = the codes.
+ * When every output tile can be resident on the device at once the codes
+ * come straight from the GEMM epilogue (no fp16 output is written); else
+ * the fp16 output goes through the workspace and the token quantizer.
+ *   ws: device workspace of at least zq_gemm_quant_workspace_bytes(M, N)
+ *       bytes, 16-byte aligned, owned by the caller; clobbered.
+ * Errors as zq_gemm_w8a8, plus ZQ_EINVAL for a null or short workspace or
+ * null qy/sy, and ZQ_EUNSUPPORTED for N > ZQ_MAX_ROW_K.
+ */
+zq_status zq_gemm_w8a8_quant(const int8_t *qx, const float *sx,
+                             const int8_t *qw, const float *sw, int G,
+                             const void *bias_fp16, int act, int M, int N,
+                             int K, int8_t *qy, float *sy, void *ws,
+                             size_t ws_bytes, void *stream);
+zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
+                             const uint8_t *qw4, const float *sw, int G,
+                             const void *bias_fp16, int act, int M, int N,
+                             int K, int8_t *qy, float *sy, void *ws,
+                             size_t ws_bytes, void *stream);
+/* Workspace bytes the _quant calls need for an M x N output (0 if M or N
+ * is not positive). */
+size_t zq_gemm_quant_workspace_bytes(int M, int N);
+
+/*
  * zq_gemm_plan -- which kernel and tile shape the GEMM calls pick for a
  * problem (the schedule chosen by token count, paper App. D), written as a
  * NUL-terminated string into buf (at most buflen bytes).  No launch.
@@ -167,7 +199,7 @@ const char *zq_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int zq_version(void);
-#define ZQ_VERSION 100
+#define ZQ_VERSION 101
 
 #ifdef __cplusplus
 }

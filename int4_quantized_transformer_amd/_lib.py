@@ -14,8 +14,9 @@ import torch
 
 __all__ = ["ZQError", "library_path", "lib", "quantize_weights",
            "ln_quant_act", "quant_act", "gemm_w8a8", "gemm_w4a8",
-           "gemm_w8a8_i32", "gemm_w4a8_i32", "gemm_plan", "ACT_NONE",
-           "ACT_GELU"]
+           "gemm_w8a8_i32", "gemm_w4a8_i32", "gemm_w8a8_quant",
+           "gemm_w4a8_quant", "gemm_quant_workspace_bytes", "gemm_plan",
+           "ACT_NONE", "ACT_GELU"]
 
 ACT_NONE = 0
 ACT_GELU = 1
@@ -56,12 +57,18 @@ def lib():
             "zq_gemm_w4a8": [P, P, P, P, I, P, I, I, I, I, P, P],
             "zq_gemm_w8a8_i32": [P, P, I, I, I, P, P],
             "zq_gemm_w4a8_i32": [P, P, I, I, I, P, P],
+            "zq_gemm_w8a8_quant": [P, P, P, P, I, P, I, I, I, I, P, P, P,
+                                   ctypes.c_size_t, P],
+            "zq_gemm_w4a8_quant": [P, P, P, P, I, P, I, I, I, I, P, P, P,
+                                   ctypes.c_size_t, P],
             "zq_gemm_plan": [I, I, I, I, ctypes.c_char_p, I],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I
+        L.zq_gemm_quant_workspace_bytes.argtypes = [I, I]
+        L.zq_gemm_quant_workspace_bytes.restype = ctypes.c_size_t
         L.zq_last_error.argtypes = []
         L.zq_last_error.restype = ctypes.c_char_p
         L.zq_version.argtypes = []
@@ -183,6 +190,50 @@ def gemm_w8a8(qx, sx, qw, sw, G, bias=None, act=ACT_NONE, y=None, stream=None):
 def gemm_w4a8(qx, sx, qw4, sw, G, bias=None, act=ACT_NONE, y=None, stream=None):
     """As gemm_w8a8 with nibble-packed W4 weights uint8 [N, K/2]."""
     return _gemm(lib().zq_gemm_w4a8, 4, qx, sx, qw4, sw, G, bias, act, y, stream)
+
+
+def gemm_quant_workspace_bytes(M, N):
+    """Device workspace bytes that the _quant GEMMs need for an M x N output."""
+    return int(lib().zq_gemm_quant_workspace_bytes(M, N))
+
+
+def _gemm_quant(fn, bits, qx, sx, qw, sw, G, bias, act, qy, sy, ws, stream):
+    _need(qx, "qx", torch.int8, dim=2)
+    M, K = qx.shape
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, qx.device, 2)
+    N = qw.shape[0]
+    if qw.shape[1] != (K if bits == 8 else K // 2):
+        raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+    _need(sx, "sx", torch.float32, qx.device)
+    _need(sw, "sw", torch.float32, qx.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, qx.device)
+    qy = torch.empty(M, N, dtype=torch.int8, device=qx.device) if qy is None else qy
+    sy = torch.empty(M, dtype=torch.float32, device=qx.device) if sy is None else sy
+    if ws is None:
+        ws = torch.empty(max(gemm_quant_workspace_bytes(M, N), 16),
+                         dtype=torch.uint8, device=qx.device)
+    _need(qy, "qy", torch.int8, qx.device)
+    _need(sy, "sy", torch.float32, qx.device)
+    _need(ws, "ws", torch.uint8, qx.device)
+    _check(fn(_p(qx), _p(sx), _p(qw), _p(sw), G, _p(bias), int(act), M, N, K,
+              _p(qy), _p(sy), _p(ws), ws.numel(), _stream(qx, stream)))
+    return qy, sy
+
+
+def gemm_w8a8_quant(qx, sx, qw, sw, G, bias=None, act=ACT_NONE, qy=None,
+                    sy=None, ws=None, stream=None):
+    """The fp16 output of gemm_w8a8 quantized token-wise for the next linear:
+    (qy int8 [M,N], sy fp32 [M]), equal to quant_act(gemm_w8a8(...))."""
+    return _gemm_quant(lib().zq_gemm_w8a8_quant, 8, qx, sx, qw, sw, G, bias,
+                       act, qy, sy, ws, stream)
+
+
+def gemm_w4a8_quant(qx, sx, qw4, sw, G, bias=None, act=ACT_NONE, qy=None,
+                    sy=None, ws=None, stream=None):
+    """As gemm_w8a8_quant with nibble-packed W4 weights uint8 [N, K/2]."""
+    return _gemm_quant(lib().zq_gemm_w4a8_quant, 4, qx, sx, qw4, sw, G, bias,
+                       act, qy, sy, ws, stream)
 
 
 def _gemm_i32(fn, bits, qx, qw, acc, stream):

@@ -80,6 +80,47 @@ zq_status gemm_fused(const int8_t *qx, const float *sx, const void *qw,
   return hip_status(zq::launch_gemm(a, (hipStream_t)stream), fn);
 }
 
+zq_status gemm_quant_out(const int8_t *qx, const float *sx, const void *qw,
+                         const float *sw, int G, const void *bias, int act,
+                         int M, int N, int K, int8_t *qy, float *sy, void *ws,
+                         size_t ws_bytes, void *stream, int bits,
+                         const char *fn) {
+  zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (!sw || ((!sx || !qy || !sy || !ws) && M != 0))
+    return fail(ZQ_EINVAL, "%s: null sx/sw/qy/sy/ws", fn);
+  if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(sy, 4) ||
+      !aligned(qy, 16) || !aligned(ws, 16) || (bias && !aligned(bias, 2)))
+    return fail(ZQ_EINVAL, "%s: misaligned sx/sw/sy/qy/ws/bias", fn);
+  if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+    return fail(ZQ_EINVAL, "%s: act=%d", fn, act);
+  if (G <= 0 || N % G != 0)
+    return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  if (N > ZQ_MAX_ROW_K)
+    return fail(ZQ_EUNSUPPORTED, "%s: N=%d exceeds %d", fn, N, ZQ_MAX_ROW_K);
+  if (M == 0) return ok();
+  const size_t need = zq::gemm_quant_ws_bytes(M, N);
+  if (ws_bytes < need)
+    return fail(ZQ_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn,
+                ws_bytes, need);
+  zq::GemmArgs a{};
+  a.qx = qx;
+  a.sx = sx;
+  a.qw = qw;
+  a.sw = sw;
+  a.bias = static_cast<const zq::half_t *>(bias);
+  a.out = nullptr;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.act = act;
+  a.bits = bits;
+  a.raw_i32 = false;
+  return hip_status(zq::launch_gemm_quant(a, qy, sy, ws, (hipStream_t)stream),
+                    fn);
+}
+
 zq_status gemm_raw(const int8_t *qx, const void *qw, int M, int N, int K,
                    int32_t *acc, void *stream, int bits, const char *fn) {
   zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
@@ -178,6 +219,29 @@ zq_status zq_gemm_w8a8_i32(const int8_t *qx, const int8_t *qw, int M, int N,
 zq_status zq_gemm_w4a8_i32(const int8_t *qx, const uint8_t *qw4, int M, int N,
                            int K, int32_t *acc, void *stream) {
   return gemm_raw(qx, qw4, M, N, K, acc, stream, 4, "zq_gemm_w4a8_i32");
+}
+
+zq_status zq_gemm_w8a8_quant(const int8_t *qx, const float *sx,
+                             const int8_t *qw, const float *sw, int G,
+                             const void *bias_fp16, int act, int M, int N,
+                             int K, int8_t *qy, float *sy, void *ws,
+                             size_t ws_bytes, void *stream) {
+  return gemm_quant_out(qx, sx, qw, sw, G, bias_fp16, act, M, N, K, qy, sy, ws,
+                        ws_bytes, stream, 8, "zq_gemm_w8a8_quant");
+}
+
+zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
+                             const uint8_t *qw4, const float *sw, int G,
+                             const void *bias_fp16, int act, int M, int N,
+                             int K, int8_t *qy, float *sy, void *ws,
+                             size_t ws_bytes, void *stream) {
+  return gemm_quant_out(qx, sx, qw4, sw, G, bias_fp16, act, M, N, K, qy, sy,
+                        ws, ws_bytes, stream, 4, "zq_gemm_w4a8_quant");
+}
+
+size_t zq_gemm_quant_workspace_bytes(int M, int N) {
+  if (M <= 0 || N <= 0) return 0;
+  return zq::gemm_quant_ws_bytes(M, N);
 }
 
 zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen) {

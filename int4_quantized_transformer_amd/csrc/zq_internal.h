@@ -142,6 +142,31 @@ __device__ __forceinline__ v2i quant8_pack(const float (&v)[8],
   return r;
 }
 
+// Four values, same per-element results as quant8_pack (the near-half
+// test and its exact fallback decide each element alone).
+__device__ __forceinline__ uint32_t quant4_pack(const float (&v)[4],
+                                                const Quantizer &z) {
+  float q[4];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[i] = __builtin_rintf(v[i] * z.r);
+    const float d = __builtin_fmaf(v[i], z.r, -q[i]);
+    near |= fabsf(d) >= 0.499969482421875f;  // 0.5 - 2^-15
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = __builtin_rintf(v[i] / z.s);
+  }
+  int c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c[i] = (int)__builtin_amdgcn_fmed3f(q[i], -z.qmax, z.qmax);
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c[1], (uint32_t)c[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c[3], (uint32_t)c[2], 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) |
          ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);
@@ -164,6 +189,43 @@ __device__ __forceinline__ float gelu_erf(float z) {
   q = fmaf(u, q, -2.3020436763763428f);
   const float e = __builtin_amdgcn_exp2f(z * q);
   return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// ------------------------------------------------------- fp16 epilogue out
+// Every GEMM epilogue produces its fp16 output through these two helpers, so
+// that the output bits do not depend on the kernel, the tile or on what the
+// compiler contracts (HIP contracts a*b+c and may fold a product and the
+// fp16 conversion into one mixed-precision fma, which rounds once instead
+// of twice):
+//  * no activation: y = a * s + b rounded once, to nearest even, from the
+//    exact value (v_fma_mix{lo,hi}_f16 with a, s as fp32 and b as fp16);
+//  * GeLU: the fp32 value z = fma(a, s, b), GeLU in fp32, then rounded to
+//    fp16 (the GeLU result is made opaque first, so its last product is
+//    never folded into the conversion).
+// Two outputs a_i * s + b_i packed low / high; bb holds b_0 low, b_1 high.
+__device__ __forceinline__ uint32_t fma_half2(float a0, float a1, float s,
+                                              uint32_t bb) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(r)
+      : "v"(a0), "v"(a1), "v"(s), "v"(bb));
+  return r;
+}
+
+__device__ __forceinline__ half_t fma_half(float a, float s, half_t b) {
+  const uint32_t bb = __builtin_bit_cast(uint16_t, b);
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,1]"
+      : "=v"(r)
+      : "v"(a), "v"(s), "v"(bb));
+  return __builtin_bit_cast(half_t, (uint16_t)r);
+}
+
+__device__ __forceinline__ half_t gelu_half(float a, float s, half_t b) {
+  float g = gelu_erf(fmaf(a, s, (float)b));
+  asm("" : "+v"(g));
+  return (half_t)g;
 }
 
 // ------------------------------------------------------------ XCD mapping
@@ -201,6 +263,11 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+// The GEMM's fp16 output quantized token-wise (codes qy [M][N], scales sy
+// [M]) for the next linear; ws: caller workspace of gemm_quant_ws_bytes.
+hipError_t launch_gemm_quant(const GemmArgs &a, int8_t *qy, float *sy,
+                             void *ws, hipStream_t s);
+size_t gemm_quant_ws_bytes(int M, int N);
 // Human-readable schedule for (M, N, K, bits); returns chars written.
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len);
 

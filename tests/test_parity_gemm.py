@@ -5,6 +5,9 @@
   above), ragged M/N tails, several k-tiles, K % 128 == 64, and extreme codes.
 * zq_gemm_{w8a8,w4a8}: fp16 outputs within 1 fp16 ulp + 1e-3 of the
   oracle's fp64 epilogue, with and without bias and GeLU.
+* The same fp16 bits from every kernel (GEMV, streaming, skinny, tiled) for
+  a token, and the linear epilogue correctly rounded (acc * fl32(sx * sw)
+  + b, one rounding to fp16).
 """
 import numpy as np
 import pytest
@@ -137,3 +140,63 @@ def test_gelu_epilogue_dense_range(M, bits):
     torch.cuda.synchronize()
     assert np.abs(z).max() > 7.5
     assert_fp16_close_to_oracle(to_np(y), z, zq.gemm_plan(M, N, K, bits))
+
+
+def _epilogue_inputs(M, N, K, G, bits, seed):
+    x = W.randn_fp16((M, K), seed=seed, std=1.0)
+    w = W.randn_fp16((N, K), seed=seed + 1, std=0.02)
+    b = W.randn_fp16((N,), seed=seed + 2, std=0.5)
+    qx, sx = oracle.quant_tokens(x.numpy())
+    q, sw = oracle.quantize_weights(w.numpy(), G, bits)
+    qw = q if bits == 8 else oracle.pack_w4(q)
+    return qx, sx, q, qw, sw, b
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("act", [0, 1])
+def test_output_bits_do_not_depend_on_plan(bits, act):
+    # a row of y depends only on that token's codes and scale, so rows
+    # computed by the one-token GEMV, the streaming (16 tokens), the skinny
+    # (40 tokens) and the tiled (256 tokens) kernels must be the same bits
+    N, K, G = 512, 2048, 64
+    qx, sx, q, qw, sw, b = _epilogue_inputs(256, N, K, G, bits, 97 + bits + act)
+    d = dev()
+    fn = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    tqw, tsw, tb = torch.from_numpy(qw).to(d), torch.from_numpy(sw).to(d), b.to(d)
+
+    def run(r0, r1):
+        return fn(torch.from_numpy(qx[r0:r1]).to(d),
+                  torch.from_numpy(sx[r0:r1]).to(d), tqw, tsw, G, tb, act)
+
+    assert zq.gemm_plan(256, N, K, bits).startswith("tiled")
+    full = to_np(run(0, 256))
+    for (r0, r1, plan) in [(5, 6, "gemv"), (200, 201, "gemv"), (16, 32, "stream"),
+                           (100, 140, "skinny")]:
+        assert zq.gemm_plan(r1 - r0, N, K, bits).startswith(plan)
+        part = to_np(run(r0, r1))
+        assert np.array_equal(part.view(np.uint16), full[r0:r1].view(np.uint16)), plan
+
+
+@pytest.mark.parametrize("M", [1, 16, 40, 300])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_linear_epilogue_is_correctly_rounded(M, bits):
+    # without an activation each output is acc * fl32(sx * sw) + b rounded
+    # once to the nearest fp16 (ties to even).  In fp64 the product is exact
+    # (|acc| < 2^25, 24-bit scale) and the sum is within 2^-53 relative of
+    # the exact value, which moves the fp16 rounding only for a value that
+    # close to an fp16 tie; numpy's fp64 -> fp16 conversion rounds
+    # correctly (once, not through fp32)
+    N, K, G = 384, 2048, 64
+    qx, sx, q, qw, sw, b = _epilogue_inputs(M, N, K, G, bits, 31 * M + bits)
+    d = dev()
+    fn = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    y = fn(torch.from_numpy(qx).to(d), torch.from_numpy(sx).to(d),
+           torch.from_numpy(qw).to(d), torch.from_numpy(sw).to(d), G, b.to(d), 0)
+    acc = oracle.gemm_i32(qx, q).astype(np.float64)
+    sc = (sx[:, None] * np.repeat(sw, G)[None, :]).astype(np.float32)
+    assert sc.dtype == np.float32 and sx.dtype == np.float32
+    ref = (acc * sc.astype(np.float64) + b.numpy().astype(np.float64)).astype(np.float16)
+    torch.cuda.synchronize()
+    got = to_np(y)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), \
+        (zq.gemm_plan(M, N, K, bits), int((got != ref).sum()))
