@@ -164,11 +164,14 @@ zq_status zq_gemm_w4a8_i32(const int8_t *qx, const uint8_t *qw4, int M, int N,
  *   qy int8 [M][N] and sy fp32 [M]  (16- and 4-byte aligned)
  * equal, bit for bit, to zq_gemm_w8a8 (fp16 y) followed by zq_quant_act(y):
  * sy[t] = max_n |y[t][n]| / 127 over the fp16 outputs, qy = the codes.
- * When every output tile can be resident on the device at once the codes
- * come straight from the GEMM epilogue (no fp16 output is written); else
- * the fp16 output goes through the workspace and the token quantizer.
+ * The fp16 output is written to the workspace and quantized from there
+ * (two kernels on the stream).  A token's scale needs all N outputs of its
+ * row, which different workgroups produce; quantizing inside the GEMM
+ * epilogue would need a device-wide barrier, which costs more on this GPU
+ * than the fp16 round trip it saves.
  *   ws: device workspace of at least zq_gemm_quant_workspace_bytes(M, N)
- *       bytes, 16-byte aligned, owned by the caller; clobbered.
+ *       (= 2 M N) bytes, 16-byte aligned, owned by the caller; clobbered.
+ *       Calls that share a workspace must be ordered (same stream).
  * Errors as zq_gemm_w8a8, plus ZQ_EINVAL for a null or short workspace or
  * null qy/sy, and ZQ_EUNSUPPORTED for N > ZQ_MAX_ROW_K.
  */

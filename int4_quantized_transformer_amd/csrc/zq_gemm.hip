@@ -23,8 +23,6 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-#include <hip/hip_cooperative_groups.h>
-
 #include "zq_internal.h"
 
 #define ZQ_GPTR(p) ((__attribute__((address_space(1))) void *)(p))
@@ -641,146 +639,6 @@ gemm_tiled_kernel(GemmArgs p) {
         store_quad<C::W4, RAW>(p, t, nb, a, sxt, qc);
       }
     }
-}
-
-// ======================================================= quantized output
-// The fp16 output of one linear is the input of the next one's token-wise
-// quantizer (attn-out and FFN2 follow a bias-add or GeLU; the pages fuse
-// that quantization into the producing kernel).  Here the tiled GEMM emits
-// the codes and scales directly, with the results of the unfused pair
-// (fp16 GEMM output, then the token quantizer) and without writing or
-// re-reading the fp16 output:
-//  1. each lane keeps the fp16 values of its outputs in registers and the
-//     tile writes, per token row, the maximum |y| over its BN columns into
-//     a workspace slot of its column tile;
-//  2. a grid-wide barrier (the kernel is launched cooperatively, so every
-//     tile is resident at once);
-//  3. each tile reads the row maxima of all column tiles, forms S = amax /
-//     127 and fl(1/S), quantizes its own values exactly as the token
-//     quantizer does, and stores the codes (staged in LDS, 16-byte stores);
-//     the first column tile writes the scales.
-struct QuantOut {
-  int8_t *qy;   // [M][N]
-  float *sy;    // [M]
-  float *part;  // [tiles_n][M] row maxima per column tile (workspace)
-};
-
-template <class C>
-__global__ void __launch_bounds__(C::NT)
-gemm_tiled_quant_kernel(GemmArgs p, QuantOut o) {
-  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
-  TileCtx<C> x;
-  v16i acc[C::FN][C::FM];
-  tile_mainloop<C, false>(p, lds, x, acc);
-  const int r32 = x.r32, h = x.h, wn0 = x.wn0, wm0 = x.wm0;
-  const int n0 = x.n0, m0 = x.m0, tid = threadIdx.x;
-  const bool gelu = p.act == ZQ_ACT_GELU, has_bias = p.bias != nullptr;
-
-  // 1. fp16 values (as the fp16 output would hold them) and row maxima
-  half_t hv[C::FN][C::FM][16];
-  float mx[C::FM];
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) mx[fm] = 0.0f;
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int tl = wm0 + fm * 32 + r32;
-      const float sc = x.sx_l[tl] * x.swv[fn];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cl = wn0 + fn * 32 + 8 * q + 4 * h;
-        half4 bb = {(half_t)0.0f, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
-        if (has_bias) bb = *reinterpret_cast<const half4 *>(x.bias_l + cl);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int a = acc[fn][fm][4 * q + r];
-          if constexpr (C::W4) a >>= 4;
-          const half_t hz = gelu ? gelu_half((float)a, sc, bb[r])
-                                 : fma_half((float)a, sc, bb[r]);
-          hv[fn][fm][4 * q + r] = hz;
-          const bool in = n0 + cl + r < p.N;  // columns past N do not count
-          mx[fm] = fmaxf(mx[fm], in ? fabsf((float)hz) : 0.0f);
-        }
-      }
-    }
-  float *red = reinterpret_cast<float *>(lds);  // [NWN][BM]
-  __syncthreads();  // every wave is done reading the operand stages
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    // lanes l and l + 32 hold the two column halves of the same token
-    const float m = fmaxf(mx[fm], __shfl_xor(mx[fm], 32));
-    if (h == 0) red[(x.wave % C::NWN) * C::BM + wm0 + fm * 32 + r32] = m;
-  }
-  __syncthreads();
-  // The maxima cross XCDs, whose L2 caches are not coherent with each
-  // other: they are stored and loaded with device-scope (coherent) accesses,
-  // and every wave completes and releases its own stores before the grid
-  // barrier (the barrier's release is issued by one wave of the block).
-  for (int i = tid; i < C::BM; i += C::NT) {
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < C::NWN; ++j) m = fmaxf(m, red[j * C::BM + i]);
-    if (m0 + i < p.M)
-      __hip_atomic_store(&o.part[(size_t)x.tn * p.M + m0 + i], m,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __threadfence();
-
-  // 2. every tile's row maxima are written
-  cooperative_groups::this_grid().sync();
-
-  // 3. scales, codes
-  float *qs = red + C::NWN * C::BM;  // [BM][2]: S, fl(1/S)
-  for (int i = tid; i < C::BM; i += C::NT) {
-    const int t = m0 + i;
-    float amax = 0.0f;
-    if (t < p.M)
-      for (int j = 0; j < x.tiles_n; ++j)
-        amax = fmaxf(amax, __hip_atomic_load(&o.part[(size_t)j * p.M + t],
-                                             __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT));
-    const Quantizer z = make_quantizer(amax, 127.0f);
-    qs[2 * i] = z.s;
-    qs[2 * i + 1] = z.r;
-    if (x.tn == 0 && t < p.M) o.sy[t] = z.s;
-  }
-  __syncthreads();
-  char *codes = lds + ((2 * C::NWN * C::BM + 2 * C::BM) * 4 + 255) / 256 * 256;  // [BM][BN]
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int tl = wm0 + fm * 32 + r32;
-      Quantizer z;
-      z.s = qs[2 * tl];
-      z.r = qs[2 * tl + 1];
-      z.qmax = 127.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cl = wn0 + fn * 32 + 8 * q + 4 * h;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (float)hv[fn][fm][4 * q + r];
-        *reinterpret_cast<uint32_t *>(codes + tl * C::BN + cl) = quant4_pack(v, z);
-      }
-    }
-  __syncthreads();
-  constexpr int CPR = C::BN / 16;  // 16-byte chunks per code row
-  const bool vec = (p.N & 15) == 0 && (((uintptr_t)o.qy) & 15) == 0;
-  for (int i = tid; i < C::BM * CPR; i += C::NT) {
-    const int row = i / CPR, c = i % CPR;
-    const int t = m0 + row, n = n0 + c * 16;
-    if (t >= p.M || n >= p.N) continue;
-    const v4i v = ld16(codes + row * C::BN + c * 16);
-    int8_t *dst = o.qy + (size_t)t * p.N + n;
-    if (vec && n + 16 <= p.N) {
-      *reinterpret_cast<v4i *>(dst) = v;
-    } else {
-      const int8_t *b = reinterpret_cast<const int8_t *>(&v);
-      for (int e = 0; e < 16 && n + e < p.N; ++e) dst[e] = b[e];
-    }
-  }
 }
 
 // ================================================================= skinny
@@ -1720,65 +1578,19 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------- quantized output
-// Cooperative launch of the quantized-output kernel when every tile can be
-// resident at once and the fused epilogue applies (group scales per 32-row
-// fragment, bias staged in LDS); hipErrorNotSupported otherwise.
-template <class C>
-static hipError_t run_tiled_quant(const GemmArgs &a, const QuantOut &o,
-                                  hipStream_t s) {
-  static_assert((2 * C::NWN * C::BM + 2 * C::BM) * 4 + 256 + C::BM * C::BN <=
-                    C::S * C::STAGE,
-                "quantized epilogue fits the operand stages");
-  const bool bias_lds = a.bias && (a.N % 2 == 0) && (((uintptr_t)a.bias & 3) == 0);
-  if ((a.G & 31) != 0 || (a.bias && !bias_lds)) return hipErrorNotSupported;
-  const int tiles = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
-  const void *f = reinterpret_cast<const void *>(&gemm_tiled_quant_kernel<C>);
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, C::NT, 0) !=
-          hipSuccess ||
-      per_cu * device_cus() < tiles)
-    return hipErrorNotSupported;
-  GemmArgs pa = a;
-  QuantOut po = o;
-  void *args[] = {&pa, &po};
-  return hipLaunchCooperativeKernel(f, dim3(tiles), dim3(C::NT), args, 0, s);
-}
-
-template <bool W4>
-static hipError_t run_tile_quant_cfg(int id, const GemmArgs &a,
-                                     const QuantOut &o, hipStream_t s) {
-  switch (id) {
-    case 0: return run_tiled_quant<Tile<128, 128, 64, 64, 2, W4>>(a, o, s);
-    case 4: return run_tiled_quant<Tile<128, 128, 64, 64, 3, W4>>(a, o, s);
-    case 12: return run_tiled_quant<Tile<256, 256, 64, 64, 2, W4>>(a, o, s);
-    case 13: return run_tiled_quant<Tile<192, 256, 64, 64, 2, W4>>(a, o, s);
-    case 14: return run_tiled_quant<Tile<288, 128, 96, 32, 2, W4>>(a, o, s);
-    case 15: return run_tiled_quant<Tile<96, 128, 96, 32, 3, W4>>(a, o, s);
-    default: return hipErrorNotSupported;
-  }
-}
-
-size_t gemm_quant_ws_bytes(int M, int N) {
-  // the fp16 output (fallback path) is the larger of the two uses
-  return (size_t)M * N * 2 + 256;
-}
+// The GEMM's fp16 output in the workspace, then the token quantizer over
+// it: the same kernels as the unfused pair of calls.  (Quantizing in the
+// GEMM epilogue needs every column tile of a token row finished before any
+// of its codes: a grid-wide barrier, whose cost on this device is larger
+// than the fp16 round trip it would save.)
+size_t gemm_quant_ws_bytes(int M, int N) { return (size_t)M * N * 2; }
 
 hipError_t launch_gemm_quant(const GemmArgs &a, int8_t *qy, float *sy,
                              void *ws, hipStream_t s) {
-  const Plan pl = choose(a.M, a.N, a.K, a.bits);
-  if (pl.kind == kTiled) {
-    QuantOut o{qy, sy, static_cast<float *>(ws)};
-    const hipError_t e = a.bits == 4 ? run_tile_quant_cfg<true>(pl.cfg, a, o, s)
-                                     : run_tile_quant_cfg<false>(pl.cfg, a, o, s);
-    if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge)
-      return e;
-    (void)hipGetLastError();  // clear a refused cooperative launch
-  }
-  // unfused: the fp16 output in the workspace, then the token quantizer
   GemmArgs g = a;
   g.out = ws;
   g.raw_i32 = false;
-  hipError_t e = launch_gemm(g, s);
+  const hipError_t e = launch_gemm(g, s);
   if (e != hipSuccess) return e;
   return launch_row_quant(ws, nullptr, nullptr, 0.0f, a.M, a.N, false, qy, sy,
                           nullptr, s);

@@ -142,31 +142,6 @@ __device__ __forceinline__ v2i quant8_pack(const float (&v)[8],
   return r;
 }
 
-// Four values, same per-element results as quant8_pack (the near-half
-// test and its exact fallback decide each element alone).
-__device__ __forceinline__ uint32_t quant4_pack(const float (&v)[4],
-                                                const Quantizer &z) {
-  float q[4];
-  bool near = false;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    q[i] = __builtin_rintf(v[i] * z.r);
-    const float d = __builtin_fmaf(v[i], z.r, -q[i]);
-    near |= fabsf(d) >= 0.499969482421875f;  // 0.5 - 2^-15
-  }
-  if (near) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = __builtin_rintf(v[i] / z.s);
-  }
-  int c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    c[i] = (int)__builtin_amdgcn_fmed3f(q[i], -z.qmax, z.qmax);
-  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c[1], (uint32_t)c[0], 0x0c0c0400u);
-  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c[3], (uint32_t)c[2], 0x0c0c0400u);
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
-
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) |
          ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);

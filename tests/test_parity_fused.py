@@ -1,11 +1,10 @@
 """GPU parity of the GEMMs with token-quantized output (zq_gemm_*_quant):
-the fused producer-side quantization of the next linear's input.
+the quantization of the next linear's input at the producing linear.
 
 * Exact: (qy, sy) equal, bit for bit, zq_gemm_* (fp16 y) followed by
-  zq_quant_act(y) on the same inputs.  Shapes cover the cooperative fused
-  epilogue (tiled plans whose tiles are all resident at once, group scales
-  per 32-row fragment) and every fallback (decode-sized M, G % 32 != 0,
-  more tiles than the device holds at once, odd N with a bias).
+  zq_quant_act(y) on the same inputs, over every GEMM plan (tiled with
+  several tile shapes, GEMV, streaming, skinny), ragged M and N, G not a
+  multiple of 32 and odd N with a bias.
 * Oracle: against the oracle's fp64 epilogue rounded to fp16 and its token
   quantizer.  The GPU fp16 y is within 1 fp16 ulp + 1e-3 of the oracle
   epilogue; with S = amax/127 a difference dy moves a code by dy/S, so codes
@@ -25,18 +24,18 @@ from _util import dev, needs_gpu, to_np
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 CASES = [  # (M, N, K, G, bits, bias, act)
-    (4096, 3072, 768, 64, 8, True, 1),     # BERT-base FFN1: fused, 192x256 tiles
-    (4096, 2304, 768, 64, 8, True, 0),     # fused, 288x128 tiles
-    (4096, 768, 3072, 64, 8, False, 0),    # fused, 96x128 tiles
-    (2048, 4096, 1024, 128, 8, True, 1),   # fused, 128x128 tiles, two per CU
-    (300, 1024, 640, 64, 4, True, 1),      # fused W4, ragged M
-    (130, 320, 192, 32, 8, True, 1),       # fused, ragged N tile
-    (8192, 4096, 1024, 64, 4, True, 1),    # fallback: more tiles than resident
-    (257, 1000, 320, 8, 8, True, 1),       # fallback: G % 32 != 0
-    (200, 999, 256, 3, 8, True, 0),        # fallback: odd N with bias
-    (1, 4096, 4096, 128, 8, True, 1),      # fallback: decode GEMV
-    (16, 2048, 1024, 64, 4, False, 1),     # fallback: decode streaming kernel
-    (64, 512, 512, 64, 8, True, 0),        # fallback: decode skinny kernel
+    (4096, 3072, 768, 64, 8, True, 1),     # BERT-base FFN1: 192x256 tiles
+    (4096, 2304, 768, 64, 8, True, 0),     # 288x128 tiles
+    (4096, 768, 3072, 64, 8, False, 0),    # 96x128 tiles
+    (2048, 4096, 1024, 128, 8, True, 1),   # 128x128 tiles
+    (300, 1024, 640, 64, 4, True, 1),      # W4, ragged M
+    (130, 320, 192, 32, 8, True, 1),       # ragged N tile
+    (8192, 4096, 1024, 64, 4, True, 1),    # BERT-large FFN1, W4
+    (257, 1000, 320, 8, 8, True, 1),       # G % 32 != 0
+    (200, 999, 256, 3, 8, True, 0),        # odd N with bias
+    (1, 4096, 4096, 128, 8, True, 1),      # decode GEMV
+    (16, 2048, 1024, 64, 4, False, 1),     # decode streaming kernel
+    (64, 512, 512, 64, 8, True, 0),        # decode skinny kernel
 ]
 
 
@@ -94,9 +93,8 @@ def test_workspace_is_checked():
 
 
 def test_repeated_calls_reuse_workspace():
-    # one workspace through consecutive calls whose per-tile row maxima land
-    # on the same words (stale values there must never be read), the last
-    # ones smaller
+    # one workspace through consecutive calls of different shapes (stale
+    # contents from a larger call must never be read), the last ones smaller
     d = dev()
     ws = torch.empty(zq.gemm_quant_workspace_bytes(4096, 3072), dtype=torch.uint8,
                      device=d)
