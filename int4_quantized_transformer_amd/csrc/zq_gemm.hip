@@ -153,8 +153,9 @@ __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
 // operand block and 16 k-bytes chosen by its lane half h = l/32; the result
 // lane l holds token t = l%32 and outputs n = 8q + 4h + (0..3), q = 0..3.
 //
-// Block tile BN (n) x BM (t), k in stages of 128 activation bytes (64
-// packed W4 bytes).  Operands travel global -> LDS directly
+// Block tile BN (n) x BM (t), k in stages of KB = 128 activation bytes
+// (64 packed W4 bytes), or KB = 64 for W8 (half the bytes per stage, so
+// twice the stages fit in LDS and more of them are in flight).  Operands travel global -> LDS directly
 // (global_load_lds_dwordx4: each lane's 16 bytes land at a wave-contiguous
 // LDS address, no register staging) through an S-stage ring; while stage k
 // is multiplied, stages k+1 .. k+S-1 are in flight.  One barrier per stage:
@@ -165,17 +166,19 @@ __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
 // LDS rows are unpadded (128 B, or 64 B for packed W4) and their 16-byte
 // chunks are XOR-swizzled so that the 16-byte fragment reads of 8
 // consecutive rows (one LDS cycle) hit 8 different bank groups:
-//   128-byte rows: slot = chunk ^ (row & 7)
-//    64-byte rows: slot = chunk ^ ((row >> 1) & 3)
-template <int BN_, int BM_, int WN_, int WM_, int S_, bool W4_>
+//   128-byte rows: slot = chunk ^ ((row >> 1) & 7)
+//    64-byte rows: slot = chunk ^ ((row >> 2) & 3)
+template <int BN_, int BM_, int WN_, int WM_, int S_, bool W4_, int KB_ = 128>
 struct Tile {
   static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, S = S_;
   static constexpr bool W4 = W4_;
+  static constexpr int KB = KB_, KS = KB_ / 32;     // k-steps of 32 per stage
+  static_assert(KB == 128 || (KB == 64 && !W4), "stage width");
   static constexpr int NWN = BN / WN, NWM = BM / WM;
   static constexpr int NWAVES = NWN * NWM, NT = NWAVES * kWave;
   static constexpr int FN = WN / 32, FM = WM / 32;
-  static constexpr int XROW = 128;                  // activation bytes/row/stage
-  static constexpr int WROW = W4 ? 64 : 128;        // weight bytes/row/stage
+  static constexpr int XROW = KB;                   // activation bytes/row/stage
+  static constexpr int WROW = W4 ? KB / 2 : KB;     // weight bytes/row/stage
   static constexpr int WCPR = WROW / 16, XCPR = XROW / 16;  // chunks per row
   static constexpr int WRPI = 64 / WCPR, XRPI = 64 / XCPR;  // rows per wave copy
   static constexpr int WINS = BN / WRPI, XINS = BM / XRPI;  // wave copies/stage
@@ -244,18 +247,20 @@ __device__ __forceinline__ void issue_stage(const GemmArgs &p, const char *W,
   }
 }
 
-// Wait until at most `left` stages of this wave's copies are in flight.
-template <class C>
+// Wait until at most `left` stages of this wave's copies are in flight
+// (left <= S - 2; each stage is P copies per wave, completed in order).
+template <class C, int L = C::S - 2>
 __device__ __forceinline__ void wait_stages(int left) {
   constexpr int P = C::IW + C::IX;
-  if constexpr (C::S >= 4) {
-    if (left >= 3) { wait_vmcnt<3 * P>(); return; }
+  if constexpr (L > 0) {
+    if (left >= L) {
+      wait_vmcnt<L * P>();
+      return;
+    }
+    wait_stages<C, L - 1>(left);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (C::S >= 3) {
-    if (left >= 2) { wait_vmcnt<2 * P>(); return; }
-  }
-  if (left >= 1) { wait_vmcnt<P>(); return; }
-  wait_vmcnt<0>();
 }
 
 // Operand fragments of one MFMA k-step (32 k): weights a[FN] (for W4 the
@@ -266,8 +271,9 @@ struct Frag {
   v4i b[C::FM];
 };
 
-// Full 128-k stage, k-step s (0..3), lane half h.
-//   W8: weight and activation chunk 2s + h (k = 32s + 16h).
+// Full stage, k-step s (0 .. KS-1), lane half h.
+//   W8: weight and activation chunk 2s + h (k = 32s + 16h) of the stage's
+//       KB-byte rows.
 //   W4: lane half h takes k = 64h + 16s: packed chunk 2h (s = 0, 1) or
 //       2h + 1 (s = 2, 3), read once per pair into raw0 / raw1, and
 //       activation chunk 4h + s.
@@ -277,13 +283,15 @@ __device__ __forceinline__ void fetch(const char *ws, const char *xs, int s,
                                       Frag<C> &f, v4i (&raw)[2][C::FN]) {
   const int x7 = sw128(r32);
   if constexpr (!C::W4) {
-    const int c = 2 * s + h;
+    // rows of XROW bytes; the swizzle depends on the row's low bits only,
+    // which r32 shares with every fragment row
+    const int c = wswz<C::XROW>(2 * s + h, r32);
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
-      f.a[fn] = ld16(ws + (wn0 + fn * 32 + r32) * 128 + ((c ^ x7) << 4));
+      f.a[fn] = ld16(ws + (wn0 + fn * 32 + r32) * C::XROW + (c << 4));
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
-      f.b[fm] = ld16(xs + (wm0 + fm * 32 + r32) * 128 + ((c ^ x7) << 4));
+      f.b[fm] = ld16(xs + (wm0 + fm * 32 + r32) * C::XROW + (c << 4));
   } else {
     const int w4 = sw64(r32);
     if (s == 0 || s == 2) {
@@ -321,6 +329,25 @@ __device__ __forceinline__ void mma(const Frag<C> &f, int s,
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
       acc[fn][fm] = mfma32_i8(a[fn], b[fm], acc[fn][fm]);
+}
+
+// Instruction order inside one k-step region: the LDS reads of the next
+// k-step (fragments for k-step SN) are issued first, then the MFMAs of the
+// current one, so that the reads complete under all of those MFMAs (left
+// to itself the scheduler sinks the reads below most of the MFMAs and the
+// next region then waits for them).
+template <class C, int SN>
+__device__ __forceinline__ void reads_then_mfma() {
+  constexpr int R = C::FM + (C::W4 ? ((SN == 0 || SN == 2) ? C::FN : 0) : C::FN);
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);             // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, C::FN * C::FM, 0);  // MFMA
+}
+
+// lgkmcnt(N), no wait on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (N << 8) | (0x3 << 14));
 }
 
 // 64-k tail stage, k-step s (0, 1): k = 32s + 16h.  W8: chunk 2s + h.
@@ -362,13 +389,13 @@ __device__ __forceinline__ void tail_stage(const char *ws, const char *xs,
 // Main loop schedule (S LDS slots; stage j is copied into slot j % S):
 //   prologue: copy stages 0 .. S-1, wait for stage 0, barrier, read the
 //             fragments of (stage 0, k-step 0).
-//   stage kt, k-step s = 0, 1, 2: read fragments of k-step s+1 into the
+//   stage kt, k-step s < KS-1: read fragments of k-step s+1 into the
 //             other register set, then issue the MFMAs of k-step s (the
 //             reads complete under the MFMAs).
-//   k-step 3: wait for stage kt+1's copies and for this wave's LDS reads,
+//   k-step KS-1: wait for stage kt+1's copies and for this wave's LDS reads,
 //             barrier (now every wave is done with slot kt % S and stage
 //             kt+1 is visible), copy stage kt+S into slot kt % S, read
-//             fragments of (stage kt+1, k-step 0), MFMAs of k-step 3.
+//             fragments of (stage kt+1, k-step 0), MFMAs of k-step KS-1.
 // Staged epilogue of the tiled kernel.  The fp16 tile goes through LDS so
 // that every global store writes whole row segments with 16 bytes per lane.
 // Layout: row t of the tile holds BN halves; its 16-byte chunks are
@@ -557,6 +584,11 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
   Frag<C> f0, f1;
   v4i raw[2][C::FN];
   if (KTF > 0) fetch<C>(lds, lds + C::WBYTES, 0, wn0, wm0, r32, h, f0, raw);
+  // Scalar loads (the group scales above) share the LDS counter and return
+  // out of order: while one is pending every LDS wait in the loop would
+  // have to be lgkmcnt(0).  Complete them here, once.
+  wait_lgkmcnt<0>();
+  __builtin_amdgcn_sched_barrier(0);
 
   // sched_barrier(0) keeps the phases in this order (the scheduler would
   // otherwise hoist the barrier above the MFMAs of k-step 2).
@@ -565,28 +597,36 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
     const char *xs = ws + C::WBYTES;
     fetch<C>(ws, xs, 1, wn0, wm0, r32, h, f1, raw);
     mma<C>(f0, 0, raw, acc);
+    reads_then_mfma<C, 1>();
     __builtin_amdgcn_sched_barrier(0);
-    fetch<C>(ws, xs, 2, wn0, wm0, r32, h, f0, raw);
-    mma<C>(f1, 1, raw, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch<C>(ws, xs, 3, wn0, wm0, r32, h, f1, raw);
-    mma<C>(f0, 2, raw, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    // k-step 3: stage boundary
+    if constexpr (C::KS == 4) {
+      fetch<C>(ws, xs, 2, wn0, wm0, r32, h, f0, raw);
+      mma<C>(f1, 1, raw, acc);
+      reads_then_mfma<C, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+      fetch<C>(ws, xs, 3, wn0, wm0, r32, h, f1, raw);
+      mma<C>(f0, 2, raw, acc);
+      reads_then_mfma<C, 3>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // last k-step (KS - 1, held in f1): stage boundary
     wait_stages<C>(max(0, min(C::S - 2, KT - 2 - kt)));
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own LDS reads done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (kt + C::S < KT)
       issue_stage<C>(p, W, X, ldw, n0, m0, kt + C::S, ws, wave, lane);
-    if (kt + 1 < KTF) {
+    {
+      // unconditional (after the last stage it reads a stale slot, in
+      // bounds, and the fragments go unused): a conditional read here
+      // makes the compiler wait for every LDS read at the loop head
       char *wn = lds + ((kt + 1) % C::S) * C::STAGE;
       fetch<C>(wn, wn + C::WBYTES, 0, wn0, wm0, r32, h, f0, raw);
     }
-    mma<C>(f1, 3, raw, acc);
+    mma<C>(f1, C::KS - 1, raw, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (half_tail) {
+  if constexpr (C::KB == 128) if (half_tail) {
     const char *ws = lds + ((KT - 1) % C::S) * C::STAGE;
     tail_stage<C>(ws, ws + C::WBYTES, wn0, wm0, r32, h, acc);
   }
@@ -1360,27 +1400,39 @@ static hipError_t run_skinny(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tiled configurations: {BN, BM, WN, WM, stages}.
+// Tiled configurations: {BN, BM, WN, WM, stages, stage k-bytes}.
 struct TileCfg {
-  int bn, bm, wn, wm, s;
+  int bn, bm, wn, wm, s, kb;
 };
 static const TileCfg kTileCfgs[] = {
-    {128, 128, 64, 64, 2},    // 0: 4 waves
-    {256, 128, 128, 64, 2},   // 1: 4 waves
-    {128, 256, 64, 128, 2},   // 2: 4 waves
-    {256, 256, 128, 128, 2},  // 3: 4 waves
-    {128, 128, 64, 64, 3},    // 4: 4 waves
-    {256, 256, 128, 64, 2},   // 5: 8 waves
-    {256, 128, 128, 64, 3},   // 6: 4 waves
-    {192, 256, 96, 128, 2},   // 7: 4 waves
-    {192, 128, 96, 64, 2},    // 8: 4 waves
-    {128, 192, 64, 96, 2},    // 9: 4 waves
-    {256, 128, 64, 64, 3},    // 10: 8 waves
-    {128, 256, 64, 64, 3},    // 11: 8 waves
-    {256, 256, 64, 64, 2},    // 12: 16 waves
-    {192, 256, 64, 64, 2},    // 13: 12 waves
-    {288, 128, 96, 32, 2},    // 14: 12 waves
-    {96, 128, 96, 32, 3},     // 15: 4 waves
+    {128, 128, 64, 64, 2, 128},    // 0: 4 waves
+    {256, 128, 128, 64, 2, 128},   // 1: 4 waves
+    {128, 256, 64, 128, 2, 128},   // 2: 4 waves
+    {256, 256, 128, 128, 2, 128},  // 3: 4 waves
+    {128, 128, 64, 64, 3, 128},    // 4: 4 waves
+    {256, 256, 128, 64, 2, 128},   // 5: 8 waves
+    {256, 128, 128, 64, 3, 128},   // 6: 4 waves
+    {192, 256, 96, 128, 2, 128},   // 7: 4 waves
+    {192, 128, 96, 64, 2, 128},    // 8: 4 waves
+    {128, 192, 64, 96, 2, 128},    // 9: 4 waves
+    {256, 128, 64, 64, 3, 128},    // 10: 8 waves
+    {128, 256, 64, 64, 3, 128},    // 11: 8 waves
+    {256, 256, 64, 64, 2, 128},    // 12: 16 waves
+    {192, 256, 64, 64, 2, 128},    // 13: 12 waves
+    {288, 128, 96, 32, 2, 128},    // 14: 12 waves
+    {96, 128, 96, 32, 3, 128},     // 15: 4 waves
+    {256, 256, 64, 64, 4, 64},   // 16: 16 waves, W8 only
+    {256, 256, 128, 64, 4, 64},  // 17: 8 waves, W8 only
+    {192, 256, 64, 64, 4, 64},   // 18: 12 waves, W8 only
+    {128, 256, 64, 64, 5, 64},   // 19: 8 waves, W8 only
+    {128, 128, 64, 64, 6, 64},   // 20: 4 waves, W8 only
+    {128, 64, 64, 32, 6, 128},   // 21: 4 waves (decode-sized M)
+    {64, 64, 32, 32, 8, 128},    // 22: 4 waves
+    {64, 64, 32, 32, 12, 64},    // 23: 4 waves, W8 only
+    {128, 32, 64, 32, 6, 128},   // 24: 2 waves
+    {64, 64, 32, 32, 9, 128},    // 25: 4 waves
+    {64, 32, 32, 32, 10, 128},   // 26: 2 waves
+    {64, 64, 64, 32, 8, 128},    // 27: 2 waves
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 
@@ -1402,8 +1454,21 @@ static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
     case 13: return run_tiled<Tile<192, 256, 64, 64, 2, W4>, RAW>(a, s);
     case 14: return run_tiled<Tile<288, 128, 96, 32, 2, W4>, RAW>(a, s);
     case 15: return run_tiled<Tile<96, 128, 96, 32, 3, W4>, RAW>(a, s);
-    default: return run_tiled<Tile<256, 256, 64, 64, 2, W4>, RAW>(a, s);
+    case 16: if constexpr (!W4) return run_tiled<Tile<256, 256, 64, 64, 4, W4, 64>, RAW>(a, s); break;
+    case 17: if constexpr (!W4) return run_tiled<Tile<256, 256, 128, 64, 4, W4, 64>, RAW>(a, s); break;
+    case 18: if constexpr (!W4) return run_tiled<Tile<192, 256, 64, 64, 4, W4, 64>, RAW>(a, s); break;
+    case 19: if constexpr (!W4) return run_tiled<Tile<128, 256, 64, 64, 5, W4, 64>, RAW>(a, s); break;
+    case 20: if constexpr (!W4) return run_tiled<Tile<128, 128, 64, 64, 6, W4, 64>, RAW>(a, s); break;
+    case 21: return run_tiled<Tile<128, 64, 64, 32, 6, W4>, RAW>(a, s);
+    case 22: return run_tiled<Tile<64, 64, 32, 32, 8, W4>, RAW>(a, s);
+    case 23: if constexpr (!W4) return run_tiled<Tile<64, 64, 32, 32, 12, W4, 64>, RAW>(a, s); break;
+    case 24: return run_tiled<Tile<128, 32, 64, 32, 6, W4>, RAW>(a, s);
+    case 25: return run_tiled<Tile<64, 64, 32, 32, 9, W4>, RAW>(a, s);
+    case 26: return run_tiled<Tile<64, 32, 32, 32, 10, W4>, RAW>(a, s);
+    case 27: return run_tiled<Tile<64, 64, 64, 32, 8, W4>, RAW>(a, s);
+    default: break;
   }
+  return run_tiled<Tile<256, 256, 64, 64, 2, W4>, RAW>(a, s);
 }
 
 enum PlanKind { kSkinny = 0, kTiled = 1, kStream = 2, kGemv = 3 };
@@ -1426,7 +1491,8 @@ static int forced_tile() {
 
 // Schedule selection by problem shape (the pages pick, per batch x seqlen,
 // the tiling with the least waste).  Decode-sized M (<= 64) goes to the
-// weight-streaming kernels.  Otherwise, from measured sweeps of every
+// weight-streaming kernels, or for 17 .. 64 tokens over wide N to 64x64
+// tiles with a deep copy ring.  Otherwise, from measured sweeps of every
 // configuration on the five workloads:
 //  * when 128x128 tiles fit one per compute unit: three-stage tiles (one
 //    block per CU, deeper prefetch) of 128x128 or 96x128, by the score below;
@@ -1489,6 +1555,8 @@ static int forced_gemv() {
 }
 
 static Plan choose(int M, int N, int K, int bits) {
+  const int f = forced_tile();
+  if (f >= 0) return Plan{kTiled, 0, f};
   if (M <= 64) {
     const int fd = forced_decode();
     const int ldw = bits == 4 ? K / 2 : K;
@@ -1498,10 +1566,13 @@ static Plan choose(int M, int N, int K, int bits) {
     if (fd == 2 && stream_ok) return Plan{kStream, M == 1 ? 1 : 16, 0};
     if (gemv_ok) return Plan{kGemv, 1, 0};
     if (stream_ok) return Plan{kStream, M == 1 ? 1 : 16, 0};
+    // 17 .. 64 tokens: 64-row weight tiles with the activations staged once
+    // per tile in LDS and an 8-deep copy ring, when there are enough tiles
+    // to keep most compute units streaming (the skinny kernel re-reads the
+    // whole activation block for every 16 weight rows)
+    if (fd < 0 && (N + 63) / 64 >= 128) return Plan{kTiled, 0, 22};
     return Plan{kSkinny, (M + 15) / 16, 0};
   }
-  const int f = forced_tile();
-  if (f >= 0) return Plan{kTiled, 0, f};
   const long tiles128 = (long)((N + 127) / 128) * ((M + 127) / 128);
   if (tiles128 <= device_cus()) return Plan{kTiled, 0, pick(kSmallCandidates, M, N)};
   if (bits == 4) return Plan{kTiled, 0, 0};
@@ -1609,8 +1680,8 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
                     pl.mf, pl.mf <= 2 ? 4 : 2, bits, (N + 15) / 16);
   const TileCfg &c = kTileCfgs[pl.cfg];
   return snprintf(buf, len,
-                  "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d W%d tiles=%d",
-                  pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, bits,
+                  "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d kb=%d W%d tiles=%d",
+                  pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, c.kb, bits,
                   ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm));
 }
 

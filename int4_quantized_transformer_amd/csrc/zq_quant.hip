@@ -18,6 +18,9 @@ namespace zq {
 // so global reads are 16-byte per lane and fully coalesced across the team,
 // and the int8 writes are 8-byte per lane.  VEC = false is the same
 // algorithm with scalar, bounds-checked accesses for K % 8 != 0.
+// Teams of 16 or 32 lanes (short rows) put several rows in one wave: the
+// rows share the reduction instructions and no lane idles; teams of 256 or
+// 1024 threads (long rows, or few rows) reduce through LDS.
 template <int TPR>
 struct RowTeam {
   static constexpr int kBlock = TPR < 256 ? 256 : TPR;
@@ -27,6 +30,11 @@ struct RowTeam {
 
 template <int TPR>
 __device__ __forceinline__ float team_sum(float v, float *lds) {
+  if constexpr (TPR == 16) return rows_of_16_sum(v);
+  if constexpr (TPR == 32) {
+    v = rows_of_16_sum(v);
+    return v + __shfl_xor(v, 16);
+  }
   v = wave_sum(v);
   if constexpr (TPR > kWave) {
     const int w = threadIdx.x / kWave;
@@ -43,6 +51,11 @@ __device__ __forceinline__ float team_sum(float v, float *lds) {
 
 template <int TPR>
 __device__ __forceinline__ float team_max(float v, float *lds) {
+  if constexpr (TPR == 16) return rows_of_16_max(v);
+  if constexpr (TPR == 32) {
+    v = rows_of_16_max(v);
+    return fmaxf(v, __shfl_xor(v, 16));
+  }
   v = wave_max(v);
   if constexpr (TPR > kWave) {
     const int w = threadIdx.x / kWave;
@@ -68,8 +81,9 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
   const int team = threadIdx.x / TPR;
   const int tl = threadIdx.x % TPR;
   const int row = blockIdx.x * T::kRows + team;
-  // Teams are whole waves (TPR >= 64); with TPR > 64 the block holds one
-  // team, so a row past the end retires the entire block together.
+  // A row past the end retires its whole team (16 or 32 lanes of a wave, a
+  // wave, or with TPR > 64 the entire block), so every cross-lane step of
+  // a live team reads live lanes only.
   if (row >= M) return;
 
   const half_t *xr = x + (size_t)row * K;
@@ -243,10 +257,19 @@ static hipError_t dispatch_tpr(const half_t *x, const half_t *g,
                                const half_t *b, float eps, int M, int K,
                                int8_t *qx, float *sx, half_t *ln_out,
                                hipStream_t s) {
+  // the smallest team that holds the row in at most 8 chunks per thread;
+  // then, while fewer than 1024 waves would run, larger teams (down to 2
+  // chunks per thread) so that a few rows still spread over the device
   const int chunks = (K + 7) / 8;
-  int tpr = chunks <= 8 * 64 ? 64 : (chunks <= 8 * 256 ? 256 : 1024);
+  auto next = [](int t) { return t < 64 ? 2 * t : 4 * t; };
+  int tpr = 16;
+  while (tpr < 1024 && (chunks + tpr - 1) / tpr > 8) tpr = next(tpr);
+  while (tpr < 1024 && (long)M * tpr < 1024L * 64 && chunks >= 2 * next(tpr))
+    tpr = next(tpr);
   const int per = (chunks + tpr - 1) / tpr;
   const int nch = per <= 4 ? per : (per <= 6 ? 6 : 8);
+  if (tpr == 16) return dispatch_nch<16, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
+  if (tpr == 32) return dispatch_nch<32, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
   if (tpr == 64) return dispatch_nch<64, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
   if (tpr == 256) return dispatch_nch<256, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
   return dispatch_nch<1024, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);

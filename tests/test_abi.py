@@ -104,7 +104,8 @@ def test_header_limits_match_int32_bound():
 def test_gemm_plan_covers_every_regime():
     # one token with whole 1 KB weight-row pieces: GEMV; other one-token or
     # up-to-16-token problems with even N: streaming kernel; up to 64
-    # tokens otherwise: skinny kernel; above: tiled
+    # tokens: 64x64 tiles when N gives at least 128 of them, else the
+    # skinny kernel; above: tiled
     assert Z.gemm_plan(1, 4096, 4096, 8).startswith("gemv")
     assert Z.gemm_plan(1, 4096, 4096, 4).startswith("gemv")
     assert Z.gemm_plan(1, 4096, 1024, 4).startswith("stream")
@@ -112,6 +113,8 @@ def test_gemm_plan_covers_every_regime():
     assert Z.gemm_plan(16, 4096, 4096, 8).startswith("stream")
     assert Z.gemm_plan(17, 4096, 4096, 8).startswith("skinny")
     assert Z.gemm_plan(64, 4096, 4096, 4).startswith("skinny")
+    assert Z.gemm_plan(17, 8192, 4096, 8).startswith("tiled cfg=22")
+    assert Z.gemm_plan(64, 16384, 4096, 4).startswith("tiled cfg=22")
     assert Z.gemm_plan(65, 4096, 4096, 8).startswith("tiled")
     assert Z.gemm_plan(2048, 4096, 4096, 8).startswith("tiled")
     with pytest.raises(Z.ZQError):

@@ -27,6 +27,7 @@ SHAPES = [  # (M, N, K)
     (65, 320, 576), (128, 128, 128), (200, 384, 1024), (257, 200, 64),
     (300, 1000, 640), (512, 768, 3072), (1, 4096, 4096), (7, 64, 24576),
     (1, 1000, 1024), (1, 77, 2048), (1, 3000, 8192), (16, 24, 2048),
+    (40, 8200, 384), (64, 12288, 256),
 ]
 
 
@@ -80,7 +81,7 @@ def test_i32_extreme_codes(M, bits):
     (16, 256, 256, 64), (1, 4096, 1024, 128), (5, 384, 768, 128),
     (64, 512, 512, 64), (100, 320, 192, 64), (300, 768, 768, 64),
     (257, 1000, 320, 8), (2048, 256, 512, 128), (3, 20, 64, 4),
-    (1, 2048, 4096, 64), (1, 72, 2048, 8)])
+    (1, 2048, 4096, 64), (1, 72, 2048, 8), (48, 8192, 512, 128)])
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("bias,act", [(True, 0), (True, 1), (False, 1),
                                       (False, 0)])
