@@ -331,18 +331,6 @@ __device__ __forceinline__ void mma(const Frag<C> &f, int s,
       acc[fn][fm] = mfma32_i8(a[fn], b[fm], acc[fn][fm]);
 }
 
-// Instruction order inside one k-step region: the LDS reads of the next
-// k-step (fragments for k-step SN) are issued first, then the MFMAs of the
-// current one, so that the reads complete under all of those MFMAs (left
-// to itself the scheduler sinks the reads below most of the MFMAs and the
-// next region then waits for them).
-template <class C, int SN>
-__device__ __forceinline__ void reads_then_mfma() {
-  constexpr int R = C::FM + (C::W4 ? ((SN == 0 || SN == 2) ? C::FN : 0) : C::FN);
-  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);             // DS reads
-  __builtin_amdgcn_sched_group_barrier(0x008, C::FN * C::FM, 0);  // MFMA
-}
-
 // lgkmcnt(N), no wait on the other counters.
 template <int N>
 __device__ __forceinline__ void wait_lgkmcnt() {
@@ -597,16 +585,13 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
     const char *xs = ws + C::WBYTES;
     fetch<C>(ws, xs, 1, wn0, wm0, r32, h, f1, raw);
     mma<C>(f0, 0, raw, acc);
-    reads_then_mfma<C, 1>();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (C::KS == 4) {
       fetch<C>(ws, xs, 2, wn0, wm0, r32, h, f0, raw);
       mma<C>(f1, 1, raw, acc);
-      reads_then_mfma<C, 2>();
       __builtin_amdgcn_sched_barrier(0);
       fetch<C>(ws, xs, 3, wn0, wm0, r32, h, f1, raw);
       mma<C>(f0, 2, raw, acc);
-      reads_then_mfma<C, 3>();
       __builtin_amdgcn_sched_barrier(0);
     }
     // last k-step (KS - 1, held in f1): stage boundary
