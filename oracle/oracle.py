@@ -17,7 +17,7 @@ from . import build as _build
 __all__ = [
     "lib", "half_to_double", "double_to_half", "quantize_weights", "pack_w4",
     "unpack_w4", "layernorm", "quant_tokens", "gemm_i32", "epilogue",
-    "linear", "threads",
+    "linear", "gemm_w8a16", "threads",
 ]
 
 _lib = None
@@ -46,6 +46,7 @@ def lib():
         L.zqo_gemm_i32.argtypes = [P, P, I, I, I, P]
         L.zqo_gemm_i32.restype = ctypes.c_long
         L.zqo_epilogue.argtypes = [P, P, P, I, P, I, I, I, P, P]
+        L.zqo_gemm_w8a16.argtypes = [P, P, P, I, P, I, I, I, I, P, P]
         L.zqo_threads.argtypes = []
         L.zqo_threads.restype = I
         _lib = L
@@ -169,6 +170,23 @@ def linear(x, qw, sw, G, bias=None, act=0, ln=False, gamma=None, beta=None,
     acc = gemm_i32(qx, qw)
     z, y = epilogue(acc, sx, sw, G, bias, act)
     return {"h": h, "qx": qx, "sx": sx, "acc": acc, "z": z, "y": y}
+
+
+def gemm_w8a16(x, q, sw, G, bias=None, act=0):
+    """W8A16 linear (fp16 activations x [M,K], int8 codes q [N,K], group
+    scales sw [N/G]): fp64 (z [M,N]) and its fp16 rounding (y)."""
+    x = _h(x)
+    q = _c(q, np.int8)
+    sw = _c(sw, np.float32)
+    M, K = x.shape
+    N, K2 = q.shape
+    assert K == K2 and N % G == 0
+    b = None if bias is None else _h(bias)
+    z = np.empty((M, N), np.float64)
+    y = np.empty((M, N), np.uint16)
+    lib().zqo_gemm_w8a16(_ptr(x), _ptr(q), _ptr(sw), G, _ptr(b), act, M, N, K,
+                         _ptr(z), _ptr(y))
+    return z, y.view(np.float16)
 
 
 def threads():

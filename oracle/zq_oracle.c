@@ -302,6 +302,45 @@ void zqo_epilogue(const int32_t *acc, const float *sx, const float *sw, int G,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* W8A16 linear: INT8 group-wise weights with FP16 activations, the mixed    */
+/* scheme of [SUM] Sec. 5 "Experiments" (Table 4: W8A16, INT8 weights and    */
+/* FP16 activations; Table 8: GPT-NeoX20B keeps the self-attention input     */
+/* activations in FP16 while its weights are INT8).  Plain definition: each  */
+/* weight is dequantized, w[n][k] = sw[n/G] * q[n][k], and                   */
+/*   z[t][n] = act( sum_k x[t][k] * w[n][k] + bias[n] ),  y = fp16(z).       */
+/* fp64 throughout (every product of a binary16 value and a dequantized      */
+/* weight is exact in fp64).  act: 0 = none, 1 = exact-erf GeLU; bias may    */
+/* be NULL.                                                                  */
+/* ------------------------------------------------------------------------ */
+void zqo_gemm_w8a16(const uint16_t *x, const int8_t *q, const float *sw, int G,
+                    const uint16_t *bias, int act, int M, int N, int K,
+                    double *z, uint16_t *y)
+{
+    long idx;
+    long total = (long)M * N;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < total; idx++) {
+        int t = (int)(idx / N), n = (int)(idx % N);
+        const uint16_t *a = x + (size_t)t * K;
+        const int8_t *b = q + (size_t)n * K;
+        double s = 0.0;
+        int k;
+        for (k = 0; k < K; k++) {
+            double w = (double)sw[n / G] * (double)b[k];
+            s += zqo_half_to_double(a[k]) * w;
+        }
+        if (bias)
+            s += zqo_half_to_double(bias[n]);
+        if (act == 1)
+            s = 0.5 * s * (1.0 + erf(s / sqrt(2.0)));
+        if (z)
+            z[idx] = s;
+        if (y)
+            y[idx] = zqo_double_to_half(s);
+    }
+}
+
 /* Threads the OpenMP loops above use (reported with CPU timings). */
 int zqo_threads(void)
 {

@@ -39,6 +39,16 @@ MUTANTS = {
     "w4_nibble_order": ("(uint8_t)(lo | (hi << 4))", "(uint8_t)(hi | (lo << 4))"),
     # binary16 rounding by truncation
     "half_truncates": ("n = rint(a / quantum);", "n = floor(a / quantum);"),
+    # W8A16: activation index off by one
+    "w8a16_shifted_k": ("s += zqo_half_to_double(a[k]) * w;",
+                        "s += zqo_half_to_double(a[(k + 1) % K]) * w;"),
+    # W8A16: group scale not applied
+    "w8a16_no_scale": ("double w = (double)sw[n / G] * (double)b[k];",
+                       "double w = (double)b[k];"),
+    # W8A16: bias dropped
+    "w8a16_no_bias": ("s += zqo_half_to_double(bias[n]);", "s += 0.0;"),
+    # W8A16: GeLU with erf(x) instead of erf(x / sqrt 2)
+    "w8a16_gelu_wrong_arg": ("erf(s / sqrt(2.0))", "erf(s)"),
 }
 
 

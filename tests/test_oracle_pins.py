@@ -356,3 +356,70 @@ def test_w48_memory_is_one_third_of_fp16():
         fp16 = sum(L.N * L.K * 2 for L in wl.linears)
         q = sum(L.N * L.K * L.bits // 8 for L in wl.linears)
         assert fp16 == 3 * q
+
+
+# ------------------------------------------------------------------ W8A16 ----
+def test_w8a16_brute_force_exact_rationals():
+    # sum_k x*(sw*q) + b evaluated exactly with Fractions on tiny inputs
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    for (M, N, K, G) in [(1, 1, 1, 1), (2, 4, 5, 2), (3, 6, 9, 3)]:
+        x = _f16(rng.normal(0, 2, (M, K)))
+        q = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        sw = rng.uniform(0.001, 0.05, N // G).astype(np.float32)
+        b = _f16(rng.normal(0, 0.5, N))
+        z, y = oracle.gemm_w8a16(x, q, sw, G, b, 0)
+        for t in range(M):
+            for n in range(N):
+                e = sum(Fraction(float(x[t, k])) * Fraction(float(sw[n // G]))
+                        * int(q[n, k]) for k in range(K)) + Fraction(float(b[n]))
+                assert abs(z[t, n] - float(e)) <= 1e-12 * max(1.0, abs(float(e)))
+                assert y[t, n] == np.float16(float(e))
+
+
+def test_w8a16_one_hot_closed_form():
+    # token c*e_j selects column j of the dequantized weights: z = c*sw*q + b
+    K, N, G = 16, 8, 4
+    rng = np.random.default_rng(37)
+    q = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    sw = np.array([0.5, 0.25], np.float32)
+    b = _f16(np.arange(N) * 0.125)
+    x = np.zeros((3, K), np.float16)
+    x[0, 3] = 2.0
+    x[1, 15] = -0.5
+    z, _ = oracle.gemm_w8a16(x, q, sw, G, b, 0)
+    for n in range(N):
+        assert z[0, n] == 2.0 * float(sw[n // G]) * int(q[n, 3]) + float(b[n])
+        assert z[1, n] == -0.5 * float(sw[n // G]) * int(q[n, 15]) + float(b[n])
+        assert z[2, n] == float(b[n])
+
+
+def test_w8a16_agrees_with_the_integer_path():
+    # activations that are exact multiples sx*qx (sx a power of two) give the
+    # same result through the integer GEMM and the dequantization epilogue
+    rng = np.random.default_rng(41)
+    M, N, K, G = 6, 64, 96, 16
+    qx = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.full(M, 2.0 ** -4, np.float32)
+    x = (qx.astype(np.float64) * 2.0 ** -4).astype(np.float16)
+    assert np.array_equal(x.astype(np.float64), qx * 2.0 ** -4)
+    q = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    sw = rng.uniform(0.001, 0.05, N // G).astype(np.float32)
+    b = _f16(rng.normal(0, 0.5, N))
+    for act in (0, 1):
+        z, y = oracle.gemm_w8a16(x, q, sw, G, b, act)
+        z2, y2 = oracle.epilogue(oracle.gemm_i32(qx, q), sx, sw, G, b, act)
+        assert np.allclose(z, z2, rtol=1e-12, atol=1e-12)
+        assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+def test_w8a16_gelu_is_erf_gelu_of_the_linear_value():
+    rng = np.random.default_rng(43)
+    x = _f16(rng.normal(0, 1, (4, 32)))
+    q = rng.integers(-127, 128, (8, 32)).astype(np.int8)
+    sw = np.full(2, 0.01, np.float32)
+    z0, _ = oracle.gemm_w8a16(x, q, sw, 4, None, 0)
+    z1, _ = oracle.gemm_w8a16(x, q, sw, 4, None, 1)
+    ref = np.vectorize(lambda v: 0.5 * v * (1 + math.erf(v / math.sqrt(2))))(z0)
+    assert np.allclose(z1, ref, rtol=1e-14, atol=1e-15)
+    assert np.abs(z0).max() > 1.0   # the GeLU sees values on both sides of 0
