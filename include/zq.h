@@ -190,6 +190,28 @@ zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
 size_t zq_gemm_quant_workspace_bytes(int M, int N);
 
 /*
+ * zq_gemm_w8a16 -- INT8 group-wise weights with FP16 activations, the mixed
+ * scheme of the summary page's Sec. 5 "Experiments" (Table 4: W8A16;
+ * Table 8: GPT-NeoX20B keeps its self-attention inputs in FP16 while the
+ * weights are INT8):
+ *     y[t][n] = fp16(act(sw[n / G] * sum_k x[t][k] * qw[n][k] + bias[n]))
+ * The codes enter an fp16 matrix multiply unchanged (every INT8 value is
+ * exact in fp16) with fp32 accumulation; the group scale, constant along k,
+ * is applied in the epilogue, so no dequantized weight is ever rounded.
+ *   x fp16 [M][K] (16-byte aligned), qw int8 [N][K], sw fp32 [N/G],
+ *   bias fp16 [N] or NULL, y fp16 [M][N].
+ * Errors: ZQ_EINVAL (null/misaligned pointer, act not 0/1), ZQ_ESHAPE
+ * (M < 0, N or K <= 0, G <= 0, N % G != 0), ZQ_EUNSUPPORTED (K % 64 != 0,
+ * K > ZQ_MAX_GEMM_K_A16).
+ */
+#define ZQ_MAX_GEMM_K_A16 1048576
+zq_status zq_gemm_w8a16(const void *x_fp16, const int8_t *qw, const float *sw,
+                        int G, const void *bias_fp16, int act, int M, int N,
+                        int K, void *y_fp16, void *stream);
+/* The tile configuration zq_gemm_w8a16 picks (as zq_gemm_plan). */
+zq_status zq_gemm_w8a16_plan(int M, int N, int K, char *buf, int buflen);
+
+/*
  * zq_gemm_plan -- which kernel and tile shape the GEMM calls pick for a
  * problem (the schedule chosen by token count, paper App. D), written as a
  * NUL-terminated string into buf (at most buflen bytes).  No launch.
@@ -202,7 +224,7 @@ const char *zq_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int zq_version(void);
-#define ZQ_VERSION 101
+#define ZQ_VERSION 102
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ __all__ = ["ZQError", "library_path", "lib", "quantize_weights",
            "ln_quant_act", "quant_act", "gemm_w8a8", "gemm_w4a8",
            "gemm_w8a8_i32", "gemm_w4a8_i32", "gemm_w8a8_quant",
            "gemm_w4a8_quant", "gemm_quant_workspace_bytes", "gemm_plan",
-           "ACT_NONE", "ACT_GELU"]
+           "gemm_w8a16", "gemm_w8a16_plan", "ACT_NONE", "ACT_GELU"]
 
 ACT_NONE = 0
 ACT_GELU = 1
@@ -62,6 +62,8 @@ def lib():
             "zq_gemm_w4a8_quant": [P, P, P, P, I, P, I, I, I, I, P, P, P,
                                    ctypes.c_size_t, P],
             "zq_gemm_plan": [I, I, I, I, ctypes.c_char_p, I],
+            "zq_gemm_w8a16": [P, P, P, I, P, I, I, I, I, P, P],
+            "zq_gemm_w8a16_plan": [I, I, I, ctypes.c_char_p, I],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -256,6 +258,31 @@ def gemm_w8a8_i32(qx, qw, acc=None, stream=None):
 
 def gemm_w4a8_i32(qx, qw4, acc=None, stream=None):
     return _gemm_i32(lib().zq_gemm_w4a8_i32, 4, qx, qw4, acc, stream)
+
+
+def gemm_w8a16(x, qw, sw, G, bias=None, act=ACT_NONE, y=None, stream=None):
+    """y[M,N] fp16 = act(sw[n//G] * sum_k x[t,k]*qw[n,k] + bias) with fp16
+    activations x [M,K] and INT8 weights qw [N,K]."""
+    _need(x, "x", torch.float16, dim=2)
+    M, K = x.shape
+    _need(qw, "qw", torch.int8, x.device, 2)
+    N = qw.shape[0]
+    if qw.shape[1] != K:
+        raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+    _need(sw, "sw", torch.float32, x.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, x.device)
+    y = torch.empty(M, N, dtype=torch.float16, device=x.device) if y is None else y
+    _need(y, "y", torch.float16, x.device)
+    _check(lib().zq_gemm_w8a16(_p(x), _p(qw), _p(sw), G, _p(bias), int(act), M,
+                               N, K, _p(y), _stream(x, stream)))
+    return y
+
+
+def gemm_w8a16_plan(M, N, K) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().zq_gemm_w8a16_plan(M, N, K, buf, 256))
+    return buf.value.decode()
 
 
 def gemm_plan(M, N, K, bits) -> str:

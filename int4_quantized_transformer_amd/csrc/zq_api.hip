@@ -244,6 +244,52 @@ size_t zq_gemm_quant_workspace_bytes(int M, int N) {
   return zq::gemm_quant_ws_bytes(M, N);
 }
 
+zq_status zq_gemm_w8a16(const void *x_fp16, const int8_t *qw, const float *sw,
+                        int G, const void *bias_fp16, int act, int M, int N,
+                        int K, void *y_fp16, void *stream) {
+  const char *fn = "zq_gemm_w8a16";
+  if ((!x_fp16 && M != 0) || !qw || !sw || (!y_fp16 && M != 0))
+    return fail(ZQ_EINVAL, "%s: null x/qw/sw/y", fn);
+  if (!aligned(x_fp16, 16) || !aligned(qw, 16) || !aligned(sw, 4) ||
+      !aligned(y_fp16, 8) || (bias_fp16 && !aligned(bias_fp16, 2)))
+    return fail(ZQ_EINVAL, "%s: misaligned x/qw/sw/y/bias", fn);
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d N=%d K=%d", fn, M, N, K);
+  if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+    return fail(ZQ_EINVAL, "%s: act=%d", fn, act);
+  if (G <= 0 || N % G != 0)
+    return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  if (K % 64 != 0)
+    return fail(ZQ_EUNSUPPORTED, "%s: K=%d is not a multiple of 64", fn, K);
+  if (K > ZQ_MAX_GEMM_K_A16)
+    return fail(ZQ_EUNSUPPORTED, "%s: K=%d exceeds %d", fn, K, ZQ_MAX_GEMM_K_A16);
+  if (M == 0) return ok();
+  zq::GemmArgs a{};
+  a.qx = static_cast<const int8_t *>(x_fp16);  // fp16 bytes
+  a.sx = nullptr;
+  a.qw = qw;
+  a.sw = sw;
+  a.bias = static_cast<const zq::half_t *>(bias_fp16);
+  a.out = y_fp16;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.act = act;
+  a.bits = 8;
+  a.raw_i32 = false;
+  return hip_status(zq::launch_gemm_w8a16(a, (hipStream_t)stream), fn);
+}
+
+zq_status zq_gemm_w8a16_plan(int M, int N, int K, char *buf, int buflen) {
+  const char *fn = "zq_gemm_w8a16_plan";
+  if (!buf || buflen <= 0) return fail(ZQ_EINVAL, "%s: null buffer", fn);
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d N=%d K=%d", fn, M, N, K);
+  zq::describe_gemm_w8a16_plan(M, N, buf, buflen);
+  return ok();
+}
+
 zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen) {
   const char *fn = "zq_gemm_plan";
   if (!buf || buflen <= 0) return fail(ZQ_EINVAL, "%s: null buffer", fn);

@@ -108,8 +108,9 @@ __device__ __forceinline__ QuadCol load_quad_col(const GemmArgs &p, int nb) {
 }
 
 // y = fp16(act(float(acc) * (sx[t] * sw[n / G]) + bias[n])), or the raw
-// int32 accumulator.  Lane holds n = nb .. nb+3 of token t.
-template <bool W4, bool RAW>
+// int32 accumulator.  Lane holds n = nb .. nb+3 of token t.  FACC: acc holds
+// fp32 sums (the fp16-activation GEMM) as raw bits.
+template <bool W4, bool RAW, bool FACC = false>
 __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
                                            v4i acc, float sxt,
                                            const QuadCol &c) {
@@ -133,8 +134,12 @@ __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float sc = sxt * c.sw[r];
-      h[r] = p.act == ZQ_ACT_GELU ? gelu_half((float)acc[r], sc, c.b[r])
-                                  : fma_half((float)acc[r], sc, c.b[r]);
+      // the element is copied out first: this compiler's __builtin_bit_cast
+      // of a vector element (acc[r]) reads element 0
+      const int ai = acc[r];
+      const float a = FACC ? __builtin_bit_cast(float, ai) : (float)ai;
+      h[r] = p.act == ZQ_ACT_GELU ? gelu_half(a, sc, c.b[r])
+                                  : fma_half(a, sc, c.b[r]);
     }
     half_t *o = static_cast<half_t *>(p.out) + (size_t)t * p.N + nb;
     if (full) {
@@ -168,17 +173,24 @@ __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
 // consecutive rows (one LDS cycle) hit 8 different bank groups:
 //   128-byte rows: slot = chunk ^ ((row >> 1) & 7)
 //    64-byte rows: slot = chunk ^ ((row >> 2) & 3)
-template <int BN_, int BM_, int WN_, int WM_, int S_, bool W4_, int KB_ = 128>
+template <int BN_, int BM_, int WN_, int WM_, int S_, bool W4_, int KB_ = 128,
+          bool A16_ = false>
 struct Tile {
   static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, S = S_;
   static constexpr bool W4 = W4_;
-  static constexpr int KB = KB_, KS = KB_ / 32;     // k-steps of 32 per stage
-  static_assert(KB == 128 || (KB == 64 && !W4), "stage width");
+  // A16: fp16 activations (2 bytes per k) with INT8 weights, on the fp16
+  // MFMA (32x32x16): a stage holds 64 k, rows of 128 activation bytes and 64
+  // weight bytes, and k advances 16 per MFMA k-step
+  static constexpr bool A16 = A16_;
+  static constexpr int KB = KB_, KS = KB_ / 32;     // MFMA k-steps per stage
+  static constexpr int KPS = A16 ? KB / 2 : KB;     // k values per stage
+  static_assert(KB == 128 || (KB == 64 && !W4 && !A16), "stage width");
+  static_assert(!(A16 && W4), "W4 with fp16 activations");
   static constexpr int NWN = BN / WN, NWM = BM / WM;
   static constexpr int NWAVES = NWN * NWM, NT = NWAVES * kWave;
   static constexpr int FN = WN / 32, FM = WM / 32;
   static constexpr int XROW = KB;                   // activation bytes/row/stage
-  static constexpr int WROW = W4 ? KB / 2 : KB;     // weight bytes/row/stage
+  static constexpr int WROW = (W4 || A16) ? KB / 2 : KB;  // weight bytes/row/stage
   static constexpr int WCPR = WROW / 16, XCPR = XROW / 16;  // chunks per row
   static constexpr int WRPI = 64 / WCPR, XRPI = 64 / XCPR;  // rows per wave copy
   static constexpr int WINS = BN / WRPI, XINS = BM / XRPI;  // wave copies/stage
@@ -239,9 +251,10 @@ __device__ __forceinline__ void issue_stage(const GemmArgs &p, const char *W,
     const int chunk = wswz<C::XROW>(lane % C::XCPR, row);
     int t = m0 + (row < C::BM ? row : C::BM - 1);
     t = t < p.M ? t : p.M - 1;
+    constexpr int XB = C::A16 ? 2 : 1;         // activation bytes per k
     int kb = kt * C::XROW + chunk * 16;
-    if (kb >= p.K) kb -= C::XROW / 2;
-    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * p.K + kb),
+    if (kb >= p.K * XB) kb -= C::XROW / 2;
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * p.K * XB + kb),
                                      ZQ_LPTR(stage + C::WBYTES + q * 1024), 16,
                                      0, 0);
   }
@@ -282,7 +295,21 @@ __device__ __forceinline__ void fetch(const char *ws, const char *xs, int s,
                                       int wn0, int wm0, int r32, int h,
                                       Frag<C> &f, v4i (&raw)[2][C::FN]) {
   const int x7 = sw128(r32);
-  if constexpr (!C::W4) {
+  if constexpr (C::A16) {
+    // activations: 8 halves (chunk 2s + h of the 128-byte row, k = 16s + 8h);
+    // weights: the matching 8 codes, half h of chunk s of the 64-byte row
+    const int c = wswz<C::XROW>(2 * s + h, r32);
+    const int cw = s ^ sw64(r32);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const v2i w = *reinterpret_cast<const v2i *>(
+          ws + (wn0 + fn * 32 + r32) * 64 + (cw << 4) + 8 * h);
+      f.a[fn] = v4i{w[0], w[1], 0, 0};
+    }
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+      f.b[fm] = ld16(xs + (wm0 + fm * 32 + r32) * C::XROW + (c << 4));
+  } else if constexpr (!C::W4) {
     // rows of XROW bytes; the swizzle depends on the row's low bits only,
     // which r32 shares with every fragment row
     const int c = wswz<C::XROW>(2 * s + h, r32);
@@ -307,10 +334,46 @@ __device__ __forceinline__ void fetch(const char *ws, const char *xs, int s,
   }
 }
 
+// Eight INT8 codes (two words) as eight fp16 values, exactly: with the
+// sign bit flipped a byte is u = q + 128; placed under the fp16 exponent of
+// 1024 (bits 0x64uu) it reads 1024 + u, and 1024 + u - 1152 = q.  The
+// halves are assembled with shifts and masks.
+__device__ __forceinline__ v4i i8x8_to_f16x8(int w0, int w1) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 bias = {(half_t)1152.0f, (half_t)1152.0f};
+  const uint32_t u[2] = {(uint32_t)w0 ^ 0x80808080u, (uint32_t)w1 ^ 0x80808080u};
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // bytes 0, 1 -> halves of word 2i; bytes 2, 3 -> halves of word 2i + 1
+    const uint32_t lo = (u[i] & 0xFFu) | ((u[i] << 8) & 0xFF0000u) | 0x64006400u;
+    const uint32_t hi = ((u[i] >> 16) & 0xFFu) | ((u[i] >> 8) & 0xFF0000u) | 0x64006400u;
+    r[2 * i] = __builtin_bit_cast(int, __builtin_bit_cast(h2, lo) - bias);
+    r[2 * i + 1] = __builtin_bit_cast(int, __builtin_bit_cast(h2, hi) - bias);
+  }
+  return r;
+}
+
 template <class C>
 __device__ __forceinline__ void mma(const Frag<C> &f, int s,
                                     const v4i (&raw)[2][C::FN],
                                     v16i (&acc)[C::FN][C::FM]) {
+  if constexpr (C::A16) {
+    typedef float v16f __attribute__((ext_vector_type(16)));
+    v4i a[C::FN];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) a[fn] = i8x8_to_f16x8(f.a[fn][0], f.a[fn][1]);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+        acc[fn][fm] = __builtin_bit_cast(
+            v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                      __builtin_bit_cast(half8, a[fn]),
+                      __builtin_bit_cast(half8, f.b[fm]),
+                      __builtin_bit_cast(v16f, acc[fn][fm]), 0, 0, 0));
+    return;
+  }
   v4i a[C::FN], b[C::FM];
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
@@ -408,7 +471,7 @@ __device__ __forceinline__ void stage_epilogue(
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int tl = wm0 + fm * 32 + r32;
-      const float sc = sx_l[tl] * swv[fn];
+      const float sc = C::A16 ? swv[fn] : sx_l[tl] * swv[fn];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cl = wn0 + fn * 32 + 8 * q + 4 * h;  // tile column
@@ -419,7 +482,7 @@ __device__ __forceinline__ void stage_epilogue(
         for (int r = 0; r < 4; ++r) {
           int a = acc[fn][fm][4 * q + r];
           if constexpr (C::W4) a >>= 4;
-          av[r] = (float)a;
+          av[r] = C::A16 ? __builtin_bit_cast(float, a) : (float)a;
         }
         half4 hv;
         if constexpr (GELU) {
@@ -535,13 +598,15 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
                                            ZQ_LPTR(aux + j * 256), 4, 0, 0);
         }
       }
+      if constexpr (!C::A16) {  // fp16 activations carry no token scale
 #pragma unroll
-      for (int j = 0; j < C::AUX_SX / 256; ++j) {
-        int t = m0 + lane + 64 * j;
-        t = t < p.M ? t : p.M - 1;
-        __builtin_amdgcn_global_load_lds(ZQ_GPTR(p.sx + t),
-                                         ZQ_LPTR(aux + C::AUX_BIAS + j * 256),
-                                         4, 0, 0);
+        for (int j = 0; j < C::AUX_SX / 256; ++j) {
+          int t = m0 + lane + 64 * j;
+          t = t < p.M ? t : p.M - 1;
+          __builtin_amdgcn_global_load_lds(ZQ_GPTR(p.sx + t),
+                                           ZQ_LPTR(aux + C::AUX_BIAS + j * 256),
+                                           4, 0, 0);
+        }
       }
     }
     const int lastg = (p.N - 1) / p.G;
@@ -559,8 +624,8 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = v16i{};
 
-  const int KT = (p.K + C::XROW - 1) / C::XROW;
-  const bool half_tail = (p.K % C::XROW) != 0;  // last stage holds 64 k
+  const int KT = (p.K + C::KPS - 1) / C::KPS;
+  const bool half_tail = (p.K % C::KPS) != 0;   // last stage holds half
   const int KTF = KT - (half_tail ? 1 : 0);      // stages with 128 k
 
   const int npro = KT < C::S ? KT : C::S;
@@ -611,7 +676,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
     mma<C>(f1, C::KS - 1, raw, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (C::KB == 128) if (half_tail) {
+  if constexpr (C::KB == 128 && !C::A16) if (half_tail) {
     const char *ws = lds + ((KT - 1) % C::S) * C::STAGE;
     tail_stage<C>(ws, ws + C::WBYTES, wn0, wm0, r32, h, acc);
   }
@@ -659,9 +724,9 @@ gemm_tiled_kernel(GemmArgs p) {
         float sxt = 0.0f;
         if constexpr (!RAW) {
           qc = load_quad_col(p, nb);
-          sxt = p.sx[t < p.M ? t : p.M - 1];
+          sxt = C::A16 ? 1.0f : p.sx[t < p.M ? t : p.M - 1];
         }
-        store_quad<C::W4, RAW>(p, t, nb, a, sxt, qc);
+        store_quad<C::W4, RAW, C::A16>(p, t, nb, a, sxt, qc);
       }
     }
 }
@@ -1650,6 +1715,59 @@ hipError_t launch_gemm_quant(const GemmArgs &a, int8_t *qy, float *sy,
   if (e != hipSuccess) return e;
   return launch_row_quant(ws, nullptr, nullptr, 0.0f, a.M, a.N, false, qy, sy,
                           nullptr, s);
+}
+
+// ------------------------------------------------ fp16 activations (W8A16)
+// INT8 weights with fp16 activations (qx points at fp16 [M][K]; sx unused):
+// the tiled kernel with A16 tiles.  {BN, BM, WN, WM, stages}.
+struct A16Cfg {
+  int bn, bm, wn, wm, s;
+};
+static const A16Cfg kA16Cfgs[] = {
+    {256, 256, 64, 64, 3},  // 0: 16 waves, 48 KB stages
+    {128, 128, 64, 64, 3},  // 1: 4 waves
+    {64, 64, 32, 32, 10},   // 2: 4 waves, decode-sized M
+    {192, 256, 64, 64, 3},  // 3: 12 waves
+    {128, 64, 64, 32, 8},   // 4: 4 waves
+};
+constexpr int kNumA16Cfgs = sizeof(kA16Cfgs) / sizeof(kA16Cfgs[0]);
+
+// ZQ_A16_TILE=<index> forces one configuration (tuning aid).
+static int forced_a16() {
+  static int v = [] {
+    const char *e = getenv("ZQ_A16_TILE");
+    if (!e) return -1;
+    const int i = atoi(e);
+    return (i >= 0 && i < kNumA16Cfgs) ? i : -1;
+  }();
+  return v;
+}
+
+static int choose_a16(int M, int N) {
+  const int f = forced_a16();
+  if (f >= 0) return f;
+  if (M <= 64) return 2;
+  const long t256 = (long)((N + 255) / 256) * ((M + 255) / 256);
+  return t256 >= 200 ? 0 : 1;
+}
+
+hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
+  switch (choose_a16(a.M, a.N)) {
+    case 0: return run_tiled<Tile<256, 256, 64, 64, 3, false, 128, true>, false>(a, s);
+    case 1: return run_tiled<Tile<128, 128, 64, 64, 3, false, 128, true>, false>(a, s);
+    case 2: return run_tiled<Tile<64, 64, 32, 32, 10, false, 128, true>, false>(a, s);
+    case 3: return run_tiled<Tile<192, 256, 64, 64, 3, false, 128, true>, false>(a, s);
+    default: return run_tiled<Tile<128, 64, 64, 32, 8, false, 128, true>, false>(a, s);
+  }
+}
+
+int describe_gemm_w8a16_plan(int M, int N, char *buf, int len) {
+  const int i = choose_a16(M, N);
+  const A16Cfg &c = kA16Cfgs[i];
+  return snprintf(buf, len,
+                  "tiled-a16 cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d tiles=%d", i,
+                  c.bn, c.bm, c.wn, c.wm, c.s,
+                  ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm));
 }
 
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert "zq_gemm_w8a8" in names and "zq_ln_quant_act" in names
     for n in names:
         assert hasattr(L, n), f"{n} declared in zq.h but not exported"
-    assert L.zq_version() == 101
+    assert L.zq_version() == 102
 
 
 def test_last_error_starts_empty_and_is_set_on_failure():
@@ -119,3 +119,21 @@ def test_gemm_plan_covers_every_regime():
     assert Z.gemm_plan(2048, 4096, 4096, 8).startswith("tiled")
     with pytest.raises(Z.ZQError):
         Z.gemm_plan(16, 256, 256, 3)
+
+
+def test_gemm_w8a16_argument_checks():
+    f = Z.lib().zq_gemm_w8a16
+    # (x, qw, sw, G, bias, act, M, N, K, y, stream)
+    assert f(A, B, C, 64, None, 0, 16, 256, 100, D, None) == EUNSUP  # K % 64
+    assert f(A, B, C, 64, None, 0, 16, 96, 256, D, None) == ESHAPE        # N % G
+    assert f(A, B, C, 0, None, 0, 16, 256, 256, D, None) == ESHAPE        # G
+    assert f(A, B, C, 64, None, 3, 16, 256, 256, D, None) == EINVAL       # act
+    assert f(A, B, C, 64, None, 0, -1, 256, 256, D, None) == ESHAPE
+    assert f(None, B, C, 64, None, 0, 16, 256, 256, D, None) == EINVAL
+    assert f(A, None, C, 64, None, 0, 16, 256, 256, D, None) == EINVAL
+    assert f(ctypes.c_void_p(0x10008), B, C, 64, None, 0, 16, 256, 256, D,
+             None) == EINVAL                                            # align
+    assert f(A, B, C, 64, None, 0, 16, 256, 1048640, D, None) == EUNSUP
+    assert f(None, B, C, 64, None, 0, 0, 256, 256, None, None) == OK      # empty
+    assert Z.gemm_w8a16_plan(1, 18432, 6144).startswith("tiled-a16 cfg=2")
+    assert Z.gemm_w8a16_plan(2048, 18432, 6144).startswith("tiled-a16 cfg=0")
