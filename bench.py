@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POP/s
+FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, 2.5 PFLOP/s
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 METRIC = ("fused W8A8/W4A8 GEMM TOPS (% INT8 peak); decode GB/s (% HBM peak)")
 ROTATE_BYTES = 600 * 2 ** 20   # > 2 x 256 MB Infinity Cache
@@ -51,6 +52,8 @@ def parse():
                     help="skip the decode (GPT-J-6B, M=1) secondary figure")
     ap.add_argument("--no-fp16", action="store_true",
                     help="skip the fp16 torch.matmul comparator")
+    ap.add_argument("--no-w8a16", action="store_true",
+                    help="skip the W8A16 (fp16 activation) figure")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "traffic.json"))
     ap.add_argument("--only", default=None,
@@ -350,6 +353,66 @@ def decode_figure(torch, zq, dev, steps=100):
             "rotating_sets": R}
 
 
+def w8a16_figure(torch, zq, dev, steps=20):
+    """GPT-NeoX20B QKV (18432 x 6144) with INT8 weights and fp16 activations
+    (the pages' W8A8/16 scheme keeps NeoX's attention inputs in fp16), at
+    prefill (M = 2048: TFLOP/s against the fp16 MFMA peak) and decode (M = 1:
+    GB/s against HBM); the torch fp16 matmul of the same shape beside it."""
+    from int4_quantized_transformer_amd import workloads as W
+    wl = W.workload("neox-20b")
+    L = wl.linears[0]
+    N, K, G = L.N, L.K, wl.G
+    w, b = W.gen_weights(wl, 0)
+    wd = w.to(dev)
+    qw, sw = zq.quantize_weights(wd, G, 8)
+    bd = b.to(dev)
+    R = max(2, -(-ROTATE_BYTES // (N * K)))
+    qws = [qw] + [qw.clone() for _ in range(R - 1)]
+    out = {"workload": f"neox-20b QKV {N}x{K} W8A16, {G}-row groups, "
+                       "HIP-graph replay over rotating weight sets"}
+    for M in (2048, 1):
+        x = W.gen_activations(wl, 0, M=M, m_index=list(wl.M).index(M)).to(dev)
+        y = torch.empty(M, N, dtype=torch.float16, device=dev)
+        for i in range(R):
+            zq.gemm_w8a16(x, qws[i], sw, G, bd, 0, y=y)
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(R):
+                zq.gemm_w8a16(x, qws[i], sw, G, bd, 0, y=y)
+        stream = torch.cuda.current_stream()
+        g.replay()
+        ms, _ = timed_graphs(torch, [g], steps, stream)
+        us = ms * 1e3 / R
+        nbytes = N * K + 2 * M * K + 2 * M * N + 4 * (N // G) + 2 * N
+        e = {"us": round(us, 2), "plan": zq.gemm_w8a16_plan(M, N, K)}
+        if M > 1:
+            tf = 2 * M * N * K / (us * 1e-6) / 1e12
+            e["TFLOPS"] = round(tf, 1)
+            e["pct_fp16_peak"] = round(100 * tf / FP16_PEAK_TFLOPS, 1)
+        else:
+            gbs = nbytes / (us * 1e-6) / 1e9
+            e["GB_per_s"] = round(gbs, 1)
+            e["pct_hbm_peak"] = round(100 * gbs / HBM_PEAK_GBS, 1)
+        # torch fp16 matmul + bias at the same shape (fp16 weights)
+        ws16 = [wd] + [wd.clone() for _ in range(max(1, R // 2) - 1)]
+        R2 = len(ws16)
+        for i in range(R2):
+            torch.addmm(bd, x, ws16[i].t())
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps * R2):
+            torch.addmm(bd, x, ws16[i % R2].t())
+        e1.record(stream)
+        torch.cuda.synchronize()
+        e["torch_fp16_us"] = round(e0.elapsed_time(e1) * 1e3 / (steps * R2), 2)
+        out[f"M={M}"] = e
+        del ws16, g
+    return out
+
+
 # -------------------------------------------------------------------- main --
 # -------------------------------------------------------- profile summary --
 COPY_BYTES = 256 * 2 ** 20
@@ -635,6 +698,8 @@ def main():
         extras["fp16_matmul"] = fp16_comparator(torch, base, M, args.steps)
     if not args.no_decode:
         extras["decode"] = decode_figure(torch, zq, dev)
+    if not args.no_w8a16:
+        extras["w8a16"] = w8a16_figure(torch, zq, dev)
     out["extras"] = extras
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(base, wl, M)

@@ -286,7 +286,7 @@ zq_status zq_gemm_w8a16_plan(int M, int N, int K, char *buf, int buflen) {
   if (!buf || buflen <= 0) return fail(ZQ_EINVAL, "%s: null buffer", fn);
   if (M < 0 || N <= 0 || K <= 0)
     return fail(ZQ_ESHAPE, "%s: bad shape M=%d N=%d K=%d", fn, M, N, K);
-  zq::describe_gemm_w8a16_plan(M, N, buf, buflen);
+  zq::describe_gemm_w8a16_plan(M, N, K, buf, buflen);
   return ok();
 }
 

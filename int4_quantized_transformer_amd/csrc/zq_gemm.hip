@@ -1213,10 +1213,13 @@ static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
 // (even k / odd k), the activation bytes permuted to match, and the row sum
 // shifted right by 4 at the end.  Rows must be a whole number of 1 KB pieces
 // (K % 1024 == 0 for W8, K % 2048 == 0 for W4).
-template <int NW_, int U_, bool W4_, int XR_>
+template <int NW_, int U_, bool W4_, int XR_, bool A16_ = false>
 struct Gemv {
   static constexpr int NW = NW_, U = U_;
   static constexpr bool W4 = W4_;
+  // A16: fp16 activation row (2 bytes per k, held in LDS), INT8 weights;
+  // fp32 row sums from v_dot2_f32_f16 on the widened codes
+  static constexpr bool A16 = A16_;
   static constexpr int NT = NW * kWave;
   static constexpr int RMAX = 1024;   // rows per block
   // XR > 0: the activation row (at most XMAX bytes) is held in LDS, loaded
@@ -1226,6 +1229,7 @@ struct Gemv {
   static constexpr int XMAX = XR * NT * 16;
   static constexpr int L = XL ? 1 : (W4 ? 3 : 2);  // loads per piece
   static_assert(U * L < 64, "vmcnt range");
+  static_assert(!A16 || (XL && !W4), "fp16 activations: W8, row in LDS");
 };
 
 template <int CTRL>
@@ -1251,6 +1255,23 @@ __device__ __forceinline__ void ds_add1(uint32_t addr, int v) {
   asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
 
+__device__ __forceinline__ void ds_add1f(uint32_t addr, float v) {
+  asm volatile("ds_add_f32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// sum_i w_i * x_i over 8 fp16 pairs in fp32 (v_dot2_f32_f16); the vector
+// elements are copied to scalars before the bit casts
+__device__ __forceinline__ float fdot8(v4i w, v4i x, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int wi = w[i], xi = x[i];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, wi),
+                                 __builtin_bit_cast(h2, xi), acc, false);
+  }
+  return acc;
+}
+
 template <class C, bool RAW>
 __global__ void __launch_bounds__(C::NT)
 gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
@@ -1260,6 +1281,7 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ldw = C::W4 ? p.K / 2 : p.K;
   const int ppr = ldw >> 10;                   // pieces per row
+  const int xbytes = C::A16 ? 2 * p.K : p.K;   // activation row bytes
   const int r0 = (int)blockIdx.x * rpb;
   const int r1 = r0 + rpb < p.N ? r0 + rpb : p.N;
   // piece order of a wave: interleaved (pieces wave, wave + NW, ... of the
@@ -1287,7 +1309,7 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
   uint16_t ebits[E];
   float esx = 0.0f;
   if constexpr (!RAW) {
-    esx = p.sx[0];
+    esx = C::A16 ? 1.0f : p.sx[0];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       int n = r0 + (int)threadIdx.x + e * C::NT;
@@ -1306,7 +1328,7 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
 #pragma unroll
     for (int e = 0; e < XR; ++e) {
       const int off = (e * C::NT + (int)threadIdx.x) * 16;
-      xr[e] = ld16(X + (off < p.K ? off : p.K - 16));
+      xr[e] = ld16(X + (off < xbytes ? off : xbytes - 16));
     }
   }
 
@@ -1353,18 +1375,25 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
 #pragma unroll
     for (int e = 0; e < XR; ++e) {
       const int off = (e * C::NT + (int)threadIdx.x) * 16;
-      if (off < p.K) *reinterpret_cast<v4i *>(xs + off) = xr[e];
+      if (off < xbytes) *reinterpret_cast<v4i *>(xs + off) = xr[e];
     }
   }
   lds_barrier();  // activation row and cleared row sums visible
 
   int acc = 0, ci = 0, cr = lr0, cp = lp0;
+  float accf = 0.0f;
   for (int c0 = 0; c0 < npieces; c0 += C::U) {
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       if (c0 + u < npieces) {
         const int kb = cp << 10;
-        if constexpr (C::W4) {
+        if constexpr (C::A16) {
+          // 16 codes (k = kb + 16 lane ..) against 16 fp16 activations
+          const v4i x0 = ld16(xs + 2 * kb + lane * 32);
+          const v4i x1 = ld16(xs + 2 * kb + lane * 32 + 16);
+          accf = fdot8(i8x8_to_f16x8(wv[u][0], wv[u][1]), x0, accf);
+          accf = fdot8(i8x8_to_f16x8(wv[u][2], wv[u][3]), x1, accf);
+        } else if constexpr (C::W4) {
           v4i x0, x1;
           if constexpr (C::XL) {
             x0 = ld16(xs + 2 * kb + lane * 32);
@@ -1387,9 +1416,15 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
         cp = wrap ? cp - ppr : cp;
         cr = wrap ? cr + wr : cr;
         if (cr != row || ci == npieces - 1) {
-          const int sum = wave_sum_i(acc);
-          if (lane == 0) ds_add1(lds_addr(&rowsum[row]), C::W4 ? (sum >> 4) : sum);
-          acc = 0;
+          if constexpr (C::A16) {
+            const float sum = wave_sum(accf);
+            if (lane == 0) ds_add1f(lds_addr(&rowsum[row]), sum);
+            accf = 0.0f;
+          } else {
+            const int sum = wave_sum_i(acc);
+            if (lane == 0) ds_add1(lds_addr(&rowsum[row]), C::W4 ? (sum >> 4) : sum);
+            acc = 0;
+          }
         }
         ++ci;
       }
@@ -1411,9 +1446,9 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
         const half_t b =
             p.bias ? __builtin_bit_cast(half_t, ebits[e]) : (half_t)0.0f;
         const float sc = esx * esw[e];
+        const float af = C::A16 ? __builtin_bit_cast(float, a) : (float)a;
         static_cast<half_t *>(p.out)[n] =
-            p.act == ZQ_ACT_GELU ? gelu_half((float)a, sc, b)
-                                 : fma_half((float)a, sc, b);
+            p.act == ZQ_ACT_GELU ? gelu_half(af, sc, b) : fma_half(af, sc, b);
       }
     }
   }
@@ -1743,15 +1778,28 @@ static int forced_a16() {
   return v;
 }
 
+// From measured sweeps (GPT-NeoX20B QKV and out shapes): decode-sized M on
+// 128x64 tiles with an 8-deep ring; prefill on 192x256 tiles, or 128x128
+// when 192x256 would leave most compute units idle.
 static int choose_a16(int M, int N) {
   const int f = forced_a16();
   if (f >= 0) return f;
-  if (M <= 64) return 2;
-  const long t256 = (long)((N + 255) / 256) * ((M + 255) / 256);
-  return t256 >= 200 ? 0 : 1;
+  if (M <= 64) return 4;
+  const long t = (long)((N + 191) / 192) * ((M + 255) / 256);
+  return t >= 128 ? 3 : 1;
+}
+
+static bool a16_gemv(int M, int K) {
+  return forced_a16() < 0 && M == 1 && K % 1024 == 0 && K <= 32768;
 }
 
 hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
+  if (a16_gemv(a.M, a.K)) {
+    // one token: weight rows streamed in 1 KB pieces, the fp16 activation
+    // row (up to 16 KB, else 64 KB) in LDS, whole rows per wave
+    if (a.K <= 8192) return run_gemv<Gemv<4, 6, false, 4, true>, false>(a, s, 2, 0);
+    return run_gemv<Gemv<4, 6, false, 16, true>, false>(a, s, 2, 0);
+  }
   switch (choose_a16(a.M, a.N)) {
     case 0: return run_tiled<Tile<256, 256, 64, 64, 3, false, 128, true>, false>(a, s);
     case 1: return run_tiled<Tile<128, 128, 64, 64, 3, false, 128, true>, false>(a, s);
@@ -1761,7 +1809,9 @@ hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
   }
 }
 
-int describe_gemm_w8a16_plan(int M, int N, char *buf, int len) {
+int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len) {
+  if (a16_gemv(M, K))
+    return snprintf(buf, len, "gemv-a16 NW=4 U=6 rows=%d x_in_lds=1", N);
   const int i = choose_a16(M, N);
   const A16Cfg &c = kA16Cfgs[i];
   return snprintf(buf, len,

@@ -245,7 +245,7 @@ hipError_t launch_gemm_quant(const GemmArgs &a, int8_t *qy, float *sy,
 size_t gemm_quant_ws_bytes(int M, int N);
 // INT8 weights with fp16 activations (a.qx holds fp16 [M][K], a.sx unused).
 hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s);
-int describe_gemm_w8a16_plan(int M, int N, char *buf, int len);
+int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len);
 // Human-readable schedule for (M, N, K, bits); returns chars written.
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len);
 

@@ -2,8 +2,9 @@
 against the oracle's fp64 definition (dequantized weights, then the product).
 
 * Tolerance: fp16 y within 1 fp16 ulp + 1e-3 of the oracle's unrounded z,
-  over decode and prefill token counts, ragged M and N tiles, G not a
-  multiple of 32, with and without bias and GeLU.
+  over decode and prefill token counts (the one-token GEMV with the
+  activation row in 16 or 64 KB of LDS, the tiled kernel), ragged M and N
+  tiles, G not a multiple of 32, with and without bias and GeLU.
 * Exact: with small integer activations and a power-of-two scale every
   partial sum is an integer below 2^24, so the kernel's fp32 accumulation is
   exact and y equals the oracle's rounded y bit for bit.
@@ -34,7 +35,8 @@ def _inputs(M, N, K, G, seed, bias=True):
     (1, 256, 128, 64), (1, 4096, 1024, 128), (5, 1000, 320, 8),
     (16, 2048, 1024, 128), (40, 640, 192, 64), (64, 512, 512, 64),
     (65, 320, 576, 64), (300, 1000, 640, 8), (513, 1536, 1024, 128),
-    (1024, 2560, 256, 64)])
+    (1024, 2560, 256, 64), (1, 1000, 2048, 8), (1, 4096, 16384, 128),
+    (1, 18432, 6144, 128), (2, 512, 1024, 64)])
 @pytest.mark.parametrize("bias,act", [(True, 0), (True, 1), (False, 1)])
 def test_w8a16_vs_oracle(M, N, K, G, bias, act):
     x, q, sw, b = _inputs(M, N, K, G, M + 3 * N + 7 * K + G, bias)
@@ -48,8 +50,9 @@ def test_w8a16_vs_oracle(M, N, K, G, bias, act):
     assert_fp16_close_to_oracle(to_np(y), z, zq.gemm_w8a16_plan(M, N, K))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 512, 1024), (16, 640, 512),
-                                   (200, 1024, 768), (256, 4096, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 512, 1024), (1, 640, 512),
+                                   (16, 640, 512), (200, 1024, 768),
+                                   (256, 4096, 1024)])
 def test_w8a16_exact_when_sums_are_exact(M, N, K):
     g = np.random.default_rng(M + N + K)
     x = g.integers(-8, 9, (M, K)).astype(np.float16)
@@ -84,3 +87,8 @@ def test_w8a16_empty_m():
                       torch.zeros(64, 128, dtype=torch.int8, device=d),
                       torch.ones(1, dtype=torch.float32, device=d), 64)
     assert y.shape == (0, 64)
+
+
+def test_w8a16_plans_cover_both_kernels():
+    assert zq.gemm_w8a16_plan(1, 4096, 16384).startswith("gemv-a16")
+    assert zq.gemm_w8a16_plan(1, 256, 128).startswith("tiled-a16")
