@@ -17,7 +17,7 @@ from . import build as _build
 __all__ = [
     "lib", "half_to_double", "double_to_half", "quantize_weights", "pack_w4",
     "unpack_w4", "layernorm", "quant_tokens", "gemm_i32", "epilogue",
-    "linear", "gemm_w8a16", "threads",
+    "linear", "gemm_w8a16", "calibrate_minmax", "quant_static", "threads",
 ]
 
 _lib = None
@@ -47,6 +47,10 @@ def lib():
         L.zqo_gemm_i32.restype = ctypes.c_long
         L.zqo_epilogue.argtypes = [P, P, P, I, P, I, I, I, P, P]
         L.zqo_gemm_w8a16.argtypes = [P, P, P, I, P, I, I, I, I, P, P]
+        L.zqo_calibrate_minmax.argtypes = [P, ctypes.c_size_t, ctypes.c_float,
+                                           I, P]
+        L.zqo_quant_static.argtypes = [P, ctypes.c_size_t, P, P]
+        L.zqo_quant_static.restype = ctypes.c_float
         L.zqo_threads.argtypes = []
         L.zqo_threads.restype = I
         _lib = L
@@ -187,6 +191,28 @@ def gemm_w8a16(x, q, sw, G, bias=None, act=0):
     lib().zqo_gemm_w8a16(_ptr(x), _ptr(q), _ptr(sw), G, _ptr(b), act, M, N, K,
                          _ptr(z), _ptr(y))
     return z, y.view(np.float16)
+
+
+def calibrate_minmax(x, state=None, momentum=0.95):
+    """One calibration step of the static per-tensor range (moving average
+    of batch min/max; the first call, state None, initializes).  Returns the
+    new state float32 [2] = (x_min, x_max)."""
+    x = _h(x)
+    first = state is None
+    st = np.zeros(2, np.float32) if first else np.array(state, np.float32)
+    lib().zqo_calibrate_minmax(_ptr(x), x.size, ctypes.c_float(momentum),
+                               int(first), _ptr(st))
+    return st
+
+
+def quant_static(x, state):
+    """Eq. (2) over the whole tensor with S = max(|x_min|, |x_max|) / 127:
+    (codes int8 of x's shape, S)."""
+    x = _h(x)
+    st = np.ascontiguousarray(state, np.float32)
+    q = np.empty(x.shape, np.int8)
+    s = lib().zqo_quant_static(_ptr(x), x.size, _ptr(st), _ptr(q))
+    return q, np.float32(s)
 
 
 def threads():

@@ -106,6 +106,9 @@ void zqo_double_to_half_array(const double *v, size_t n, uint16_t *out)
 /* The unit is n contiguous fp16 values: one token row for activations, one  */
 /* group of whole weight rows for weights.  Returns S.                        */
 /* ------------------------------------------------------------------------ */
+static void quantize_with_scale(const uint16_t *v, size_t n, float s, int qmax,
+                                int8_t *q);
+
 static float quantize_unit(const uint16_t *v, size_t n, int qmax, int8_t *q)
 {
     float amax = 0.0f;
@@ -117,6 +120,16 @@ static float quantize_unit(const uint16_t *v, size_t n, int qmax, int8_t *q)
             amax = a;
     }
     s = amax / (float)qmax;
+    quantize_with_scale(v, n, s, qmax, q);
+    return s;
+}
+
+/* Eq. (2) with a given scale S (the clamp applies to values beyond the     */
+/* range S was taken from).                                                  */
+static void quantize_with_scale(const uint16_t *v, size_t n, float s, int qmax,
+                                int8_t *q)
+{
+    size_t i;
     for (i = 0; i < n; i++) {
         float x, r;
         if (s == 0.0f) {
@@ -131,7 +144,6 @@ static float quantize_unit(const uint16_t *v, size_t n, int qmax, int8_t *q)
         r = rintf(x);                              /* ties to even */
         q[i] = (int8_t)r;
     }
-    return s;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -242,6 +254,51 @@ void zqo_quant_tokens(const uint16_t *h, int M, int K, int8_t *q, float *sx)
     for (t = 0; t < M; t++)
         sx[t] = quantize_unit(h + (size_t)t * K, (size_t)K, 127,
                               q + (size_t)t * K);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Static per-tensor activation quantization, the prior-PTQ scheme that      */
+/* [SUM] 3.4 "Token-wise Activation Quantization" contrasts with token-wise  */
+/* scales (paper App. B.1): the range is calibrated offline as a moving      */
+/* average over calibration batches,                                          */
+/*   x_max = m * x_max + (1 - m) * max(batch),  x_min likewise (m = 0.95),   */
+/* and frozen; S = max(|x_min|, |x_max|), read as for the token scale with    */
+/* qmax: S = max(|x_min|, |x_max|) / 127.  Readings where the pages are      */
+/* silent: the first batch initializes (x_min, x_max); the state and the      */
+/* update are fp32, each product and the sum rounded separately.             */
+/* state = {x_min, x_max}; x is n fp16 values (one calibration batch).       */
+/* ------------------------------------------------------------------------ */
+void zqo_calibrate_minmax(const uint16_t *x, size_t n, float momentum,
+                          int first, float *state)
+{
+    float mn = INFINITY, mx = -INFINITY;
+    size_t i;
+    for (i = 0; i < n; i++) {
+        float v = (float)zqo_half_to_double(x[i]);
+        if (v < mn)
+            mn = v;
+        if (v > mx)
+            mx = v;
+    }
+    if (first) {
+        state[0] = mn;
+        state[1] = mx;
+    } else {
+        float w = 1.0f - momentum;
+        float a0 = momentum * state[0], b0 = w * mn;
+        float a1 = momentum * state[1], b1 = w * mx;
+        state[0] = a0 + b0;
+        state[1] = a1 + b1;
+    }
+}
+
+/* Eq. (2) over the whole tensor with the frozen scale; returns S. */
+float zqo_quant_static(const uint16_t *x, size_t n, const float *state,
+                       int8_t *q)
+{
+    float s = fmaxf(fabsf(state[0]), fabsf(state[1])) / 127.0f;
+    quantize_with_scale(x, n, s, 127, q);
+    return s;
 }
 
 /* ------------------------------------------------------------------------ */

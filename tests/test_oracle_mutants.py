@@ -49,6 +49,14 @@ MUTANTS = {
     "w8a16_no_bias": ("s += zqo_half_to_double(bias[n]);", "s += 0.0;"),
     # W8A16: GeLU with erf(x) instead of erf(x / sqrt 2)
     "w8a16_gelu_wrong_arg": ("erf(s / sqrt(2.0))", "erf(s)"),
+    # static range: momentum applied to the batch instead of the state
+    "static_momentum_swapped": ("float a1 = momentum * state[1], b1 = w * mx;",
+                                "float a1 = w * state[1], b1 = momentum * mx;"),
+    # static scale without qmax
+    "static_scale_no_qmax": ("fabsf(state[1])) / 127.0f;", "fabsf(state[1]));"),
+    # first batch not used to initialize
+    "static_first_ignored": ("    if (first) {\n        state[0] = mn;",
+                             "    if (0) {\n        state[0] = mn;"),
 }
 
 

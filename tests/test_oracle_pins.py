@@ -423,3 +423,50 @@ def test_w8a16_gelu_is_erf_gelu_of_the_linear_value():
     ref = np.vectorize(lambda v: 0.5 * v * (1 + math.erf(v / math.sqrt(2))))(z0)
     assert np.allclose(z1, ref, rtol=1e-14, atol=1e-15)
     assert np.abs(z0).max() > 1.0   # the GeLU sees values on both sides of 0
+
+
+# ------------------------------------------------------ static per-tensor ----
+def test_static_first_batch_initializes_to_its_min_max():
+    rng = np.random.default_rng(47)
+    x = _f16(rng.normal(0, 3, (64, 96)))
+    st = oracle.calibrate_minmax(x)
+    assert st[0] == np.float32(x.astype(np.float32).min())
+    assert st[1] == np.float32(x.astype(np.float32).max())
+
+
+def test_static_moving_average_closed_form():
+    # start at (-m0, m0), then batches whose range is exactly [-c, c]:
+    # x_max(N) = c + 0.95^N (m0 - c) in exact arithmetic
+    m0, c = 40.0, 10.0
+    x0 = _f16([[-m0, m0, 0.5]])
+    xc = _f16([[-c, c, 1.25, -3.0]])
+    st = oracle.calibrate_minmax(x0)
+    for n in range(1, 61):
+        st = oracle.calibrate_minmax(xc, st)
+        exp = c + 0.95 ** n * (m0 - c)
+        assert abs(st[1] - exp) <= 1e-5 * exp
+        assert abs(st[0] + exp) <= 1e-5 * exp
+        assert c <= st[1] <= m0
+
+
+def test_static_quantizer_reduces_to_token_quantizer():
+    # with the range (-a, a) of a token, the static scale is that token's
+    # scale and the codes are the token quantizer's
+    rng = np.random.default_rng(53)
+    x = _f16(rng.normal(0, 2, (1, 300)))
+    a = np.float32(np.abs(x.astype(np.float32)).max())
+    q, s = oracle.quant_static(x, np.array([-a, a], np.float32))
+    q_t, s_t = oracle.quant_tokens(x)
+    assert s == s_t[0]
+    assert np.array_equal(q, q_t)
+
+
+def test_static_quantizer_clamps_and_bounds_error():
+    st = np.array([-2.0, 4.0], np.float32)   # S = 4 / 127
+    x = _f16([[-10.0, -4.0, -2.0, 0.0, 1.0, 3.99, 4.0, 9.0]])
+    q, s = oracle.quant_static(x, st)
+    assert s == np.float32(4.0) / np.float32(127.0)
+    assert q[0, 0] == -127 and q[0, 1] == -127 and q[0, -1] == 127 and q[0, -2] == 127
+    inside = np.abs(x.astype(np.float64)) <= 127 * float(s)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * float(s))
+    assert np.all(err[inside] <= float(s) / 2 * (1 + 1e-6))
