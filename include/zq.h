@@ -190,6 +190,28 @@ zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
 size_t zq_gemm_quant_workspace_bytes(int M, int N);
 
 /*
+ * zq_calibrate_minmax / zq_quant_act_static -- static per-tensor activation
+ * quantization, the prior-PTQ scheme that token-wise scales replace
+ * (summary page Sec. 3.4 "Token-wise Activation Quantization"; paper
+ * App. B.1), kept as a comparator.
+ * zq_calibrate_minmax: one calibration batch x fp16 [M][K] moves the device
+ * state fp32 [2] = {x_min, x_max}:  first != 0 sets it to the batch's min
+ * and max; otherwise x = momentum * x + (1 - momentum) * batch value, fp32
+ * with each product and the sum rounded once (the pages use momentum 0.95).
+ * One workgroup (an offline step).
+ * zq_quant_act_static: Eq. (2) over the whole tensor with the frozen scale
+ * S = max(|x_min|, |x_max|) / 127 read from the device state; values beyond
+ * the range clamp to +-127.  qx int8 [M][K]; s_out fp32 [1] receives S.
+ * Errors: ZQ_EINVAL (null/misaligned pointer, momentum outside [0, 1]),
+ * ZQ_ESHAPE (M < 0 (calibration: M <= 0), K <= 0).
+ */
+zq_status zq_calibrate_minmax(const void *x_fp16, int M, int K, float momentum,
+                              int first, float *state, void *stream);
+zq_status zq_quant_act_static(const void *x_fp16, int M, int K,
+                              const float *state, int8_t *qx, float *s_out,
+                              void *stream);
+
+/*
  * zq_gemm_w8a16 -- INT8 group-wise weights with FP16 activations, the mixed
  * scheme of the summary page's Sec. 5 "Experiments" (Table 4: W8A16;
  * Table 8: GPT-NeoX20B keeps its self-attention inputs in FP16 while the
@@ -224,7 +246,7 @@ const char *zq_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int zq_version(void);
-#define ZQ_VERSION 102
+#define ZQ_VERSION 103
 
 #ifdef __cplusplus
 }

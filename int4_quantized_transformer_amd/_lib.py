@@ -16,7 +16,8 @@ __all__ = ["ZQError", "library_path", "lib", "quantize_weights",
            "ln_quant_act", "quant_act", "gemm_w8a8", "gemm_w4a8",
            "gemm_w8a8_i32", "gemm_w4a8_i32", "gemm_w8a8_quant",
            "gemm_w4a8_quant", "gemm_quant_workspace_bytes", "gemm_plan",
-           "gemm_w8a16", "gemm_w8a16_plan", "ACT_NONE", "ACT_GELU"]
+           "gemm_w8a16", "gemm_w8a16_plan", "calibrate_minmax",
+           "quant_act_static", "ACT_NONE", "ACT_GELU"]
 
 ACT_NONE = 0
 ACT_GELU = 1
@@ -64,6 +65,8 @@ def lib():
             "zq_gemm_plan": [I, I, I, I, ctypes.c_char_p, I],
             "zq_gemm_w8a16": [P, P, P, I, P, I, I, I, I, P, P],
             "zq_gemm_w8a16_plan": [I, I, I, ctypes.c_char_p, I],
+            "zq_calibrate_minmax": [P, I, I, F, I, P, P],
+            "zq_quant_act_static": [P, I, I, P, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -283,6 +286,36 @@ def gemm_w8a16_plan(M, N, K) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib().zq_gemm_w8a16_plan(M, N, K, buf, 256))
     return buf.value.decode()
+
+
+def calibrate_minmax(x, state=None, momentum=0.95, stream=None):
+    """One calibration batch of the static per-tensor range: state (device
+    fp32 [2] = x_min, x_max) is created from x when None, else moved by the
+    moving average.  Returns the state tensor."""
+    _need(x, "x", torch.float16, dim=2)
+    M, K = x.shape
+    first = state is None
+    if first:
+        state = torch.zeros(2, dtype=torch.float32, device=x.device)
+    _need(state, "state", torch.float32, x.device)
+    _check(lib().zq_calibrate_minmax(_p(x), M, K, ctypes.c_float(momentum),
+                                     int(first), _p(state), _stream(x, stream)))
+    return state
+
+
+def quant_act_static(x, state, qx=None, s_out=None, stream=None):
+    """Eq. (2) over the whole of x with the frozen scale of ``state``:
+    (qx int8 [M,K], S fp32 [1])."""
+    _need(x, "x", torch.float16, dim=2)
+    M, K = x.shape
+    _need(state, "state", torch.float32, x.device)
+    qx = torch.empty(M, K, dtype=torch.int8, device=x.device) if qx is None else qx
+    s_out = torch.empty(1, dtype=torch.float32, device=x.device) if s_out is None else s_out
+    _need(qx, "qx", torch.int8, x.device)
+    _need(s_out, "s_out", torch.float32, x.device)
+    _check(lib().zq_quant_act_static(_p(x), M, K, _p(state), _p(qx), _p(s_out),
+                                     _stream(x, stream)))
+    return qx, s_out
 
 
 def gemm_plan(M, N, K, bits) -> str:

@@ -244,6 +244,38 @@ size_t zq_gemm_quant_workspace_bytes(int M, int N) {
   return zq::gemm_quant_ws_bytes(M, N);
 }
 
+zq_status zq_calibrate_minmax(const void *x_fp16, int M, int K, float momentum,
+                              int first, float *state, void *stream) {
+  const char *fn = "zq_calibrate_minmax";
+  if (!state || (!x_fp16 && M != 0)) return fail(ZQ_EINVAL, "%s: null x/state", fn);
+  if (!aligned(x_fp16, 2) || !aligned(state, 4))
+    return fail(ZQ_EINVAL, "%s: misaligned pointer", fn);
+  if (M <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d K=%d", fn, M, K);
+  if (!(momentum >= 0.0f && momentum <= 1.0f))
+    return fail(ZQ_EINVAL, "%s: momentum must be in [0, 1]", fn);
+  return hip_status(zq::launch_calibrate(x_fp16, (size_t)M * K, momentum,
+                                         first ? 1 : 0, state,
+                                         (hipStream_t)stream),
+                    fn);
+}
+
+zq_status zq_quant_act_static(const void *x_fp16, int M, int K,
+                              const float *state, int8_t *qx, float *s_out,
+                              void *stream) {
+  const char *fn = "zq_quant_act_static";
+  if (!state || !s_out || ((!x_fp16 || !qx) && M != 0))
+    return fail(ZQ_EINVAL, "%s: null x/state/qx/s_out", fn);
+  if (!aligned(x_fp16, 2) || !aligned(state, 4) || !aligned(s_out, 4))
+    return fail(ZQ_EINVAL, "%s: misaligned pointer", fn);
+  if (M < 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d K=%d", fn, M, K);
+  if (M == 0) return ok();
+  return hip_status(zq::launch_static_quant(x_fp16, (size_t)M * K, state, qx,
+                                            s_out, (hipStream_t)stream),
+                    fn);
+}
+
 zq_status zq_gemm_w8a16(const void *x_fp16, const int8_t *qw, const float *sw,
                         int G, const void *bias_fp16, int act, int M, int N,
                         int K, void *y_fp16, void *stream) {

@@ -243,6 +243,12 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm_quant(const GemmArgs &a, int8_t *qy, float *sy,
                              void *ws, hipStream_t s);
 size_t gemm_quant_ws_bytes(int M, int N);
+// Static per-tensor range: one calibration step (state = {x_min, x_max}) and
+// the frozen-scale quantizer (s_out: S).
+hipError_t launch_calibrate(const void *x, size_t n, float momentum, int first,
+                            float *state, hipStream_t s);
+hipError_t launch_static_quant(const void *x, size_t n, const float *state,
+                               int8_t *q, float *s_out, hipStream_t s);
 // INT8 weights with fp16 activations (a.qx holds fp16 [M][K], a.sx unused).
 hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s);
 int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len);

@@ -292,6 +292,121 @@ hipError_t launch_row_quant(const void *x, const void *gamma, const void *beta,
              : dispatch_tpr<false, false>(xh, g, b, eps, M, K, qx, sx, lo, s);
 }
 
+// ============================================================ static range
+// The prior-PTQ scheme that token-wise scales replace (summary page,
+// Sec. 3.4 "Token-wise Activation Quantization"; paper App. B.1): one
+// activation range per tensor, calibrated offline as a moving average of
+// batch minima and maxima, then frozen.
+//  * calibrate_kernel (offline): one workgroup reduces the batch's min and
+//    max (exact, independent of order), then updates state = {x_min, x_max}:
+//    the first batch initializes, later ones move it by
+//    x = m * x + (1 - m) * batch, in fp32 with each product and the sum
+//    rounded separately.
+//  * static_quant_kernel: Eq. (2) over the whole tensor with
+//    S = max(|x_min|, |x_max|) / 127 taken from the device-side state; values
+//    beyond the calibrated range clamp to +-127.
+constexpr int kCalThreads = 1024;
+
+__global__ void __launch_bounds__(kCalThreads)
+calibrate_kernel(const half_t *__restrict__ x, size_t n, float momentum,
+                 int first, float *__restrict__ state) {
+  __shared__ float rmn[kCalThreads / kWave], rmx[kCalThreads / kWave];
+  float mn = INFINITY, mx = -INFINITY;
+  if (((uintptr_t)x & 15) == 0) {
+    const size_t n8 = n / 8;
+    for (size_t c = threadIdx.x; c < n8; c += kCalThreads) {
+      const half8 h = *reinterpret_cast<const half8 *>(x + c * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (float)h[e];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+    }
+    for (size_t k = n8 * 8 + threadIdx.x; k < n; k += kCalThreads) {
+      const float v = (float)x[k];
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+  } else {
+    for (size_t k = threadIdx.x; k < n; k += kCalThreads) {
+      const float v = (float)x[k];
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+  }
+  mn = -wave_max(-mn);
+  mx = wave_max(mx);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    rmn[w] = mn;
+    rmx[w] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bmn = rmn[0], bmx = rmx[0];
+    for (int i = 1; i < kCalThreads / kWave; ++i) {
+      bmn = fminf(bmn, rmn[i]);
+      bmx = fmaxf(bmx, rmx[i]);
+    }
+    if (first) {
+      state[0] = bmn;
+      state[1] = bmx;
+    } else {
+#pragma clang fp contract(off)
+      const float wgt = 1.0f - momentum;
+      const float a0 = momentum * state[0], b0 = wgt * bmn;
+      const float a1 = momentum * state[1], b1 = wgt * bmx;
+      state[0] = a0 + b0;
+      state[1] = a1 + b1;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+static_quant_kernel(const half_t *__restrict__ x, size_t n,
+                    const float *__restrict__ state, int8_t *__restrict__ q,
+                    float *__restrict__ s_out, int vec) {
+  const Quantizer z =
+      make_quantizer(fmaxf(fabsf(state[0]), fabsf(state[1])), 127.0f);
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nth = (size_t)gridDim.x * blockDim.x;
+  if (tid == 0) *s_out = z.s;
+  size_t done = 0;
+  if (vec) {
+    const size_t n8 = n / 8;
+    for (size_t c = tid; c < n8; c += nth) {
+      const half8 h = *reinterpret_cast<const half8 *>(x + c * 8);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (float)h[e];
+      *reinterpret_cast<v2i *>(q + c * 8) = quant8_pack(v, z);
+    }
+    done = n8 * 8;
+  }
+  for (size_t k = done + tid; k < n; k += nth)
+    q[k] = (int8_t)quant_code((float)x[k], z);
+}
+
+hipError_t launch_calibrate(const void *x, size_t n, float momentum, int first,
+                            float *state, hipStream_t s) {
+  hipLaunchKernelGGL(calibrate_kernel, dim3(1), dim3(kCalThreads), 0, s,
+                     static_cast<const half_t *>(x), n, momentum, first, state);
+  return hipGetLastError();
+}
+
+hipError_t launch_static_quant(const void *x, size_t n, const float *state,
+                               int8_t *q, float *s_out, hipStream_t s) {
+  const int vec = (((uintptr_t)x & 15) == 0) && (((uintptr_t)q & 7) == 0);
+  const size_t chunks = (n + 7) / 8;
+  size_t blocks = (chunks + 255) / 256;
+  if (blocks > 4096) blocks = 4096;  // grid-stride beyond
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(static_quant_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     s, static_cast<const half_t *>(x), n, state, q, s_out, vec);
+  return hipGetLastError();
+}
+
 // ================================================================= weights
 constexpr int kWQThreads = 1024;
 

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert "zq_gemm_w8a8" in names and "zq_ln_quant_act" in names
     for n in names:
         assert hasattr(L, n), f"{n} declared in zq.h but not exported"
-    assert L.zq_version() == 102
+    assert L.zq_version() == 103
 
 
 def test_last_error_starts_empty_and_is_set_on_failure():
@@ -140,3 +140,14 @@ def test_gemm_w8a16_argument_checks():
     assert Z.gemm_w8a16_plan(2, 18432, 6144).startswith("tiled-a16 cfg=4")
     assert Z.gemm_w8a16_plan(2048, 18432, 6144).startswith("tiled-a16 cfg=3")
     assert Z.gemm_w8a16_plan(100, 256, 512).startswith("tiled-a16 cfg=1")
+
+
+def test_static_range_argument_checks():
+    L = Z.lib()
+    F = ctypes.c_float
+    assert L.zq_calibrate_minmax(A, 4, 64, F(0.95), 0, None, None) == EINVAL
+    assert L.zq_calibrate_minmax(A, 0, 64, F(0.95), 0, B, None) == ESHAPE
+    assert L.zq_calibrate_minmax(A, 4, 64, F(1.5), 0, B, None) == EINVAL
+    assert L.zq_quant_act_static(A, 4, 64, None, C, D, None) == EINVAL
+    assert L.zq_quant_act_static(A, -1, 64, B, C, D, None) == ESHAPE
+    assert L.zq_quant_act_static(None, 0, 64, B, None, D, None) == OK
