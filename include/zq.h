@@ -12,9 +12,11 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *    library never allocates, frees or synchronizes; each call enqueues its
+ *    compute calls never allocate, free or synchronize; each enqueues its
  *    kernels on `stream` (a hipStream_t; NULL means the null stream) and
  *    returns at once.  Results are ready when the stream reaches them.
+ *    (The schedule tuner synchronizes, and a chain owns host memory, one
+ *    HIP stream and its graphs; both are described where declared.)
  *  - All matrices are row-major and dense.  Activations are [M][K] (one
  *    row per token = batch*seqlen entry), weights [N][K] (one row per output
  *    feature, K contiguous), outputs [M][N].
@@ -32,6 +34,7 @@
 #ifndef ZQ_H
 #define ZQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -241,12 +244,123 @@ zq_status zq_gemm_w8a16_plan(int M, int N, int K, char *buf, int buflen);
  */
 zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen);
 
+/*
+ * Schedule table -- the pages profile several GEMM schedules (tilings) for
+ * each input-size combination and, at run time, use the one profiled for
+ * the current batch x seqlen (summary page Sec. 3 "Quantization-Optimized
+ * Transformer Kernels", the schedule profiling and small-batch paragraphs;
+ * paper Sec. 4.3, App. D).  Here a process-wide table maps (bits, N, K,
+ * M range) to a kernel and tile; zq_gemm_w8a8/w4a8 (and their _i32 and
+ * _quant forms) and zq_gemm_plan consult it before the built-in rules.
+ * A plan never changes results: every kernel and tile gives the same bits.
+ * The table is shared by all threads and devices of the process (guarded
+ * by a lock); an empty table gives the built-in rules.
+ *
+ * zq_gemm_tune: times every kernel and tile that applies at each token
+ * count ms[0 .. nm-1] (strictly ascending, >= 1) for the problem described
+ * by the arguments (the same as zq_gemm_w8a8, bits 8 or 4, on buffers
+ * sized for M = ms[nm-1]; y is overwritten), `reps` launches each after
+ * one warm-up, and stores the fastest for the token range (ms[i-1], ms[i]]
+ * (ms[-1] = 0).  chosen (nm x 2 ints: kind 0 skinny, 1 tiled, 2 stream,
+ * 3 gemv; tile index or -1) and us (nm floats, the winner's average
+ * launch time in microseconds) may be NULL.  Synchronizes `stream`; must
+ * not be called while `stream` is being captured.
+ * Errors: as zq_gemm_w8a8; ZQ_EINVAL (ms not ascending or < 1, nm < 1 or
+ * > 64, reps < 1 or > 10000, stream under capture).
+ *
+ * zq_sched_export: the table as text, one entry per line:
+ *     "<bits> <N> <K> <M lo> <M hi> <skinny|tiled|stream|gemv> <tile>"
+ * written NUL-terminated into buf (truncated to buflen - 1 chars; buf may
+ * be NULL with buflen 0); *needed (may be NULL) receives the full size
+ * including the NUL.  zq_sched_import: adds the entries of such a text
+ * (blank lines and '#' comments are skipped), replacing what the table
+ * holds for the same (bits, N, K) over each range; either every line is
+ * valid and all are added, or nothing is (ZQ_EINVAL, the first bad line
+ * named in zq_last_error).  A kernel must apply at both ends of its range
+ * (gemv: M = 1 with whole 1 KB weight-row pieces; stream: M <= 16, even N;
+ * skinny: M <= 64; tile indices of W8-only tiles are refused for bits 4).
+ * zq_sched_clear empties the table.  zq_sched_entries: entry count.
+ */
+zq_status zq_gemm_tune(int bits, const int8_t *qx, const float *sx,
+                       const void *qw, const float *sw, int G,
+                       const void *bias_fp16, int act, const int *ms, int nm,
+                       int N, int K, void *y_fp16, int reps, int *chosen,
+                       float *us, void *stream);
+zq_status zq_sched_export(char *buf, size_t buflen, size_t *needed);
+zq_status zq_sched_import(const char *text);
+void zq_sched_clear(void);
+int zq_sched_entries(void);
+
+/*
+ * zq_chain -- a recorded sequence of the calls above, replayed as one HIP
+ * graph: the pages record a small model's whole launch sequence on the
+ * first inference call and replay it with a single submission afterwards,
+ * removing per-kernel launch overhead (summary page Sec. 3
+ * "Quantization-Optimized Transformer Kernels", the CUDA Graph paragraph;
+ * paper App. D).
+ *
+ * zq_chain_create(max_m): an empty chain whose buffers hold up to max_m
+ * token rows.  The zq_chain_add_* calls append one call each, with the
+ * arguments of the call of the same name minus M and stream; every buffer
+ * sized by M must hold max_m rows (row r of each begins at the same offset
+ * as in a dense [max_m][...] tensor) and stays owned by the caller, who
+ * keeps it allocated while the chain lives.  Arguments are checked when
+ * added, as the call itself checks them (with M = max_m; ws_bytes against
+ * max_m), and a failing add appends nothing.  Host only: no GPU is touched.
+ *
+ * zq_chain_run(chain, M, stream): runs the sequence over the first M rows
+ * of every buffer.  The first run with a given M (or the first after the
+ * schedule table changed) captures the launches into a HIP graph on a
+ * stream of the chain's own (created then, on the current device, which
+ * must hold the buffers) and instantiates it; every run launches the
+ * graph for its M on `stream`.  If `stream` is itself being captured, the
+ * calls are launched directly instead, so they join that capture.  At most
+ * ZQ_CHAIN_MAX_GRAPHS graphs are kept (the least recently used is dropped).
+ * zq_chain_run_eager launches the same calls one by one, without a graph.
+ * M == 0 launches nothing.  The graphs read the buffers' contents at each
+ * launch, so new inputs need no new capture.  A chain is used by one
+ * thread at a time; runs on different streams that share buffers race.
+ * zq_chain_graphs: graphs currently held; zq_chain_length: calls recorded.
+ * zq_chain_destroy waits for the chain's graph launches still in flight,
+ * then frees the graphs, the stream and the chain (NULL is ignored); a
+ * dropped graph is likewise waited for before it is freed.
+ * Errors: ZQ_EINVAL (null chain, max_m < 1, M outside [0, max_m]), the
+ * add errors of the matching call, ZQ_EHIP (capture or launch refused).
+ */
+typedef struct zq_chain zq_chain;
+#define ZQ_CHAIN_MAX_GRAPHS 64
+zq_status zq_chain_create(int max_m, zq_chain **out);
+zq_status zq_chain_add_ln_quant(zq_chain *c, const void *x_fp16,
+                                const void *gamma_fp16, const void *beta_fp16,
+                                float eps, int K, int8_t *qx, float *sx,
+                                void *ln_out_fp16);
+zq_status zq_chain_add_quant(zq_chain *c, const void *x_fp16, int K,
+                             int8_t *qx, float *sx);
+zq_status zq_chain_add_gemm(zq_chain *c, int bits, const int8_t *qx,
+                            const float *sx, const void *qw, const float *sw,
+                            int G, const void *bias_fp16, int act, int N, int K,
+                            void *y_fp16);
+zq_status zq_chain_add_gemm_quant(zq_chain *c, int bits, const int8_t *qx,
+                                  const float *sx, const void *qw,
+                                  const float *sw, int G, const void *bias_fp16,
+                                  int act, int N, int K, int8_t *qy, float *sy,
+                                  void *ws, size_t ws_bytes);
+zq_status zq_chain_add_gemm_w8a16(zq_chain *c, const void *x_fp16,
+                                  const int8_t *qw, const float *sw, int G,
+                                  const void *bias_fp16, int act, int N, int K,
+                                  void *y_fp16);
+zq_status zq_chain_run(zq_chain *c, int M, void *stream);
+zq_status zq_chain_run_eager(zq_chain *c, int M, void *stream);
+int zq_chain_graphs(const zq_chain *c);
+int zq_chain_length(const zq_chain *c);
+void zq_chain_destroy(zq_chain *c);
+
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char *zq_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int zq_version(void);
-#define ZQ_VERSION 103
+#define ZQ_VERSION 104
 
 #ifdef __cplusplus
 }

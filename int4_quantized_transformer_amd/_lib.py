@@ -17,7 +17,8 @@ __all__ = ["ZQError", "library_path", "lib", "quantize_weights",
            "gemm_w8a8_i32", "gemm_w4a8_i32", "gemm_w8a8_quant",
            "gemm_w4a8_quant", "gemm_quant_workspace_bytes", "gemm_plan",
            "gemm_w8a16", "gemm_w8a16_plan", "calibrate_minmax",
-           "quant_act_static", "ACT_NONE", "ACT_GELU"]
+           "quant_act_static", "gemm_tune", "sched_export", "sched_import",
+           "sched_clear", "sched_entries", "Chain", "ACT_NONE", "ACT_GELU"]
 
 ACT_NONE = 0
 ACT_GELU = 1
@@ -67,6 +68,18 @@ def lib():
             "zq_gemm_w8a16_plan": [I, I, I, ctypes.c_char_p, I],
             "zq_calibrate_minmax": [P, I, I, F, I, P, P],
             "zq_quant_act_static": [P, I, I, P, P, P, P],
+            "zq_gemm_tune": [I, P, P, P, P, I, P, I, P, I, I, I, P, I, P, P, P],
+            "zq_sched_export": [P, ctypes.c_size_t, P],
+            "zq_sched_import": [ctypes.c_char_p],
+            "zq_chain_create": [I, P],
+            "zq_chain_add_ln_quant": [P, P, P, P, F, I, P, P, P],
+            "zq_chain_add_quant": [P, P, I, P, P],
+            "zq_chain_add_gemm": [P, I, P, P, P, P, I, P, I, I, I, P],
+            "zq_chain_add_gemm_quant": [P, I, P, P, P, P, I, P, I, I, I, P, P,
+                                        P, ctypes.c_size_t],
+            "zq_chain_add_gemm_w8a16": [P, P, P, P, I, P, I, I, I, P],
+            "zq_chain_run": [P, I, P],
+            "zq_chain_run_eager": [P, I, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -74,6 +87,15 @@ def lib():
             fn.restype = I
         L.zq_gemm_quant_workspace_bytes.argtypes = [I, I]
         L.zq_gemm_quant_workspace_bytes.restype = ctypes.c_size_t
+        for name in ("zq_chain_graphs", "zq_chain_length"):
+            getattr(L, name).argtypes = [P]
+            getattr(L, name).restype = I
+        L.zq_chain_destroy.argtypes = [P]
+        L.zq_chain_destroy.restype = None
+        L.zq_sched_clear.argtypes = []
+        L.zq_sched_clear.restype = None
+        L.zq_sched_entries.argtypes = []
+        L.zq_sched_entries.restype = I
         L.zq_last_error.argtypes = []
         L.zq_last_error.restype = ctypes.c_char_p
         L.zq_version.argtypes = []
@@ -322,3 +344,189 @@ def gemm_plan(M, N, K, bits) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib().zq_gemm_plan(M, N, K, bits, buf, 256))
     return buf.value.decode()
+
+
+PLAN_KINDS = {0: "skinny", 1: "tiled", 2: "stream", 3: "gemv"}
+
+
+def gemm_tune(qx, sx, qw, sw, G, ms, bias=None, act=ACT_NONE, y=None, reps=10,
+              stream=None):
+    """Times every GEMM kernel and tile that applies at each token count of
+    ``ms`` (ascending) on these buffers (qx/sx/y sized for the largest) and
+    stores the fastest in the schedule table for (previous count, count].
+    Returns [(kind, tile or -1, microseconds)] per count.  Synchronizes."""
+    _need(qx, "qx", torch.int8, dim=2)
+    bits = 8 if qw.dtype == torch.int8 else 4
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, qx.device, 2)
+    _need(sx, "sx", torch.float32, qx.device)
+    _need(sw, "sw", torch.float32, qx.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, qx.device)
+    ms = [int(m) for m in ms]
+    M, K = qx.shape
+    N = qw.shape[0]
+    if not ms or ms[-1] > M or sx.numel() < ms[-1]:
+        raise ValueError(f"token counts {ms} exceed the buffers' {M} rows")
+    if y is None:
+        y = torch.empty(ms[-1], N, dtype=torch.float16, device=qx.device)
+    _need(y, "y", torch.float16, qx.device)
+    if y.numel() < ms[-1] * N:
+        raise ValueError("y is smaller than the largest token count needs")
+    n = len(ms)
+    arr = (ctypes.c_int * n)(*ms)
+    chosen = (ctypes.c_int * (2 * n))()
+    us = (ctypes.c_float * n)()
+    _check(lib().zq_gemm_tune(bits, _p(qx), _p(sx), _p(qw), _p(sw), G, _p(bias),
+                              int(act), arr, n, N, K, _p(y), int(reps), chosen,
+                              us, _stream(qx, stream)))
+    return [(PLAN_KINDS[chosen[2 * i]], chosen[2 * i + 1], us[i])
+            for i in range(n)]
+
+
+def sched_export() -> str:
+    """The schedule table as text, one entry per line."""
+    need = ctypes.c_size_t(0)
+    _check(lib().zq_sched_export(None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(need.value)
+    _check(lib().zq_sched_export(buf, need.value, None))
+    return buf.value.decode()
+
+
+def sched_import(text: str):
+    _check(lib().zq_sched_import(text.encode()))
+
+
+def sched_clear():
+    lib().zq_sched_clear()
+
+
+def sched_entries() -> int:
+    return lib().zq_sched_entries()
+
+
+class Chain:
+    """A recorded sequence of libzq calls over buffers of ``max_m`` token
+    rows, replayed as one HIP graph per token count (zq_chain_*).  The
+    chain keeps a reference to every tensor it was given, so they stay
+    allocated while it lives."""
+
+    def __init__(self, max_m):
+        h = ctypes.c_void_p()
+        _check(lib().zq_chain_create(int(max_m), ctypes.byref(h)))
+        self._h = h
+        self.max_m = int(max_m)
+        self._keep = []
+        self.device = None
+
+    def _rows(self, t, name, dtype, width=None):
+        _need(t, name, dtype, self.device)
+        if self.device is None:
+            self.device = t.device
+        if t.shape[0] < self.max_m or (width is not None and t.dim() == 2
+                                       and t.shape[1] != width):
+            raise ValueError(f"{name} {tuple(t.shape)} must hold {self.max_m} "
+                             f"rows" + (f" of {width}" if width else ""))
+        self._keep.append(t)
+
+    def _dev(self, t, name, dtype):
+        if t is None:
+            return
+        _need(t, name, dtype, self.device)
+        if self.device is None:
+            self.device = t.device
+        self._keep.append(t)
+
+    def ln_quant(self, x, qx, sx, gamma=None, beta=None, eps=1e-5, ln_out=None):
+        K = x.shape[1]
+        self._rows(x, "x", torch.float16, K)
+        self._rows(qx, "qx", torch.int8, K)
+        self._rows(sx, "sx", torch.float32)
+        self._dev(gamma, "gamma", torch.float16)
+        self._dev(beta, "beta", torch.float16)
+        if ln_out is not None:
+            self._rows(ln_out, "ln_out", torch.float16, K)
+        _check(lib().zq_chain_add_ln_quant(self._h, _p(x), _p(gamma), _p(beta),
+                                           ctypes.c_float(eps), K, _p(qx),
+                                           _p(sx), _p(ln_out)))
+
+    def quant(self, x, qx, sx):
+        K = x.shape[1]
+        self._rows(x, "x", torch.float16, K)
+        self._rows(qx, "qx", torch.int8, K)
+        self._rows(sx, "sx", torch.float32)
+        _check(lib().zq_chain_add_quant(self._h, _p(x), K, _p(qx), _p(sx)))
+
+    def _gemm_common(self, qx, sx, qw, sw, bias):
+        K = qx.shape[1]
+        bits = 8 if qw.dtype == torch.int8 else 4
+        self._rows(qx, "qx", torch.int8, K)
+        self._rows(sx, "sx", torch.float32)
+        self._dev(qw, "qw", torch.int8 if bits == 8 else torch.uint8)
+        self._dev(sw, "sw", torch.float32)
+        self._dev(bias, "bias", torch.float16)
+        if qw.shape[1] != (K if bits == 8 else K // 2):
+            raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+        return bits, qw.shape[0], K
+
+    def gemm(self, qx, sx, qw, sw, G, y, bias=None, act=ACT_NONE):
+        bits, N, K = self._gemm_common(qx, sx, qw, sw, bias)
+        self._rows(y, "y", torch.float16, N)
+        _check(lib().zq_chain_add_gemm(self._h, bits, _p(qx), _p(sx), _p(qw),
+                                       _p(sw), G, _p(bias), int(act), N, K,
+                                       _p(y)))
+
+    def gemm_quant(self, qx, sx, qw, sw, G, qy, sy, ws, bias=None,
+                   act=ACT_NONE):
+        bits, N, K = self._gemm_common(qx, sx, qw, sw, bias)
+        self._rows(qy, "qy", torch.int8, N)
+        self._rows(sy, "sy", torch.float32)
+        self._dev(ws, "ws", torch.uint8)
+        _check(lib().zq_chain_add_gemm_quant(self._h, bits, _p(qx), _p(sx),
+                                             _p(qw), _p(sw), G, _p(bias),
+                                             int(act), N, K, _p(qy), _p(sy),
+                                             _p(ws), ws.numel()))
+
+    def gemm_w8a16(self, x, qw, sw, G, y, bias=None, act=ACT_NONE):
+        K = x.shape[1]
+        self._rows(x, "x", torch.float16, K)
+        self._dev(qw, "qw", torch.int8)
+        self._dev(sw, "sw", torch.float32)
+        self._dev(bias, "bias", torch.float16)
+        N = qw.shape[0]
+        self._rows(y, "y", torch.float16, N)
+        _check(lib().zq_chain_add_gemm_w8a16(self._h, _p(x), _p(qw), _p(sw), G,
+                                             _p(bias), int(act), N, K, _p(y)))
+
+    def _stream(self, stream):
+        if stream is not None:
+            return ctypes.c_void_p(int(stream))
+        if self.device is None:
+            return None
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    def run(self, M, stream=None):
+        """Launches the graph for M rows (captured on first use)."""
+        _check(lib().zq_chain_run(self._h, int(M), self._stream(stream)))
+
+    def run_eager(self, M, stream=None):
+        """Launches the recorded calls one by one."""
+        _check(lib().zq_chain_run_eager(self._h, int(M), self._stream(stream)))
+
+    @property
+    def graphs(self) -> int:
+        return lib().zq_chain_graphs(self._h)
+
+    def __len__(self):
+        return lib().zq_chain_length(self._h)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().zq_chain_destroy(self._h)
+            self._h = ctypes.c_void_p()
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

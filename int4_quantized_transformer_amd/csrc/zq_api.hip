@@ -5,9 +5,9 @@
 
 #include "zq_internal.h"
 
-namespace {
+namespace zq {
 
-thread_local char g_err[512] = "";
+static thread_local char g_err[512] = "";
 
 zq_status fail(zq_status st, const char *fmt, ...) {
   va_list ap;
@@ -21,6 +21,13 @@ zq_status ok() {
   g_err[0] = '\0';
   return ZQ_OK;
 }
+
+}  // namespace zq
+
+namespace {
+
+using zq::fail;
+using zq::ok;
 
 zq_status hip_status(hipError_t e, const char *what) {
   if (e != hipSuccess)
@@ -332,7 +339,77 @@ zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen) {
   return ok();
 }
 
-const char *zq_last_error(void) { return g_err; }
+zq_status zq_gemm_tune(int bits, const int8_t *qx, const float *sx,
+                       const void *qw, const float *sw, int G,
+                       const void *bias_fp16, int act, const int *ms, int nm,
+                       int N, int K, void *y_fp16, int reps, int *chosen,
+                       float *us, void *stream) {
+  const char *fn = "zq_gemm_tune";
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  if (!ms || nm < 1 || nm > 64)
+    return fail(ZQ_EINVAL, "%s: need 1 .. 64 token counts (nm=%d)", fn, nm);
+  for (int i = 0; i < nm; ++i)
+    if (ms[i] < 1 || (i > 0 && ms[i] <= ms[i - 1]))
+      return fail(ZQ_EINVAL, "%s: token counts must be >= 1 and ascending", fn);
+  if (reps < 1 || reps > 10000)
+    return fail(ZQ_EINVAL, "%s: reps=%d outside [1, 10000]", fn, reps);
+  if (!qx || !sx || !y_fp16) return fail(ZQ_EINVAL, "%s: null qx/sx/y", fn);
+  // the remaining checks of the GEMM call itself (with no launch)
+  zq_status st = gemm_fused(qx, sx, qw, sw, G, bias_fp16, act, 0, N, K,
+                            y_fp16, stream, bits, fn);
+  if (st != ZQ_OK) return st;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  st = hip_status(hipStreamIsCapturing((hipStream_t)stream, &cs), fn);
+  if (st != ZQ_OK) return st;
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(ZQ_EINVAL, "%s: the stream is being captured", fn);
+  zq::GemmArgs a{};
+  a.qx = qx;
+  a.sx = sx;
+  a.qw = qw;
+  a.sw = sw;
+  a.bias = static_cast<const zq::half_t *>(bias_fp16);
+  a.out = y_fp16;
+  a.G = G;
+  a.N = N;
+  a.K = K;
+  a.act = act;
+  a.bits = bits;
+  a.raw_i32 = false;
+  int kinds[64], cfgs[64];
+  st = hip_status(zq::tune_gemm(a, ms, nm, reps, (hipStream_t)stream, kinds,
+                                cfgs, us),
+                  fn);
+  if (st != ZQ_OK) return st;
+  if (chosen)
+    for (int i = 0; i < nm; ++i) {
+      chosen[2 * i] = kinds[i];
+      chosen[2 * i + 1] = cfgs[i];
+    }
+  return ok();
+}
+
+zq_status zq_sched_export(char *buf, size_t buflen, size_t *needed) {
+  if (!buf && buflen > 0)
+    return fail(ZQ_EINVAL, "zq_sched_export: null buffer with buflen > 0");
+  const size_t n = zq::sched_export(buf, buflen);
+  if (needed) *needed = n;
+  return ok();
+}
+
+zq_status zq_sched_import(const char *text) {
+  if (!text) return fail(ZQ_EINVAL, "zq_sched_import: null text");
+  const int r = zq::sched_import(text);
+  if (r < 0)
+    return fail(ZQ_EINVAL, "zq_sched_import: line %d is not a valid entry", -r);
+  return ok();
+}
+
+void zq_sched_clear(void) { zq::sched_clear(); }
+
+int zq_sched_entries(void) { return zq::sched_entries(); }
+
+const char *zq_last_error(void) { return zq::g_err; }
 
 int zq_version(void) { return ZQ_VERSION; }
 

@@ -22,6 +22,13 @@
 // result is shifted right by 4 (exact: every product is a multiple of 16).
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+#include <string>
+#include <vector>
 
 #include "zq_internal.h"
 
@@ -1561,7 +1568,86 @@ struct Plan {
   PlanKind kind;
   int mf;   // skinny: 16-token fragments
   int cfg;  // tiled: index into kTileCfgs
+  bool tuned = false;  // taken from the schedule table
 };
+
+static bool w8_only(int cfg) {
+  return (cfg >= 16 && cfg <= 20) || cfg == 23;
+}
+
+// Whether a plan of this kind / tile applies to a problem.  The tiled
+// kernels take any M and N; the decode kernels have their own limits.
+static bool plan_applies(PlanKind kind, int cfg, int M, int N, int K, int bits) {
+  const int ldw = bits == 4 ? K / 2 : K;
+  switch (kind) {
+    case kGemv: return M == 1 && ldw % 1024 == 0;
+    case kStream: return M >= 1 && M <= 16 && (N & 1) == 0;
+    case kSkinny: return M >= 1 && M <= 64;
+    case kTiled: return cfg >= 0 && cfg < kNumTileCfgs && !(bits == 4 && w8_only(cfg));
+  }
+  return false;
+}
+
+// The decode kernels' launch parameters follow from M.
+static Plan make_plan(PlanKind kind, int cfg, int M, bool tuned) {
+  Plan p{kind, 0, cfg, tuned};
+  if (kind == kSkinny) p.mf = (M + 15) / 16;
+  if (kind == kStream) p.mf = M == 1 ? 1 : 16;
+  if (kind == kGemv) p.mf = 1;
+  if (kind != kTiled) p.cfg = 0;
+  return p;
+}
+
+// ------------------------------------------------------- schedule table
+// The pages profile several schedules per input-size combination and keep
+// the best one per batch x seqlen.  Here a process-wide table maps
+// (bits, N, K, M range) to a plan; the tuner fills it by timing every plan
+// that applies, and choose() looks it up before its own rules.  The
+// generation counter changes with every edit, so captured launch sequences
+// know when their plans went stale.
+struct SchedEntry {
+  int bits, N, K, mlo, mhi;
+  PlanKind kind;
+  int cfg;
+};
+static std::mutex g_sched_mu;
+static std::vector<SchedEntry> g_sched;
+static std::atomic<unsigned> g_sched_gen{0};
+
+static bool sched_lookup(int M, int N, int K, int bits, Plan *out) {
+  std::lock_guard<std::mutex> lk(g_sched_mu);
+  for (const SchedEntry &e : g_sched)
+    if (e.bits == bits && e.N == N && e.K == K && M >= e.mlo && M <= e.mhi) {
+      *out = make_plan(e.kind, e.cfg, M, true);
+      return true;
+    }
+  return false;
+}
+
+// Replaces what the table holds for the same (bits, N, K) over [mlo, mhi]
+// (overlapping entries are trimmed or split).
+static void sched_put_locked(const SchedEntry &n) {
+  std::vector<SchedEntry> keep;
+  for (const SchedEntry &e : g_sched) {
+    if (e.bits != n.bits || e.N != n.N || e.K != n.K || e.mhi < n.mlo ||
+        e.mlo > n.mhi) {
+      keep.push_back(e);
+      continue;
+    }
+    if (e.mlo < n.mlo) {
+      SchedEntry l = e;
+      l.mhi = n.mlo - 1;
+      keep.push_back(l);
+    }
+    if (e.mhi > n.mhi) {
+      SchedEntry r = e;
+      r.mlo = n.mhi + 1;
+      keep.push_back(r);
+    }
+  }
+  keep.push_back(n);
+  g_sched.swap(keep);
+}
 
 // ZQ_GEMM_TILE=<index> forces one tiled configuration (tuning aid).
 static int forced_tile() {
@@ -1642,6 +1728,8 @@ static int forced_gemv() {
 static Plan choose(int M, int N, int K, int bits) {
   const int f = forced_tile();
   if (f >= 0) return Plan{kTiled, 0, f};
+  Plan tp;
+  if (sched_lookup(M, N, K, bits, &tp)) return tp;
   if (M <= 64) {
     const int fd = forced_decode();
     const int ldw = bits == 4 ? K / 2 : K;
@@ -1687,8 +1775,7 @@ static hipError_t run_skinny_mf(int id, const GemmArgs &a, hipStream_t s) {
 }
 
 template <bool W4, bool RAW>
-static hipError_t run(const GemmArgs &a, hipStream_t s) {
-  const Plan pl = choose(a.M, a.N, a.K, a.bits);
+static hipError_t run(const Plan &pl, const GemmArgs &a, hipStream_t s) {
   if (pl.kind == kGemv) {
     // activation row in LDS when it fits in 8 KB (2 pieces per thread) or
     // 32 KB (8 pieces)
@@ -1727,10 +1814,179 @@ static hipError_t run(const GemmArgs &a, hipStream_t s) {
   return run_tile_cfg<W4, RAW>(pl.cfg, a, s);
 }
 
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
+static hipError_t run_plan(const Plan &pl, const GemmArgs &a, hipStream_t s) {
   if (a.bits == 4)
-    return a.raw_i32 ? run<true, true>(a, s) : run<true, false>(a, s);
-  return a.raw_i32 ? run<false, true>(a, s) : run<false, false>(a, s);
+    return a.raw_i32 ? run<true, true>(pl, a, s) : run<true, false>(pl, a, s);
+  return a.raw_i32 ? run<false, true>(pl, a, s) : run<false, false>(pl, a, s);
+}
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
+  return run_plan(choose(a.M, a.N, a.K, a.bits), a, s);
+}
+
+// ------------------------------------------------------------- tuner
+static const char *kind_name(PlanKind k) {
+  switch (k) {
+    case kGemv: return "gemv";
+    case kStream: return "stream";
+    case kSkinny: return "skinny";
+    case kTiled: return "tiled";
+  }
+  return "?";
+}
+
+static bool kind_from_name(const char *s, PlanKind *k) {
+  static const PlanKind all[] = {kGemv, kStream, kSkinny, kTiled};
+  for (PlanKind c : all)
+    if (strcmp(s, kind_name(c)) == 0) {
+      *k = c;
+      return true;
+    }
+  return false;
+}
+
+unsigned sched_generation() { return g_sched_gen.load(); }
+
+void sched_clear() {
+  std::lock_guard<std::mutex> lk(g_sched_mu);
+  g_sched.clear();
+  g_sched_gen++;
+}
+
+int sched_entries() {
+  std::lock_guard<std::mutex> lk(g_sched_mu);
+  return (int)g_sched.size();
+}
+
+// One line per entry: "<bits> <N> <K> <M lo> <M hi> <kind> <tile cfg>".
+size_t sched_export(char *buf, size_t len) {
+  std::string out;
+  {
+    std::lock_guard<std::mutex> lk(g_sched_mu);
+    std::vector<SchedEntry> v = g_sched;
+    std::sort(v.begin(), v.end(), [](const SchedEntry &x, const SchedEntry &y) {
+      if (x.bits != y.bits) return x.bits < y.bits;
+      if (x.N != y.N) return x.N < y.N;
+      if (x.K != y.K) return x.K < y.K;
+      return x.mlo < y.mlo;
+    });
+    char line[96];
+    for (const SchedEntry &e : v) {
+      snprintf(line, sizeof line, "%d %d %d %d %d %s %d\n", e.bits, e.N, e.K,
+               e.mlo, e.mhi, kind_name(e.kind), e.kind == kTiled ? e.cfg : 0);
+      out += line;
+    }
+  }
+  if (buf && len > 0) {
+    const size_t n = out.size() < len - 1 ? out.size() : len - 1;
+    memcpy(buf, out.data(), n);
+    buf[n] = '\0';
+  }
+  return out.size() + 1;
+}
+
+// Parses the whole text first; nothing is applied unless every line is a
+// valid entry.  Returns the number of entries, or -(line number) of the
+// first bad line.
+int sched_import(const char *text) {
+  std::vector<SchedEntry> add;
+  int lineno = 0;
+  const char *p = text;
+  while (*p) {
+    const char *e = strchr(p, '\n');
+    const size_t n = e ? (size_t)(e - p) : strlen(p);
+    ++lineno;
+    std::string line(p, n);
+    p += n + (e ? 1 : 0);
+    const size_t h = line.find('#');
+    if (h != std::string::npos) line.resize(h);
+    if (line.find_first_not_of(" \t\r") == std::string::npos) continue;
+    SchedEntry s{};
+    char kind[16];
+    int used = 0;
+    if (sscanf(line.c_str(), "%d %d %d %d %d %15s %d %n", &s.bits, &s.N, &s.K,
+               &s.mlo, &s.mhi, kind, &s.cfg, &used) != 7 ||
+        line.find_first_not_of(" \t\r", used) != std::string::npos)
+      return -lineno;
+    if ((s.bits != 8 && s.bits != 4) || s.N <= 0 || s.K <= 0 || s.K % 64 != 0 ||
+        s.mlo < 1 || s.mhi < s.mlo || !kind_from_name(kind, &s.kind))
+      return -lineno;
+    // the plan must apply at both ends of its range (and so in between)
+    if (!plan_applies(s.kind, s.cfg, s.mlo, s.N, s.K, s.bits) ||
+        !plan_applies(s.kind, s.cfg, s.mhi, s.N, s.K, s.bits))
+      return -lineno;
+    if (s.kind != kTiled) s.cfg = 0;
+    add.push_back(s);
+  }
+  std::lock_guard<std::mutex> lk(g_sched_mu);
+  for (const SchedEntry &s : add) sched_put_locked(s);
+  g_sched_gen++;
+  return (int)add.size();
+}
+
+// Every plan that applies to (M, N, K, bits).
+static std::vector<Plan> candidates(int M, int N, int K, int bits) {
+  std::vector<Plan> v;
+  for (PlanKind k : {kGemv, kStream, kSkinny})
+    if (plan_applies(k, 0, M, N, K, bits)) v.push_back(make_plan(k, 0, M, false));
+  for (int c = 0; c < kNumTileCfgs; ++c)
+    if (plan_applies(kTiled, c, M, N, K, bits)) v.push_back(make_plan(kTiled, c, M, false));
+  return v;
+}
+
+// Times every applicable plan at each M of ms[] (ascending) on the caller's
+// buffers (sized for the largest M) and records the fastest for the range
+// (previous M, M].  Synchronizes the stream; not for use under capture.
+hipError_t tune_gemm(const GemmArgs &base, const int *ms, int nm, int reps,
+                     hipStream_t s, int *chosen_kind, int *chosen_cfg,
+                     float *chosen_us) {
+  hipEvent_t e0, e1;
+  hipError_t err = hipEventCreate(&e0);
+  if (err != hipSuccess) return err;
+  err = hipEventCreate(&e1);
+  if (err != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return err;
+  }
+  std::vector<SchedEntry> found;
+  int prev = 0;
+  for (int i = 0; i < nm && err == hipSuccess; ++i) {
+    GemmArgs a = base;
+    a.M = ms[i];
+    float best = 0.0f;
+    bool have = false;
+    Plan bp{kTiled, 0, 0};
+    for (const Plan &pl : candidates(a.M, a.N, a.K, a.bits)) {
+      err = run_plan(pl, a, s);  // warm-up (and code-object load)
+      if (err == hipSuccess) err = hipEventRecord(e0, s);
+      for (int r = 0; r < reps && err == hipSuccess; ++r) err = run_plan(pl, a, s);
+      if (err == hipSuccess) err = hipEventRecord(e1, s);
+      if (err == hipSuccess) err = hipEventSynchronize(e1);
+      float ms_ = 0.0f;
+      if (err == hipSuccess) err = hipEventElapsedTime(&ms_, e0, e1);
+      if (err != hipSuccess) break;
+      const float us = 1e3f * ms_ / reps;
+      if (!have || us < best) {
+        best = us;
+        bp = pl;
+        have = true;
+      }
+    }
+    if (err != hipSuccess) break;
+    found.push_back(SchedEntry{a.bits, a.N, a.K, prev + 1, a.M, bp.kind,
+                               bp.kind == kTiled ? bp.cfg : 0});
+    if (chosen_kind) chosen_kind[i] = (int)bp.kind;
+    if (chosen_cfg) chosen_cfg[i] = bp.kind == kTiled ? bp.cfg : -1;
+    if (chosen_us) chosen_us[i] = best;
+    prev = a.M;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lk(g_sched_mu);
+  for (const SchedEntry &e : found) sched_put_locked(e);
+  g_sched_gen++;
+  return hipSuccess;
 }
 
 // ---------------------------------------------------- quantized output
@@ -1822,20 +2078,21 @@ int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len) {
 
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
   const Plan pl = choose(M, N, K, bits);
+  const char *src = pl.tuned ? " [table]" : "";
   if (pl.kind == kGemv)
-    return snprintf(buf, len, "gemv NW=4 U=6 W%d rows=%d x_in_lds=%d", bits,
-                    N, K <= 32768 ? 1 : 0);
+    return snprintf(buf, len, "gemv NW=4 U=6 W%d rows=%d x_in_lds=%d%s", bits,
+                    N, K <= 32768 ? 1 : 0, src);
   if (pl.kind == kStream)
-    return snprintf(buf, len, "stream BN=16 MX=%d NW=4 W%d row_blocks=%d",
-                    pl.mf, bits, (N + 15) / 16);
+    return snprintf(buf, len, "stream BN=16 MX=%d NW=4 W%d row_blocks=%d%s",
+                    pl.mf, bits, (N + 15) / 16, src);
   if (pl.kind == kSkinny)
-    return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d",
-                    pl.mf, pl.mf <= 2 ? 4 : 2, bits, (N + 15) / 16);
+    return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d%s",
+                    pl.mf, pl.mf <= 2 ? 4 : 2, bits, (N + 15) / 16, src);
   const TileCfg &c = kTileCfgs[pl.cfg];
   return snprintf(buf, len,
-                  "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d kb=%d W%d tiles=%d",
+                  "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d kb=%d W%d tiles=%d%s",
                   pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, c.kb, bits,
-                  ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm));
+                  ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm), src);
 }
 
 }  // namespace zq

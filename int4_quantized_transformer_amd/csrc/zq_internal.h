@@ -255,4 +255,22 @@ int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len);
 // Human-readable schedule for (M, N, K, bits); returns chars written.
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len);
 
+// Schedule table (bits, N, K, M range) -> plan, consulted before the
+// built-in rules.  tune_gemm times every applicable plan at each M of ms[]
+// (ascending, buffers of base sized for the last) and stores the fastest
+// for (previous M, M]; chosen_kind/cfg/us (nm entries, may be null) report
+// what it picked.  The generation changes with every edit.
+hipError_t tune_gemm(const GemmArgs &base, const int *ms, int nm, int reps,
+                     hipStream_t s, int *chosen_kind, int *chosen_cfg,
+                     float *chosen_us);
+unsigned sched_generation();
+void sched_clear();
+int sched_entries();
+size_t sched_export(char *buf, size_t len);  // returns bytes needed (with NUL)
+int sched_import(const char *text);          // entries added, or -(bad line)
+
+// Error reporting of the C ABI (the thread-local zq_last_error string).
+zq_status fail(zq_status st, const char *fmt, ...);
+zq_status ok();
+
 }  // namespace zq

@@ -33,7 +33,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["Linear", "Workload", "WORKLOADS", "workload", "gen_weights",
-           "gen_activations", "outlier_channels", "randn_fp16"]
+           "gen_activations", "outlier_channels", "randn_fp16", "layer_chain"]
 
 
 @dataclass(frozen=True)
@@ -135,3 +135,54 @@ def randn_fp16(shape, seed: int, std: float = 1.0, mean: float = 0.0):
     """Generic seeded fp16 draw for edge-case tests."""
     g = _gen(seed)
     return (torch.randn(*shape, generator=g) * std + mean).to(torch.float16)
+
+
+def layer_chain(wl: Workload, max_m: int, device, seed: int = 0):
+    """The four linears of one encoder layer of ``wl`` over ``max_m`` tokens,
+    recorded as a zq Chain: LN + token quantization -> QKV; token
+    quantization -> attention output; LN + token quantization -> FFN1 (GeLU,
+    output quantized for FFN2) -> FFN2.  The attention core and the residual
+    adds lie outside the quantized linear path, so the attention context and
+    the FFN block's input are seeded inputs of their own (N(0,1) with the
+    workload's outlier channels, like the layer input).  Weights are the
+    workload's, quantized on the device.  Returns (chain, buffers)."""
+    from . import _lib as zq
+    qkv, ao, f1, f2 = wl.linears
+    h = qkv.K
+    g = _gen(seed)
+
+    def act(K):
+        x = torch.randn(max_m, K, generator=g)
+        x[:, torch.randperm(K, generator=g)[: wl.n_outliers(K)]] *= wl.outlier_factor
+        return x.to(torch.float16).to(device)
+
+    def lin(i):
+        w, b = gen_weights(wl, i)
+        qw, sw = zq.quantize_weights(w.to(device), wl.G, wl.linears[i].bits)
+        return qw, sw, b.to(device)
+
+    def empty(*shape, dtype=torch.float16):
+        return torch.empty(*shape, dtype=dtype, device=device)
+
+    B = {"x": act(h), "ctx": act(h), "h1": act(h),
+         "gamma": (1.0 + 0.1 * torch.randn(h, generator=g)).half().to(device),
+         "beta": (0.1 * torch.randn(h, generator=g)).half().to(device)}
+    for i, L in enumerate(wl.linears):
+        B[f"qw{i}"], B[f"sw{i}"], B[f"b{i}"] = lin(i)
+    for i, K in enumerate((h, h, h, f2.K)):
+        B[f"qx{i}"] = empty(max_m, K, dtype=torch.int8)
+        B[f"sx{i}"] = empty(max_m, dtype=torch.float32)
+    B["y_qkv"] = empty(max_m, qkv.N)
+    B["y_ao"] = empty(max_m, ao.N)
+    B["y_out"] = empty(max_m, f2.N)
+    B["ws"] = empty(zq.gemm_quant_workspace_bytes(max_m, f1.N), dtype=torch.uint8)
+    c = zq.Chain(max_m)
+    c.ln_quant(B["x"], B["qx0"], B["sx0"], B["gamma"], B["beta"], wl.ln_eps)
+    c.gemm(B["qx0"], B["sx0"], B["qw0"], B["sw0"], wl.G, B["y_qkv"], B["b0"])
+    c.quant(B["ctx"], B["qx1"], B["sx1"])
+    c.gemm(B["qx1"], B["sx1"], B["qw1"], B["sw1"], wl.G, B["y_ao"], B["b1"])
+    c.ln_quant(B["h1"], B["qx2"], B["sx2"], B["gamma"], B["beta"], wl.ln_eps)
+    c.gemm_quant(B["qx2"], B["sx2"], B["qw2"], B["sw2"], wl.G, B["qx3"],
+                 B["sx3"], B["ws"], B["b2"], zq.ACT_GELU if f1.gelu else zq.ACT_NONE)
+    c.gemm(B["qx3"], B["sx3"], B["qw3"], B["sw3"], wl.G, B["y_out"], B["b3"])
+    return c, B

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert "zq_gemm_w8a8" in names and "zq_ln_quant_act" in names
     for n in names:
         assert hasattr(L, n), f"{n} declared in zq.h but not exported"
-    assert L.zq_version() == 103
+    assert L.zq_version() == 104
 
 
 def test_last_error_starts_empty_and_is_set_on_failure():
@@ -151,3 +151,156 @@ def test_static_range_argument_checks():
     assert L.zq_quant_act_static(A, 4, 64, None, C, D, None) == EINVAL
     assert L.zq_quant_act_static(A, -1, 64, B, C, D, None) == ESHAPE
     assert L.zq_quant_act_static(None, 0, 64, B, None, D, None) == OK
+
+
+@pytest.fixture
+def empty_table():
+    Z.sched_clear()
+    yield
+    Z.sched_clear()
+
+
+def test_sched_table_import_export(empty_table):
+    assert Z.sched_entries() == 0 and Z.sched_export() == ""
+    assert Z.gemm_plan(128, 3072, 1024, 8).startswith("tiled")
+    assert "[table]" not in Z.gemm_plan(128, 3072, 1024, 8)
+    text = ("# bits N K lo hi kind tile\n"
+            "8 3072 1024 65 256 tiled 22\n"
+            "\n"
+            "8 3072 1024 1 1 gemv 0\n"
+            "8 3072 1024 2 16 stream 0\n"
+            "4 3072 1024 17 64 skinny 0\n")
+    Z.sched_import(text)
+    assert Z.sched_entries() == 4
+    assert Z.gemm_plan(128, 3072, 1024, 8).startswith("tiled cfg=22")
+    assert Z.gemm_plan(128, 3072, 1024, 8).endswith("[table]")
+    assert Z.gemm_plan(1, 3072, 1024, 8).startswith("gemv")
+    assert Z.gemm_plan(9, 3072, 1024, 8).startswith("stream")
+    assert Z.gemm_plan(40, 3072, 1024, 4).startswith("skinny BN=16 MF=3")
+    # outside every range, or another shape: the built-in rules
+    assert "[table]" not in Z.gemm_plan(257, 3072, 1024, 8)
+    assert "[table]" not in Z.gemm_plan(128, 3072, 768, 8)
+    assert "[table]" not in Z.gemm_plan(40, 3072, 1024, 8)
+    # export is sorted by (bits, N, K, lo) and reads back the same
+    out = Z.sched_export()
+    assert out.splitlines() == ["4 3072 1024 17 64 skinny 0",
+                                "8 3072 1024 1 1 gemv 0",
+                                "8 3072 1024 2 16 stream 0",
+                                "8 3072 1024 65 256 tiled 22"]
+    Z.sched_clear()
+    Z.sched_import(out)
+    assert Z.sched_export() == out
+
+
+def test_sched_import_overlap_splits_ranges(empty_table):
+    Z.sched_import("8 1024 512 1 1000 tiled 0\n")
+    Z.sched_import("8 1024 512 100 199 tiled 4\n")
+    assert Z.sched_export().splitlines() == ["8 1024 512 1 99 tiled 0",
+                                             "8 1024 512 100 199 tiled 4",
+                                             "8 1024 512 200 1000 tiled 0"]
+    assert Z.gemm_plan(150, 1024, 512, 8).startswith("tiled cfg=4")
+    assert Z.gemm_plan(250, 1024, 512, 8).startswith("tiled cfg=0")
+
+
+@pytest.mark.parametrize("line", [
+    "8 3072 768 1 2 gemv 0",        # gemv is for one token only
+    "8 3072 768 1 17 stream 0",     # stream: at most 16 tokens
+    "8 3073 768 1 16 stream 0",     # stream: even N
+    "8 3072 768 1 65 skinny 0",     # skinny: at most 64 tokens
+    "4 3072 768 1 64 tiled 16",     # W8-only tile for W4
+    "8 3072 768 1 64 tiled 28",     # no such tile
+    "8 3072 768 0 64 tiled 0",      # M from 1
+    "8 3072 768 9 8 tiled 0",       # empty range
+    "8 3072 700 1 8 tiled 0",       # K % 64
+    "5 3072 768 1 8 tiled 0",       # bits
+    "8 3072 768 1 8 huge 0",        # kind
+    "8 3072 768 1 8 tiled 0 extra",
+    "8 3072 768 1 8 tiled",
+])
+def test_sched_import_rejects_bad_lines(empty_table, line):
+    L = Z.lib()
+    good = b"8 1024 512 1 8 tiled 0\n"
+    assert L.zq_sched_import(good + line.encode() + b"\n") == EINVAL
+    assert b"line 2" in L.zq_last_error()
+    assert Z.sched_entries() == 0       # all or nothing
+
+
+def test_sched_export_buffer_handling(empty_table):
+    L = Z.lib()
+    Z.sched_import("8 1024 512 1 8 tiled 0\n")
+    need = ctypes.c_size_t(0)
+    assert L.zq_sched_export(None, 0, ctypes.byref(need)) == OK
+    assert need.value == len("8 1024 512 1 8 tiled 0\n") + 1
+    small = ctypes.create_string_buffer(5)
+    assert L.zq_sched_export(small, 5, None) == OK
+    assert small.value == b"8 10"                   # truncated, NUL-terminated
+    assert L.zq_sched_export(None, 4, None) == EINVAL
+    assert L.zq_sched_import(None) == EINVAL
+
+
+def test_gemm_tune_argument_checks():
+    f = Z.lib().zq_gemm_tune
+    ms = (ctypes.c_int * 3)(16, 64, 128)
+    bad = (ctypes.c_int * 3)(16, 16, 128)
+    zero = (ctypes.c_int * 1)(0)
+    # (bits, qx, sx, qw, sw, G, bias, act, ms, nm, N, K, y, reps, chosen, us, stream)
+    assert f(5, A, B, C, D, 64, None, 0, ms, 3, 256, 256, E, 5, None, None, None) == EINVAL
+    assert f(8, A, B, C, D, 64, None, 0, bad, 3, 256, 256, E, 5, None, None, None) == EINVAL
+    assert f(8, A, B, C, D, 64, None, 0, zero, 1, 256, 256, E, 5, None, None, None) == EINVAL
+    assert f(8, A, B, C, D, 64, None, 0, ms, 0, 256, 256, E, 5, None, None, None) == EINVAL
+    assert f(8, A, B, C, D, 64, None, 0, ms, 3, 256, 256, E, 0, None, None, None) == EINVAL
+    assert f(8, A, B, C, D, 64, None, 0, ms, 3, 256, 256, None, 5, None, None, None) == EINVAL
+    assert f(8, A, B, C, D, 64, None, 0, ms, 3, 96, 256, E, 5, None, None, None) == ESHAPE
+    assert f(8, A, B, C, D, 64, None, 0, ms, 3, 256, 100, E, 5, None, None, None) == EUNSUP
+    assert Z.sched_entries() == 0
+
+
+def test_chain_host_side():
+    L = Z.lib()
+    h = ctypes.c_void_p()
+    assert L.zq_chain_create(0, ctypes.byref(h)) == EINVAL
+    assert L.zq_chain_create(128, None) == EINVAL
+    assert L.zq_chain_create(128, ctypes.byref(h)) == OK
+    try:
+        assert L.zq_chain_length(h) == 0 and L.zq_chain_graphs(h) == 0
+        F = ctypes.c_float
+        assert L.zq_chain_add_ln_quant(h, A, None, None, F(1e-5), 768, B, C,
+                                       None) == OK
+        assert L.zq_chain_add_ln_quant(h, A, None, None, F(-1.0), 768, B, C,
+                                       None) == EINVAL
+        assert L.zq_chain_add_quant(h, A, 70000, B, C) == EUNSUP
+        assert L.zq_chain_add_quant(h, None, 768, B, C) == EINVAL
+        # (c, bits, qx, sx, qw, sw, G, bias, act, N, K, y)
+        assert L.zq_chain_add_gemm(h, 8, B, C, D, E, 64, None, 1, 3072, 768,
+                                   A) == OK
+        assert L.zq_chain_add_gemm(h, 8, B, C, D, E, 64, None, 1, 3000, 768,
+                                   A) == ESHAPE
+        assert L.zq_chain_add_gemm(h, 3, B, C, D, E, 64, None, 1, 3072, 768,
+                                   A) == EINVAL
+        assert L.zq_chain_add_gemm(h, 8, B, C, D, E, 64, None, 1, 3072, 768,
+                                   None) == EINVAL
+        ws_need = Z.lib().zq_gemm_quant_workspace_bytes(128, 3072)
+        assert ws_need == 128 * 3072 * 2
+        # (c, bits, qx, sx, qw, sw, G, bias, act, N, K, qy, sy, ws, ws_bytes)
+        assert L.zq_chain_add_gemm_quant(h, 4, B, C, D, E, 64, None, 1, 3072,
+                                         768, A, B, C, ws_need - 1) == EINVAL
+        assert b"workspace" in L.zq_last_error()
+        assert L.zq_chain_add_gemm_quant(h, 4, B, C, D, E, 64, None, 1, 3072,
+                                         768, A, B, C, ws_need) == OK
+        # (c, x, qw, sw, G, bias, act, N, K, y)
+        assert L.zq_chain_add_gemm_w8a16(h, A, B, C, 64, None, 0, 768, 3072,
+                                         D) == OK
+        assert L.zq_chain_add_gemm_w8a16(h, A, B, C, 64, None, 0, 768, 3000,
+                                         D) == EUNSUP
+        assert L.zq_chain_length(h) == 4
+        assert L.zq_chain_run(h, 129, None) == EINVAL
+        assert L.zq_chain_run(h, -1, None) == EINVAL
+        assert L.zq_chain_run_eager(h, 129, None) == EINVAL
+        assert L.zq_chain_run(h, 0, None) == OK          # empty: no launch
+        assert L.zq_chain_run_eager(h, 0, None) == OK
+        assert L.zq_chain_graphs(h) == 0
+        assert L.zq_chain_run(None, 1, None) == EINVAL
+        assert L.zq_chain_add_quant(None, A, 768, B, C) == EINVAL
+    finally:
+        L.zq_chain_destroy(h)
+    L.zq_chain_destroy(None)

@@ -1,0 +1,206 @@
+"""GPU tests of the recorded call chains (zq_chain_*) and the schedule table
+with its tuner (zq_gemm_tune).
+
+* A chain's calls launched one by one give, bit for bit, what the same calls
+  made through the binding give (those are checked against the oracle in the
+  parity tests), and every graph replay gives bit for bit what the eager
+  launches give, over several token counts of one chain, with the inputs
+  changed and other work run between replays.
+* Tuning changes plans, never results: the GEMM's bits are the same before
+  and after, and chains re-capture their graphs once the table changes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_quantized_transformer_amd as zq
+from int4_quantized_transformer_amd import workloads as W
+
+from _util import dev, needs_gpu, to_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+OUTS = ("y_qkv", "y_ao", "qx3", "sx3", "y_out", "qx0", "sx0", "qx2", "sx2")
+
+
+@pytest.fixture(autouse=True)
+def empty_table():
+    zq.sched_clear()
+    yield
+    zq.sched_clear()
+
+
+def snap(B, M):
+    torch.cuda.synchronize()
+    return {k: to_np(B[k][:M]).copy() for k in OUTS}
+
+
+def wipe(B):
+    for k in OUTS:
+        B[k].fill_(0)   # a fill kernel on the stream (no memset node)
+
+
+def same(a, b, M):
+    for k in OUTS:
+        assert np.array_equal(a[k], b[k]), f"{k} differs at M={M}"
+
+
+def direct(B, wl, M):
+    """The chain's calls made one by one through the binding."""
+    qkv, ao, f1, f2 = wl.linears
+    G = wl.G
+    out = {}
+    qx0, sx0 = zq.ln_quant_act(B["x"][:M], B["gamma"], B["beta"], wl.ln_eps)
+    out["y_qkv"] = zq.gemm_w8a8(qx0, sx0, B["qw0"], B["sw0"], G, B["b0"])
+    qx1, sx1 = zq.quant_act(B["ctx"][:M])
+    out["y_ao"] = zq.gemm_w8a8(qx1, sx1, B["qw1"], B["sw1"], G, B["b1"])
+    qx2, sx2 = zq.ln_quant_act(B["h1"][:M], B["gamma"], B["beta"], wl.ln_eps)
+    fq = zq.gemm_w8a8_quant if f1.bits == 8 else zq.gemm_w4a8_quant
+    qy, sy = fq(qx2, sx2, B["qw2"], B["sw2"], G, B["b2"], zq.ACT_GELU)
+    g2 = zq.gemm_w8a8 if f2.bits == 8 else zq.gemm_w4a8
+    out["y_out"] = g2(qy, sy, B["qw3"], B["sw3"], G, B["b3"])
+    out.update(qx3=qy, sx3=sy, qx0=qx0, sx0=sx0, qx2=qx2, sx2=sx2)
+    torch.cuda.synchronize()
+    return {k: to_np(v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("name,max_m,ms", [
+    ("bert-base", 320, (320, 77, 1, 128)),
+    ("bert-large", 192, (192, 17, 64)),      # W4 FFN weights
+    ("gptj-6b", 64, (1, 16, 64)),            # decode kernels
+])
+def test_chain_eager_matches_direct_calls_and_graph_matches_eager(name, max_m, ms):
+    wl = W.workload(name)
+    c, B = W.layer_chain(wl, max_m, dev(), seed=11)
+    assert len(c) == 7
+    for i, M in enumerate(ms):
+        wipe(B)
+        c.run_eager(M)
+        eager = snap(B, M)
+        same(eager, direct(B, wl, M), M)
+        wipe(B)
+        c.run(M)
+        same(snap(B, M), eager, M)
+        assert c.graphs == i + 1
+    # replays of a held graph, with other work and new inputs in between
+    M = ms[0]
+    for rep in range(3):
+        B["x"].mul_(-1.0)
+        B["h1"][: M // 2 + 1].mul_(0.5)
+        torch.cuda.synchronize()
+        wipe(B)
+        c.run_eager(M)
+        eager = snap(B, M)
+        wipe(B)
+        c.run(M)
+        c.run(M)              # twice in a row: same inputs, same outputs
+        same(snap(B, M), eager, M)
+    assert c.graphs == len(ms)
+    c.close()
+
+
+def test_chain_rows_beyond_m_untouched():
+    wl = W.workload("bert-base")
+    c, B = W.layer_chain(wl, 96, dev(), seed=3)
+    for k in OUTS:
+        B[k].fill_(7)
+    c.run(40)
+    torch.cuda.synchronize()
+    for k in OUTS:
+        assert bool((B[k][40:] == 7).all()), k
+
+
+def test_chain_inside_a_torch_graph_capture():
+    wl = W.workload("bert-base")
+    c, B = W.layer_chain(wl, 128, dev(), seed=5)
+    wipe(B)
+    c.run_eager(100)
+    eager = snap(B, 100)
+    wipe(B)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        c.run(100, stream=s.cuda_stream)   # joins the outer capture
+    assert c.graphs == 0
+    for _ in range(3):
+        wipe(B)
+        torch.cuda.synchronize()
+        g.replay()
+        same(snap(B, 100), eager, 100)
+
+
+def test_chain_graph_cache_is_bounded():
+    c, B = W.layer_chain(W.workload("bert-base"), 80, dev(), seed=9)
+    for M in range(1, 71):
+        c.run(M)
+    assert c.graphs == 64
+    wipe(B)
+    c.run_eager(3)
+    eager = snap(B, 3)
+    wipe(B)
+    c.run(3)              # dropped earlier: captured again
+    same(snap(B, 3), eager, 3)
+    assert c.graphs == 64
+    c.close()
+
+
+@pytest.mark.parametrize("bits,N,K,ms", [
+    (8, 3072, 768, (1, 16, 64, 128, 600)),
+    (4, 4096, 1024, (1, 40, 256)),
+])
+def test_tune_changes_plans_not_results(bits, N, K, ms):
+    d = dev()
+    Mx = ms[-1]
+    x = W.randn_fp16((Mx, K), seed=N + K, std=1.0).to(d)
+    w = W.randn_fp16((N, K), seed=N + K + 1, std=0.02).to(d)
+    b = W.randn_fp16((N,), seed=N + K + 2, std=0.5).to(d)
+    qx, sx = zq.quant_act(x)
+    qw, sw = zq.quantize_weights(w, 64, bits)
+    gemm = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    before = {M: to_np(gemm(qx[:M], sx[:M], qw, sw, 64, b, zq.ACT_GELU)) for M in ms}
+    plans0 = {M: zq.gemm_plan(M, N, K, bits) for M in ms}
+    res = zq.gemm_tune(qx, sx, qw, sw, 64, ms, bias=b, act=zq.ACT_GELU, reps=5)
+    assert len(res) == len(ms)
+    assert zq.sched_entries() == len(ms)
+    lines = zq.sched_export().splitlines()
+    lo = 1
+    for (kind, cfg, us), M, line in zip(res, ms, lines):
+        assert us > 0
+        assert line.split()[:6] == [str(bits), str(N), str(K), str(lo), str(M), kind]
+        p = zq.gemm_plan(M, N, K, bits)
+        assert p.startswith(kind) and p.endswith("[table]")
+        if kind == "tiled":
+            assert p.startswith(f"tiled cfg={cfg} ")
+        lo = M + 1
+    for M in ms:
+        after = to_np(gemm(qx[:M], sx[:M], qw, sw, 64, b, zq.ACT_GELU))
+        assert np.array_equal(after, before[M]), (M, plans0[M], zq.gemm_plan(M, N, K, bits))
+    # a token count between two tuned ones takes the upper one's plan
+    if len(ms) > 2:
+        mid = (ms[1] + ms[2]) // 2 + 1
+        pm, p2 = zq.gemm_plan(mid, N, K, bits), zq.gemm_plan(ms[2], N, K, bits)
+        assert pm.endswith("[table]") and pm.split()[0] == p2.split()[0]
+        if p2.startswith("tiled"):
+            assert pm.split()[1] == p2.split()[1]
+
+
+def test_chain_recaptures_after_table_change():
+    wl = W.workload("bert-base")
+    c, B = W.layer_chain(wl, 256, dev(), seed=21)
+    wipe(B)
+    c.run_eager(256)
+    eager = snap(B, 256)
+    c.run(256)
+    assert c.graphs == 1
+    # force a different tile for every GEMM of the layer through the table
+    text = "".join(f"{L.bits} {L.N} {L.K} 1 256 tiled 22\n" for L in wl.linears)
+    zq.sched_import(text)
+    assert zq.gemm_plan(256, 3072, 768, 8).startswith("tiled cfg=22")
+    wipe(B)
+    c.run(256)            # stale graph dropped, captured with the new plans
+    same(snap(B, 256), eager, 256)
+    assert c.graphs == 1
+    zq.sched_clear()
+    wipe(B)
+    c.run(256)
+    same(snap(B, 256), eager, 256)
