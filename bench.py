@@ -19,6 +19,7 @@ Prints one JSON line (stdout).  Details go to stderr.
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -54,6 +55,10 @@ def parse():
                     help="skip the fp16 torch.matmul comparator")
     ap.add_argument("--no-w8a16", action="store_true",
                     help="skip the W8A16 (fp16 activation) figure")
+    ap.add_argument("--no-static", action="store_true",
+                    help="skip the static per-tensor quantization comparator")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the layer-chain graph / schedule-table figure")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "traffic.json"))
     ap.add_argument("--only", default=None,
@@ -413,6 +418,142 @@ def w8a16_figure(torch, zq, dev, steps=20):
     return out
 
 
+def static_figure(torch, zq, dev, batches=100, steps=50):
+    """Static per-tensor vs token-wise INT8 activations on the BERT-base FFN1
+    linear (4096 tokens x 768 -> 3072, W8 weights): the range is calibrated
+    as a moving average over `batches` seeded synthetic batches, then a
+    held-out batch goes through both quantizers and the same INT8 GEMM; the
+    relative RMS error of each output against the fp32 product, and the
+    static quantizer's own bandwidth."""
+    from int4_quantized_transformer_amd import workloads as W
+    wl = W.workload("bert-base")
+    L = wl.linears[2]
+    M, K, N = 4096, L.K, L.N
+
+    oc = W.outlier_channels(wl, 2)
+
+    def batch(seed):
+        # N(0,1) tokens with the workload's outlier channels scaled, each
+        # token's range multiplied by a log-uniform factor in [1, 4]
+        g = torch.Generator().manual_seed(seed)
+        x = torch.randn(M, K, generator=g)
+        x[:, oc] *= wl.outlier_factor
+        x *= torch.exp(torch.rand(M, 1, generator=g) * math.log(4.0))
+        return x.half().to(dev)
+
+    st = None
+    for i in range(batches):
+        st = zq.calibrate_minmax(batch(1000 + i), st)
+    x = batch(7)
+    w, b = W.gen_weights(wl, 2)
+    wd, bd = w.to(dev), b.to(dev)
+    qw, sw = zq.quantize_weights(wd, wl.G, 8)
+    ref = torch.addmm(bd.float(), x.float(), wd.float().t())
+    qt, sxt = zq.quant_act(x)
+    yt = zq.gemm_w8a8(qt, sxt, qw, sw, wl.G, bd, 0).float()
+    qs, s = zq.quant_act_static(x, st)
+    ys = zq.gemm_w8a8(qs, s.expand(M).contiguous(), qw, sw, wl.G, bd, 0).float()
+    rel = lambda y: float(torch.linalg.norm(y - ref) / torch.linalg.norm(ref))
+    xq_t = (qt.float() * sxt[:, None]).sub(x.float()).pow(2).mean().sqrt()
+    xq_s = (qs.float() * s).sub(x.float()).pow(2).mean().sqrt()
+    # static quantizer bandwidth (inputs rotated past the Infinity Cache)
+    R = max(2, -(-ROTATE_BYTES // (3 * M * K)))
+    xs = [x] + [x.clone() for _ in range(R - 1)]
+    q = torch.empty_like(qs)
+    so = torch.empty(1, dtype=torch.float32, device=dev)
+    st_ = torch.empty(M, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    times = {}
+    for name, call in (("static", lambda i: zq.quant_act_static(xs[i], st, qx=q,
+                                                                s_out=so)),
+                       ("token_wise", lambda i: zq.quant_act(xs[i], qx=q, sx=st_))):
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(R):
+                call(i)
+        g.replay()
+        ms, _ = timed_graphs(torch, [g], steps, stream)
+        times[name] = ms * 1e3 / R
+        del g
+    us = times["static"]
+    return {"workload": "bert-base FFN1 input 4096x768 (outlier channels, token "
+                        "ranges varying up to 4x), W8 FFN1 weights; range "
+                        f"calibrated over {batches} batches, momentum 0.95",
+            "rel_rms_error_output": {"token_wise": round(rel(yt), 5),
+                                     "static_per_tensor": round(rel(ys), 5)},
+            "rms_error_activations": {"token_wise": round(float(xq_t), 5),
+                                      "static_per_tensor": round(float(xq_s), 5)},
+            "static_quant_us": round(us, 2),
+            "static_quant_GB_per_s": round(3 * M * K / (us * 1e-6) / 1e9, 1),
+            "token_wise_quant_us": round(times["token_wise"], 2)}
+
+
+def chain_figure(torch, zq, dev, steps=50, reps=20):
+    """Encoder layers' linear chains (per layer: LN+quant -> QKV, quant ->
+    attention output, LN+quant -> FFN1 with quantized output -> FFN2, seven
+    launches) launched one call at a time from native code, replayed as one
+    HIP graph per token count, and replayed again after tuning the schedule
+    table at those token counts: a 12-layer BERT-base stack at seq 128 with
+    batch 1, 16 and 128 (the pages' Table 6 shapes), one BERT-base layer,
+    and a 4-layer GPT-J decode stack.  Times are per stack, from events
+    around `steps` back-to-back runs (so launch gaps count), with the host
+    time per run beside them."""
+    from int4_quantized_transformer_amd import workloads as W
+    stream = torch.cuda.current_stream()
+
+    def per_run_us(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        host = (time.perf_counter() - t0) * 1e6 / steps
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps, host
+
+    out = {"note": "layers of a stack share one layer's weights and buffers "
+                   "(cache-resident across runs): a launch-overhead figure"}
+    for name, layers, ms in (("bert-base", 12, (128, 2048, 16384)),
+                             ("bert-base", 1, (128,)),
+                             ("gptj-6b", 4, (1, 16, 64))):
+        wl = W.workload(name)
+        zq.sched_clear()
+        c, B = W.layer_chain(wl, max(ms), dev, seed=1, layers=layers)
+        c.run_eager(max(ms))
+        res = {"launches": len(c)}
+        for M in ms:
+            ge, he = per_run_us(lambda: c.run_eager(M))
+            gg, hg = per_run_us(lambda: c.run(M))
+            res[f"M={M}"] = {"eager_us": round(ge, 2), "eager_host_us": round(he, 2),
+                             "graph_us": round(gg, 2), "graph_host_us": round(hg, 2)}
+        # tune each GEMM of the layer at these token counts
+        yq = B["ws"].view(torch.float16)
+        for i, L in enumerate(wl.linears):
+            y = {0: B["y_qkv"], 1: B["y_ao"], 3: B["y_out"]}.get(i)
+            if y is None:
+                y = yq[: max(ms) * L.N].view(max(ms), L.N)
+            zq.gemm_tune(B[f"qx{i}"], B[f"sx{i}"], B[f"qw{i}"], B[f"sw{i}"],
+                         wl.G, ms, bias=B[f"b{i}"],
+                         act=zq.ACT_GELU if L.gelu else zq.ACT_NONE, y=y,
+                         reps=reps)
+        for M in ms:
+            gt, _ = per_run_us(lambda: c.run(M))
+            e = res[f"M={M}"]
+            e["tuned_graph_us"] = round(gt, 2)
+            e["tuned_plans"] = [zq.gemm_plan(M, L.N, L.K, L.bits).split(" W")[0]
+                                for L in wl.linears]
+        out[f"{name} x{layers}"] = res
+        zq.sched_clear()
+        c.close()
+        del B
+    return out
+
+
 # -------------------------------------------------------------------- main --
 # -------------------------------------------------------- profile summary --
 COPY_BYTES = 256 * 2 ** 20
@@ -700,6 +841,10 @@ def main():
         extras["decode"] = decode_figure(torch, zq, dev)
     if not args.no_w8a16:
         extras["w8a16"] = w8a16_figure(torch, zq, dev)
+    if not args.no_static:
+        extras["static_vs_tokenwise"] = static_figure(torch, zq, dev)
+    if not args.no_chain:
+        extras["layer_chain"] = chain_figure(torch, zq, dev)
     out["extras"] = extras
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(base, wl, M)

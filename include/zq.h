@@ -321,9 +321,11 @@ int zq_sched_entries(void);
  * launch, so new inputs need no new capture.  A chain is used by one
  * thread at a time; runs on different streams that share buffers race.
  * zq_chain_graphs: graphs currently held; zq_chain_length: calls recorded.
- * zq_chain_destroy waits for the chain's graph launches still in flight,
- * then frees the graphs, the stream and the chain (NULL is ignored); a
- * dropped graph is likewise waited for before it is freed.
+ * zq_chain_destroy frees the graphs, the stream and the chain (NULL is
+ * ignored).  Freeing a graph that was ever launched (on destruction, when
+ * the cache drops one, or when the schedule table changed) first waits for
+ * the whole device (hipDeviceSynchronize), since its launches went to the
+ * callers' streams; runs themselves add nothing to the stream.
  * Errors: ZQ_EINVAL (null chain, max_m < 1, M outside [0, max_m]), the
  * add errors of the matching call, ZQ_EHIP (capture or launch refused).
  */

@@ -46,7 +46,6 @@ struct GraphEntry {
   int M;
   unsigned gen;
   hipGraphExec_t exec;
-  hipEvent_t done;  // recorded after this graph's latest launch
   bool launched;
   uint64_t last_use;
 };
@@ -98,11 +97,13 @@ struct zq_chain {
 
 namespace {
 
-// Waits for the graph's last launch, then frees it.
+// Frees a graph once no launch of it can still be in flight.  Its launches
+// went to callers' streams, which may be gone by now, so the whole device
+// is waited for (this happens only on eviction, a table change or
+// destruction; a run records nothing extra on the stream).
 void drop(GraphEntry &g) {
-  if (g.launched) (void)hipEventSynchronize(g.done);
+  if (g.launched) (void)hipDeviceSynchronize();
   (void)hipGraphExecDestroy(g.exec);
-  (void)hipEventDestroy(g.done);
 }
 
 // Appends op after checking it as its call would check it over max_m rows
@@ -175,13 +176,7 @@ zq_status capture(zq_chain *c, int M, GraphEntry *out) {
   st = hip_err(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), fn);
   (void)hipGraphDestroy(graph);
   if (st != ZQ_OK) return st;
-  hipEvent_t done = nullptr;
-  st = hip_err(hipEventCreateWithFlags(&done, hipEventDisableTiming), fn);
-  if (st != ZQ_OK) {
-    (void)hipGraphExecDestroy(exec);
-    return st;
-  }
-  *out = GraphEntry{M, gen, exec, done, false, 0};
+  *out = GraphEntry{M, gen, exec, false, 0};
   return ZQ_OK;
 }
 
@@ -333,12 +328,9 @@ zq_status zq_chain_run(zq_chain *c, int M, void *stream) {
     g = &c->graphs.back();
   }
   g->last_use = ++c->tick;
-  st = hip_err(hipGraphLaunch(g->exec, (hipStream_t)stream), fn);
-  if (st != ZQ_OK) return st;
-  st = hip_err(hipEventRecord(g->done, (hipStream_t)stream), fn);
-  if (st != ZQ_OK) return st;
   g->launched = true;
-  return zq::ok();
+  st = hip_err(hipGraphLaunch(g->exec, (hipStream_t)stream), fn);
+  return st == ZQ_OK ? zq::ok() : st;
 }
 
 int zq_chain_graphs(const zq_chain *c) { return c ? (int)c->graphs.size() : 0; }

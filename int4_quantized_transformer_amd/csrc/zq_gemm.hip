@@ -1664,14 +1664,20 @@ static int forced_tile() {
 // the tiling with the least waste).  Decode-sized M (<= 64) goes to the
 // weight-streaming kernels, or for 17 .. 64 tokens over wide N to 64x64
 // tiles with a deep copy ring.  Otherwise, from measured sweeps of every
-// configuration on the five workloads:
-//  * when 128x128 tiles fit one per compute unit: three-stage tiles (one
-//    block per CU, deeper prefetch) of 128x128 or 96x128, by the score below;
-//  * W4: 128x128 with two stages (two blocks per CU);
-//  * W8: the candidate with the best score = fill x quality, where fill is
-//    the fraction of the CU slots that the rounds of tiles keep busy (tiles
-//    / (rounds x slots)) and quality the measured per-CU efficiency of the
-//    configuration relative to 256x256 with 16 waves.
+// configuration (the schedule tuner over the five workloads' shapes at 128
+// to 16384 tokens):
+//  * when one round of tiles covers the problem: the smallest of 64x64,
+//    128x64, 96x128 and 128x128 (deep-ring tiles, one block per CU) whose
+//    tile count fits the compute units.  Every tile runs the whole K loop
+//    and its per-stage MFMA work shrinks with the tile, so with a single
+//    round the smallest tile that still fits finishes first (up to 1.7x
+//    over 96x128 when K is long);
+//  * W4 with K < 4096: 128x128 with two stages (two blocks per CU, so one
+//    block's prologue and epilogue overlap the other's main loop);
+//  * otherwise the candidate with the best score = fill x quality, where
+//    fill is the fraction of the CU slots that the rounds of tiles keep busy
+//    (tiles / (rounds x slots)) and quality the measured per-CU efficiency
+//    of the configuration relative to 256x256 with 16 waves.
 struct Candidate {
   int cfg, slots_per_cu;
   double quality;
@@ -1683,10 +1689,9 @@ static const Candidate kW8Candidates[] = {
     {0, 2, 0.87},   // 128x128, 4 waves, two blocks per CU
 };
 
-static const Candidate kSmallCandidates[] = {
-    {4, 1, 1.00},   // 128x128, 3 stages
-    {15, 1, 0.81},  // 96x128, 3 stages
-};
+// One-round candidates, smallest tile first: 64x64 (8 stages), 128x64
+// (6 stages), 96x128 (3 stages), 128x128 (3 stages).
+static const int kOneRound[] = {22, 21, 15, 4};
 
 template <int NC>
 static int pick(const Candidate (&cands)[NC], int M, int N) {
@@ -1746,9 +1751,13 @@ static Plan choose(int M, int N, int K, int bits) {
     if (fd < 0 && (N + 63) / 64 >= 128) return Plan{kTiled, 0, 22};
     return Plan{kSkinny, (M + 15) / 16, 0};
   }
-  const long tiles128 = (long)((N + 127) / 128) * ((M + 127) / 128);
-  if (tiles128 <= device_cus()) return Plan{kTiled, 0, pick(kSmallCandidates, M, N)};
-  if (bits == 4) return Plan{kTiled, 0, 0};
+  const int cus = device_cus();
+  for (int c : kOneRound) {
+    const TileCfg &t = kTileCfgs[c];
+    const long tiles = (long)((N + t.bn - 1) / t.bn) * ((M + t.bm - 1) / t.bm);
+    if (tiles <= cus) return Plan{kTiled, 0, c};
+  }
+  if (bits == 4 && K < 4096) return Plan{kTiled, 0, 0};
   return Plan{kTiled, 0, pick(kW8Candidates, M, N)};
 }
 
@@ -1953,26 +1962,29 @@ hipError_t tune_gemm(const GemmArgs &base, const int *ms, int nm, int reps,
   for (int i = 0; i < nm && err == hipSuccess; ++i) {
     GemmArgs a = base;
     a.M = ms[i];
-    float best = 0.0f;
-    bool have = false;
-    Plan bp{kTiled, 0, 0};
-    for (const Plan &pl : candidates(a.M, a.N, a.K, a.bits)) {
-      err = run_plan(pl, a, s);  // warm-up (and code-object load)
-      if (err == hipSuccess) err = hipEventRecord(e0, s);
-      for (int r = 0; r < reps && err == hipSuccess; ++r) err = run_plan(pl, a, s);
-      if (err == hipSuccess) err = hipEventRecord(e1, s);
-      if (err == hipSuccess) err = hipEventSynchronize(e1);
-      float ms_ = 0.0f;
-      if (err == hipSuccess) err = hipEventElapsedTime(&ms_, e0, e1);
-      if (err != hipSuccess) break;
-      const float us = 1e3f * ms_ / reps;
-      if (!have || us < best) {
-        best = us;
-        bp = pl;
-        have = true;
+    // two passes over the candidates, each keeping its faster pass, so that
+    // a clock or power transient during one timing does not decide
+    const std::vector<Plan> cands = candidates(a.M, a.N, a.K, a.bits);
+    std::vector<float> t(cands.size(), 0.0f);
+    for (int pass = 0; pass < 2 && err == hipSuccess; ++pass)
+      for (size_t c = 0; c < cands.size() && err == hipSuccess; ++c) {
+        const Plan &pl = cands[c];
+        err = run_plan(pl, a, s);  // warm-up (and code-object load)
+        if (err == hipSuccess) err = hipEventRecord(e0, s);
+        for (int r = 0; r < reps && err == hipSuccess; ++r) err = run_plan(pl, a, s);
+        if (err == hipSuccess) err = hipEventRecord(e1, s);
+        if (err == hipSuccess) err = hipEventSynchronize(e1);
+        float ms_ = 0.0f;
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms_, e0, e1);
+        const float us = 1e3f * ms_ / reps;
+        if (pass == 0 || us < t[c]) t[c] = us;
       }
-    }
     if (err != hipSuccess) break;
+    size_t bi = 0;
+    for (size_t c = 1; c < cands.size(); ++c)
+      if (t[c] < t[bi]) bi = c;
+    const Plan bp = cands[bi];
+    const float best = t[bi];
     found.push_back(SchedEntry{a.bits, a.N, a.K, prev + 1, a.M, bp.kind,
                                bp.kind == kTiled ? bp.cfg : 0});
     if (chosen_kind) chosen_kind[i] = (int)bp.kind;

@@ -137,7 +137,8 @@ def randn_fp16(shape, seed: int, std: float = 1.0, mean: float = 0.0):
     return (torch.randn(*shape, generator=g) * std + mean).to(torch.float16)
 
 
-def layer_chain(wl: Workload, max_m: int, device, seed: int = 0):
+def layer_chain(wl: Workload, max_m: int, device, seed: int = 0,
+                layers: int = 1):
     """The four linears of one encoder layer of ``wl`` over ``max_m`` tokens,
     recorded as a zq Chain: LN + token quantization -> QKV; token
     quantization -> attention output; LN + token quantization -> FFN1 (GeLU,
@@ -145,7 +146,10 @@ def layer_chain(wl: Workload, max_m: int, device, seed: int = 0):
     adds lie outside the quantized linear path, so the attention context and
     the FFN block's input are seeded inputs of their own (N(0,1) with the
     workload's outlier channels, like the layer input).  Weights are the
-    workload's, quantized on the device.  Returns (chain, buffers)."""
+    workload's, quantized on the device.  ``layers`` > 1 records the layer's
+    calls that many times over the same weights and buffers (a stand-in for
+    a model's stack of layers when timing launches).  Returns (chain,
+    buffers)."""
     from . import _lib as zq
     qkv, ao, f1, f2 = wl.linears
     h = qkv.K
@@ -177,12 +181,14 @@ def layer_chain(wl: Workload, max_m: int, device, seed: int = 0):
     B["y_out"] = empty(max_m, f2.N)
     B["ws"] = empty(zq.gemm_quant_workspace_bytes(max_m, f1.N), dtype=torch.uint8)
     c = zq.Chain(max_m)
-    c.ln_quant(B["x"], B["qx0"], B["sx0"], B["gamma"], B["beta"], wl.ln_eps)
-    c.gemm(B["qx0"], B["sx0"], B["qw0"], B["sw0"], wl.G, B["y_qkv"], B["b0"])
-    c.quant(B["ctx"], B["qx1"], B["sx1"])
-    c.gemm(B["qx1"], B["sx1"], B["qw1"], B["sw1"], wl.G, B["y_ao"], B["b1"])
-    c.ln_quant(B["h1"], B["qx2"], B["sx2"], B["gamma"], B["beta"], wl.ln_eps)
-    c.gemm_quant(B["qx2"], B["sx2"], B["qw2"], B["sw2"], wl.G, B["qx3"],
-                 B["sx3"], B["ws"], B["b2"], zq.ACT_GELU if f1.gelu else zq.ACT_NONE)
-    c.gemm(B["qx3"], B["sx3"], B["qw3"], B["sw3"], wl.G, B["y_out"], B["b3"])
+    for _ in range(layers):
+        c.ln_quant(B["x"], B["qx0"], B["sx0"], B["gamma"], B["beta"], wl.ln_eps)
+        c.gemm(B["qx0"], B["sx0"], B["qw0"], B["sw0"], wl.G, B["y_qkv"], B["b0"])
+        c.quant(B["ctx"], B["qx1"], B["sx1"])
+        c.gemm(B["qx1"], B["sx1"], B["qw1"], B["sw1"], wl.G, B["y_ao"], B["b1"])
+        c.ln_quant(B["h1"], B["qx2"], B["sx2"], B["gamma"], B["beta"], wl.ln_eps)
+        c.gemm_quant(B["qx2"], B["sx2"], B["qw2"], B["sw2"], wl.G, B["qx3"],
+                     B["sx3"], B["ws"], B["b2"],
+                     zq.ACT_GELU if f1.gelu else zq.ACT_NONE)
+        c.gemm(B["qx3"], B["sx3"], B["qw3"], B["sw3"], wl.G, B["y_out"], B["b3"])
     return c, B

@@ -193,9 +193,10 @@ def test_chain_recaptures_after_table_change():
     c.run(256)
     assert c.graphs == 1
     # force a different tile for every GEMM of the layer through the table
-    text = "".join(f"{L.bits} {L.N} {L.K} 1 256 tiled 22\n" for L in wl.linears)
+    assert not zq.gemm_plan(256, 3072, 768, 8).startswith("tiled cfg=4 ")
+    text = "".join(f"{L.bits} {L.N} {L.K} 1 256 tiled 4\n" for L in wl.linears)
     zq.sched_import(text)
-    assert zq.gemm_plan(256, 3072, 768, 8).startswith("tiled cfg=22")
+    assert zq.gemm_plan(256, 3072, 768, 8).startswith("tiled cfg=4 ")
     wipe(B)
     c.run(256)            # stale graph dropped, captured with the new plans
     same(snap(B, 256), eager, 256)
