@@ -361,8 +361,9 @@ def decode_figure(torch, zq, dev, steps=100):
 def w8a16_figure(torch, zq, dev, steps=20):
     """GPT-NeoX20B QKV (18432 x 6144) with INT8 weights and fp16 activations
     (the pages' W8A8/16 scheme keeps NeoX's attention inputs in fp16), at
-    prefill (M = 2048: TFLOP/s against the fp16 MFMA peak) and decode (M = 1:
-    GB/s against HBM); the torch fp16 matmul of the same shape beside it."""
+    prefill (M = 2048: TFLOP/s against the fp16 MFMA peak) and decode (M = 16
+    and 1: GB/s against HBM); the torch fp16 matmul of the same shape beside
+    it."""
     from int4_quantized_transformer_amd import workloads as W
     wl = W.workload("neox-20b")
     L = wl.linears[0]
@@ -375,7 +376,7 @@ def w8a16_figure(torch, zq, dev, steps=20):
     qws = [qw] + [qw.clone() for _ in range(R - 1)]
     out = {"workload": f"neox-20b QKV {N}x{K} W8A16, {G}-row groups, "
                        "HIP-graph replay over rotating weight sets"}
-    for M in (2048, 1):
+    for M in (2048, 16, 1):
         x = W.gen_activations(wl, 0, M=M, m_index=list(wl.M).index(M)).to(dev)
         y = torch.empty(M, N, dtype=torch.float16, device=dev)
         for i in range(R):
@@ -391,7 +392,7 @@ def w8a16_figure(torch, zq, dev, steps=20):
         us = ms * 1e3 / R
         nbytes = N * K + 2 * M * K + 2 * M * N + 4 * (N // G) + 2 * N
         e = {"us": round(us, 2), "plan": zq.gemm_w8a16_plan(M, N, K)}
-        if M > 1:
+        if M > 64:
             tf = 2 * M * N * K / (us * 1e-6) / 1e12
             e["TFLOPS"] = round(tf, 1)
             e["pct_fp16_peak"] = round(100 * tf / FP16_PEAK_TFLOPS, 1)

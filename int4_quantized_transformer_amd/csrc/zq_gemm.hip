@@ -905,14 +905,25 @@ gemm_skinny_kernel(GemmArgs p) {
 // the copies stay in flight, and the fragments are finished by the waves in
 // turn.  The buffer alternates between two halves by row-block parity, so
 // a half is cleared by its reader one barrier before it is used again.
-template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_>
+//
+// A16 (fp16 activations, INT8 weights): the activation slot holds 2*CK
+// bytes of each token row (CK k values), as for packed W4.  A lane's 16
+// weight codes of a k-step (k = 16g .. 16g+15) are widened exactly to fp16
+// and meet its two 16-byte activation columns in two
+// v_mfma_f32_16x16x32_f16 (codes 0..7, then 8..15: the MFMA's k order is a
+// summation order, the same for both operands).  fp32 partials are not
+// order-free, so each wave writes its own partial fragments and the
+// finishing wave adds them in wave order: the result does not depend on
+// timing.
+template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_, bool A16_ = false>
 struct Stream {
   static constexpr int FN = FN_, MX = MX_, NW = NW_, CK = CK_, D = D_;
-  static constexpr bool W4 = W4_;
+  static constexpr bool W4 = W4_, A16 = A16_;
+  static_assert(!(W4 && A16), "A16 takes INT8 weights");
   static constexpr int BN = 16 * FN;
   static constexpr int MF = (MX + 15) / 16;
   static constexpr int NT = NW * kWave;
-  static constexpr int XCK = W4 ? 2 * CK : CK;
+  static constexpr int XCK = (W4 || A16) ? 2 * CK : CK;
   static constexpr int SPC = CK / 64;                // k-steps per chunk
   static constexpr int IW = BN * CK / 1024;          // weight copies
   static constexpr int IX = (MX * XCK + 1023) / 1024;  // activation copies
@@ -921,7 +932,7 @@ struct Stream {
   static constexpr int P = IW + IX + IA;             // copies per chunk
   static constexpr int XOFF = IW * 1024, AOFF = (IW + IX) * 1024;
   static constexpr int SLOT = AOFF + IA * 256;
-  static constexpr int RED = FN * MF * 1024;         // one half
+  static constexpr int RED = (A16 ? NW : 1) * FN * MF * 1024;  // one half
   static constexpr int LDS = NW * D * SLOT + 2 * RED;
   static constexpr int WSW = (CK / 16 < 16 ? CK / 16 : 16) - 1;
   static constexpr int XSW = (XCK / 16 < 16 ? XCK / 16 : 16) - 1;
@@ -965,6 +976,9 @@ __device__ __forceinline__ void ds_zero16(uint32_t addr) {
   asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v4i{0, 0, 0, 0})
                : "memory");
 }
+__device__ __forceinline__ void ds_write16(uint32_t addr, v4i v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
 
 // Wait until at most `later` chunks of copies issued after the one needed
 // are still in flight.
@@ -997,6 +1011,7 @@ __device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
     __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + (size_t)n * ldw + kb),
                                      ZQ_LPTR(slot + q * 1024), 16, 0, 0);
   }
+  const int xrow = C::A16 ? 2 * p.K : p.K;     // activation row bytes
 #pragma unroll
   for (int q = 0; q < C::IX; ++q) {
     const int o = q * 1024 + lane * 16;
@@ -1005,8 +1020,8 @@ __device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
     const int col = ((o % C::XCK) >> 4) ^ (row & C::XSW);
     const int t = row < p.M ? row : p.M - 1;
     int kb = c * C::XCK + col * 16;
-    kb = kb < p.K ? kb : p.K - 16;
-    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * p.K + kb),
+    kb = kb < xrow ? kb : xrow - 16;
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * xrow + kb),
                                      ZQ_LPTR(slot + C::XOFF + q * 1024), 16,
                                      0, 0);
   }
@@ -1047,7 +1062,39 @@ __device__ __forceinline__ void stream_compute(const GemmArgs &p,
       const int row = fn * 16 + r16;
       a[fn] = ld16(slot + row * C::CK + (((4 * s + g) ^ (row & C::WSW)) << 4));
     }
-    if constexpr (!C::W4) {
+    if constexpr (C::A16) {
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      const bool kok = k0 + 64 * s + 16 * g < p.K;
+      v4i wl[C::FN], wh[C::FN];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int w0 = a[fn][0], w1 = a[fn][1], w2 = a[fn][2], w3 = a[fn][3];
+        wl[fn] = i8x8_to_f16x8(w0, w1);
+        wh[fn] = i8x8_to_f16x8(w2, w3);
+      }
+#pragma unroll
+      for (int fm = 0; fm < C::MF; ++fm) {
+        int row = fm * 16 + r16;
+        row = row < p.M ? row : p.M - 1;
+        const char *xr = slot + C::XOFF + row * C::XCK;
+        const int cx = 8 * s + 2 * g;
+        v4i b0 = ld16(xr + ((cx ^ (row & C::XSW)) << 4));
+        v4i b1 = ld16(xr + (((cx + 1) ^ (row & C::XSW)) << 4));
+        b0 = kok ? b0 : zero;
+        b1 = kok ? b1 : zero;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          v4f f = __builtin_bit_cast(v4f, acc[fn][fm]);
+          f = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(half8, wl[fn]), __builtin_bit_cast(half8, b0),
+              f, 0, 0, 0);
+          f = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(half8, wh[fn]), __builtin_bit_cast(half8, b1),
+              f, 0, 0, 0);
+          acc[fn][fm] = __builtin_bit_cast(v4i, f);
+        }
+      }
+    } else if constexpr (!C::W4) {
       const bool kok = k0 + 64 * s + 16 * g < p.K;
 #pragma unroll
       for (int fm = 0; fm < C::MF; ++fm) {
@@ -1137,12 +1184,18 @@ gemm_stream_kernel(GemmArgs p) {
     }
 
     int *rh = red + (rbi & 1) * (C::RED / 4);
+    constexpr int NPR = C::FN * C::MF;         // fragments per row block
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int fm = 0; fm < C::MF; ++fm)
-        ds_add4(lds_addr(&rh[((fn * C::MF + fm) * kWave + lane) * 4]),
-                acc[fn][fm]);
+      for (int fm = 0; fm < C::MF; ++fm) {
+        if constexpr (C::A16)
+          ds_write16(lds_addr(&rh[((wave * NPR + fn * C::MF + fm) * kWave + lane) * 4]),
+                     acc[fn][fm]);
+        else
+          ds_add4(lds_addr(&rh[((fn * C::MF + fm) * kWave + lane) * 4]),
+                  acc[fn][fm]);
+      }
     lds_barrier();
 
     if (wave < nact) {
@@ -1152,16 +1205,30 @@ gemm_stream_kernel(GemmArgs p) {
           ring + ((unsigned)(j - 1) % C::D) * C::SLOT + C::AOFF);
       for (int pr = wave; pr < C::FN * C::MF; pr += nact) {
         const int fn = pr / C::MF, fm = pr % C::MF;
-        int *rp = &rh[(pr * kWave + lane) * 4];
-        const v4i a = *reinterpret_cast<const v4i *>(rp);
-        ds_zero16(lds_addr(rp));
+        v4i a;
+        if constexpr (C::A16) {
+          // the waves' fp32 partials, added in wave order
+          typedef float v4f __attribute__((ext_vector_type(4)));
+          v4f sum = __builtin_bit_cast(
+              v4f, *reinterpret_cast<const v4i *>(&rh[(pr * kWave + lane) * 4]));
+#pragma unroll
+          for (int w = 1; w < C::NW; ++w)
+            sum += __builtin_bit_cast(
+                v4f, *reinterpret_cast<const v4i *>(
+                         &rh[((w * NPR + pr) * kWave + lane) * 4]));
+          a = __builtin_bit_cast(v4i, sum);
+        } else {
+          int *rp = &rh[(pr * kWave + lane) * 4];
+          a = *reinterpret_cast<const v4i *>(rp);
+          ds_zero16(lds_addr(rp));
+        }
         const int t = fm * 16 + r16;
         const int cb = fn * 16 + 4 * g;          // column within the row block
         const int nb = rb * C::BN + cb;
         QuadCol qc;
         float sxt = 0.0f;
         if constexpr (!RAW) {
-          sxt = __int_as_float(aux[t < p.M ? t : p.M - 1]);
+          sxt = C::A16 ? 1.0f : __int_as_float(aux[t < p.M ? t : p.M - 1]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             qc.sw[r] = __int_as_float(aux[C::MX + cb + r]);
@@ -1170,7 +1237,7 @@ gemm_stream_kernel(GemmArgs p) {
             qc.b[r] = p.bias ? __builtin_bit_cast(half_t, hb) : (half_t)0.0f;
           }
         }
-        store_quad<C::W4, RAW>(p, t, nb, a, sxt, qc);
+        store_quad<C::W4, RAW, C::A16>(p, t, nb, a, sxt, qc);
       }
     }
   }
@@ -2061,12 +2128,40 @@ static bool a16_gemv(int M, int K) {
   return forced_a16() < 0 && M == 1 && K % 1024 == 0 && K <= 32768;
 }
 
+// ZQ_A16_STREAM=<index> picks the stream configuration for up to 16 tokens
+// (tuning aid).
+static int a16_stream_cfg() {
+  static int v = [] {
+    const char *e = getenv("ZQ_A16_STREAM");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+// Up to 16 tokens with even N (bias pairs): the streaming kernel.
+static bool a16_stream(int M, int N, int K) {
+  return forced_a16() < 0 && !a16_gemv(M, K) && M >= 1 && M <= 16 &&
+         (N & 1) == 0;
+}
+
 hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
   if (a16_gemv(a.M, a.K)) {
     // one token: weight rows streamed in 1 KB pieces, the fp16 activation
     // row (up to 16 KB, else 64 KB) in LDS, whole rows per wave
     if (a.K <= 8192) return run_gemv<Gemv<4, 6, false, 4, true>, false>(a, s, 2, 0);
     return run_gemv<Gemv<4, 6, false, 16, true>, false>(a, s, 2, 0);
+  }
+  if (a16_stream(a.M, a.N, a.K)) {
+    if (a.M == 1) return run_stream<Stream<1, 1, 4, 512, 4, false, true>, false>(a, s);
+    // {FN, MX, NW, CK, D}; the default (32-row blocks, 128-byte chunks,
+    // 4-deep rings) measured fastest on NeoX QKV at 16 tokens (2.83 TB/s,
+    // against 2.3 - 2.6 for the others)
+    switch (a16_stream_cfg()) {
+      case 1: return run_stream<Stream<1, 16, 4, 128, 6, false, true>, false>(a, s);
+      case 2: return run_stream<Stream<1, 16, 4, 256, 3, false, true>, false>(a, s);
+      case 3: return run_stream<Stream<1, 16, 4, 128, 5, false, true>, false>(a, s);
+      default: return run_stream<Stream<2, 16, 4, 128, 4, false, true>, false>(a, s);
+    }
   }
   switch (choose_a16(a.M, a.N)) {
     case 0: return run_tiled<Tile<256, 256, 64, 64, 3, false, 128, true>, false>(a, s);
@@ -2080,6 +2175,12 @@ hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
 int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len) {
   if (a16_gemv(M, K))
     return snprintf(buf, len, "gemv-a16 NW=4 U=6 rows=%d x_in_lds=1", N);
+  if (a16_stream(M, N, K)) {
+    const int cfg = M == 1 ? 0 : a16_stream_cfg();
+    const int bn = (M > 1 && cfg == 0) ? 32 : 16;
+    return snprintf(buf, len, "stream-a16 MX=%d NW=4 cfg=%d BN=%d row_blocks=%d",
+                    M == 1 ? 1 : 16, cfg, bn, (N + bn - 1) / bn);
+  }
   const int i = choose_a16(M, N);
   const A16Cfg &c = kA16Cfgs[i];
   return snprintf(buf, len,

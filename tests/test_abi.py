@@ -136,8 +136,10 @@ def test_gemm_w8a16_argument_checks():
     assert f(A, B, C, 64, None, 0, 16, 256, 1048640, D, None) == EUNSUP
     assert f(None, B, C, 64, None, 0, 0, 256, 256, None, None) == OK      # empty
     assert Z.gemm_w8a16_plan(1, 18432, 6144).startswith("gemv-a16")
-    assert Z.gemm_w8a16_plan(1, 18432, 6000 + 64).startswith("tiled-a16 cfg=4")
-    assert Z.gemm_w8a16_plan(2, 18432, 6144).startswith("tiled-a16 cfg=4")
+    assert Z.gemm_w8a16_plan(1, 18432, 6000 + 64).startswith("stream-a16 MX=1")
+    assert Z.gemm_w8a16_plan(2, 18432, 6144).startswith("stream-a16 MX=16")
+    assert Z.gemm_w8a16_plan(2, 18431, 6144).startswith("tiled-a16 cfg=4")
+    assert Z.gemm_w8a16_plan(17, 18432, 6144).startswith("tiled-a16 cfg=4")
     assert Z.gemm_w8a16_plan(2048, 18432, 6144).startswith("tiled-a16 cfg=3")
     assert Z.gemm_w8a16_plan(100, 256, 512).startswith("tiled-a16 cfg=1")
 

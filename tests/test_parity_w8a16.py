@@ -3,8 +3,9 @@ against the oracle's fp64 definition (dequantized weights, then the product).
 
 * Tolerance: fp16 y within 1 fp16 ulp + 1e-3 of the oracle's unrounded z,
   over decode and prefill token counts (the one-token GEMV with the
-  activation row in 16 or 64 KB of LDS, the tiled kernel), ragged M and N
-  tiles, G not a multiple of 32, with and without bias and GeLU.
+  activation row in 16 or 64 KB of LDS, the streaming kernel for up to 16
+  tokens, the tiled kernel), ragged M and N tiles and row blocks, K tails
+  inside a chunk, G not a multiple of 32, with and without bias and GeLU.
 * Exact: with small integer activations and a power-of-two scale every
   partial sum is an integer below 2^24, so the kernel's fp32 accumulation is
   exact and y equals the oracle's rounded y bit for bit.
@@ -36,7 +37,9 @@ def _inputs(M, N, K, G, seed, bias=True):
     (16, 2048, 1024, 128), (40, 640, 192, 64), (64, 512, 512, 64),
     (65, 320, 576, 64), (300, 1000, 640, 8), (513, 1536, 1024, 128),
     (1024, 2560, 256, 64), (1, 1000, 2048, 8), (1, 4096, 16384, 128),
-    (1, 18432, 6144, 128), (2, 512, 1024, 64)])
+    (1, 18432, 6144, 128), (2, 512, 1024, 64),
+    (7, 998, 448, 2), (16, 18432, 6144, 128), (3, 64, 64, 64),
+    (1, 768, 576, 64), (16, 2, 64, 1), (9, 999, 256, 3), (12, 4096, 4160, 128)])
 @pytest.mark.parametrize("bias,act", [(True, 0), (True, 1), (False, 1)])
 def test_w8a16_vs_oracle(M, N, K, G, bias, act):
     x, q, sw, b = _inputs(M, N, K, G, M + 3 * N + 7 * K + G, bias)
@@ -89,6 +92,23 @@ def test_w8a16_empty_m():
     assert y.shape == (0, 64)
 
 
-def test_w8a16_plans_cover_both_kernels():
+def test_w8a16_plans_cover_every_kernel():
     assert zq.gemm_w8a16_plan(1, 4096, 16384).startswith("gemv-a16")
-    assert zq.gemm_w8a16_plan(1, 256, 128).startswith("tiled-a16")
+    assert zq.gemm_w8a16_plan(1, 256, 128).startswith("stream-a16 MX=1")
+    assert zq.gemm_w8a16_plan(16, 18432, 6144).startswith("stream-a16 MX=16")
+    assert zq.gemm_w8a16_plan(9, 999, 256).startswith("tiled-a16")   # odd N
+    assert zq.gemm_w8a16_plan(17, 4096, 256).startswith("tiled-a16")
+
+
+def test_w8a16_stream_is_deterministic():
+    # fp32 partials of the waves are added in a fixed order
+    M, N, K, G = 16, 4096, 6144, 128
+    x, q, sw, b = _inputs(M, N, K, G, 5)
+    d = dev()
+    args = (x.to(d), torch.from_numpy(q).to(d), torch.from_numpy(sw).to(d), G,
+            b.to(d), 0)
+    assert zq.gemm_w8a16_plan(M, N, K).startswith("stream-a16")
+    y0 = to_np(zq.gemm_w8a16(*args))
+    for _ in range(3):
+        assert np.array_equal(to_np(zq.gemm_w8a16(*args)).view(np.uint16),
+                              y0.view(np.uint16))
