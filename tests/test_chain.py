@@ -205,3 +205,39 @@ def test_chain_recaptures_after_table_change():
     wipe(B)
     c.run(256)
     same(snap(B, 256), eager, 256)
+
+
+def test_chain_with_fp16_activation_gemm():
+    # NeoX-style attention input kept in fp16: LN output (fp16) -> W8A16 QKV,
+    # alongside the INT8 path, in one chain; every token count reaches a
+    # different W8A16 kernel (GEMV, stream, tiled)
+    d = dev()
+    M0, K, N, G = 80, 1024, 1536, 128
+    x = W.randn_fp16((M0, K), seed=41).to(d)
+    w = W.randn_fp16((N, K), seed=42, std=0.02).to(d)
+    b = W.randn_fp16((N,), seed=43, std=0.5).to(d)
+    qw, sw = zq.quantize_weights(w, G, 8)
+    qx = torch.empty(M0, K, dtype=torch.int8, device=d)
+    sx = torch.empty(M0, dtype=torch.float32, device=d)
+    h = torch.empty(M0, K, dtype=torch.float16, device=d)
+    y16 = torch.empty(M0, N, dtype=torch.float16, device=d)
+    y8 = torch.empty(M0, N, dtype=torch.float16, device=d)
+    c = zq.Chain(M0)
+    c.ln_quant(x, qx, sx, ln_out=h)
+    c.gemm_w8a16(h, qw, sw, G, y16, b, zq.ACT_GELU)
+    c.gemm(qx, sx, qw, sw, G, y8, b, zq.ACT_GELU)
+    assert len(c) == 3
+    for M in (1, 16, 80):
+        y16.fill_(0)
+        y8.fill_(0)
+        c.run(M)
+        torch.cuda.synchronize()
+        qx_r, sx_r, h_r = zq.ln_quant_act(x[:M], ln_out=True)
+        ref16 = zq.gemm_w8a16(h_r, qw, sw, G, b, zq.ACT_GELU)
+        ref8 = zq.gemm_w8a8(qx_r, sx_r, qw, sw, G, b, zq.ACT_GELU)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(h[:M]).view(np.uint16), to_np(h_r).view(np.uint16))
+        assert np.array_equal(to_np(y16[:M]).view(np.uint16), to_np(ref16).view(np.uint16)), \
+            zq.gemm_w8a16_plan(M, N, K)
+        assert np.array_equal(to_np(y8[:M]).view(np.uint16), to_np(ref8).view(np.uint16))
+    assert c.graphs == 3
