@@ -155,6 +155,36 @@ def make_step(zq, lins, wl, M, stream_ptr):
     return calls
 
 
+def make_chain(zq, lins, wl, M):
+    """The same step as a chain of the library's own executor (zq_chain),
+    whose eager run launches the calls from native code."""
+    c = zq.Chain(M)
+    for s in lins:
+        L = s.L
+        if L.ln:
+            c.ln_quant(s.x, s.qx, s.sx, None, None, wl.ln_eps)
+        else:
+            c.quant(s.x, s.qx, s.sx)
+        c.gemm(s.qx, s.sx, s.qw, s.sw, wl.G, s.y, s.b, int(L.gelu))
+    return c
+
+
+def timed_native(torch, chains, M, steps, stream):
+    """Exactly `steps` steps launched one call at a time from native code
+    (zq_chain_run_eager over the rotating sets); events around them."""
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        chains[i % len(chains)].run_eager(M, stream=stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
 def run_calls(calls):
     for name, fn, args in calls:
         rc = fn(*args)
@@ -209,6 +239,25 @@ def timed_graphs(torch, graphs, steps, stream):
     e0.record(stream)
     for i in range(steps):
         graphs[i % len(graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def timed_steps(torch, g_all, R, graphs, steps, stream):
+    """Exactly `steps` steps: steps // R replays of the graph holding all R
+    rotating steps, then the remaining steps from the one-step graphs;
+    events around them on the replay stream."""
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps // R):
+        g_all.replay()
+    for i in range(steps % R):
+        graphs[i].replay()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -314,15 +363,17 @@ def step_entries(zq, wl, M):
 
 
 # ------------------------------------------------------------------ decode --
-def decode_figure(torch, zq, dev, steps=100):
-    """GPT-J-6B decoder linears at M = 1 (W8A8): GEMM GB/s against HBM."""
+def decode_case(torch, zq, dev, name, M, steps=100):
+    """One decoder layer's four linears at decode-sized M: GEMM GB/s against
+    HBM for the layer (graph replay of the four launches over rotating
+    weight sets larger than the Infinity Cache) and per linear."""
     from int4_quantized_transformer_amd import workloads as W
-    wl = W.workload("gptj-6b")
-    M = 1
+    wl = W.workload(name)
+    mi = list(wl.M).index(M)
     lin = []
     for li, L in enumerate(wl.linears):
         w, b = W.gen_weights(wl, li)
-        x = W.gen_activations(wl, li, m_index=0)
+        x = W.gen_activations(wl, li, m_index=mi)
         qw, sw = zq.quantize_weights(w.to(dev), wl.G, L.bits)
         qx, sx = zq.quant_act(x.to(dev))
         lin.append((L, qx, sx, qw, sw, b.to(dev)))
@@ -333,29 +384,69 @@ def decode_figure(torch, zq, dev, steps=100):
                      in lin] for _ in range(R - 1)]
     ys = [torch.empty(M, l[0].N, dtype=torch.float16, device=dev) for l in lin]
 
-    def step(s):
-        for (L, qx, sx, qw, sw, b), y in zip(s, ys):
-            zq.gemm_w8a8(qx, sx, qw, sw, wl.G, b, int(L.gelu), y=y)
+    def call(entry, y):
+        L, qx, sx, qw, sw, b = entry
+        g = zq.gemm_w8a8 if L.bits == 8 else zq.gemm_w4a8
+        g(qx, sx, qw, sw, wl.G, b, int(L.gelu), y=y)
+
+    def graph(which):
+        # every rotating set in one graph (consecutive layers, each with its
+        # own weights)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for s_ in sets:
+                for i in which:
+                    call(s_[i], ys[i])
+        return gr
 
     stream = torch.cuda.current_stream()
     for i in range(2 * R):
-        step(sets[i % R])
-    g = []
-    for s in sets:
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            step(s)
-        g.append(gr)
-    ms, _ = timed_graphs(torch, g, steps, stream)
-    nbytes = sum(gemm_bytes(M, L.N, L.K, L.bits, wl.G)
-                 for (L, *_r) in lin)
+        for e, y in zip(sets[i % R], ys):
+            call(e, y)
+    ms_g, _ = timed_graphs(torch, [graph(range(4))], steps, stream)
+    ms_g /= R
+    # the same launches from native code (the library's chain executor)
+    chains = []
+    for s_ in sets:
+        c = zq.Chain(M)
+        for (L, qx, sx, qw, sw, b), y in zip(s_, ys):
+            c.gemm(qx, sx, qw, sw, wl.G, y, b, int(L.gelu))
+        chains.append(c)
+    for c in chains:
+        c.run_eager(M, stream=stream.cuda_stream)
+    ms_n, _ = timed_native(torch, chains, M, steps * R, stream)
+    by_launch = {"graph": round(ms_g * 1e3, 2), "native_eager": round(ms_n * 1e3, 2)}
+    ms = min(ms_g, ms_n)
+    nbytes = sum(gemm_bytes(M, L.N, L.K, L.bits, wl.G) for (L, *_r) in lin)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": "gptj-6b decoder linears W8A8, M=1 (QKV, out, FFN1"
-                        "+GeLU, FFN2), 128-row groups, HIP-graph replay",
-            "GB_per_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs /
-                                                             HBM_PEAK_GBS, 1),
-            "us_per_step": round(ms * 1e3, 2), "bytes_per_step": nbytes,
-            "rotating_sets": R}
+    per = {}
+    for i, (L, *_r) in enumerate(lin):
+        mi_, _ = timed_graphs(torch, [graph([i])], steps, stream)
+        mi_ /= R
+        b_ = gemm_bytes(M, L.N, L.K, L.bits, wl.G)
+        per[f"{L.name} W{L.bits}"] = {
+            "us": round(mi_ * 1e3, 2),
+            "GB_per_s": round(b_ / (mi_ * 1e-3) / 1e9, 1),
+            "plan": zq.gemm_plan(M, L.N, L.K, L.bits).split(" W")[0]}
+    return {"GB_per_s": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "us_per_step": round(ms * 1e3, 2), "us_by_launch": by_launch,
+            "bytes_per_step": nbytes, "rotating_sets": R, "per_linear": per}
+
+
+def decode_figure(torch, zq, dev, steps=100):
+    """Decoder linears at decode-sized M (QKV, out, FFN1+GeLU, FFN2): GPT-J-6B
+    (W8A8, 128-row groups) at M = 1, 16 and 64, and GPT-NeoX-20B (W8 attention,
+    W4 FFN) at M = 1 and 16; GEMM GB/s against 8 TB/s."""
+    out = {"workload": "decoder linears (QKV, out, FFN1+GeLU, FFN2), "
+                       "one HIP graph over all rotating weight sets (as "
+                       "consecutive layers); bytes = the GEMMs' algorithmic "
+                       "bytes"}
+    for name, ms in (("gptj-6b", (1, 16, 64)), ("neox-20b", (1, 16))):
+        for M in ms:
+            out[f"{name} M={M}"] = decode_case(torch, zq, dev, name, M, steps)
+            torch.cuda.empty_cache()
+    return out
 
 
 def w8a16_figure(torch, zq, dev, steps=20):
@@ -770,13 +861,33 @@ def main():
                 run_calls(make_step(zq, [c for c in sets[len(graphs)]], wl, M,
                                     s.cuda_stream))
             graphs.append(g)
+        # the R steps back to back in one graph, each with its own weights
+        # and inputs, as consecutive layers of a model are: the pages replay
+        # a whole model's launch sequence as one graph
+        g_all = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.graph(g_all, stream=s):
+            for r in range(R):
+                run_calls(make_step(zq, [c for c in sets[r]], wl, M,
+                                    s.cuda_stream))
         for i in range(args.warmup):
             graphs[i % R].replay()
+        g_all.replay()
         torch.cuda.synchronize()
-        ms, wall_ms = timed_graphs(torch, graphs, args.steps, stream)
-    else:
-        ms = timed_eager(torch, step_calls, args.steps, stream)
-        wall_ms = ms
+        ms_g, wall_g = timed_steps(torch, g_all, R, graphs, args.steps, stream)
+    # the same K steps launched from native code by the library's chain
+    # executor; the step is timed both ways and `value` takes the faster
+    # (on this runtime a graph node costs more than a native launch once
+    # the host keeps ahead of the GPU)
+    chains = [make_chain(zq, sets[r], wl, M) for r in range(R)]
+    for i in range(args.warmup):
+        chains[i % R].run_eager(M, stream=stream.cuda_stream)
+    ms_n, wall_n = timed_native(torch, chains, M, args.steps, stream)
+    by_launch = {"native_eager": round(ms_n, 5)}
+    if not args.no_graph:
+        by_launch["graph"] = round(ms_g, 5)
+    launch = min(by_launch, key=by_launch.get)
+    ms, wall_ms = (ms_g, wall_g) if launch == "graph" else (ms_n, wall_n)
     if args.only:
         print(json.dumps({"ms_per_step": ms}))
         return
@@ -829,10 +940,12 @@ def main():
                                + (" +LN" if L.ln else "")
                                + (" +GeLU" if L.gelu else "")
                                for L in wl.linears},
-                   "rotating_sets": R, "graph": not args.no_graph},
+                   "rotating_sets": R, "launch": launch,
+                   "steps_per_graph_replay": R if not args.no_graph else 0},
         "roofline": roof,
     }
-    extras = {"eager_ms_per_step": round(eager_ms, 5),
+    extras = {"ms_per_step_by_launch": by_launch,
+              "eager_ms_per_step": round(eager_ms, 5),
               "host_wall_ms_per_step": round(wall_ms, 5),
               "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
               "breakdown": breakdown}
