@@ -383,11 +383,18 @@ def decode_case(torch, zq, dev, name, M, steps=100):
     sets = [lin] + [[(L, qx, sx, qw.clone(), sw, b) for (L, qx, sx, qw, sw, b)
                      in lin] for _ in range(R - 1)]
     ys = [torch.empty(M, l[0].N, dtype=torch.float16, device=dev) for l in lin]
+    # the calls with a workspace (decode-sized M over few weight tiles splits
+    # K); one workspace per linear, reused by every rotating set
+    wss = []
+    for (L, *_r) in lin:
+        need = zq.gemm_workspace_bytes(M, L.N, L.K, L.bits)
+        wss.append(torch.empty(need, dtype=torch.uint8, device=dev) if need else None)
+    wsidx = {id(y): i for i, y in enumerate(ys)}
 
     def call(entry, y):
         L, qx, sx, qw, sw, b = entry
-        g = zq.gemm_w8a8 if L.bits == 8 else zq.gemm_w4a8
-        g(qx, sx, qw, sw, wl.G, b, int(L.gelu), y=y)
+        g = zq.gemm_w8a8_ws if L.bits == 8 else zq.gemm_w4a8_ws
+        g(qx, sx, qw, sw, wl.G, b, int(L.gelu), y=y, ws=wss[wsidx[id(y)]])
 
     def graph(which):
         # every rotating set in one graph (consecutive layers, each with its
@@ -409,8 +416,8 @@ def decode_case(torch, zq, dev, name, M, steps=100):
     chains = []
     for s_ in sets:
         c = zq.Chain(M)
-        for (L, qx, sx, qw, sw, b), y in zip(s_, ys):
-            c.gemm(qx, sx, qw, sw, wl.G, y, b, int(L.gelu))
+        for (L, qx, sx, qw, sw, b), y, ws in zip(s_, ys, wss):
+            c.gemm_ws(qx, sx, qw, sw, wl.G, y, ws, b, int(L.gelu))
         chains.append(c)
     for c in chains:
         c.run_eager(M, stream=stream.cuda_stream)
@@ -427,7 +434,7 @@ def decode_case(torch, zq, dev, name, M, steps=100):
         per[f"{L.name} W{L.bits}"] = {
             "us": round(mi_ * 1e3, 2),
             "GB_per_s": round(b_ / (mi_ * 1e-3) / 1e9, 1),
-            "plan": zq.gemm_plan(M, L.N, L.K, L.bits).split(" W")[0]}
+            "plan": zq.gemm_ws_plan(M, L.N, L.K, L.bits).split(" W")[0]}
     return {"GB_per_s": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
             "us_per_step": round(ms * 1e3, 2), "us_by_launch": by_launch,

@@ -193,6 +193,39 @@ zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
 size_t zq_gemm_quant_workspace_bytes(int M, int N);
 
 /*
+ * zq_gemm_w8a8_ws / zq_gemm_w4a8_ws -- zq_gemm_w8a8 / zq_gemm_w4a8 with a
+ * caller workspace, for decode-sized token counts over few weight tiles
+ * (the small-batch schedules of the summary page's Sec. 3
+ * "Quantization-Optimized Transformer Kernels", paper App. D: at small
+ * batch the GEMM is bound by weight bandwidth, and every compute unit must
+ * stream).  For 17 .. 64 tokens where 64 x 64 tiles would leave compute
+ * units idle, K is split over several workgroups per tile: each writes
+ * exact int32 partial sums into the workspace, and a second kernel adds
+ * them and applies the same epilogue, so y is bit-identical to the call
+ * without a workspace.  Other shapes run exactly as that call.
+ *   ws: device memory of at least zq_gemm_workspace_bytes(M, N, K, bits)
+ *   bytes, 16-byte aligned, owned by the caller; its contents on entry do
+ *   not matter and are overwritten (two calls sharing one workspace on
+ *   different streams race).  When that size is 0, ws may be NULL.
+ * A schedule-table entry for the shape takes precedence (no split).
+ * Errors: as zq_gemm_w8a8; ZQ_EINVAL (workspace NULL, misaligned or
+ * smaller than needed).
+ * zq_gemm_workspace_bytes: the bytes these calls need for the shape (0
+ * when they would not split; also 0 for invalid arguments).
+ * zq_gemm_ws_plan: the plan these calls run, as zq_gemm_plan.
+ */
+zq_status zq_gemm_w8a8_ws(const int8_t *qx, const float *sx, const int8_t *qw,
+                          const float *sw, int G, const void *bias_fp16,
+                          int act, int M, int N, int K, void *y_fp16, void *ws,
+                          size_t ws_bytes, void *stream);
+zq_status zq_gemm_w4a8_ws(const int8_t *qx, const float *sx, const uint8_t *qw4,
+                          const float *sw, int G, const void *bias_fp16,
+                          int act, int M, int N, int K, void *y_fp16, void *ws,
+                          size_t ws_bytes, void *stream);
+size_t zq_gemm_workspace_bytes(int M, int N, int K, int bits);
+zq_status zq_gemm_ws_plan(int M, int N, int K, int bits, char *buf, int buflen);
+
+/*
  * zq_calibrate_minmax / zq_quant_act_static -- static per-tensor activation
  * quantization, the prior-PTQ scheme that token-wise scales replace
  * (summary page Sec. 3.4 "Token-wise Activation Quantization"; paper
@@ -306,7 +339,9 @@ int zq_sched_entries(void);
  * as in a dense [max_m][...] tensor) and stays owned by the caller, who
  * keeps it allocated while the chain lives.  Arguments are checked when
  * added, as the call itself checks them (with M = max_m; ws_bytes against
- * max_m), and a failing add appends nothing.  Host only: no GPU is touched.
+ * the largest workspace any token count up to max_m needs), and a failing
+ * add appends nothing.  Host only: no GPU is touched.  zq_chain_add_gemm_ws
+ * records zq_gemm_w8a8_ws (bits 8) or zq_gemm_w4a8_ws (bits 4).
  *
  * zq_chain_run(chain, M, stream): runs the sequence over the first M rows
  * of every buffer.  The first run with a given M (or the first after the
@@ -347,6 +382,10 @@ zq_status zq_chain_add_gemm_quant(zq_chain *c, int bits, const int8_t *qx,
                                   const float *sw, int G, const void *bias_fp16,
                                   int act, int N, int K, int8_t *qy, float *sy,
                                   void *ws, size_t ws_bytes);
+zq_status zq_chain_add_gemm_ws(zq_chain *c, int bits, const int8_t *qx,
+                               const float *sx, const void *qw, const float *sw,
+                               int G, const void *bias_fp16, int act, int N,
+                               int K, void *y_fp16, void *ws, size_t ws_bytes);
 zq_status zq_chain_add_gemm_w8a16(zq_chain *c, const void *x_fp16,
                                   const int8_t *qw, const float *sw, int G,
                                   const void *bias_fp16, int act, int N, int K,
@@ -362,7 +401,7 @@ const char *zq_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int zq_version(void);
-#define ZQ_VERSION 104
+#define ZQ_VERSION 105
 
 #ifdef __cplusplus
 }

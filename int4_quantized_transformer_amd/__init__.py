@@ -10,7 +10,8 @@ __all__ = ["quantize_weights", "ln_quant_act", "quant_act", "gemm_w8a8",
            "gemm_w4a8_quant", "gemm_quant_workspace_bytes", "gemm_plan",
            "gemm_w8a16", "gemm_w8a16_plan", "calibrate_minmax",
            "quant_act_static", "gemm_tune", "sched_export", "sched_import",
-           "sched_clear", "sched_entries", "Chain", "lib",
+           "sched_clear", "sched_entries", "Chain", "gemm_w8a8_ws",
+           "gemm_w4a8_ws", "gemm_workspace_bytes", "gemm_ws_plan", "lib",
            "ZQError", "library_path", "ACT_NONE", "ACT_GELU"]
 
 

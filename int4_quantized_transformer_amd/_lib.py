@@ -18,7 +18,9 @@ __all__ = ["ZQError", "library_path", "lib", "quantize_weights",
            "gemm_w4a8_quant", "gemm_quant_workspace_bytes", "gemm_plan",
            "gemm_w8a16", "gemm_w8a16_plan", "calibrate_minmax",
            "quant_act_static", "gemm_tune", "sched_export", "sched_import",
-           "sched_clear", "sched_entries", "Chain", "ACT_NONE", "ACT_GELU"]
+           "sched_clear", "sched_entries", "Chain", "gemm_w8a8_ws",
+           "gemm_w4a8_ws", "gemm_workspace_bytes", "gemm_ws_plan",
+           "ACT_NONE", "ACT_GELU"]
 
 ACT_NONE = 0
 ACT_GELU = 1
@@ -78,13 +80,22 @@ def lib():
             "zq_chain_add_gemm_quant": [P, I, P, P, P, P, I, P, I, I, I, P, P,
                                         P, ctypes.c_size_t],
             "zq_chain_add_gemm_w8a16": [P, P, P, P, I, P, I, I, I, P],
+            "zq_chain_add_gemm_ws": [P, I, P, P, P, P, I, P, I, I, I, P, P,
+                                     ctypes.c_size_t],
             "zq_chain_run": [P, I, P],
+            "zq_gemm_w8a8_ws": [P, P, P, P, I, P, I, I, I, I, P, P,
+                                ctypes.c_size_t, P],
+            "zq_gemm_w4a8_ws": [P, P, P, P, I, P, I, I, I, I, P, P,
+                                ctypes.c_size_t, P],
+            "zq_gemm_ws_plan": [I, I, I, I, ctypes.c_char_p, I],
             "zq_chain_run_eager": [P, I, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I
+        L.zq_gemm_workspace_bytes.argtypes = [I, I, I, I]
+        L.zq_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.zq_gemm_quant_workspace_bytes.argtypes = [I, I]
         L.zq_gemm_quant_workspace_bytes.restype = ctypes.c_size_t
         for name in ("zq_chain_graphs", "zq_chain_length"):
@@ -486,6 +497,17 @@ class Chain:
                                              int(act), N, K, _p(qy), _p(sy),
                                              _p(ws), ws.numel()))
 
+    def gemm_ws(self, qx, sx, qw, sw, G, y, ws, bias=None, act=ACT_NONE):
+        """gemm_w8a8_ws / gemm_w4a8_ws (ws: uint8 workspace, or None when no
+        token count up to max_m needs one)."""
+        bits, N, K = self._gemm_common(qx, sx, qw, sw, bias)
+        self._rows(y, "y", torch.float16, N)
+        self._dev(ws, "ws", torch.uint8)
+        _check(lib().zq_chain_add_gemm_ws(self._h, bits, _p(qx), _p(sx), _p(qw),
+                                          _p(sw), G, _p(bias), int(act), N, K,
+                                          _p(y), _p(ws),
+                                          0 if ws is None else ws.numel()))
+
     def gemm_w8a16(self, x, qw, sw, G, y, bias=None, act=ACT_NONE):
         K = x.shape[1]
         self._rows(x, "x", torch.float16, K)
@@ -530,3 +552,53 @@ class Chain:
             self.close()
         except Exception:
             pass
+
+
+def gemm_workspace_bytes(M, N, K, bits) -> int:
+    """Workspace bytes gemm_w8a8_ws / gemm_w4a8_ws use for this shape (0:
+    they run without one)."""
+    return int(lib().zq_gemm_workspace_bytes(int(M), int(N), int(K), int(bits)))
+
+
+def gemm_ws_plan(M, N, K, bits) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().zq_gemm_ws_plan(M, N, K, bits, buf, 256))
+    return buf.value.decode()
+
+
+def _gemm_ws(fn, bits, qx, sx, qw, sw, G, bias, act, y, ws, stream):
+    _need(qx, "qx", torch.int8, dim=2)
+    M, K = qx.shape
+    N = qw.shape[0]
+    need = gemm_workspace_bytes(M, N, K, bits)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=qx.device)
+    if ws is not None:
+        _need(ws, "ws", torch.uint8, qx.device)
+    y = torch.empty(M, N, dtype=torch.float16, device=qx.device) if y is None else y
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, qx.device, 2)
+    if qw.shape[1] != (K if bits == 8 else K // 2):
+        raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+    _need(sx, "sx", torch.float32, qx.device)
+    _need(sw, "sw", torch.float32, qx.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, qx.device)
+    _need(y, "y", torch.float16, qx.device)
+    _check(fn(_p(qx), _p(sx), _p(qw), _p(sw), G, _p(bias), int(act), M, N, K,
+              _p(y), _p(ws), 0 if ws is None else ws.numel(),
+              _stream(qx, stream)))
+    return y
+
+
+def gemm_w8a8_ws(qx, sx, qw, sw, G, bias=None, act=ACT_NONE, y=None, ws=None,
+                 stream=None):
+    """gemm_w8a8 with a workspace (allocated here when not given): decode-
+    sized M over few weight tiles splits K; y is bit-identical."""
+    return _gemm_ws(lib().zq_gemm_w8a8_ws, 8, qx, sx, qw, sw, G, bias, act, y,
+                    ws, stream)
+
+
+def gemm_w4a8_ws(qx, sx, qw, sw, G, bias=None, act=ACT_NONE, y=None, ws=None,
+                 stream=None):
+    return _gemm_ws(lib().zq_gemm_w4a8_ws, 4, qx, sx, qw, sw, G, bias, act, y,
+                    ws, stream)

@@ -87,6 +87,46 @@ zq_status gemm_fused(const int8_t *qx, const float *sx, const void *qw,
   return hip_status(zq::launch_gemm(a, (hipStream_t)stream), fn);
 }
 
+zq_status gemm_with_ws(const int8_t *qx, const float *sx, const void *qw,
+                       const float *sw, int G, const void *bias, int act,
+                       int M, int N, int K, void *y, void *ws,
+                       size_t ws_bytes, void *stream, int bits,
+                       const char *fn) {
+  zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (!sw || ((!sx || !y) && M != 0))
+    return fail(ZQ_EINVAL, "%s: null sx/sw/y", fn);
+  if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 8) ||
+      !aligned(ws, 16) || (bias && !aligned(bias, 2)))
+    return fail(ZQ_EINVAL, "%s: misaligned sx/sw/y/ws/bias", fn);
+  if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+    return fail(ZQ_EINVAL, "%s: act=%d", fn, act);
+  if (G <= 0 || N % G != 0)
+    return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  if (M == 0) return ok();
+  const size_t need = zq::gemm_ws_bytes(M, N, K, bits);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(ZQ_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn,
+                ws ? ws_bytes : 0, need);
+  zq::GemmArgs a{};
+  a.qx = qx;
+  a.sx = sx;
+  a.qw = qw;
+  a.sw = sw;
+  a.bias = static_cast<const zq::half_t *>(bias);
+  a.out = y;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.act = act;
+  a.bits = bits;
+  a.raw_i32 = false;
+  return hip_status(zq::launch_gemm_ws(a, need > 0 ? ws : nullptr,
+                                       (hipStream_t)stream),
+                    fn);
+}
+
 zq_status gemm_quant_out(const int8_t *qx, const float *sx, const void *qw,
                          const float *sw, int G, const void *bias, int act,
                          int M, int N, int K, int8_t *qy, float *sy, void *ws,
@@ -244,6 +284,37 @@ zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
                              size_t ws_bytes, void *stream) {
   return gemm_quant_out(qx, sx, qw4, sw, G, bias_fp16, act, M, N, K, qy, sy,
                         ws, ws_bytes, stream, 4, "zq_gemm_w4a8_quant");
+}
+
+zq_status zq_gemm_w8a8_ws(const int8_t *qx, const float *sx, const int8_t *qw,
+                          const float *sw, int G, const void *bias_fp16,
+                          int act, int M, int N, int K, void *y_fp16, void *ws,
+                          size_t ws_bytes, void *stream) {
+  return gemm_with_ws(qx, sx, qw, sw, G, bias_fp16, act, M, N, K, y_fp16, ws,
+                      ws_bytes, stream, 8, "zq_gemm_w8a8_ws");
+}
+
+zq_status zq_gemm_w4a8_ws(const int8_t *qx, const float *sx, const uint8_t *qw4,
+                          const float *sw, int G, const void *bias_fp16,
+                          int act, int M, int N, int K, void *y_fp16, void *ws,
+                          size_t ws_bytes, void *stream) {
+  return gemm_with_ws(qx, sx, qw4, sw, G, bias_fp16, act, M, N, K, y_fp16, ws,
+                      ws_bytes, stream, 4, "zq_gemm_w4a8_ws");
+}
+
+size_t zq_gemm_workspace_bytes(int M, int N, int K, int bits) {
+  if (M <= 0 || N <= 0 || K <= 0 || (bits != 8 && bits != 4)) return 0;
+  return zq::gemm_ws_bytes(M, N, K, bits);
+}
+
+zq_status zq_gemm_ws_plan(int M, int N, int K, int bits, char *buf, int buflen) {
+  const char *fn = "zq_gemm_ws_plan";
+  if (!buf || buflen <= 0) return fail(ZQ_EINVAL, "%s: null buffer", fn);
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d N=%d K=%d", fn, M, N, K);
+  zq::describe_gemm_ws_plan(M, N, K, bits, buf, buflen);
+  return ok();
 }
 
 size_t zq_gemm_quant_workspace_bytes(int M, int N) {

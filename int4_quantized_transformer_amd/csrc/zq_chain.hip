@@ -16,7 +16,7 @@
 
 namespace {
 
-enum OpKind { kLnQuant, kQuant, kGemm, kGemmQuant, kGemmA16 };
+enum OpKind { kLnQuant, kQuant, kGemm, kGemmQuant, kGemmA16, kGemmWs };
 
 struct ChainOp {
   OpKind kind;
@@ -74,6 +74,14 @@ zq_status run_op(const ChainOp &o, int M, void *s) {
     case kGemmA16:
       return zq_gemm_w8a16(o.x, (const int8_t *)o.qw, o.sw, o.G, o.bias, o.act,
                            M, o.N, o.K, o.y, s);
+    case kGemmWs:
+      return o.bits == 8
+                 ? zq_gemm_w8a8_ws(o.gqx, o.gsx, (const int8_t *)o.qw, o.sw,
+                                   o.G, o.bias, o.act, M, o.N, o.K, o.y, o.ws,
+                                   o.ws_bytes, s)
+                 : zq_gemm_w4a8_ws(o.gqx, o.gsx, (const uint8_t *)o.qw, o.sw,
+                                   o.G, o.bias, o.act, M, o.N, o.K, o.y, o.ws,
+                                   o.ws_bytes, s);
   }
   return zq::fail(ZQ_EINVAL, "zq_chain: unknown call kind");
 }
@@ -120,6 +128,17 @@ zq_status add(zq_chain *c, const ChainOp &op, const char *fn,
     return zq::fail(ZQ_EINVAL, "%s: workspace of %zu bytes, %zu needed for %d rows",
                     fn, op.ws_bytes,
                     zq_gemm_quant_workspace_bytes(c->max_m, op.N), c->max_m);
+  if (op.kind == kGemmWs) {
+    // the largest workspace any token count up to max_m uses
+    size_t need = 0;
+    for (int m = 1; m <= c->max_m && m <= 64; ++m) {
+      const size_t b = zq_gemm_workspace_bytes(m, op.N, op.K, op.bits);
+      need = b > need ? b : need;
+    }
+    if (need > 0 && (!op.ws || op.ws_bytes < need))
+      return zq::fail(ZQ_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn,
+                      op.ws ? op.ws_bytes : 0, need);
+  }
   c->ops.push_back(op);
   return zq::ok();
 }
@@ -264,6 +283,29 @@ zq_status zq_chain_add_gemm_quant(zq_chain *c, int bits, const int8_t *qx,
   o.ws = ws;
   o.ws_bytes = ws_bytes;
   return add(c, o, "zq_chain_add_gemm_quant", !qx || !sx || !qy || !sy || !ws);
+}
+
+zq_status zq_chain_add_gemm_ws(zq_chain *c, int bits, const int8_t *qx,
+                               const float *sx, const void *qw, const float *sw,
+                               int G, const void *bias_fp16, int act, int N,
+                               int K, void *y_fp16, void *ws, size_t ws_bytes) {
+  if (bits != 8 && bits != 4)
+    return zq::fail(ZQ_EINVAL, "zq_chain_add_gemm_ws: bits=%d", bits);
+  ChainOp o{kGemmWs};
+  o.bits = bits;
+  o.gqx = qx;
+  o.gsx = sx;
+  o.qw = qw;
+  o.sw = sw;
+  o.G = G;
+  o.bias = bias_fp16;
+  o.act = act;
+  o.N = N;
+  o.K = K;
+  o.y = y_fp16;
+  o.ws = ws;
+  o.ws_bytes = ws_bytes;
+  return add(c, o, "zq_chain_add_gemm_ws", !qx || !sx || !y_fp16);
 }
 
 zq_status zq_chain_add_gemm_w8a16(zq_chain *c, const void *x_fp16,

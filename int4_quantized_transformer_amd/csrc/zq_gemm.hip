@@ -631,13 +631,18 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = v16i{};
 
-  const int KT = (p.K + C::KPS - 1) / C::KPS;
+  // A split over K (grid y > 1) gives this workgroup the stages [kbase,
+  // kbase + KT); the launcher makes K a multiple of the slices' stages, so
+  // there is no half tail then.
+  const int KT = ((p.K + C::KPS - 1) / C::KPS) / (int)gridDim.y;
+  const int kbase = (int)blockIdx.y * KT;
   const bool half_tail = (p.K % C::KPS) != 0;   // last stage holds half
   const int KTF = KT - (half_tail ? 1 : 0);      // stages with 128 k
 
   const int npro = KT < C::S ? KT : C::S;
   for (int j = 0; j < npro; ++j)
-    issue_stage<C>(p, W, X, ldw, n0, m0, j, lds + j * C::STAGE, wave, lane);
+    issue_stage<C>(p, W, X, ldw, n0, m0, kbase + j, lds + j * C::STAGE, wave,
+                   lane);
   wait_stages<C>(npro - 1);
   __builtin_amdgcn_s_barrier();
 
@@ -672,7 +677,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (kt + C::S < KT)
-      issue_stage<C>(p, W, X, ldw, n0, m0, kt + C::S, ws, wave, lane);
+      issue_stage<C>(p, W, X, ldw, n0, m0, kbase + kt + C::S, ws, wave, lane);
     {
       // unconditional (after the last stage it reads a stale slot, in
       // bounds, and the fragments go unused): a conditional read here
@@ -693,6 +698,9 @@ template <class C, bool RAW>
 __global__ void __launch_bounds__(C::NT)
 gemm_tiled_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  // split over K: each slice writes its raw sums to its own M x N plane
+  if constexpr (RAW)
+    p.out = static_cast<int32_t *>(p.out) + (size_t)blockIdx.y * p.M * p.N;
   TileCtx<C> x;
   v16i acc[C::FN][C::FM];
   tile_mainloop<C, RAW>(p, lds, x, acc);
@@ -1898,6 +1906,104 @@ static hipError_t run_plan(const Plan &pl, const GemmArgs &a, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
   return run_plan(choose(a.M, a.N, a.K, a.bits), a, s);
+}
+
+// ------------------------------------------------------------- split K
+// 17 .. 64 tokens over few weight tiles (N up to about 8K): 64x64 tiles
+// leave most compute units idle, and the skinny kernel moves four
+// activation bytes per weight byte.  With a caller workspace the K range
+// is split over SK workgroups per tile (grid y): each writes its exact
+// int32 sums to its own M x N plane of the workspace, and a second kernel
+// adds the planes and finishes the same epilogue as every other kernel, so
+// y is bit-identical to the unsplit call.
+static constexpr int kSplitCfg = 22;  // 64x64 tiles, 8-stage ring
+
+static int splitk_factor(int M, int N, int K) {
+  if (M < 17 || M > 64) return 1;
+  const TileCfg &t = kTileCfgs[kSplitCfg];
+  const long tiles = (long)((N + t.bn - 1) / t.bn) * ((M + t.bm - 1) / t.bm);
+  if (tiles >= 128) return 1;
+  const int cus = device_cus();
+  for (int sk : {8, 4, 2}) {
+    // whole 128-k stages, slices of at least 3072 k and at least 128
+    // workgroups: shorter slices or fewer workgroups pay more in prologue,
+    // partial stores and the reduction than they gain (K = 4096 in 2 or 4
+    // slices measured equal or slower than the skinny kernel; K = 6144 in
+    // 2 slices and K = 16384 in 4 about 1.9x faster)
+    if (K % (sk * 128) == 0 && K / sk >= 3072 && tiles * sk >= 128 &&
+        tiles * sk <= cus)
+      return sk;
+  }
+  return 1;
+}
+
+size_t gemm_ws_bytes(int M, int N, int K, int bits) {
+  (void)bits;
+  if (M <= 0) return 0;
+  Plan tp;
+  if (forced_tile() >= 0 || sched_lookup(M, N, K, bits, &tp)) return 0;
+  const int sk = splitk_factor(M, N, K);
+  return sk > 1 ? (size_t)sk * M * N * 4 : 0;
+}
+
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(GemmArgs p, const int32_t *__restrict__ ws, int sk) {
+  const int nq = (p.N + 3) / 4;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)p.M * nq) return;
+  const int t = (int)(i / nq), nb = (int)(i % nq) * 4;
+  const size_t plane = (size_t)p.M * p.N;
+  const bool vec = (p.N & 3) == 0;
+  v4i a = {0, 0, 0, 0};
+  for (int z = 0; z < sk; ++z) {
+    const int32_t *src = ws + z * plane + (size_t)t * p.N + nb;
+    if (vec) {
+      a += *reinterpret_cast<const v4i *>(src);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (nb + r < p.N) a[r] += src[r];
+    }
+  }
+  const QuadCol qc = load_quad_col(p, nb);
+  store_quad<false, false>(p, t, nb, a, p.sx[t], qc);
+}
+
+hipError_t launch_gemm_ws(const GemmArgs &a, void *ws, hipStream_t s) {
+  Plan tp;
+  const int sk = (forced_tile() >= 0 || sched_lookup(a.M, a.N, a.K, a.bits, &tp))
+                     ? 1
+                     : splitk_factor(a.M, a.N, a.K);
+  if (sk <= 1 || a.raw_i32) return launch_gemm(a, s);
+  GemmArgs r = a;
+  r.out = ws;
+  r.raw_i32 = true;
+  using C8 = Tile<64, 64, 32, 32, 8, false>;
+  using C4 = Tile<64, 64, 32, 32, 8, true>;
+  const int tiles = ((a.N + 63) / 64) * ((a.M + 63) / 64);
+  if (a.bits == 4)
+    hipLaunchKernelGGL((gemm_tiled_kernel<C4, true>), dim3(tiles, sk),
+                       dim3(C4::NT), 0, s, r);
+  else
+    hipLaunchKernelGGL((gemm_tiled_kernel<C8, true>), dim3(tiles, sk),
+                       dim3(C8::NT), 0, s, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long quads = (long)a.M * ((a.N + 3) / 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)),
+                     dim3(256), 0, s, a, static_cast<const int32_t *>(ws), sk);
+  return hipGetLastError();
+}
+
+int describe_gemm_ws_plan(int M, int N, int K, int bits, char *buf, int len) {
+  Plan tp;
+  const int sk = (forced_tile() >= 0 || sched_lookup(M, N, K, bits, &tp))
+                     ? 1
+                     : splitk_factor(M, N, K);
+  if (sk <= 1) return describe_gemm_plan(M, N, K, bits, buf, len);
+  return snprintf(buf, len,
+                  "splitk SK=%d tiled cfg=%d BN=64 BM=64 W%d tiles=%d + reduce",
+                  sk, kSplitCfg, bits, ((N + 63) / 64) * ((M + 63) / 64) * sk);
 }
 
 // ------------------------------------------------------------- tuner

@@ -254,6 +254,12 @@ hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s);
 int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len);
 // Human-readable schedule for (M, N, K, bits); returns chars written.
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len);
+// With a caller workspace (gemm_ws_bytes of it): decode-sized M over few
+// weight tiles splits K over several workgroups per tile plus a reduction
+// kernel; otherwise the same launches as launch_gemm.
+size_t gemm_ws_bytes(int M, int N, int K, int bits);
+hipError_t launch_gemm_ws(const GemmArgs &a, void *ws, hipStream_t s);
+int describe_gemm_ws_plan(int M, int N, int K, int bits, char *buf, int len);
 
 // Schedule table (bits, N, K, M range) -> plan, consulted before the
 // built-in rules.  tune_gemm times every applicable plan at each M of ms[]

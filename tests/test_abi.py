@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert "zq_gemm_w8a8" in names and "zq_ln_quant_act" in names
     for n in names:
         assert hasattr(L, n), f"{n} declared in zq.h but not exported"
-    assert L.zq_version() == 104
+    assert L.zq_version() == 105
 
 
 def test_last_error_starts_empty_and_is_set_on_failure():
@@ -306,3 +306,64 @@ def test_chain_host_side():
     finally:
         L.zq_chain_destroy(h)
     L.zq_chain_destroy(None)
+
+
+def test_gemm_ws_plans_and_checks(empty_table):
+    L = Z.lib()
+    # 17 .. 64 tokens over few 64 x 64 tiles: K split, workspace sk * M * N * 4
+    assert Z.gemm_workspace_bytes(64, 6144, 6144, 8) == 2 * 64 * 6144 * 4
+    assert Z.gemm_ws_plan(64, 6144, 6144, 8).startswith("splitk SK=2 tiled cfg=22")
+    assert Z.gemm_workspace_bytes(64, 4096, 16384, 4) == 4 * 64 * 4096 * 4
+    assert Z.gemm_workspace_bytes(64, 1024, 24576, 8) == 8 * 64 * 1024 * 4
+    # no split: too few or too many tokens, enough tiles, K not in whole
+    # slices, slices shorter than 3072 k, fewer than 128 workgroups
+    for shape in [(16, 4096, 16384, 8), (65, 4096, 16384, 8), (64, 8192, 16384, 8),
+                  (64, 4096, 16448, 8), (64, 4096, 4096, 8), (64, 4096, 768, 8),
+                  (33, 1024, 16384, 8)]:
+        assert Z.gemm_workspace_bytes(*shape) == 0, shape
+        assert not Z.gemm_ws_plan(*shape).startswith("splitk")
+    assert Z.gemm_workspace_bytes(0, 4096, 4096, 8) == 0
+    assert Z.gemm_workspace_bytes(64, 4096, 4096, 5) == 0
+    # a table entry for the shape wins
+    Z.sched_import("8 6144 6144 17 64 skinny 0\n")
+    assert Z.gemm_workspace_bytes(64, 6144, 6144, 8) == 0
+    assert Z.gemm_ws_plan(64, 6144, 6144, 8).startswith("skinny")
+    Z.sched_clear()
+    f = L.zq_gemm_w8a8_ws
+    # (qx, sx, qw, sw, G, bias, act, M, N, K, y, ws, ws_bytes, stream)
+    need = Z.gemm_workspace_bytes(64, 6144, 6144, 8)
+    assert f(A, B, C, D, 128, None, 0, 64, 6144, 6144, E, None, 0, None) == EINVAL
+    assert f(A, B, C, D, 128, None, 0, 64, 6144, 6144, E, A, need - 1, None) == EINVAL
+    assert b"workspace" in L.zq_last_error()
+    assert f(A, B, C, D, 128, None, 0, 64, 6144, 6144, E,
+             ctypes.c_void_p(0x10008), need, None) == EINVAL     # misaligned
+    assert f(A, B, C, D, 128, None, 0, 64, 6144, 6000, E, A, need, None) == EUNSUP
+    assert f(A, B, C, D, 100, None, 0, 64, 6144, 6144, E, A, need, None) == ESHAPE
+    # a shape that does not split needs no workspace
+    assert f(None, B, C, D, 128, None, 0, 0, 4096, 4096, E, None, 0, None) == OK
+    assert f(None, None, C, D, 128, None, 0, 0, 4096, 4096, None, None, 0, None) == OK
+    assert L.zq_gemm_ws_plan(64, 4096, 4096, 3, ctypes.create_string_buffer(8), 8) == EINVAL
+
+
+def test_chain_ws_gemm_host_side():
+    L = Z.lib()
+    h = ctypes.c_void_p()
+    assert L.zq_chain_create(128, ctypes.byref(h)) == OK
+    try:
+        need = max(Z.gemm_workspace_bytes(m, 6144, 6144, 8) for m in range(1, 65))
+        assert need == Z.gemm_workspace_bytes(64, 6144, 6144, 8) > 0
+        # (c, bits, qx, sx, qw, sw, G, bias, act, N, K, y, ws, ws_bytes)
+        assert L.zq_chain_add_gemm_ws(h, 8, A, B, C, D, 128, None, 0, 6144, 6144,
+                                      E, A, need - 1) == EINVAL
+        assert L.zq_chain_add_gemm_ws(h, 8, A, B, C, D, 128, None, 0, 6144, 6144,
+                                      E, None, 0) == EINVAL
+        assert L.zq_chain_add_gemm_ws(h, 8, A, B, C, D, 128, None, 0, 6144, 6144,
+                                      E, A, need) == OK
+        # a shape no token count splits needs no workspace
+        assert L.zq_chain_add_gemm_ws(h, 4, A, B, C, D, 128, None, 0, 4096, 4096,
+                                      E, None, 0) == OK
+        assert L.zq_chain_add_gemm_ws(h, 5, A, B, C, D, 128, None, 0, 4096, 4096,
+                                      E, None, 0) == EINVAL
+        assert L.zq_chain_length(h) == 2
+    finally:
+        L.zq_chain_destroy(h)

@@ -241,3 +241,39 @@ def test_chain_with_fp16_activation_gemm():
             zq.gemm_w8a16_plan(M, N, K)
         assert np.array_equal(to_np(y8[:M]).view(np.uint16), to_np(ref8).view(np.uint16))
     assert c.graphs == 3
+
+
+def test_chain_with_workspace_gemms_at_decode_sizes():
+    # NeoX-shaped attention output and FFN2 (W4) through the workspace calls
+    # at 1 .. 64 tokens: the split runs where it applies, the graph replays
+    # equal the eager launches and the calls without a workspace
+    d = dev()
+    Mx = 64
+    specs = [(6144, 6144, 8), (6144, 24576, 4)]
+    c = zq.Chain(Mx)
+    bufs = []
+    for i, (N, K, bits) in enumerate(specs):
+        x = W.randn_fp16((Mx, K), seed=60 + i).to(d)
+        w = W.randn_fp16((N, K), seed=70 + i, std=0.02).to(d)
+        b = W.randn_fp16((N,), seed=80 + i, std=0.5).to(d)
+        qx, sx = zq.quant_act(x)
+        qw, sw = zq.quantize_weights(w, 128, bits)
+        need = max(zq.gemm_workspace_bytes(m, N, K, bits) for m in range(1, Mx + 1))
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+        y = torch.empty(Mx, N, dtype=torch.float16, device=d)
+        c.gemm_ws(qx, sx, qw, sw, 128, y, ws, b, zq.ACT_NONE)
+        bufs.append((qx, sx, qw, sw, b, y, bits, N, K))
+    assert zq.gemm_ws_plan(64, 6144, 6144, 8).startswith("splitk")
+    for M in (1, 16, 40, 64):
+        for (*_, y, bits, N, K) in bufs:
+            y.fill_(0)
+        c.run(M)
+        torch.cuda.synchronize()
+        got = [to_np(y[:M]).copy() for (*_, y, _b, _n, _k) in bufs]
+        c.run_eager(M)
+        torch.cuda.synchronize()
+        for (qx, sx, qw, sw, b, y, bits, N, K), g in zip(bufs, got):
+            plain = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+            ref = to_np(plain(qx[:M], sx[:M], qw, sw, 128, b, 0))
+            assert np.array_equal(g.view(np.uint16), ref.view(np.uint16)), (M, N, K)
+            assert np.array_equal(to_np(y[:M]).view(np.uint16), ref.view(np.uint16))
