@@ -1797,6 +1797,14 @@ static int forced_decode() {
   return v;
 }
 
+static int forced_stream() {
+  static int v = [] {
+    const char *e = getenv("ZQ_STREAM");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 static int forced_gemv() {
   static int v = [] {
     const char *e = getenv("ZQ_GEMV");
@@ -1883,8 +1891,27 @@ static hipError_t run(const Plan &pl, const GemmArgs &a, hipStream_t s) {
   }
   if (pl.kind == kStream) {
     if (pl.mf == 1) return run_stream<Stream<1, 1, 4, 512, 4, W4>, RAW>(a, s);
-    if constexpr (W4) return run_stream<Stream<1, 16, 4, 256, 3, W4>, RAW>(a, s);
-    else return run_stream<Stream<1, 16, 4, 256, 4, W4>, RAW>(a, s);
+    // {FN, MX, NW, CK, D}; ZQ_STREAM=<index> picks another ring shape
+    // (tuning aid)
+    const int v = forced_stream();
+    if constexpr (W4) {
+      // packed W4 moves two activation bytes per weight byte: 32-row
+      // blocks halve that, and measured fastest (NeoX FFN1 / FFN2 at 16
+      // tokens: 27.3 -> 22.1 us, 30.7 -> 25.0 us)
+      switch (v) {
+        case 1: return run_stream<Stream<1, 16, 4, 256, 3, W4>, RAW>(a, s);
+        case 2: return run_stream<Stream<1, 16, 4, 128, 6, W4>, RAW>(a, s);
+        case 3: return run_stream<Stream<2, 16, 4, 64, 8, W4>, RAW>(a, s);
+        default: return run_stream<Stream<2, 16, 4, 128, 4, W4>, RAW>(a, s);
+      }
+    } else {
+      switch (v) {
+        case 1: return run_stream<Stream<2, 16, 4, 128, 6, W4>, RAW>(a, s);
+        case 2: return run_stream<Stream<2, 16, 4, 256, 3, W4>, RAW>(a, s);
+        case 3: return run_stream<Stream<1, 16, 4, 128, 8, W4>, RAW>(a, s);
+        default: return run_stream<Stream<1, 16, 4, 256, 4, W4>, RAW>(a, s);
+      }
+    }
   }
   if (pl.kind == kSkinny) {
     const int id = forced_skinny();
@@ -2301,9 +2328,11 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
   if (pl.kind == kGemv)
     return snprintf(buf, len, "gemv NW=4 U=6 W%d rows=%d x_in_lds=%d%s", bits,
                     N, K <= 32768 ? 1 : 0, src);
-  if (pl.kind == kStream)
-    return snprintf(buf, len, "stream BN=16 MX=%d NW=4 W%d row_blocks=%d%s",
-                    pl.mf, bits, (N + 15) / 16, src);
+  if (pl.kind == kStream) {
+    const int bn = (bits == 4 && pl.mf > 1 && forced_stream() == 0) ? 32 : 16;
+    return snprintf(buf, len, "stream BN=%d MX=%d NW=4 W%d row_blocks=%d%s", bn,
+                    pl.mf, bits, (N + bn - 1) / bn, src);
+  }
   if (pl.kind == kSkinny)
     return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d%s",
                     pl.mf, pl.mf <= 2 ? 4 : 2, bits, (N + 15) / 16, src);
