@@ -297,7 +297,9 @@ zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen);
  * (ms[-1] = 0).  chosen (nm x 2 ints: kind 0 skinny, 1 tiled, 2 stream,
  * 3 gemv; tile index or -1) and us (nm floats, the winner's average
  * launch time in microseconds) may be NULL.  Synchronizes `stream`; must
- * not be called while `stream` is being captured.
+ * not be called while `stream` is being captured.  The split over K of the
+ * workspace calls (zq_gemm_w8a8_ws) is not among the timed plans; a table
+ * entry for a shape turns that split off.
  * Errors: as zq_gemm_w8a8; ZQ_EINVAL (ms not ascending or < 1, nm < 1 or
  * > 64, reps < 1 or > 10000, stream under capture).
  *
