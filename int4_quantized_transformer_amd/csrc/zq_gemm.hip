@@ -1973,27 +1973,35 @@ size_t gemm_ws_bytes(int M, int N, int K, int bits) {
   return sk > 1 ? (size_t)sk * M * N * 4 : 0;
 }
 
+// One thread per 4 outputs of a row: the SK partial quads (all loads in
+// flight together), then the shared epilogue.
+template <int SK>
 __global__ void __launch_bounds__(256)
-splitk_reduce_kernel(GemmArgs p, const int32_t *__restrict__ ws, int sk) {
+splitk_reduce_kernel(GemmArgs p, const int32_t *__restrict__ ws) {
   const int nq = (p.N + 3) / 4;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)p.M * nq) return;
   const int t = (int)(i / nq), nb = (int)(i % nq) * 4;
+  const QuadCol qc = load_quad_col(p, nb);
+  const float sxt = p.sx[t];
   const size_t plane = (size_t)p.M * p.N;
-  const bool vec = (p.N & 3) == 0;
-  v4i a = {0, 0, 0, 0};
-  for (int z = 0; z < sk; ++z) {
-    const int32_t *src = ws + z * plane + (size_t)t * p.N + nb;
-    if (vec) {
-      a += *reinterpret_cast<const v4i *>(src);
-    } else {
+  const int32_t *src = ws + (size_t)t * p.N + nb;
+  v4i part[SK];
+  if ((p.N & 3) == 0) {
+#pragma unroll
+    for (int z = 0; z < SK; ++z)
+      part[z] = *reinterpret_cast<const v4i *>(src + z * plane);
+  } else {
+#pragma unroll
+    for (int z = 0; z < SK; ++z)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (nb + r < p.N) a[r] += src[r];
-    }
+        part[z][r] = nb + r < p.N ? src[z * plane + r] : 0;
   }
-  const QuadCol qc = load_quad_col(p, nb);
-  store_quad<false, false>(p, t, nb, a, p.sx[t], qc);
+  v4i a = part[0];
+#pragma unroll
+  for (int z = 1; z < SK; ++z) a += part[z];
+  store_quad<false, false>(p, t, nb, a, sxt, qc);
 }
 
 hipError_t launch_gemm_ws(const GemmArgs &a, void *ws, hipStream_t s) {
@@ -2017,8 +2025,14 @@ hipError_t launch_gemm_ws(const GemmArgs &a, void *ws, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long quads = (long)a.M * ((a.N + 3) / 4);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)),
-                     dim3(256), 0, s, a, static_cast<const int32_t *>(ws), sk);
+  const dim3 grid((unsigned)((quads + 255) / 256));
+  const int32_t *w32 = static_cast<const int32_t *>(ws);
+  if (sk == 2)
+    hipLaunchKernelGGL(splitk_reduce_kernel<2>, grid, dim3(256), 0, s, a, w32);
+  else if (sk == 4)
+    hipLaunchKernelGGL(splitk_reduce_kernel<4>, grid, dim3(256), 0, s, a, w32);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<8>, grid, dim3(256), 0, s, a, w32);
   return hipGetLastError();
 }
 
