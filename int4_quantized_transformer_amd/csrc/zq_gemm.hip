@@ -1251,19 +1251,20 @@ gemm_stream_kernel(GemmArgs p) {
   }
 }
 
-// Number of compute units of the current device (cached per device).
+// Number of compute units of the current device (cached per device; host
+// threads may race to fill an entry, all with the same value).
 static int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) !=
             hipSuccess || v <= 0)
       v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 template <class C, bool RAW>

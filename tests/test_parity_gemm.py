@@ -201,3 +201,36 @@ def test_linear_epilogue_is_correctly_rounded(M, bits):
     got = to_np(y)
     assert np.array_equal(got.view(np.uint16), ref.view(np.uint16)), \
         (zq.gemm_plan(M, N, K, bits), int((got != ref).sum()))
+
+
+@pytest.mark.parametrize("bits,K", [(8, 133120), (4, 150912)])
+@pytest.mark.parametrize("M", [1, 16, 40, 100])
+def test_gemm_at_the_int32_bound(bits, K, M):
+    # every code at its extreme: |acc| = 127 * qmax * K, within 2^31 by less
+    # than 0.05% for W8 (and 16 * acc for the W4 path); token signs and
+    # weight-row signs vary so both bounds are reached
+    assert K <= (133144 if bits == 8 else 150976) and K % 64 == 0
+    qmax = 127 if bits == 8 else 7
+    N, G = 64, 32
+    ts = np.where(np.arange(M) % 2 == 0, 1, -1).astype(np.int8)
+    rs = np.where((np.arange(N) // 3) % 2 == 0, 1, -1).astype(np.int8)
+    qx = np.repeat((127 * ts)[:, None], K, axis=1).astype(np.int8)
+    q = np.repeat((qmax * rs)[:, None], K, axis=1).astype(np.int8)
+    qw = q if bits == 8 else oracle.pack_w4(q)
+    sx = np.full(M, 1e-5, np.float32)
+    sw = np.full(N // G, 1e-4, np.float32)
+    d = dev()
+    tqx, tqw = torch.from_numpy(qx).to(d), torch.from_numpy(qw).to(d)
+    tsx, tsw = torch.from_numpy(sx).to(d), torch.from_numpy(sw).to(d)
+    hook = zq.gemm_w8a8_i32 if bits == 8 else zq.gemm_w4a8_i32
+    fn = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    fws = zq.gemm_w8a8_ws if bits == 8 else zq.gemm_w4a8_ws
+    acc = to_np(hook(tqx, tqw))
+    y = to_np(fn(tqx, tsx, tqw, tsw, G, None, 0))
+    y_ws = to_np(fws(tqx, tsx, tqw, tsw, G, None, 0))
+    ref = oracle.gemm_i32(qx, q)
+    assert np.abs(ref.astype(np.int64)).max() == 127 * qmax * K
+    assert np.array_equal(acc, ref), zq.gemm_plan(M, N, K, bits)
+    z, _ = oracle.epilogue(ref, sx, sw, G, None, 0)
+    assert_fp16_close_to_oracle(y, z, zq.gemm_plan(M, N, K, bits))
+    assert np.array_equal(y_ws.view(np.uint16), y.view(np.uint16))
