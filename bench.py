@@ -59,6 +59,8 @@ def parse():
                     help="skip the static per-tensor quantization comparator")
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the layer-chain graph / schedule-table figure")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill GEMM figure of the larger configs")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "traffic.json"))
     ap.add_argument("--only", default=None,
@@ -453,6 +455,58 @@ def decode_figure(torch, zq, dev, steps=100):
         for M in ms:
             out[f"{name} M={M}"] = decode_case(torch, zq, dev, name, M, steps)
             torch.cuda.empty_cache()
+    return out
+
+
+def prefill_figure(torch, zq, dev, steps=20):
+    """Fused W8A8 / W4A8 GEMMs at the prefill token counts of the larger
+    configs (BERT-large 8192 tokens with W4 FFN, GPT-J-6B 2048, GPT-NeoX-20B
+    2048 with W4 FFN): per linear, the average launch from a graph holding
+    it for every rotating set, TOPS and % of the 5.0 POP/s INT8 peak."""
+    from int4_quantized_transformer_amd import workloads as W
+    stream = torch.cuda.current_stream()
+    out = {"note": "GEMM with the fused epilogue only (inputs already "
+                   "quantized); one graph per linear over rotating sets"}
+    for name, M in (("bert-large", 8192), ("gptj-6b", 2048), ("neox-20b", 2048)):
+        wl = W.workload(name)
+        mi = list(wl.M).index(M)
+        res = {}
+        tot_ops = tot_us = 0.0
+        for li, L in enumerate(wl.linears):
+            w, b = W.gen_weights(wl, li)
+            qw, sw = zq.quantize_weights(w.to(dev), wl.G, L.bits)
+            del w
+            qx, sx = zq.quant_act(W.gen_activations(wl, li, m_index=mi).to(dev))
+            per = qw.numel() + qx.numel() + 2 * M * L.N
+            R = max(2, -(-ROTATE_BYTES // per))
+            sets = [(qx, sx, qw, b.to(dev))] + [
+                (qx.clone(), sx.clone(), qw.clone(), b.to(dev)) for _ in range(R - 1)]
+            y = torch.empty(M, L.N, dtype=torch.float16, device=dev)
+            g8 = zq.gemm_w8a8 if L.bits == 8 else zq.gemm_w4a8
+            for (a_, s_, w_, b_) in sets:
+                g8(a_, s_, w_, sw, wl.G, b_, int(L.gelu), y=y)
+            gr = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            with torch.cuda.graph(gr, stream=cs):
+                for (a_, s_, w_, b_) in sets:
+                    g8(a_, s_, w_, sw, wl.G, b_, int(L.gelu), y=y)
+            gr.replay()
+            ms, _ = timed_graphs(torch, [gr], steps, stream)
+            us = ms * 1e3 / R
+            ops = 2.0 * M * L.N * L.K
+            tops = ops / (us * 1e-6) / 1e12
+            res[f"{L.name} {L.N}x{L.K} W{L.bits}"] = {
+                "us": round(us, 2), "TOPS": round(tops, 1),
+                "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1),
+                "plan": zq.gemm_plan(M, L.N, L.K, L.bits).split(" W")[0]}
+            tot_ops += ops
+            tot_us += us
+            del sets, gr, y
+            torch.cuda.empty_cache()
+        tops = tot_ops / (tot_us * 1e-6) / 1e12
+        res["all four"] = {"TOPS": round(tops, 1),
+                           "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1)}
+        out[f"{name} M={M}"] = res
     return out
 
 
@@ -960,6 +1014,8 @@ def main():
         extras["fp16_matmul"] = fp16_comparator(torch, base, M, args.steps)
     if not args.no_decode:
         extras["decode"] = decode_figure(torch, zq, dev)
+    if not args.no_prefill:
+        extras["prefill"] = prefill_figure(torch, zq, dev)
     if not args.no_w8a16:
         extras["w8a16"] = w8a16_figure(torch, zq, dev)
     if not args.no_static:
