@@ -195,7 +195,7 @@ size_t zq_gemm_quant_workspace_bytes(int M, int N);
 /*
  * zq_gemm_w8a8_ws / zq_gemm_w4a8_ws -- zq_gemm_w8a8 / zq_gemm_w4a8 with a
  * caller workspace, for decode-sized token counts over few weight tiles
- * (the small-batch schedules of the summary page's Sec. 3
+ * (the small-batch schedules of the summary page's Sec. 3.4
  * "Quantization-Optimized Transformer Kernels", paper App. D: at small
  * batch the GEMM is bound by weight bandwidth, and every compute unit must
  * stream).  For 17 .. 64 tokens where 64 x 64 tiles would leave compute
@@ -249,7 +249,7 @@ zq_status zq_quant_act_static(const void *x_fp16, int M, int K,
 
 /*
  * zq_gemm_w8a16 -- INT8 group-wise weights with FP16 activations, the mixed
- * scheme of the summary page's Sec. 5 "Experiments" (Table 4: W8A16;
+ * scheme of the summary page's Sec. 5 "Experimental Analysis" (Table 4: W8A16;
  * Table 8: GPT-NeoX20B keeps its self-attention inputs in FP16 while the
  * weights are INT8):
  *     y[t][n] = fp16(act(sw[n / G] * sum_k x[t][k] * qw[n][k] + bias[n]))
@@ -280,7 +280,7 @@ zq_status zq_gemm_plan(int M, int N, int K, int bits, char *buf, int buflen);
 /*
  * Schedule table -- the pages profile several GEMM schedules (tilings) for
  * each input-size combination and, at run time, use the one profiled for
- * the current batch x seqlen (summary page Sec. 3 "Quantization-Optimized
+ * the current batch x seqlen (summary page Sec. 3.4 "Quantization-Optimized
  * Transformer Kernels", the schedule profiling and small-batch paragraphs;
  * paper Sec. 4.3, App. D).  Here a process-wide table maps (bits, N, K,
  * M range) to a kernel and tile; zq_gemm_w8a8/w4a8 (and their _i32 and
@@ -330,7 +330,7 @@ int zq_sched_entries(void);
  * zq_chain -- a recorded sequence of the calls above, replayed as one HIP
  * graph: the pages record a small model's whole launch sequence on the
  * first inference call and replay it with a single submission afterwards,
- * removing per-kernel launch overhead (summary page Sec. 3
+ * removing per-kernel launch overhead (summary page Sec. 3.4
  * "Quantization-Optimized Transformer Kernels", the CUDA Graph paragraph;
  * paper App. D).
  *

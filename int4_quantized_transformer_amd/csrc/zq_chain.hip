@@ -3,7 +3,7 @@
 // The pages record a small model's whole launch sequence on the first
 // inference call and replay it with one submission afterwards, which takes
 // the per-kernel launch cost off the critical path ("ZeroQuant" summary
-// page, Sec. 3 "Quantization-Optimized Transformer Kernels", the CUDA Graph
+// page, Sec. 3.4 "Quantization-Optimized Transformer Kernels", the CUDA Graph
 // paragraph; paper App. D).  A chain holds the calls with their buffers
 // (sized for max_m token rows); a run over M rows launches the graph
 // captured for that M, capturing it first if there is none yet or if the

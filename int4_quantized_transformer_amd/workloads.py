@@ -5,7 +5,7 @@ arithmetic.  Both the HIP path's tests/benchmarks and the CPU oracle draw
 their inputs from here, so both see identical bytes.
 
 Five workloads (shapes from the ZeroQuant summary page, Sec. 5
-"Experiments": BERT-base/large encoders, GPT-J-6B and GPT-NeoX-20B decoders;
+"Experimental Analysis": BERT-base/large encoders, GPT-J-6B and GPT-NeoX-20B decoders;
 W4/8 puts INT4 on the feed-forward weights and INT8 on attention weights,
 Sec. 3.4 "Group-wise Weight Quantization"):
 

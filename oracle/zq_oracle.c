@@ -361,9 +361,10 @@ void zqo_epilogue(const int32_t *acc, const float *sx, const float *sw, int G,
 
 /* ------------------------------------------------------------------------ */
 /* W8A16 linear: INT8 group-wise weights with FP16 activations, the mixed    */
-/* scheme of [SUM] Sec. 5 "Experiments" (Table 4: W8A16, INT8 weights and    */
-/* FP16 activations; Table 8: GPT-NeoX20B keeps the self-attention input     */
-/* activations in FP16 while its weights are INT8).  Plain definition: each  */
+/* scheme of [SUM] Sec. 5 "Experimental Analysis" (Table 4: W8A16, INT8      */
+/* weights and FP16 activations; Table 8: GPT-NeoX20B keeps the             */
+/* self-attention input activations in FP16 while its weights are INT8).    */
+/* Plain definition: each                                                    */
 /* weight is dequantized, w[n][k] = sw[n/G] * q[n][k], and                   */
 /*   z[t][n] = act( sum_k x[t][k] * w[n][k] + bias[n] ),  y = fp16(z).       */
 /* fp64 throughout (every product of a binary16 value and a dequantized      */
