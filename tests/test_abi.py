@@ -367,3 +367,26 @@ def test_chain_ws_gemm_host_side():
         assert L.zq_chain_length(h) == 2
     finally:
         L.zq_chain_destroy(h)
+
+
+@pytest.mark.parametrize("shape,plan", [
+    # one round of tiles: the smallest tile that fits the 256 compute units
+    ((128, 768, 3072, 8), "tiled cfg=22 "),
+    ((2048, 768, 3072, 8), "tiled cfg=21 "),
+    ((4096, 768, 3072, 8), "tiled cfg=15 "),      # BERT-base FFN2
+    ((128, 18432, 6144, 8), "tiled cfg=15 "),
+    # larger problems: fill x quality among the big tiles
+    ((4096, 3072, 768, 8), "tiled cfg=13 "),      # BERT-base FFN1
+    ((4096, 2304, 768, 8), "tiled cfg=14 "),      # BERT-base QKV
+    # W4: two-block 128x128 below K = 4096, the W8 picker above
+    ((8192, 4096, 1024, 4), "tiled cfg=0 "),
+    ((2048, 24576, 6144, 4), "tiled cfg=12 "),
+    # decode-sized token counts
+    ((64, 16384, 4096, 8), "tiled cfg=22 "),
+    ((64, 4096, 4096, 8), "skinny "),
+    ((16, 24576, 6144, 4), "stream BN=32 MX=16 "),
+    ((16, 12288, 4096, 8), "stream BN=16 MX=16 "),
+])
+def test_tile_rule_regression(empty_table, shape, plan):
+    # the plans the schedule tuner measured best for these shapes
+    assert Z.gemm_plan(*shape).startswith(plan), Z.gemm_plan(*shape)
