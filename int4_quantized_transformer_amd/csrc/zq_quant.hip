@@ -112,6 +112,21 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
     }
   }
 
+  // LayerNorm weight and bias chunks: requested with the row, so that their
+  // latency overlaps the row's instead of following the two reductions
+  half8 hg[LN && VEC ? NCH : 1], hb[LN && VEC ? NCH : 1];
+  if constexpr (LN && VEC) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tl + j * TPR;
+      const int cc = ok[j] ? c : K / 8 - 1;
+      hg[j] = gamma ? *reinterpret_cast<const half8 *>(gamma + cc * 8)
+                    : half8{1, 1, 1, 1, 1, 1, 1, 1};
+      hb[j] = beta ? *reinterpret_cast<const half8 *>(beta + cc * 8)
+                   : half8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
   if constexpr (LN) {
     // mean and biased variance (two passes over the registers, fp32)
     float s = 0.0f;
@@ -153,14 +168,10 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
       }
       float g[8], b[8];
       if constexpr (VEC) {
-        const half8 hg = gamma ? *reinterpret_cast<const half8 *>(gamma + c * 8)
-                               : half8{1, 1, 1, 1, 1, 1, 1, 1};
-        const half8 hb = beta ? *reinterpret_cast<const half8 *>(beta + c * 8)
-                              : half8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          g[i] = (float)hg[i];
-          b[i] = (float)hb[i];
+          g[i] = (float)hg[j][i];
+          b[i] = (float)hb[j][i];
         }
       } else {
 #pragma unroll
@@ -260,16 +271,23 @@ static hipError_t dispatch_tpr(const half_t *x, const half_t *g,
   // Rows of 1024 or more elements: the smallest team that holds the row in
   // at most 2 chunks of 8 per thread (a sweep of team sizes at 2048 - 8192
   // tokens found these faster than fewer, fuller threads: 8192 x 1024 LN
-  // 11.2 -> 9.8 us, 4096 x 3072 10.7 -> 9.8 us).  Shorter rows: the
-  // smallest team that holds the row in at most 8 chunks (16 lanes for 768
-  // elements: several rows per wave share the reduction instructions);
-  // then, while fewer than 1024 waves would run, larger teams (down to 2
-  // chunks per thread) so that a few rows still spread over the device.
+  // 11.2 -> 9.8 us, 4096 x 3072 10.7 -> 9.8 us), except that a 256-thread
+  // team keeps rows of up to 4 chunks per thread rather than spreading them
+  // over 1024 threads (2048 x 6144 LN: 22.4 us with 1024 threads of one
+  // chunk, 13.3 us with 256 threads of three; one token of 6144: 4.0 ->
+  // 3.2 us).  Shorter rows: the smallest team that holds the row in at most
+  // 8 chunks (16 lanes for 768 elements: several rows per wave share the
+  // reduction instructions); then, while fewer than 1024 waves would run,
+  // larger teams (down to 2 chunks per thread) so that a few rows still
+  // spread over the device.  (Teams that own several rows and request them
+  // all before finishing the first measured slower at every shape tried.)
   const int chunks = (K + 7) / 8;
   auto next = [](int t) { return t < 64 ? 2 * t : 4 * t; };
   const int cap = chunks >= 128 ? 2 : 8;
   int tpr = 16;
-  while (tpr < 1024 && (chunks + tpr - 1) / tpr > cap) tpr = next(tpr);
+  while (tpr < 1024 && (chunks + tpr - 1) / tpr > cap &&
+         !(tpr == 256 && (chunks + 255) / 256 <= 4))
+    tpr = next(tpr);
   while (tpr < 1024 && (long)M * tpr < 1024L * 64 && chunks >= 2 * next(tpr))
     tpr = next(tpr);
   const int per = (chunks + tpr - 1) / tpr;

@@ -31,11 +31,12 @@ def _x(M, K, seed, outliers=True):
 
 
 # team sizes: 16 lanes (4096 x 768, 4097 x 776 ragged, 8192 x 1024), 32
-# (17 x 768), 64, 256 and 1024 threads per row
+# (17 x 768), 64, 256 (up to 4 chunks of 8 per thread: 6144, 6152, 8192)
+# and 1024 threads per row (16384 and longer)
 QUANT_SHAPES = [(1, 8), (16, 256), (17, 768), (63, 1024), (65, 3072),
-                (4, 1000), (3, 13), (33, 4096), (5, 6144), (7, 16384),
-                (3, 24576), (2, 65536), (1, 1), (4096, 768), (4097, 776),
-                (8192, 1024)]
+                (4, 1000), (3, 13), (33, 4096), (5, 6144), (2, 6152),
+                (3, 8192), (7, 16384), (3, 24576), (2, 65536), (1, 1),
+                (4096, 768), (4097, 776), (8192, 1024)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)
@@ -53,7 +54,8 @@ def test_quant_act_bit_exact(M, K):
 
 
 @pytest.mark.parametrize("M,K", [(16, 256), (17, 768), (64, 1024), (3, 1000),
-                                 (9, 4096), (5, 6144), (2, 16384), (1, 24),
+                                 (9, 4096), (5, 6144), (2, 6152), (3, 8192),
+                                 (2, 16384), (1, 24),
                                  (130, 768), (4096, 768), (4097, 776),
                                  (8192, 1024)])
 @pytest.mark.parametrize("affine", [False, True])
