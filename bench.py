@@ -90,6 +90,16 @@ def quant_bytes(M, K):
     return 2 * M * K + M * K + 4 * M
 
 
+def pct_attainable(ops, nbytes, seconds):
+    """Percent of the attainable roofline: min(INT8 MFMA peak, arithmetic
+    intensity x HBM peak) for a GEMM, the HBM peak for a kernel with no
+    contraction (ops = 0)."""
+    if ops:
+        att = min(INT8_PEAK_TOPS * 1e12, ops / nbytes * HBM_PEAK_GBS * 1e9)
+        return round(100 * ops / seconds / att, 1)
+    return round(100 * nbytes / seconds / (HBM_PEAK_GBS * 1e9), 1)
+
+
 def build_sets(wl, M, dev, rotate_bytes):
     import torch
     import int4_quantized_transformer_amd as zq
@@ -278,14 +288,29 @@ def timed_eager(torch, step_calls, steps, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def replay_percentiles(torch, g, n, stream, per):
+    """p10 / p50 / p90 over n replays of graph g, each between its own pair
+    of events, divided by the `per` launches a replay holds (ms)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n):
+        g.replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(evs[i].elapsed_time(evs[i + 1]) / per for i in range(n))
+    return [ts[min(n - 1, int(f * n))] for f in (0.1, 0.5, 0.9)]
+
+
 def entry_timings(torch, zq, sets, wl, M, steps):
     """Average duration of each step entry's launch: one HIP graph per entry
     holding that launch for every rotating set (so its inputs come from HBM
     as in the step), replayed `steps` times and timed with events around
     the replays.  Graph launches carry no host gaps, so this is the kernel's
-    own duration plus the small inter-kernel gap of a graph."""
+    own duration plus the small inter-kernel gap of a graph.  Also returns
+    p10 / p50 / p90 of the per-launch time over separately timed replays."""
     names = [c[0] for c in make_step(zq, sets[0], wl, M, 0)]
-    out = {}
+    out, pct = {}, {}
     for j, name in enumerate(names):
         g = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
@@ -298,8 +323,9 @@ def entry_timings(torch, zq, sets, wl, M, steps):
             g.replay()
         ms, _ = timed_graphs(torch, [g], steps, stream)
         out[name] = ms / len(sets)
+        pct[name] = replay_percentiles(torch, g, steps, stream, len(sets))
         del g
-    return out
+    return out, pct
 
 
 def grid_threads(name, L, M, G, zq):
@@ -436,6 +462,7 @@ def decode_case(torch, zq, dev, name, M, steps=100):
         per[f"{L.name} W{L.bits}"] = {
             "us": round(mi_ * 1e3, 2),
             "GB_per_s": round(b_ / (mi_ * 1e-3) / 1e9, 1),
+            "pct_attainable": pct_attainable(2 * M * L.N * L.K, b_, mi_ * 1e-3),
             "plan": zq.gemm_ws_plan(M, L.N, L.K, L.bits).split(" W")[0]}
     return {"GB_per_s": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
@@ -498,6 +525,8 @@ def prefill_figure(torch, zq, dev, steps=20):
             res[f"{L.name} {L.N}x{L.K} W{L.bits}"] = {
                 "us": round(us, 2), "TOPS": round(tops, 1),
                 "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1),
+                "pct_attainable": pct_attainable(
+                    ops, gemm_bytes(M, L.N, L.K, L.bits, wl.G), us * 1e-6),
                 "plan": zq.gemm_plan(M, L.N, L.K, L.bits).split(" W")[0]}
             tot_ops += ops
             tot_us += us
@@ -954,7 +983,7 @@ def main():
         return
 
     eager_ms = timed_eager(torch, step_calls, max(20, args.steps // 4), stream)
-    bd = entry_timings(torch, zq, sets, wl, M, max(20, args.steps // 4))
+    bd, bdq = entry_timings(torch, zq, sets, wl, M, max(20, args.steps // 4))
 
     ops_step = sum(2 * M * d["L"].N * d["L"].K for d in base)
     tops = ops_step / (ms * 1e-3) / 1e12
@@ -968,6 +997,8 @@ def main():
             e["TOPS"] = round(ops / (t * 1e-3) / 1e12, 1)
             e["pct_int8_peak"] = round(100 * e["TOPS"] / INT8_PEAK_TOPS, 1)
         e["GB_per_s"] = round(nbytes / (t * 1e-3) / 1e9, 1)
+        e["pct_attainable"] = pct_attainable(ops, nbytes, t * 1e-3)
+        e["us_p10_p50_p90"] = [round(v * 1e3, 2) for v in bdq[n]]
         breakdown[n] = e
     dom = max(bd, key=bd.get)
     Ld = lin_by[dom.split(".")[0]]
