@@ -235,11 +235,30 @@ def cpu_baseline(base, wl, M, target_s=12.0):
     S = int(min(M, max(S, S * target_s / max(t, 1e-3))))
     t = run(S)
     tops = ops_per_token * S / t / 1e12
-    return {"value": round(tops, 6), "unit": "TOPS", "cores": oracle.threads(),
+    threads = oracle.threads()
+    # once more on one thread, over a sample sized for about a third of the
+    # time above
+    S1 = max(16, min(S, int(S / threads / 3)))
+    oracle.set_threads(1)
+    try:
+        t1 = run(S1)
+    finally:
+        oracle.set_threads(threads)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f
+                          if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": threads,
             "kind": "oracle",
             "sample": (f"first {S} of {M} tokens through all {len(base)} "
                        f"linears (LN/quant, int64 GEMM, fp64 epilogue); "
-                       f"{t:.1f} s")}
+                       f"{t:.1f} s"),
+            "single_thread": {"value": round(ops_per_token * S1 / t1 / 1e12, 6),
+                              "sample": f"first {S1} tokens; {t1:.1f} s"},
+            "host": {"cpu": model, "nproc": os.cpu_count()}}
 
 
 # ----------------------------------------------------------------- timing --

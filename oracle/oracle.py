@@ -18,6 +18,7 @@ __all__ = [
     "lib", "half_to_double", "double_to_half", "quantize_weights", "pack_w4",
     "unpack_w4", "layernorm", "quant_tokens", "gemm_i32", "epilogue",
     "linear", "gemm_w8a16", "calibrate_minmax", "quant_static", "threads",
+    "set_threads",
 ]
 
 _lib = None
@@ -53,6 +54,7 @@ def lib():
         L.zqo_quant_static.restype = ctypes.c_float
         L.zqo_threads.argtypes = []
         L.zqo_threads.restype = I
+        L.zqo_set_threads.argtypes = [I]
         _lib = L
     return _lib
 
@@ -218,3 +220,8 @@ def quant_static(x, state):
 def threads():
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().zqo_threads())
+
+
+def set_threads(n):
+    """Thread count of the oracle's later parallel loops (timing only)."""
+    lib().zqo_set_threads(int(n))

@@ -404,3 +404,10 @@ int zqo_threads(void)
 {
     return omp_get_max_threads();
 }
+
+/* Sets the thread count of later OpenMP loops (CPU timings only; the
+ * results do not depend on it: every loop writes disjoint outputs). */
+void zqo_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}
