@@ -1647,6 +1647,11 @@ struct Plan {
   bool tuned = false;  // taken from the schedule table
 };
 
+// Token rows a streaming ring holds: 1, 16, 32 or 64.
+static int stream_mx(int M) {
+  return M == 1 ? 1 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
+}
+
 static bool w8_only(int cfg) {
   return (cfg >= 16 && cfg <= 20) || cfg == 23;
 }
@@ -1657,7 +1662,7 @@ static bool plan_applies(PlanKind kind, int cfg, int M, int N, int K, int bits) 
   const int ldw = bits == 4 ? K / 2 : K;
   switch (kind) {
     case kGemv: return M == 1 && ldw % 1024 == 0;
-    case kStream: return M >= 1 && M <= 16 && (N & 1) == 0;
+    case kStream: return M >= 1 && M <= 64 && (N & 1) == 0;
     case kSkinny: return M >= 1 && M <= 64;
     case kTiled: return cfg >= 0 && cfg < kNumTileCfgs && !(bits == 4 && w8_only(cfg));
   }
@@ -1668,7 +1673,7 @@ static bool plan_applies(PlanKind kind, int cfg, int M, int N, int K, int bits) 
 static Plan make_plan(PlanKind kind, int cfg, int M, bool tuned) {
   Plan p{kind, 0, cfg, tuned};
   if (kind == kSkinny) p.mf = (M + 15) / 16;
-  if (kind == kStream) p.mf = M == 1 ? 1 : 16;
+  if (kind == kStream) p.mf = stream_mx(M);
   if (kind == kGemv) p.mf = 1;
   if (kind != kTiled) p.cfg = 0;
   return p;
@@ -1824,15 +1829,21 @@ static Plan choose(int M, int N, int K, int bits) {
     const int ldw = bits == 4 ? K / 2 : K;
     const bool gemv_ok = M == 1 && ldw % 1024 == 0;
     const bool stream_ok = M <= 16 && (N & 1) == 0;
+    const bool stream17_ok = (N & 1) == 0;
     if (fd == 0) return Plan{kSkinny, (M + 15) / 16, 0};
-    if (fd == 2 && stream_ok) return Plan{kStream, M == 1 ? 1 : 16, 0};
+    if (fd == 2 && stream17_ok) return Plan{kStream, stream_mx(M), 0};
     if (gemv_ok) return Plan{kGemv, 1, 0};
-    if (stream_ok) return Plan{kStream, M == 1 ? 1 : 16, 0};
-    // 17 .. 64 tokens: 64-row weight tiles with the activations staged once
-    // per tile in LDS and an 8-deep copy ring, when there are enough tiles
-    // to keep most compute units streaming (the skinny kernel re-reads the
-    // whole activation block for every 16 weight rows)
-    if (fd < 0 && (N + 63) / 64 >= 128) return Plan{kTiled, 0, 22};
+    if (stream_ok) return Plan{kStream, stream_mx(M), 0};
+    // 17 .. 64 tokens: W8 over N >= 8192 with more than 32 tokens: 64-row
+    // weight tiles with the activations staged once per tile in LDS and an
+    // 8-deep copy ring (GPT-J QKV at 64 tokens 17.9 us against 25.3 us for
+    // a 64-token ring); otherwise the streaming rings of 32 or 64 token
+    // rows (64 x 4096 x 4096 13.9 -> 10.4 us, 64 x 6144 x 24576 W4
+    // 100.6 -> 43.8 us against the skinny kernel, which re-reads the whole
+    // activation block for every 16 weight rows); odd N: skinny
+    if (fd < 0 && (N + 63) / 64 >= 128 && (bits == 8 && M > 32 || !stream17_ok))
+      return Plan{kTiled, 0, 22};
+    if (stream17_ok) return Plan{kStream, stream_mx(M), 0};
     return Plan{kSkinny, (M + 15) / 16, 0};
   }
   const int cus = device_cus();
@@ -1892,6 +1903,27 @@ static hipError_t run(const Plan &pl, const GemmArgs &a, hipStream_t s) {
   }
   if (pl.kind == kStream) {
     if (pl.mf == 1) return run_stream<Stream<1, 1, 4, 512, 4, W4>, RAW>(a, s);
+    if (pl.mf > 16) {
+      // 17 .. 64 tokens: 16-row blocks while they number at most one per
+      // CU, else 32-row blocks (64 x 6144 x 6144: 23.0 -> 20.5 us; 64 x
+      // 6144 x 24576 W4: 67.0 -> 43.8 us); the activation bytes per chunk
+      // grow with the token rows, so the chunks shrink to keep the ring in
+      // LDS
+      const bool fn1 = (a.N + 15) / 16 <= device_cus();
+      if constexpr (W4) {
+        if (pl.mf == 32)
+          return fn1 ? run_stream<Stream<1, 32, 4, 128, 3, W4>, RAW>(a, s)
+                     : run_stream<Stream<2, 32, 4, 64, 4, W4>, RAW>(a, s);
+        return fn1 ? run_stream<Stream<1, 64, 4, 64, 3, W4>, RAW>(a, s)
+                   : run_stream<Stream<2, 64, 4, 64, 3, W4>, RAW>(a, s);
+      } else {
+        if (pl.mf == 32)
+          return fn1 ? run_stream<Stream<1, 32, 4, 128, 4, W4>, RAW>(a, s)
+                     : run_stream<Stream<2, 32, 4, 128, 3, W4>, RAW>(a, s);
+        return fn1 ? run_stream<Stream<1, 64, 4, 128, 3, W4>, RAW>(a, s)
+                   : run_stream<Stream<2, 64, 4, 64, 3, W4>, RAW>(a, s);
+      }
+    }
     // {FN, MX, NW, CK, D}; ZQ_STREAM=<index> picks another ring shape
     // (tuning aid)
     const int v = forced_stream();
@@ -2344,7 +2376,8 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
     return snprintf(buf, len, "gemv NW=4 U=6 W%d rows=%d x_in_lds=%d%s", bits,
                     N, K <= 32768 ? 1 : 0, src);
   if (pl.kind == kStream) {
-    const int bn = (bits == 4 && pl.mf > 1 && forced_stream() == 0) ? 32 : 16;
+    const int bn = pl.mf > 16 ? ((N + 15) / 16 <= device_cus() ? 16 : 32)
+                   : (bits == 4 && pl.mf > 1 && forced_stream() == 0) ? 32 : 16;
     return snprintf(buf, len, "stream BN=%d MX=%d NW=4 W%d row_blocks=%d%s", bn,
                     pl.mf, bits, (N + bn - 1) / bn, src);
   }

@@ -102,19 +102,25 @@ def test_header_limits_match_int32_bound():
 
 
 def test_gemm_plan_covers_every_regime():
-    # one token with whole 1 KB weight-row pieces: GEMV; other one-token or
-    # up-to-16-token problems with even N: streaming kernel; up to 64
-    # tokens: 64x64 tiles when N gives at least 128 of them, else the
-    # skinny kernel; above: tiled
+    # one token with whole 1 KB weight-row pieces: GEMV; other problems of
+    # up to 64 tokens with even N: streaming rings of 1, 16, 32 or 64 token
+    # rows, except W8 over N >= 8192 with more than 32 tokens (64x64
+    # tiles); odd N: the skinny kernel (64x64 tiles when N gives at least
+    # 128 of them); above 64 tokens: tiled
     assert Z.gemm_plan(1, 4096, 4096, 8).startswith("gemv")
     assert Z.gemm_plan(1, 4096, 4096, 4).startswith("gemv")
     assert Z.gemm_plan(1, 4096, 1024, 4).startswith("stream")
     assert Z.gemm_plan(1, 77, 192, 8).startswith("skinny")
-    assert Z.gemm_plan(16, 4096, 4096, 8).startswith("stream")
-    assert Z.gemm_plan(17, 4096, 4096, 8).startswith("skinny")
-    assert Z.gemm_plan(64, 4096, 4096, 4).startswith("skinny")
-    assert Z.gemm_plan(17, 8192, 4096, 8).startswith("tiled cfg=22")
-    assert Z.gemm_plan(64, 16384, 4096, 4).startswith("tiled cfg=22")
+    assert Z.gemm_plan(16, 4096, 4096, 8).startswith("stream BN=16 MX=16")
+    assert Z.gemm_plan(17, 4096, 4096, 8).startswith("stream BN=16 MX=32")
+    assert Z.gemm_plan(33, 4096, 4096, 8).startswith("stream BN=16 MX=64")
+    assert Z.gemm_plan(64, 4096, 4096, 4).startswith("stream BN=16 MX=64")
+    assert Z.gemm_plan(64, 6144, 6144, 8).startswith("stream BN=32 MX=64")
+    assert Z.gemm_plan(17, 8192, 4096, 8).startswith("stream BN=32 MX=32")
+    assert Z.gemm_plan(33, 8192, 4096, 8).startswith("tiled cfg=22")
+    assert Z.gemm_plan(64, 16384, 4096, 4).startswith("stream BN=32 MX=64")
+    assert Z.gemm_plan(40, 77, 4096, 8).startswith("skinny")
+    assert Z.gemm_plan(40, 8191, 4096, 8).startswith("tiled cfg=22")
     assert Z.gemm_plan(65, 4096, 4096, 8).startswith("tiled")
     assert Z.gemm_plan(2048, 4096, 4096, 8).startswith("tiled")
     with pytest.raises(Z.ZQError):
@@ -206,7 +212,7 @@ def test_sched_import_overlap_splits_ranges(empty_table):
 
 @pytest.mark.parametrize("line", [
     "8 3072 768 1 2 gemv 0",        # gemv is for one token only
-    "8 3072 768 1 17 stream 0",     # stream: at most 16 tokens
+    "8 3072 768 1 65 stream 0",     # stream: at most 64 tokens
     "8 3073 768 1 16 stream 0",     # stream: even N
     "8 3072 768 1 65 skinny 0",     # skinny: at most 64 tokens
     "4 3072 768 1 64 tiled 16",     # W8-only tile for W4
@@ -383,7 +389,9 @@ def test_chain_ws_gemm_host_side():
     ((2048, 24576, 6144, 4), "tiled cfg=12 "),
     # decode-sized token counts
     ((64, 16384, 4096, 8), "tiled cfg=22 "),
-    ((64, 4096, 4096, 8), "skinny "),
+    ((64, 4096, 4096, 8), "stream BN=16 MX=64 "),
+    ((32, 12288, 4096, 8), "stream BN=32 MX=32 "),
+    ((64, 6144, 24576, 4), "stream BN=32 MX=64 "),
     ((16, 24576, 6144, 4), "stream BN=32 MX=16 "),
     ((16, 12288, 4096, 8), "stream BN=16 MX=16 "),
 ])

@@ -1,8 +1,10 @@
 """GPU parity of the INT8 GEMMs against the CPU oracle.
 
 * zq_gemm_{w8a8,w4a8}_i32 on the oracle's codes: int32 accumulators
-  bit-exact, over shapes that cover both kernels (skinny for M <= 64, tiled
-  above), ragged M/N tails, several k-tiles, K % 128 == 64, and extreme codes.
+  bit-exact, over shapes that cover every kernel (GEMV, streaming rings of
+  1 / 16 / 32 / 64 token rows with 16- and 32-row blocks, skinny for odd N,
+  tiled), ragged M/N tails, several k-tiles, K % 128 == 64, and extreme
+  codes.
 * zq_gemm_{w8a8,w4a8}: fp16 outputs within 1 fp16 ulp + 1e-3 of the
   oracle's fp64 epilogue, with and without bias and GeLU.
 * The same fp16 bits from every kernel (GEMV, streaming, skinny, tiled) for
@@ -28,6 +30,10 @@ SHAPES = [  # (M, N, K)
     (300, 1000, 640), (512, 768, 3072), (1, 4096, 4096), (7, 64, 24576),
     (1, 1000, 1024), (1, 77, 2048), (1, 3000, 8192), (16, 24, 2048),
     (40, 8200, 384), (64, 12288, 256),
+    # 17 .. 64 tokens: rings of 32 / 64 token rows, 16-row blocks (N <= 4096)
+    # and 32-row blocks with a ragged last block, K tails; odd N: skinny
+    (64, 4098, 640), (20, 6144, 1088), (48, 200, 4160), (33, 4096, 2048),
+    (40, 77, 1024),
 ]
 
 
@@ -157,8 +163,9 @@ def _epilogue_inputs(M, N, K, G, bits, seed):
 @pytest.mark.parametrize("act", [0, 1])
 def test_output_bits_do_not_depend_on_plan(bits, act):
     # a row of y depends only on that token's codes and scale, so rows
-    # computed by the one-token GEMV, the streaming (16 tokens), the skinny
-    # (40 tokens) and the tiled (256 tokens) kernels must be the same bits
+    # computed by the one-token GEMV, the streaming rings (16, 20 and 40
+    # tokens), the skinny kernel (40 tokens, forced through the schedule
+    # table) and the tiled (256 tokens) kernels must be the same bits
     N, K, G = 512, 2048, 64
     qx, sx, q, qw, sw, b = _epilogue_inputs(256, N, K, G, bits, 97 + bits + act)
     d = dev()
@@ -172,9 +179,15 @@ def test_output_bits_do_not_depend_on_plan(bits, act):
     assert zq.gemm_plan(256, N, K, bits).startswith("tiled")
     full = to_np(run(0, 256))
     for (r0, r1, plan) in [(5, 6, "gemv"), (200, 201, "gemv"), (16, 32, "stream"),
-                           (100, 140, "skinny")]:
-        assert zq.gemm_plan(r1 - r0, N, K, bits).startswith(plan)
-        part = to_np(run(r0, r1))
+                           (100, 120, "stream BN=16 MX=32"),
+                           (100, 140, "stream BN=16 MX=64"), (100, 140, "skinny")]:
+        if plan == "skinny":
+            zq.sched_import(f"{bits} {N} {K} 17 64 skinny 0\n")
+        try:
+            assert zq.gemm_plan(r1 - r0, N, K, bits).startswith(plan)
+            part = to_np(run(r0, r1))
+        finally:
+            zq.sched_clear()
         assert np.array_equal(part.view(np.uint16), full[r0:r1].view(np.uint16)), plan
 
 
