@@ -198,8 +198,9 @@ size_t zq_gemm_quant_workspace_bytes(int M, int N);
  * (the small-batch schedules of the summary page's Sec. 3.4
  * "Quantization-Optimized Transformer Kernels", paper App. D: at small
  * batch the GEMM is bound by weight bandwidth, and every compute unit must
- * stream).  For 17 .. 64 tokens where 64 x 64 tiles would leave compute
- * units idle, K is split over several workgroups per tile: each writes
+ * stream).  For 33 .. 64 tokens where 64 x 64 tiles would leave compute
+ * units idle (packed W4: when K splits into at least 4 slices), K is split
+ * over several workgroups per tile: each writes
  * exact int32 partial sums into the workspace, and a second kernel adds
  * them and applies the same epilogue, so y is bit-identical to the call
  * without a workspace.  Other shapes run exactly as that call.

@@ -1978,8 +1978,10 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
 // y is bit-identical to the unsplit call.
 static constexpr int kSplitCfg = 22;  // 64x64 tiles, 8-stage ring
 
-static int splitk_factor(int M, int N, int K) {
-  if (M < 17 || M > 64) return 1;
+static int splitk_factor(int M, int N, int K, int bits) {
+  // up to 32 tokens the streaming rings of the plain call are as fast or
+  // faster (32 x 6144 x 6144: 13.9 us against 17.0 us split in 2)
+  if (M <= 32 || M > 64) return 1;
   const TileCfg &t = kTileCfgs[kSplitCfg];
   const long tiles = (long)((N + t.bn - 1) / t.bn) * ((M + t.bm - 1) / t.bm);
   if (tiles >= 128) return 1;
@@ -1988,21 +1990,23 @@ static int splitk_factor(int M, int N, int K) {
     // whole 128-k stages, slices of at least 3072 k and at least 128
     // workgroups: shorter slices or fewer workgroups pay more in prologue,
     // partial stores and the reduction than they gain (K = 4096 in 2 or 4
-    // slices measured equal or slower than the skinny kernel; K = 6144 in
-    // 2 slices and K = 16384 in 4 about 1.9x faster)
+    // slices measured equal or slower than the plain call; K = 6144 in 2
+    // slices and K = 16384 in 4 faster: 64 x 6144 x 6144 20.6 -> 18.8 us,
+    // 64 x 4096 x 16384 28.2 -> 23.5 us).  Packed W4 halves the weight
+    // bytes per slice, and two slices lose to the W4 ring (48 x 6144 x
+    // 6144: 15.5 us against 18.4 us).
     if (K % (sk * 128) == 0 && K / sk >= 3072 && tiles * sk >= 128 &&
-        tiles * sk <= cus)
+        tiles * sk <= cus && (bits == 8 || sk >= 4))
       return sk;
   }
   return 1;
 }
 
 size_t gemm_ws_bytes(int M, int N, int K, int bits) {
-  (void)bits;
   if (M <= 0) return 0;
   Plan tp;
   if (forced_tile() >= 0 || sched_lookup(M, N, K, bits, &tp)) return 0;
-  const int sk = splitk_factor(M, N, K);
+  const int sk = splitk_factor(M, N, K, bits);
   return sk > 1 ? (size_t)sk * M * N * 4 : 0;
 }
 
@@ -2041,7 +2045,7 @@ hipError_t launch_gemm_ws(const GemmArgs &a, void *ws, hipStream_t s) {
   Plan tp;
   const int sk = (forced_tile() >= 0 || sched_lookup(a.M, a.N, a.K, a.bits, &tp))
                      ? 1
-                     : splitk_factor(a.M, a.N, a.K);
+                     : splitk_factor(a.M, a.N, a.K, a.bits);
   if (sk <= 1 || a.raw_i32) return launch_gemm(a, s);
   GemmArgs r = a;
   r.out = ws;
@@ -2073,7 +2077,7 @@ int describe_gemm_ws_plan(int M, int N, int K, int bits, char *buf, int len) {
   Plan tp;
   const int sk = (forced_tile() >= 0 || sched_lookup(M, N, K, bits, &tp))
                      ? 1
-                     : splitk_factor(M, N, K);
+                     : splitk_factor(M, N, K, bits);
   if (sk <= 1) return describe_gemm_plan(M, N, K, bits, buf, len);
   return snprintf(buf, len,
                   "splitk SK=%d tiled cfg=%d BN=64 BM=64 W%d tiles=%d + reduce",

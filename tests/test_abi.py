@@ -316,16 +316,18 @@ def test_chain_host_side():
 
 def test_gemm_ws_plans_and_checks(empty_table):
     L = Z.lib()
-    # 17 .. 64 tokens over few 64 x 64 tiles: K split, workspace sk * M * N * 4
+    # 33 .. 64 tokens over few 64 x 64 tiles: K split, workspace sk * M * N * 4
     assert Z.gemm_workspace_bytes(64, 6144, 6144, 8) == 2 * 64 * 6144 * 4
     assert Z.gemm_ws_plan(64, 6144, 6144, 8).startswith("splitk SK=2 tiled cfg=22")
     assert Z.gemm_workspace_bytes(64, 4096, 16384, 4) == 4 * 64 * 4096 * 4
     assert Z.gemm_workspace_bytes(64, 1024, 24576, 8) == 8 * 64 * 1024 * 4
     # no split: too few or too many tokens, enough tiles, K not in whole
     # slices, slices shorter than 3072 k, fewer than 128 workgroups
+    # (and at most 32 tokens, or packed W4 in two slices: the plain call's
+    # streaming rings are as fast)
     for shape in [(16, 4096, 16384, 8), (65, 4096, 16384, 8), (64, 8192, 16384, 8),
                   (64, 4096, 16448, 8), (64, 4096, 4096, 8), (64, 4096, 768, 8),
-                  (33, 1024, 16384, 8)]:
+                  (33, 1024, 16384, 8), (32, 6144, 6144, 8), (48, 6144, 6144, 4)]:
         assert Z.gemm_workspace_bytes(*shape) == 0, shape
         assert not Z.gemm_ws_plan(*shape).startswith("splitk")
     assert Z.gemm_workspace_bytes(0, 4096, 4096, 8) == 0

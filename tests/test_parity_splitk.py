@@ -1,5 +1,5 @@
 """GPU parity of the GEMM calls with a workspace (zq_gemm_w8a8_ws /
-zq_gemm_w4a8_ws): for 17 .. 64 tokens over few weight tiles the K range is
+zq_gemm_w4a8_ws): for 33 .. 64 tokens over few weight tiles the K range is
 split over several workgroups whose exact int32 partial sums a second
 kernel adds before the shared epilogue.
 
@@ -36,8 +36,8 @@ def _inputs(M, N, K, G, bits, seed):
 CASES = [  # (M, N, K, G, bits, act)
     (64, 4096, 16384, 128, 8, 0),    # GPT-J FFN2, 64 tokens: 4 slices
     (64, 6144, 6144, 128, 8, 0),     # NeoX attention output: 2 slices
-    (17, 4096, 12288, 128, 8, 1),
-    (48, 6144, 6144, 128, 4, 1),     # NeoX-shaped W4
+    (33, 4096, 12288, 128, 8, 1),
+    (48, 4096, 16384, 128, 4, 1),    # W4 in 4 slices
     (64, 1024, 24576, 128, 4, 0),    # 8 slices
     (40, 2046, 12288, 2, 8, 1),      # N % 4 != 0: scalar reduction path
     (64, 4104, 6144, 8, 8, 0),       # ragged N tile
