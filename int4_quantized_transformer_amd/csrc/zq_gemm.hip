@@ -7,10 +7,15 @@
 // separate dequantization kernel runs; the tiling is picked per token count
 // (throughput-oriented for large batches, bandwidth-oriented for small).
 //
-// Both kernels use v_mfma_i32_16x16x64_i8.  The weight tile is the MFMA
-// "A" operand (rows = output features n) and the activation tile the "B"
-// operand (columns = tokens t), so each lane ends with 4 consecutive n of
-// one token: y[t][n..n+3] is one 8-byte store.  Within one MFMA the
+// Kernels: gemm_tiled_kernel (v_mfma_i32_32x32x32_i8; more than 64 tokens,
+// and W8 with 33..64 tokens over N >= 8192), gemm_stream_kernel (per-wave
+// LDS rings of 1, 16, 32 or 64 token rows; up to 64 tokens, even N),
+// gemm_skinny_kernel (up to 64 tokens, odd N) and gemm_gemv_kernel
+// (v_dot4_i32_i8; one token).  In the v_mfma_i32_16x16x64_i8 kernels
+// (streaming, skinny) the weight tile is the MFMA "A" operand (rows =
+// output features n) and the activation tile the "B" operand (columns =
+// tokens t), so each lane ends with 4 consecutive n of one token:
+// y[t][n..n+3] is one 8-byte store.  Within one MFMA the
 // assignment of k to (lane group, byte) only has to agree between the two
 // operands, since the integer sum does not depend on the order of k.
 //
@@ -747,7 +752,8 @@ gemm_tiled_kernel(GemmArgs p) {
 }
 
 // ================================================================= skinny
-// Decode-sized M (<= 64): the weights are streamed from HBM once, straight
+// Decode-sized M (<= 64; chosen for odd N, where the streaming rings do not
+// apply, or when forced): the weights are streamed from HBM once, straight
 // into MFMA operand registers (no LDS staging).  A block owns BN weight rows
 // and all M tokens; its NW waves split K (wave w takes k-steps w, w+NW, ...
 // so the block reads NW adjacent 64-byte segments of every row at a time),
