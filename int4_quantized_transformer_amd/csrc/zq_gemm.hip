@@ -2328,10 +2328,14 @@ static int a16_stream_cfg() {
   return v;
 }
 
-// Up to 16 tokens with even N (bias pairs): the streaming kernel.
+// Up to 64 tokens with even N (bias pairs): the streaming kernel, except
+// more than 32 tokens over N >= 8192, where the 128x64 tiles are faster
+// (64 x 18432 x 6144: 77.9 us against 90.6 us for a 64-row ring).  Against
+// those tiles elsewhere: 32 x 4096 x 4096 53.5 -> 11.3 us, 48 x 6144 x 6144
+// 74.8 -> 37.0 us, 24 x 18432 x 6144 76.9 -> 54.1 us.
 static bool a16_stream(int M, int N, int K) {
-  return forced_a16() < 0 && !a16_gemv(M, K) && M >= 1 && M <= 16 &&
-         (N & 1) == 0;
+  return forced_a16() < 0 && !a16_gemv(M, K) && M >= 1 && M <= 64 &&
+         (N & 1) == 0 && !(M > 32 && N >= 8192);
 }
 
 hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
@@ -2343,6 +2347,16 @@ hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
   }
   if (a16_stream(a.M, a.N, a.K)) {
     if (a.M == 1) return run_stream<Stream<1, 1, 4, 512, 4, false, true>, false>(a, s);
+    if (a.M > 16) {
+      // 17 .. 64 tokens: the per-wave fp32 partials and the activation
+      // bytes grow with the token rows, so the chunks shrink to keep the
+      // ring in LDS; 32-row blocks once 16-row blocks outnumber the CUs
+      // (up to 32 tokens; a 64-row ring of 32-row blocks does not fit)
+      if (a.M > 32) return run_stream<Stream<1, 64, 4, 64, 3, false, true>, false>(a, s);
+      if ((a.N + 15) / 16 <= device_cus())
+        return run_stream<Stream<1, 32, 4, 128, 3, false, true>, false>(a, s);
+      return run_stream<Stream<2, 32, 4, 64, 3, false, true>, false>(a, s);
+    }
     // {FN, MX, NW, CK, D}; the default (32-row blocks, 128-byte chunks,
     // 4-deep rings) measured fastest on NeoX QKV at 16 tokens (2.83 TB/s,
     // against 2.3 - 2.6 for the others)
@@ -2366,10 +2380,12 @@ int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len) {
   if (a16_gemv(M, K))
     return snprintf(buf, len, "gemv-a16 NW=4 U=6 rows=%d x_in_lds=1", N);
   if (a16_stream(M, N, K)) {
-    const int cfg = M == 1 ? 0 : a16_stream_cfg();
-    const int bn = (M > 1 && cfg == 0) ? 32 : 16;
+    const int cfg = M == 1 || M > 16 ? 0 : a16_stream_cfg();
+    const int mx = M == 1 ? 1 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
+    const int bn = mx > 16 ? (mx == 32 && (N + 15) / 16 > device_cus() ? 32 : 16)
+                           : (M > 1 && cfg == 0) ? 32 : 16;
     return snprintf(buf, len, "stream-a16 MX=%d NW=4 cfg=%d BN=%d row_blocks=%d",
-                    M == 1 ? 1 : 16, cfg, bn, (N + bn - 1) / bn);
+                    mx, cfg, bn, (N + bn - 1) / bn);
   }
   const int i = choose_a16(M, N);
   const A16Cfg &c = kA16Cfgs[i];

@@ -145,7 +145,11 @@ def test_gemm_w8a16_argument_checks():
     assert Z.gemm_w8a16_plan(1, 18432, 6000 + 64).startswith("stream-a16 MX=1")
     assert Z.gemm_w8a16_plan(2, 18432, 6144).startswith("stream-a16 MX=16")
     assert Z.gemm_w8a16_plan(2, 18431, 6144).startswith("tiled-a16 cfg=4")
-    assert Z.gemm_w8a16_plan(17, 18432, 6144).startswith("tiled-a16 cfg=4")
+    assert Z.gemm_w8a16_plan(17, 18432, 6144).startswith("stream-a16 MX=32 NW=4 cfg=0 BN=32")
+    assert Z.gemm_w8a16_plan(17, 4096, 6144).startswith("stream-a16 MX=32 NW=4 cfg=0 BN=16")
+    assert Z.gemm_w8a16_plan(33, 6144, 6144).startswith("stream-a16 MX=64 NW=4 cfg=0 BN=16")
+    assert Z.gemm_w8a16_plan(33, 18432, 6144).startswith("tiled-a16 cfg=4")
+    assert Z.gemm_w8a16_plan(40, 999, 256).startswith("tiled-a16 cfg=4")
     assert Z.gemm_w8a16_plan(2048, 18432, 6144).startswith("tiled-a16 cfg=3")
     assert Z.gemm_w8a16_plan(100, 256, 512).startswith("tiled-a16 cfg=1")
 

@@ -39,7 +39,12 @@ def _inputs(M, N, K, G, seed, bias=True):
     (1024, 2560, 256, 64), (1, 1000, 2048, 8), (1, 4096, 16384, 128),
     (1, 18432, 6144, 128), (2, 512, 1024, 64),
     (7, 998, 448, 2), (16, 18432, 6144, 128), (3, 64, 64, 64),
-    (1, 768, 576, 64), (16, 2, 64, 1), (9, 999, 256, 3), (12, 4096, 4160, 128)])
+    (1, 768, 576, 64), (16, 2, 64, 1), (9, 999, 256, 3), (12, 4096, 4160, 128),
+    # 17 .. 64 tokens: rings of 32 token rows in 16- and 32-row blocks, of 64
+    # rows in 16-row blocks (ragged last block, K tails), tiles above 32
+    # tokens over N >= 8192
+    (24, 4096, 1088, 128), (20, 4098, 640, 2), (64, 6146, 576, 2),
+    (48, 200, 4160, 8), (33, 8192, 256, 128)])
 @pytest.mark.parametrize("bias,act", [(True, 0), (True, 1), (False, 1)])
 def test_w8a16_vs_oracle(M, N, K, G, bias, act):
     x, q, sw, b = _inputs(M, N, K, G, M + 3 * N + 7 * K + G, bias)
@@ -97,12 +102,15 @@ def test_w8a16_plans_cover_every_kernel():
     assert zq.gemm_w8a16_plan(1, 256, 128).startswith("stream-a16 MX=1")
     assert zq.gemm_w8a16_plan(16, 18432, 6144).startswith("stream-a16 MX=16")
     assert zq.gemm_w8a16_plan(9, 999, 256).startswith("tiled-a16")   # odd N
-    assert zq.gemm_w8a16_plan(17, 4096, 256).startswith("tiled-a16")
+    assert zq.gemm_w8a16_plan(17, 4096, 256).startswith("stream-a16 MX=32")
+    assert zq.gemm_w8a16_plan(64, 4096, 256).startswith("stream-a16 MX=64")
+    assert zq.gemm_w8a16_plan(40, 8192, 256).startswith("tiled-a16")
 
 
-def test_w8a16_stream_is_deterministic():
+@pytest.mark.parametrize("M", [16, 24, 64])
+def test_w8a16_stream_is_deterministic(M):
     # fp32 partials of the waves are added in a fixed order
-    M, N, K, G = 16, 4096, 6144, 128
+    N, K, G = 4096, 6144, 128
     x, q, sw, b = _inputs(M, N, K, G, 5)
     d = dev()
     args = (x.to(d), torch.from_numpy(q).to(d), torch.from_numpy(sw).to(d), G,
