@@ -1653,6 +1653,13 @@ struct Plan {
   bool tuned = false;  // taken from the schedule table
 };
 
+// W8 rings of 16 token rows: 32-row weight blocks when 16-row blocks would
+// outnumber the compute units and 32-row blocks would not.
+static bool stream_w8_wide(int N) {
+  const int cus = device_cus();
+  return (N + 15) / 16 > cus && (N + 31) / 32 <= cus;
+}
+
 // Token rows a streaming ring holds: 1, 16, 32 or 64.
 static int stream_mx(int M) {
   return M == 1 ? 1 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
@@ -1948,7 +1955,14 @@ static hipError_t run(const Plan &pl, const GemmArgs &a, hipStream_t s) {
         case 1: return run_stream<Stream<2, 16, 4, 128, 6, W4>, RAW>(a, s);
         case 2: return run_stream<Stream<2, 16, 4, 256, 3, W4>, RAW>(a, s);
         case 3: return run_stream<Stream<1, 16, 4, 128, 8, W4>, RAW>(a, s);
-        default: return run_stream<Stream<1, 16, 4, 256, 4, W4>, RAW>(a, s);
+        default:
+          // 32-row blocks when 16-row blocks would outnumber the CUs and
+          // 32-row blocks would not (NeoX attention output, 16 x 6144 x
+          // 6144: 11.5 -> 10.0 us; with more blocks than CUs either way,
+          // 16-row blocks stay: GPT-J QKV 13.3 us against 14.1 us)
+          if (stream_w8_wide(a.N))
+            return run_stream<Stream<2, 16, 4, 256, 3, W4>, RAW>(a, s);
+          return run_stream<Stream<1, 16, 4, 256, 4, W4>, RAW>(a, s);
       }
     }
   }
@@ -2403,7 +2417,8 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
                     N, K <= 32768 ? 1 : 0, src);
   if (pl.kind == kStream) {
     const int bn = pl.mf > 16 ? ((N + 15) / 16 <= device_cus() ? 16 : 32)
-                   : (bits == 4 && pl.mf > 1 && forced_stream() == 0) ? 32 : 16;
+                   : (pl.mf > 1 && forced_stream() == 0 &&
+                      (bits == 4 || stream_w8_wide(N))) ? 32 : 16;
     return snprintf(buf, len, "stream BN=%d MX=%d NW=4 W%d row_blocks=%d%s", bn,
                     pl.mf, bits, (N + bn - 1) / bn, src);
   }

@@ -400,6 +400,7 @@ def test_chain_ws_gemm_host_side():
     ((64, 6144, 24576, 4), "stream BN=32 MX=64 "),
     ((16, 24576, 6144, 4), "stream BN=32 MX=16 "),
     ((16, 12288, 4096, 8), "stream BN=16 MX=16 "),
+    ((16, 6144, 6144, 8), "stream BN=32 MX=16 "),
 ])
 def test_tile_rule_regression(empty_table, shape, plan):
     # the plans the schedule tuner measured best for these shapes

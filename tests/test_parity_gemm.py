@@ -34,6 +34,8 @@ SHAPES = [  # (M, N, K)
     # and 32-row blocks with a ragged last block, K tails; odd N: skinny
     (64, 4098, 640), (20, 6144, 1088), (48, 200, 4160), (33, 4096, 2048),
     (40, 77, 1024),
+    # up to 16 tokens, 4096 < N <= 8192: W8 rings of 32-row blocks
+    (16, 6144, 512), (9, 8190, 1088),
 ]
 
 
