@@ -6,8 +6,12 @@ A step is one pass of the whole hot path over one batch: for every linear of
 the workload, LayerNorm + token-wise INT8 quantization (QKV and FFN1 inputs)
 or plain token-wise quantization (attn-out and FFN2 inputs), then the INT8
 GEMM with the fused dequant/bias(/GeLU) epilogue.  Default workload: the
-BERT-base encoder linears at 4096 tokens (batch 32 x seq 128), hidden 768,
-W8A8 with 64-row weight groups.
+GPT-NeoX-20B-shaped linears at 2048 tokens (prefill), hidden 6144, INT8
+attention weights (QKV 18432x6144, out 6144x6144) and nibble-packed INT4
+feed-forward weights (FFN1 24576x6144 with GeLU, FFN2 6144x24576), 128-row
+weight groups: the largest of the five workloads that fits one GPU.  Its
+activations follow the GPT-J recipe (0.5% outlier channels x30): "the same
+distributions as config 3" is read 0-indexed.
 
 Memory: R rotating sets of weights, inputs, intermediates and outputs (each
 set one "layer") make the working set larger than twice the 256 MB Infinity
@@ -43,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="bert-base")
+    ap.add_argument("--workload", default="neox-20b")
     ap.add_argument("--m-index", type=int, default=None,
                     help="which token count of the workload (default: largest)")
     ap.add_argument("--no-graph", action="store_true")
@@ -86,8 +90,10 @@ def gemm_bytes(M, N, K, bits, G):
     return M * K + N * K * bits // 8 + 4 * (N // G) + 4 * M + 2 * N + 2 * M * N
 
 
-def quant_bytes(M, K):
-    return 2 * M * K + M * K + 4 * M
+def quant_bytes(M, K, ln=False):
+    """Read x (2MK), write the codes (MK) and scales (4M); LayerNorm rows
+    also read gamma and beta (4K)."""
+    return 2 * M * K + M * K + 4 * M + (4 * K if ln else 0)
 
 
 def pct_attainable(ops, nbytes, seconds):
@@ -208,7 +214,7 @@ def kernel_work(name, L, M, G):
     """(ops, bytes, bound) of one launch."""
     if ".gemm" in name:
         return (2 * M * L.N * L.K, gemm_bytes(M, L.N, L.K, L.bits, G), "mfma")
-    return (0, quant_bytes(M, L.K), "hbm")
+    return (0, quant_bytes(M, L.K, L.ln), "hbm")
 
 
 # ------------------------------------------------------------- CPU oracle --
@@ -394,7 +400,7 @@ def step_entries(zq, wl, M):
     for L in wl.linears:
         qn = f"{L.name}.ln_quant" if L.ln else f"{L.name}.quant"
         out.append({"name": qn, "kernel": "row_quant_kernel", "grid": None,
-                    "ops": 0, "bytes": quant_bytes(M, L.K)})
+                    "ops": 0, "bytes": quant_bytes(M, L.K, L.ln)})
         gn = f"{L.name}.gemm_w{L.bits}a8"
         plan = zq.gemm_plan(M, L.N, L.K, L.bits)
         kern = {"tiled": "gemm_tiled_kernel", "stream": "gemm_stream_kernel",
@@ -409,8 +415,44 @@ def step_entries(zq, wl, M):
     return out
 
 
+# ----------------------------------------------------- fp16 comparator --
+def fp16_linear_us(torch, dev, wl, li, M, steps=20):
+    """torch fp16 addmm + bias (+ GeLU) of linear `li` of `wl` at M tokens,
+    with fp16 weights (run as a library, never inspected): the average
+    launch from a CUDA graph holding one call per rotating weight copy, the
+    copies together larger than twice the Infinity Cache, as for the INT8
+    kernels."""
+    from int4_quantized_transformer_amd import workloads as W
+    L = wl.linears[li]
+    w, b = W.gen_weights(wl, li)
+    wd, bd = w.to(dev), b.to(dev)
+    x = W.gen_activations(wl, li, M=M, m_index=list(wl.M).index(M)).to(dev)
+    R = max(1, -(-ROTATE_BYTES // (2 * L.N * L.K)))
+    ws = [wd] + [wd.clone() for _ in range(R - 1)]
+    y = torch.empty(M, L.N, dtype=torch.float16, device=dev)
+
+    def run():
+        for w_ in ws:
+            torch.addmm(bd, x, w_.t(), out=y)
+            if L.gelu:
+                torch.nn.functional.gelu(y)
+
+    stream = torch.cuda.current_stream()
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cs):
+        run()
+    g.replay()
+    ms, _ = timed_graphs(torch, [g], steps, stream)
+    del g, ws, wd
+    torch.cuda.empty_cache()
+    return ms * 1e3 / R
+
+
 # ------------------------------------------------------------------ decode --
-def decode_case(torch, zq, dev, name, M, steps=100):
+def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True):
     """One decoder layer's four linears at decode-sized M: GEMM GB/s against
     HBM for the layer (graph replay of the four launches over rotating
     weight sets larger than the Infinity Cache) and per linear."""
@@ -482,14 +524,27 @@ def decode_case(torch, zq, dev, name, M, steps=100):
             "us": round(mi_ * 1e3, 2),
             "GB_per_s": round(b_ / (mi_ * 1e-3) / 1e9, 1),
             "pct_attainable": pct_attainable(2 * M * L.N * L.K, b_, mi_ * 1e-3),
-            "plan": zq.gemm_ws_plan(M, L.N, L.K, L.bits).split(" W")[0]}
-    return {"GB_per_s": round(gbs, 1),
-            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
-            "us_per_step": round(ms * 1e3, 2), "us_by_launch": by_launch,
-            "bytes_per_step": nbytes, "rotating_sets": R, "per_linear": per}
+            "plan": zq.gemm_ws_plan(M, L.N, L.K, L.bits).split(" W")[0],
+            "bytes": b_}
+    del sets, chains
+    torch.cuda.empty_cache()
+    fp16 = {}
+    if with_fp16:
+        for i, (L, *_r) in enumerate(lin):
+            fp16[f"{L.name}"] = round(fp16_linear_us(torch, dev, wl, i, M,
+                                                     steps // 4 or 1), 2)
+        fp16["layer"] = round(sum(fp16.values()), 2)
+    out = {"GB_per_s": round(gbs, 1),
+           "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+           "us_per_step": round(ms * 1e3, 2), "us_by_launch": by_launch,
+           "bytes_per_step": nbytes, "rotating_sets": R, "per_linear": per}
+    if fp16:
+        out["torch_fp16_us"] = fp16
+        out["speedup_vs_fp16"] = round(fp16["layer"] / (ms * 1e3), 2)
+    return out
 
 
-def decode_figure(torch, zq, dev, steps=100):
+def decode_figure(torch, zq, dev, steps=100, with_fp16=True):
     """Decoder linears at decode-sized M (QKV, out, FFN1+GeLU, FFN2): GPT-J-6B
     (W8A8, 128-row groups) at M = 1, 16 and 64, and GPT-NeoX-20B (W8 attention,
     W4 FFN) at M = 1 and 16; GEMM GB/s against 8 TB/s."""
@@ -499,25 +554,27 @@ def decode_figure(torch, zq, dev, steps=100):
                        "bytes"}
     for name, ms in (("gptj-6b", (1, 16, 64)), ("neox-20b", (1, 16))):
         for M in ms:
-            out[f"{name} M={M}"] = decode_case(torch, zq, dev, name, M, steps)
+            out[f"{name} M={M}"] = decode_case(torch, zq, dev, name, M, steps,
+                                               with_fp16)
             torch.cuda.empty_cache()
     return out
 
 
 def prefill_figure(torch, zq, dev, steps=20):
-    """Fused W8A8 / W4A8 GEMMs at the prefill token counts of the larger
-    configs (BERT-large 8192 tokens with W4 FFN, GPT-J-6B 2048, GPT-NeoX-20B
-    2048 with W4 FFN): per linear, the average launch from a graph holding
-    it for every rotating set, TOPS and % of the 5.0 POP/s INT8 peak."""
+    """Fused W8A8 / W4A8 GEMMs at the prefill token counts of the other
+    large configs (BERT-large 8192 tokens with W4 FFN, GPT-J-6B 2048; the
+    GPT-NeoX-20B step is the headline): per linear, the average launch from
+    a graph holding it for every rotating set, TOPS and % of the 5.0 POP/s
+    INT8 peak, beside the torch fp16 matmul of the same shape."""
     from int4_quantized_transformer_amd import workloads as W
     stream = torch.cuda.current_stream()
     out = {"note": "GEMM with the fused epilogue only (inputs already "
                    "quantized); one graph per linear over rotating sets"}
-    for name, M in (("bert-large", 8192), ("gptj-6b", 2048), ("neox-20b", 2048)):
+    for name, M in (("bert-large", 8192), ("gptj-6b", 2048)):
         wl = W.workload(name)
         mi = list(wl.M).index(M)
         res = {}
-        tot_ops = tot_us = 0.0
+        tot_ops = tot_us = tot_f16 = 0.0
         for li, L in enumerate(wl.linears):
             w, b = W.gen_weights(wl, li)
             qw, sw = zq.quantize_weights(w.to(dev), wl.G, L.bits)
@@ -551,9 +608,16 @@ def prefill_figure(torch, zq, dev, steps=20):
             tot_us += us
             del sets, gr, y
             torch.cuda.empty_cache()
+            f16 = fp16_linear_us(torch, dev, wl, li, M, steps)
+            e = res[f"{L.name} {L.N}x{L.K} W{L.bits}"]
+            e["torch_fp16_us"] = round(f16, 2)
+            e["speedup_vs_fp16"] = round(f16 / us, 2)
+            tot_f16 += f16
         tops = tot_ops / (tot_us * 1e-6) / 1e12
         res["all four"] = {"TOPS": round(tops, 1),
-                           "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1)}
+                           "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1),
+                           "torch_fp16_TFLOPS": round(tot_ops / (tot_f16 * 1e-6) / 1e12, 1),
+                           "speedup_vs_fp16": round(tot_f16 / tot_us, 2)}
         out[f"{name} M={M}"] = res
     return out
 
@@ -796,7 +860,7 @@ def _split(values, entries, key):
     return {e["name"]: vs[i * n:(i + 1) * n] for i, e in enumerate(es)}
 
 
-def summarize(d, traffic_out=None, workload="bert-base", m_index=None):
+def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
     """Per step entry: durations from the kernel trace and, when present,
     FETCH_SIZE / WRITE_SIZE per dispatch scaled by the same counters of the
     plain copy of COPY_BYTES bytes (GEMM entries; quantizer launches are
@@ -1045,14 +1109,22 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": f"{wl.name} encoder linears"
-                   if wl.name.startswith("bert") else f"{wl.name} linears",
+                   if wl.name.startswith("bert") else
+                   f"{wl.name} decoder linears (prefill)",
                    "tokens": M, "hidden": wl.linears[0].K, "group_rows": wl.G,
                    "linears": {L.name: f"{L.N}x{L.K} W{L.bits}A8"
                                + (" +LN" if L.ln else "")
                                + (" +GeLU" if L.gelu else "")
                                for L in wl.linears},
                    "rotating_sets": R, "launch": launch,
-                   "steps_per_graph_replay": R if not args.no_graph else 0},
+                   "steps_per_graph_replay": R if not args.no_graph else 0,
+                   "activations": (
+                       f"N(0,1), {wl.n_outliers(wl.linears[0].K)} of "
+                       f"{wl.linears[0].K} channels x{wl.outlier_factor:g}"
+                       + ("; the BASELINE distribution reference ('as in "
+                          "config 3' / 'config 1') read 0-indexed: GPT-J's "
+                          "recipe for NeoX, BERT-base's for BERT-large"
+                          if wl.name in ("neox-20b", "bert-large") else ""))},
         "roofline": roof,
     }
     extras = {"ms_per_step_by_launch": by_launch,
@@ -1061,9 +1133,12 @@ def main():
               "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
               "breakdown": breakdown}
     if not args.no_fp16:
-        extras["fp16_matmul"] = fp16_comparator(torch, base, M, args.steps)
+        extras["fp16_matmul"] = fp16_comparator(torch, zq, dev, wl, M, ms,
+                                                max(10, args.steps // 2))
     if not args.no_decode:
-        extras["decode"] = decode_figure(torch, zq, dev)
+        extras["decode"] = decode_figure(torch, zq, dev,
+                                         with_fp16=not args.no_fp16)
+        out["roofline_decode"] = decode_roofline(extras["decode"], args.traffic)
     if not args.no_prefill:
         extras["prefill"] = prefill_figure(torch, zq, dev)
     if not args.no_w8a16:
@@ -1080,36 +1155,53 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def fp16_comparator(torch, base, M, steps):
-    """torch fp16 matmul + bias (+GeLU) at the same shapes (library run)."""
-    mats = []
-    for d in base:
-        L = d["L"]
-        mats.append((d["x"], d["w_cpu"].to(d["x"].device), d["b"], L.gelu))
-    stream = torch.cuda.current_stream()
-
-    def step():
-        for x, w, b, gelu in mats:
-            y = torch.addmm(b, x, w.t())
-            if gelu:
-                y = torch.nn.functional.gelu(y)
-
-    for _ in range(5):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    n = max(10, steps // 4)
-    e0.record(stream)
-    for _ in range(n):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
-    ops = sum(2 * M * d["L"].N * d["L"].K for d in base)
+def fp16_comparator(torch, zq, dev, wl, M, int8_ms, steps):
+    """torch fp16 matmul + bias (+GeLU) of the step's linears at the same
+    shapes, with fp16 weights (library run), each from a CUDA graph over
+    rotating weight copies as the INT8 step rotates its sets; the step time
+    is the sum of the four."""
+    per = {L.name: fp16_linear_us(torch, dev, wl, i, M, steps)
+           for i, L in enumerate(wl.linears)}
+    ms = sum(per.values()) / 1e3
+    ops = sum(2 * M * L.N * L.K for L in wl.linears)
     return {"ms_per_step": round(ms, 5),
             "TFLOPS": round(ops / (ms * 1e-3) / 1e12, 1),
-            "note": "torch.addmm fp16 (+gelu), eager, same shapes, no quant"}
+            "pct_fp16_peak": round(100 * ops / (ms * 1e-3) / 1e12
+                                   / FP16_PEAK_TFLOPS, 1),
+            "us_by_linear": {k: round(v, 2) for k, v in per.items()},
+            "int8_step_speedup": round(ms / int8_ms, 3),
+            "note": "torch.addmm fp16 + bias (+gelu), graph replay over "
+                    "rotating fp16 weight copies, same shapes, no "
+                    "quantization; the INT8 step includes its LN+quant and "
+                    "quant launches"}
+
+
+def decode_roofline(dec, traffic_path):
+    """Roofline entry of the decode regime: the slowest GEMM of the
+    GPT-NeoX-20B one-token layer (weight streaming, HBM-bound)."""
+    case = dec.get("neox-20b M=1")
+    if not case:
+        return None
+    name, e = max(case["per_linear"].items(), key=lambda kv: kv[1]["us"])
+    t = e["us"] * 1e-6
+    achieved = e["bytes"] / t / 1e9
+    try:
+        with open(traffic_path) as f:
+            tr = json.load(f).get("decode", {}).get(f"neox-20b M=1 {name}")
+        if tr and tr.get("sources") != source_shas():
+            tr = None
+    except (OSError, ValueError):
+        tr = None
+    return {"bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": tr.get("hbm_bytes_per_launch") if tr else None,
+            "kernel": f"neox-20b M=1 {name} ({e['plan']})",
+            "avg_launch_us": e["us"], "algorithmic": {"bytes": e["bytes"]},
+            "layer_GB_per_s": case["GB_per_s"],
+            "layer_pct_hbm_peak": case["pct_hbm_peak"],
+            "timing": "per-launch average from a HIP graph of this launch "
+                      "over rotating weight sets, events around the replays"}
 
 
 if __name__ == "__main__":

@@ -26,8 +26,13 @@
  *    in a thread-local string returned by zq_last_error().  M == 0 is a
  *    valid empty call (ZQ_OK, nothing launched); buffers sized by M may
  *    then be NULL.
- *  - Base pointers of int8/uint8/fp16 tensors must be 16-byte aligned
- *    (PyTorch allocations are); fp32 scale arrays 4-byte aligned.
+ *  - Alignment (PyTorch allocations satisfy all of it): GEMM operands (qx,
+ *    qw, qw4, the fp16 x of zq_gemm_w8a16), int32 outputs, quantized
+ *    outputs qy and workspaces 16 bytes; GEMM outputs y 8
+ *    bytes; fp32 arrays 4 bytes; other fp16 tensors (x of the quantizers,
+ *    gamma, beta, bias, ln_out) 2 bytes.  A misaligned pointer returns
+ *    ZQ_EINVAL.  fp16 tensors that are not 16-byte aligned take slower
+ *    element-wise loads; the results are the same.
  *  - Calls on one stream run in order; calls on different streams that
  *    write the same memory race, as with any kernel.
  */
@@ -54,11 +59,15 @@ typedef enum { ZQ_ACT_NONE = 0, ZQ_ACT_GELU = 1 } zq_act;
 /* Largest K accepted by zq_ln_quant_act / zq_quant_act (a token row is held
  * in registers).  Larger K returns ZQ_EUNSUPPORTED. */
 #define ZQ_MAX_ROW_K 65536
-/* Largest K accepted by the GEMMs: the int32 accumulator of an 8-bit
- * product cannot overflow while K * 127 * 127 < 2^31 (W8) and, for the
- * W4 path which accumulates 16 * acc, K * 127 * 7 * 16 < 2^31. */
-#define ZQ_MAX_GEMM_K_W8 133144
-#define ZQ_MAX_GEMM_K_W4 150976
+/* Largest K accepted by the GEMMs.  The calls take any two's-complement
+ * code, including -128 (int8) and -8 (nibble), which Eq. (2)'s integer
+ * range [-2^(b-1), 2^(b-1) - 1] admits although the quantizer never emits
+ * them.  The largest product magnitude is then 128 * 128 = 16384 for W8,
+ * and 16 * 8 * 128 = 16384 for the W4 path, which accumulates 16 * acc;
+ * K * 16384 <= 2^31 - 1 holds up to K = 131071, and the largest multiple
+ * of 64 below that is 131008. */
+#define ZQ_MAX_GEMM_K_W8 131008
+#define ZQ_MAX_GEMM_K_W4 131008
 
 /*
  * zq_quantize_weights -- group-wise symmetric weight quantization

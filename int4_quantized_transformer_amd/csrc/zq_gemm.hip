@@ -1914,6 +1914,13 @@ static hipError_t run(const Plan &pl, const GemmArgs &a, hipStream_t s) {
     if (u6) return run_gemv<Gemv<4, 6, W4, 0>, RAW>(a, s, 2, il);
     return run_gemv<Gemv<4, 8, W4, 0>, RAW>(a, s, 2, il);
   }
+  if (pl.kind == kStream && !RAW && a.bias && ((uintptr_t)a.bias & 3)) {
+    // The rings gather bias pairs as 4-byte words with their copies; a bias
+    // that is only 2-byte aligned (a view such as b[1:]) goes to the skinny
+    // kernel, which reads it per element.  (A per-element load in the ring
+    // epilogue would wait for every copy in flight: vmcnt is in order.)
+    return run<W4, RAW>(Plan{kSkinny, (a.M + 15) / 16, 0}, a, s);
+  }
   if (pl.kind == kStream) {
     if (pl.mf == 1) return run_stream<Stream<1, 1, 4, 512, 4, W4>, RAW>(a, s);
     if (pl.mf > 16) {
@@ -2359,7 +2366,10 @@ hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s) {
     if (a.K <= 8192) return run_gemv<Gemv<4, 6, false, 4, true>, false>(a, s, 2, 0);
     return run_gemv<Gemv<4, 6, false, 16, true>, false>(a, s, 2, 0);
   }
-  if (a16_stream(a.M, a.N, a.K)) {
+  // the rings gather bias pairs as 4-byte words: a bias that is only 2-byte
+  // aligned takes the tiles, which read it per element
+  const bool bias2 = a.bias && ((uintptr_t)a.bias & 3);
+  if (a16_stream(a.M, a.N, a.K) && !bias2) {
     if (a.M == 1) return run_stream<Stream<1, 1, 4, 512, 4, false, true>, false>(a, s);
     if (a.M > 16) {
       // 17 .. 64 tokens: the per-wave fp32 partials and the activation

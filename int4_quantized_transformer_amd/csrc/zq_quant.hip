@@ -306,9 +306,13 @@ hipError_t launch_row_quant(const void *x, const void *gamma, const void *beta,
   const half_t *g = static_cast<const half_t *>(gamma);
   const half_t *b = static_cast<const half_t *>(beta);
   half_t *lo = static_cast<half_t *>(ln_out);
+  // the vector path reads x, gamma and beta as 16-byte chunks and writes
+  // 8-byte code chunks
   const bool vec = (K % 8 == 0) && ((uintptr_t)x % 16 == 0) &&
                    ((uintptr_t)qx % 8 == 0) &&
-                   (!lo || (uintptr_t)lo % 16 == 0);
+                   (!lo || (uintptr_t)lo % 16 == 0) &&
+                   (!g || (uintptr_t)g % 16 == 0) &&
+                   (!b || (uintptr_t)b % 16 == 0);
   if (ln)
     return vec ? dispatch_tpr<true, true>(xh, g, b, eps, M, K, qx, sx, lo, s)
                : dispatch_tpr<true, false>(xh, g, b, eps, M, K, qx, sx, lo, s);

@@ -50,3 +50,47 @@ def assert_ln_close(h_gpu, h_oracle, what=""):
                                                 2.0 ** -24, 0.0))
     bad = np.abs(h - r) > tol
     assert not bad.any(), f"{what}: {bad.sum()} LN outputs outside 2e-3"
+
+
+def assert_linear_matches_oracle(y, qx, sx, ref, q, sw, G, act, ln, what=""):
+    """One quantized linear of the HIP path (its codes qx, scales sx and
+    output y) against the oracle's linear computed from the same CPU inputs
+    (``ref`` = oracle.linear(...), ``q`` the oracle's int8 weight codes).
+
+    * Codes: with LayerNorm, within 1 of the oracle's and different in at
+      most 0.1% of them, scales within 2e-3 relative; without LayerNorm
+      (identical quantizer inputs) bit-exact.
+    * y: in every token row whose codes and scale equal the oracle's, within
+      1 fp16 ulp + 1e-3 of the oracle's fp64 epilogue.  In a row where LN
+      moved a code or the scale, the tolerance widens by the derived bound
+      L * sw[n/G] * (|sx - sx_ref| * (|acc_ref| + D) + sx * D) with
+      D = sum over moved codes of |dq| * |q[n, k]| (L = 1.13 bounds the GeLU
+      slope; 1 without GeLU)."""
+    qx = np.asarray(qx)
+    sx = np.asarray(sx, np.float32)
+    dq = qx.astype(np.int64) - ref["qx"].astype(np.int64)
+    if ln:
+        assert_codes_within_one(qx, ref["qx"], 1e-3, what + " codes")
+        assert np.allclose(sx, ref["sx"], rtol=2e-3, atol=0), what + " scales"
+    else:
+        assert np.array_equal(qx, ref["qx"]), what + " codes"
+        assert np.array_equal(sx, ref["sx"]), what + " scales"
+    z = ref["z"]
+    tol = fp16_ulp(z) + 1e-3
+    moved = (dq != 0).any(axis=1) | (sx != ref["sx"])
+    if moved.any():
+        rows = np.nonzero(moved)[0]
+        D = np.abs(dq[rows]).astype(np.float64) @ np.abs(q.astype(np.float64)).T
+        swn = np.repeat(np.asarray(sw, np.float64), G)[None, :]
+        dsx = np.abs(sx[rows].astype(np.float64) - ref["sx"][rows])[:, None]
+        L = 1.13 if act == 1 else 1.0
+        acc = np.abs(ref["acc"][rows].astype(np.float64))
+        tol[rows] += L * swn * (dsx * (acc + D) + sx[rows, None] * D)
+    err = np.abs(np.asarray(y, np.float64) - z)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} outputs outside the tolerance; "
+            f"worst at {i}: gpu {float(np.asarray(y)[i])!r} oracle {z[i]!r} "
+            f"(row moved: {bool(moved[i[0]])})")

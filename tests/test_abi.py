@@ -77,7 +77,7 @@ def test_gemm_argument_checks(fn):
     assert f(A, None, C, D, 64, None, 0, 16, 256, 256, E, None) == EINVAL
     assert f(ctypes.c_void_p(0x10008), B, C, D, 64, None, 0, 16, 256, 256, E,
              None) == EINVAL                                            # align
-    big = 133_184 if fn == "zq_gemm_w8a8" else 151_040
+    big = 131_072                                   # K > ZQ_MAX_GEMM_K_*
     assert f(A, B, C, D, 64, None, 0, 16, 256, big, E, None) == EUNSUP   # int32 bound
     assert f(A, B, C, D, 64, None, 0, 0, 256, 256, E, None) == OK       # empty
 
@@ -95,10 +95,35 @@ def test_gemm_i32_argument_checks():
     assert L.zq_gemm_w8a8_i32(None, B, 1, 64, 128, C, None) == EINVAL
 
 
+def _header_define(name):
+    import re
+    hdr = os.path.join(os.path.dirname(__file__), "..", "include", "zq.h")
+    with open(hdr) as f:
+        m = re.search(rf"#define {name} (\d+)", f.read())
+    return int(m.group(1))
+
+
 def test_header_limits_match_int32_bound():
-    # K * 127 * 127 < 2^31 for W8 and K * 127 * 7 * 16 < 2^31 for the W4 path
-    assert 133_144 * 127 * 127 < 2 ** 31 <= 133_145 * 127 * 127
-    assert 150_976 * 127 * 7 * 16 < 2 ** 31 <= 150_977 * 127 * 7 * 16
+    # The calls take any two's-complement code: -128 * -128 for W8, and
+    # 16 * (-8) * (-128) on the W4 path (which accumulates 16 * acc).  The
+    # bound is the largest multiple of 64 with K * 16384 <= 2^31 - 1.
+    worst = max(128 * 128, 16 * 8 * 128)
+    for name in ("ZQ_MAX_GEMM_K_W8", "ZQ_MAX_GEMM_K_W4"):
+        k = _header_define(name)
+        assert k % 64 == 0
+        assert k * worst <= 2 ** 31 - 1 < (k + 64) * worst
+
+
+@pytest.mark.parametrize("fn,bits", [("zq_gemm_w8a8", 8), ("zq_gemm_w4a8", 4)])
+def test_gemm_k_limit_is_enforced(fn, bits):
+    # the largest K passes the checks (M == 0: nothing is launched), the next
+    # multiple of 64 is refused before any launch
+    L = Z.lib()
+    f = getattr(L, fn)
+    k = _header_define("ZQ_MAX_GEMM_K_W8" if bits == 8 else "ZQ_MAX_GEMM_K_W4")
+    assert f(None, None, B, C, 64, None, 0, 0, 64, k, None, None) == OK
+    assert f(A, B, B, C, 64, None, 0, 16, 64, k + 64, E, None) == EUNSUP
+    assert "int32" in Z.lib().zq_last_error().decode()
 
 
 def test_gemm_plan_covers_every_regime():

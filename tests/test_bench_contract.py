@@ -1,7 +1,8 @@
 """CPU checks of bench.py's contract: it refuses more than one GPU before
 touching any device, and its algorithmic byte counts (the numerators of the
 roofline's achieved rate) follow the per-launch formulas of the design:
-GEMM  MK + NK*bits/8 + 4N/G + 4M + 2N + 2MN,  quantizer  2MK + MK + 4M."""
+GEMM  MK + NK*bits/8 + 4N/G + 4M + 2N + 2MN,  quantizer  2MK + MK + 4M
+(+ 4K of gamma and beta for a LayerNorm row)."""
 import os
 import subprocess
 import sys
@@ -45,3 +46,18 @@ def test_gemm_bytes_formula():
 
 def test_quant_bytes_formula():
     assert bench.quant_bytes(4096, 768) == 2 * 4096 * 768 + 4096 * 768 + 4 * 4096
+    assert bench.quant_bytes(2048, 6144, ln=True) == (2 * 2048 * 6144 + 2048 * 6144
+                                                      + 4 * 2048 + 4 * 6144)
+
+
+def test_default_workload_is_the_largest_single_gpu_config():
+    # the headline step is GPT-NeoX-20B at 2048 tokens: four linears, INT4
+    # feed-forward weights, and the largest integer work of the five
+    from int4_quantized_transformer_amd import workloads as W
+    wl = W.workload("neox-20b")
+    ops = {w.name: sum(2 * max(w.M) * L.N * L.K for L in w.linears)
+           for w in W.WORKLOADS}
+    assert max(ops, key=ops.get) == "neox-20b"
+    assert max(wl.M) == 2048
+    import inspect
+    assert 'default="neox-20b"' in inspect.getsource(bench.parse)

@@ -6,6 +6,12 @@ with its tuner (zq_gemm_tune).
   parity tests), and every graph replay gives bit for bit what the eager
   launches give, over several token counts of one chain, with the inputs
   changed and other work run between replays.
+* Every eager and graph output of the BERT-base, BERT-large (W4 FFN) and
+  GPT-J decode chains, and the GEMMs after tuning, against the oracle's
+  linears computed from the same CPU inputs: codes within 1 after LN,
+  y within 1 fp16 ulp + 1e-3 (widened by the derived bound in rows where
+  LN moved a code), and FFN2's codes equal to the token quantizer applied
+  to FFN1's own fp16 output.
 * Tuning changes plans, never results: the GEMM's bits are the same before
   and after, and chains re-capture their graphs once the table changes.
 """
@@ -16,7 +22,8 @@ import torch
 import int4_quantized_transformer_amd as zq
 from int4_quantized_transformer_amd import workloads as W
 
-from _util import dev, needs_gpu, to_np
+import oracle
+from _util import assert_linear_matches_oracle, dev, needs_gpu, to_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -277,3 +284,119 @@ def test_chain_with_workspace_gemms_at_decode_sizes():
             ref = to_np(plain(qx[:M], sx[:M], qw, sw, 128, b, 0))
             assert np.array_equal(g.view(np.uint16), ref.view(np.uint16)), (M, N, K)
             assert np.array_equal(to_np(y[:M]).view(np.uint16), ref.view(np.uint16))
+
+
+class OracleLayer:
+    """The oracle's four linears of a layer chain, from the chain's CPU-side
+    inputs (the seeded activations and the workload's fp16 weights; nothing
+    the HIP path computed)."""
+
+    def __init__(self, wl, B):
+        self.wl = wl
+        self.x = to_np(B["x"])
+        self.ctx = to_np(B["ctx"])
+        self.h1 = to_np(B["h1"])
+        self.gamma = to_np(B["gamma"])
+        self.beta = to_np(B["beta"])
+        self.w = []
+        for i, L in enumerate(wl.linears):
+            w, b = W.gen_weights(wl, i)
+            q, sw = oracle.quantize_weights(w.numpy(), wl.G, L.bits)
+            self.w.append((q, sw, b.numpy()))
+        self.cache = {}
+
+    def at(self, M):
+        if M not in self.cache:
+            wl, G = self.wl, self.wl.G
+            (q0, s0, b0), (q1, s1, b1), (q2, s2, b2), (q3, s3, b3) = self.w
+            r = {}
+            r["qkv"] = oracle.linear(self.x[:M], q0, s0, G, b0, 0, ln=True,
+                                     gamma=self.gamma, beta=self.beta,
+                                     eps=wl.ln_eps)
+            r["ao"] = oracle.linear(self.ctx[:M], q1, s1, G, b1, 0)
+            r["ffn1"] = oracle.linear(self.h1[:M], q2, s2, G, b2, 1, ln=True,
+                                      gamma=self.gamma, beta=self.beta,
+                                      eps=wl.ln_eps)
+            r["ffn2"] = oracle.linear(r["ffn1"]["y"], q3, s3, G, b3, 0)
+            self.cache[M] = r
+        return self.cache[M]
+
+    def check(self, out, B, M, what):
+        r = self.at(M)
+        wl, G = self.wl, self.wl.G
+        q = [w[0] for w in self.w]
+        sw = [w[1] for w in self.w]
+        assert_linear_matches_oracle(out["y_qkv"], out["qx0"], out["sx0"],
+                                     r["qkv"], q[0], sw[0], G, 0, True,
+                                     f"{what} qkv M={M}")
+        qx1 = to_np(B["qx1"][:M])
+        sx1 = to_np(B["sx1"][:M])
+        assert_linear_matches_oracle(out["y_ao"], qx1, sx1, r["ao"], q[1],
+                                     sw[1], G, 0, False, f"{what} attn_out M={M}")
+        # FFN1's codes after LN; its fp16 output is quantized for FFN2 and
+        # never leaves the device as y, so FFN2's codes are checked (a) as
+        # codes of an input within the epilogue tolerance of the oracle's
+        # (within 1, in at most 0.1%) and (b) bit-exact against the token
+        # quantizer applied to FFN1's own fp16 output (the workspace)
+        f1 = r["ffn1"]
+        from _util import assert_codes_within_one
+        assert_codes_within_one(out["qx2"], f1["qx"], 1e-3, f"{what} ffn1 codes")
+        assert np.allclose(out["sx2"], f1["sx"], rtol=2e-3, atol=0)
+        N1 = wl.linears[2].N
+        y1 = to_np(B["ws"][: 2 * M * N1].view(torch.float16)).reshape(M, N1)
+        acc1 = oracle.gemm_i32(out["qx2"], q[2])
+        z1, _ = oracle.epilogue(acc1, out["sx2"], sw[2], G, self.w[2][2], 1)
+        from _util import assert_fp16_close_to_oracle
+        assert_fp16_close_to_oracle(y1, z1, f"{what} ffn1 y (own codes) M={M}")
+        q3_own, s3_own = oracle.quant_tokens(y1)
+        assert np.array_equal(out["qx3"], q3_own), f"{what} ffn2 codes M={M}"
+        assert np.array_equal(out["sx3"], s3_own), f"{what} ffn2 scales M={M}"
+        assert_linear_matches_oracle(out["y_out"], out["qx3"], out["sx3"],
+                                     r["ffn2"], q[3], sw[3], G, 0, True,
+                                     f"{what} ffn2 M={M}")
+
+
+@pytest.mark.parametrize("name,max_m,ms", [
+    ("bert-base", 320, (320, 77, 1)),
+    ("bert-large", 192, (192, 17)),          # W4 FFN weights
+    ("gptj-6b", 64, (1, 16, 64)),            # decode kernels
+])
+def test_chain_eager_and_graph_outputs_vs_oracle(name, max_m, ms):
+    wl = W.workload(name)
+    c, B = W.layer_chain(wl, max_m, dev(), seed=13)
+    ref = OracleLayer(wl, B)
+    for M in ms:
+        wipe(B)
+        c.run_eager(M)
+        ref.check(snap(B, M), B, M, f"{name} eager")
+        wipe(B)
+        c.run(M)
+        ref.check(snap(B, M), B, M, f"{name} graph")
+        c.run(M)             # a second replay of the held graph
+        ref.check(snap(B, M), B, M, f"{name} graph replay")
+    c.close()
+
+
+@pytest.mark.parametrize("name,ms", [("bert-base", (16, 128, 320)),
+                                     ("gptj-6b", (1, 16, 64))])
+def test_tuned_chain_vs_oracle(name, ms):
+    wl = W.workload(name)
+    c, B = W.layer_chain(wl, max(ms), dev(), seed=17)
+    ref = OracleLayer(wl, B)
+    yq = B["ws"].view(torch.float16)
+    for i, L in enumerate(wl.linears):
+        y = {0: B["y_qkv"], 1: B["y_ao"], 3: B["y_out"]}.get(i)
+        if y is None:
+            y = yq[: max(ms) * L.N].view(max(ms), L.N)
+        zq.gemm_tune(B[f"qx{i}"], B[f"sx{i}"], B[f"qw{i}"], B[f"sw{i}"], wl.G,
+                     ms, bias=B[f"b{i}"],
+                     act=zq.ACT_GELU if L.gelu else zq.ACT_NONE, y=y, reps=3)
+    assert zq.sched_entries() == 4 * len(ms)
+    for M in ms:
+        wipe(B)
+        c.run(M)
+        ref.check(snap(B, M), B, M, f"{name} tuned graph")
+        wipe(B)
+        c.run_eager(M)
+        ref.check(snap(B, M), B, M, f"{name} tuned eager")
+    c.close()

@@ -218,22 +218,26 @@ def test_linear_epilogue_is_correctly_rounded(M, bits):
         (zq.gemm_plan(M, N, K, bits), int((got != ref).sum()))
 
 
-@pytest.mark.parametrize("bits,K", [(8, 133120), (4, 150912)])
+@pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("M", [1, 16, 40, 100])
-def test_gemm_at_the_int32_bound(bits, K, M):
-    # every code at its extreme: |acc| = 127 * qmax * K, within 2^31 by less
-    # than 0.05% for W8 (and 16 * acc for the W4 path); token signs and
-    # weight-row signs vary so both bounds are reached
-    assert K <= (133144 if bits == 8 else 150976) and K % 64 == 0
-    qmax = 127 if bits == 8 else 7
+def test_gemm_at_the_int32_bound(bits, M):
+    # K = ZQ_MAX_GEMM_K_W8/W4 = 131008 with every code at its two's-complement
+    # extreme (-128 for int8 activations and W8 weights, -8 for nibbles):
+    # the W8 sum reaches 128 * 128 * K and the W4 path's 16 * acc reaches
+    # 16 * 8 * 128 * K, both within 2^31 - 1 by 0.05%.  Token signs and
+    # weight-row signs vary so both the largest positive and the largest
+    # negative sums occur.
+    K = 131008
+    assert K * 16384 <= 2 ** 31 - 1 < (K + 64) * 16384
+    lo, hi = (-128, 127) if bits == 8 else (-8, 7)
     N, G = 64, 32
-    ts = np.where(np.arange(M) % 2 == 0, 1, -1).astype(np.int8)
-    rs = np.where((np.arange(N) // 3) % 2 == 0, 1, -1).astype(np.int8)
-    qx = np.repeat((127 * ts)[:, None], K, axis=1).astype(np.int8)
-    q = np.repeat((qmax * rs)[:, None], K, axis=1).astype(np.int8)
+    ts = np.where(np.arange(M) % 2 == 0, -128, 127).astype(np.int8)
+    rs = np.where((np.arange(N) // 3) % 2 == 0, lo, hi).astype(np.int8)
+    qx = np.repeat(ts[:, None], K, axis=1).astype(np.int8)
+    q = np.repeat(rs[:, None], K, axis=1).astype(np.int8)
     qw = q if bits == 8 else oracle.pack_w4(q)
     sx = np.full(M, 1e-5, np.float32)
-    sw = np.full(N // G, 1e-4, np.float32)
+    sw = np.full(N // G, 1e-4 if bits == 8 else 1e-3, np.float32)
     d = dev()
     tqx, tqw = torch.from_numpy(qx).to(d), torch.from_numpy(qw).to(d)
     tsx, tsw = torch.from_numpy(sx).to(d), torch.from_numpy(sw).to(d)
@@ -244,8 +248,67 @@ def test_gemm_at_the_int32_bound(bits, K, M):
     y = to_np(fn(tqx, tsx, tqw, tsw, G, None, 0))
     y_ws = to_np(fws(tqx, tsx, tqw, tsw, G, None, 0))
     ref = oracle.gemm_i32(qx, q)
-    assert np.abs(ref.astype(np.int64)).max() == 127 * qmax * K
+    assert np.abs(ref.astype(np.int64)).max() == 128 * (-lo) * K
     assert np.array_equal(acc, ref), zq.gemm_plan(M, N, K, bits)
     z, _ = oracle.epilogue(ref, sx, sw, G, None, 0)
     assert_fp16_close_to_oracle(y, z, zq.gemm_plan(M, N, K, bits))
     assert np.array_equal(y_ws.view(np.uint16), y.view(np.uint16))
+
+
+def _fused_inputs(M, N, K, G, bits, seed):
+    x = W.randn_fp16((M, K), seed=seed, std=1.0)
+    w = W.randn_fp16((N, K), seed=seed + 1, std=0.02)
+    b = W.randn_fp16((N + 1,), seed=seed + 2, std=0.5)
+    qx, sx = oracle.quant_tokens(x.numpy())
+    q, sw = oracle.quantize_weights(w.numpy(), G, bits)
+    qw = q if bits == 8 else oracle.pack_w4(q)
+    return qx, sx, q, qw, sw, b
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_w8_ring_with_32_row_blocks_fused_vs_oracle_and_tiles(act, empty_table):
+    # 16 tokens over 4096 < N <= 8192: the W8 ring of 32-row blocks (two row
+    # fragments per block share the gathered group scales and bias pairs).
+    # Its fp16 output against the oracle, and bit-identical to the same rows
+    # from the tiled kernel (forced through the schedule table).
+    M, N, K, G = 16, 6144, 512, 128
+    qx, sx, q, qw, sw, b = _fused_inputs(M, N, K, G, 8, 4242 + act)
+    assert zq.gemm_plan(M, N, K, 8).startswith("stream BN=32 MX=16")
+    d = dev()
+    args = (torch.from_numpy(qx).to(d), torch.from_numpy(sx).to(d),
+            torch.from_numpy(qw).to(d), torch.from_numpy(sw).to(d), G,
+            b[:N].to(d), act)
+    y = to_np(zq.gemm_w8a8(*args))
+    z, _ = oracle.epilogue(oracle.gemm_i32(qx, q), sx, sw, G, b[:N].numpy(), act)
+    assert_fp16_close_to_oracle(y, z, zq.gemm_plan(M, N, K, 8))
+    zq.sched_import(f"8 {N} {K} 1 64 tiled 22\n")
+    assert zq.gemm_plan(M, N, K, 8).startswith("tiled cfg=22")
+    y_t = to_np(zq.gemm_w8a8(*args))
+    assert np.array_equal(y.view(np.uint16), y_t.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K,bits", [(16, 6144, 512, 8), (16, 4096, 1024, 8),
+                                        (9, 2048, 1024, 4), (1, 1000, 1024, 8),
+                                        (40, 4098, 640, 8), (300, 1000, 640, 8)])
+def test_bias_only_2_byte_aligned(M, N, K, bits):
+    # a bias view that starts 2 bytes into its allocation (b[1:]); the ring
+    # kernels read bias pairs as 4-byte words when they can and per element
+    # otherwise
+    G = 8 if N % 8 == 0 else 2
+    qx, sx, q, qw, sw, b = _fused_inputs(M, N, K, G, bits, 77 * M + N)
+    d = dev()
+    bd = b.to(d)[1:]
+    assert bd.data_ptr() % 4 == 2
+    fn = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    y = to_np(fn(torch.from_numpy(qx).to(d), torch.from_numpy(sx).to(d),
+                 torch.from_numpy(qw).to(d), torch.from_numpy(sw).to(d), G,
+                 bd, 1))
+    z, _ = oracle.epilogue(oracle.gemm_i32(qx, q), sx, sw, G, b[1:].numpy(), 1)
+    assert_fp16_close_to_oracle(y, z, zq.gemm_plan(M, N, K, bits))
+
+
+@pytest.fixture
+def empty_table():
+    zq.sched_clear()
+    yield
+    zq.sched_clear()

@@ -116,3 +116,26 @@ def test_quantize_weights_bit_exact(N, K, G, bits):
         assert np.array_equal(to_np(qw), q_ref)
     else:
         assert np.array_equal(to_np(qw), oracle.pack_w4(q_ref))
+
+
+@pytest.mark.parametrize("M,K", [(40, 768), (3, 4096), (17, 1024)])
+def test_ln_quant_act_with_offset_gamma_beta(M, K):
+    # gamma / beta views that start 2 bytes into their allocations: the
+    # vector path reads them as 16-byte chunks, so such views take the
+    # element-wise path; the result is the same as with aligned copies
+    x = (_x(M, K, seed=5 * M + K) * 2).half()
+    gb = W.randn_fp16((K + 1,), seed=K + 11, std=0.3, mean=1.0)
+    bb = W.randn_fp16((K + 1,), seed=K + 12, std=0.2)
+    d = dev()
+    g_off, b_off = gb.to(d)[1:], bb.to(d)[1:]
+    assert g_off.data_ptr() % 16 == 2 and b_off.data_ptr() % 16 == 2
+    qa, sa, ha = zq.ln_quant_act(x.to(d), g_off, b_off, 1e-5, ln_out=True)
+    h_ref = oracle.layernorm(x.numpy(), gb[1:].numpy(), bb[1:].numpy(), 1e-5)
+    assert_ln_close(to_np(ha), h_ref, "ln_out")
+    q_own, s_own = oracle.quant_tokens(to_np(ha))
+    assert np.array_equal(to_np(qa), q_own)
+    assert np.array_equal(to_np(sa), s_own)
+    qb, sb, hb = zq.ln_quant_act(x.to(d), g_off.clone(), b_off.clone(), 1e-5,
+                                 ln_out=True)
+    torch.cuda.synchronize()
+    assert torch.equal(qa, qb) and torch.equal(sa, sb) and torch.equal(ha, hb)

@@ -120,3 +120,22 @@ def test_w8a16_stream_is_deterministic(M):
     for _ in range(3):
         assert np.array_equal(to_np(zq.gemm_w8a16(*args)).view(np.uint16),
                               y0.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 1024), (1, 2048, 2048), (40, 1024, 512)])
+def test_w8a16_bias_only_2_byte_aligned(M, N, K):
+    # a bias view 2 bytes into its allocation: the ring kernels gather bias
+    # pairs as words, so such a bias takes the tiles; same tolerance
+    G = 128
+    x = W.randn_fp16((M, K), seed=M + N + K, std=1.0)
+    w = W.randn_fp16((N, K), seed=M + N + K + 1, std=0.02)
+    b = W.randn_fp16((N + 1,), seed=M + N + K + 2, std=0.5)
+    q, sw = oracle.quantize_weights(w.numpy(), G, 8)
+    d = dev()
+    bd = b.to(d)[1:]
+    assert bd.data_ptr() % 4 == 2
+    y = zq.gemm_w8a16(x.to(d), torch.from_numpy(q).to(d),
+                      torch.from_numpy(sw).to(d), G, bd, 1)
+    z, _ = oracle.gemm_w8a16(x.numpy(), q, sw, G, b[1:].numpy(), 1)
+    torch.cuda.synchronize()
+    assert_fp16_close_to_oracle(to_np(y), z, zq.gemm_w8a16_plan(M, N, K))
