@@ -751,6 +751,290 @@ gemm_tiled_kernel(GemmArgs p) {
     }
 }
 
+// ============================================================== ping-pong
+// Prefill GEMM with packed W4 weights over wide N (the GPT-NeoX-20B FFN1
+// shape): a persistent kernel, one workgroup per compute unit looping over
+// 256 x 256 tiles, with the operand copies forming one continuous ring
+// across tile boundaries (the next tile's first stages are in flight while
+// a tile's epilogue runs).  The LDS layout and the fragment / MFMA helpers
+// are those of gemm_tiled_kernel.
+//
+// Epilogue operands of each tile (bias of its columns, scales of its tokens,
+// the group scale of each 32-column fragment) travel into one of two LDS
+// buffers with the tile's first stage (before its operand copies, so the
+// wait for that stage covers them); the fp16 (or int32) results are stored
+// straight from registers, each lane writing 4 consecutive outputs of one
+// token.
+template <class C>
+struct PAux {
+  static constexpr int BIAS = C::BN * 2;
+  static constexpr int SX = C::BM * 4;
+  static constexpr int SW = (C::BN / 32) * 4;
+  static constexpr int DW = (BIAS + SX + SW) / 4;          // dwords per tile
+  static constexpr int NCOPY = (DW + 63) / 64;              // wave copies
+  static constexpr int BYTES = NCOPY * 256;
+  static constexpr int LDS = C::S * C::STAGE + 2 * BYTES;
+  static_assert(C::BN % 32 == 0 && LDS <= 160 * 1024, "persistent LDS");
+};
+
+// Tile of logical index L: token tiles vary fastest, so the workgroups of
+// one XCD (contiguous logical slots, see xcd_remap) share weight tiles.
+__device__ __forceinline__ void persist_tile(int L, int tiles_m, int &tm,
+                                             int &tn) {
+  tm = L % tiles_m;
+  tn = L / tiles_m;
+}
+
+template <class C>
+__device__ __forceinline__ void persist_aux_copy(const GemmArgs &p, char *ab,
+                                                 int n0, int m0, int wave,
+                                                 int lane) {
+  using A = PAux<C>;
+  for (int c = wave; c < A::NCOPY; c += C::NWAVES) {
+    const int e = c * 64 + lane;
+    const void *src = p.qw;                    // padding lanes: any dword
+    if (e < A::BIAS / 4) {
+      src = reinterpret_cast<const int *>(p.bias ? (const void *)p.bias
+                                                 : (const void *)p.sx) +
+            (p.bias ? n0 / 2 + e : 0);
+    } else if (e < (A::BIAS + A::SX) / 4) {
+      int t = m0 + e - A::BIAS / 4;
+      t = t < p.M ? t : p.M - 1;
+      src = p.sx + t;
+    } else if (e < A::DW) {
+      const int n = n0 + 32 * (e - (A::BIAS + A::SX) / 4);
+      src = p.sw + n / p.G;
+    }
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(src), ZQ_LPTR(ab + c * 256), 4,
+                                     0, 0);
+  }
+}
+
+template <class C, bool RAW>
+__device__ __forceinline__ void persist_epilogue(
+    const GemmArgs &p, const char *ab, const v16i (&acc)[C::FN][C::FM],
+    int n0, int m0, int wn0, int wm0, int r32, int h) {
+  using A = PAux<C>;
+  const half_t *bias_l = reinterpret_cast<const half_t *>(ab);
+  const float *sx_l = reinterpret_cast<const float *>(ab + A::BIAS);
+  const float *sw_l = reinterpret_cast<const float *>(ab + A::BIAS + A::SX);
+  float swv[C::FN];
+  if constexpr (!RAW) {
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) swv[fn] = sw_l[(wn0 + fn * 32) / 32];
+  }
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int tl = wm0 + fm * 32 + r32;
+    const int t = m0 + tl;
+    const bool tok = t < p.M;
+    float sxt = 0.0f;
+    if constexpr (!RAW) sxt = sx_l[tl];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cl = wn0 + fn * 32 + 8 * q + 4 * h;  // tile column
+        int a[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          a[r] = acc[fn][fm][4 * q + r];
+          if constexpr (C::W4) a[r] >>= 4;
+        }
+        if constexpr (RAW) {
+          int32_t *o = static_cast<int32_t *>(p.out) + (size_t)t * p.N + n0 + cl;
+          if (tok) *reinterpret_cast<v4i *>(o) = v4i{a[0], a[1], a[2], a[3]};
+        } else {
+          const float sc = sxt * swv[fn];
+          half4 bb = {(half_t)0.0f, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
+          if (p.bias) bb = *reinterpret_cast<const half4 *>(bias_l + cl);
+          half4 hv;
+          if (p.act == ZQ_ACT_GELU) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = gelu_half((float)a[r], sc, bb[r]);
+          } else {
+            typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+            const u2 b2 = __builtin_bit_cast(u2, bb);
+            const u2 y2 = {fma_half2((float)a[0], (float)a[1], sc, b2[0]),
+                           fma_half2((float)a[2], (float)a[3], sc, b2[1])};
+            hv = __builtin_bit_cast(half4, y2);
+          }
+          half_t *o = static_cast<half_t *>(p.out) + (size_t)t * p.N + n0 + cl;
+          if (tok) *reinterpret_cast<half4 *>(o) = hv;
+        }
+      }
+    }
+  }
+}
+
+// The two wave groups of a workgroup alternate between memory and compute: in every barrier-delimited slot one group
+// reads a whole stage of operand fragments from LDS into registers (and,
+// for group A, issues the global -> LDS copies of a later stage) while the
+// other group runs that stage's MFMAs back to back from registers.  Waves
+// w and w + 4 share a SIMD and belong to different groups, so each SIMD
+// always has one wave feeding the matrix core.  Block tile 256 x 256; group
+// A owns tokens 0..127 of the tile, group B tokens 128..255; each wave 64
+// outputs x 128 tokens.
+//
+// Slot schedule (g = global stage): slot 2g: A reads stage g and issues
+// the copies of stage g + S - 1 (into the slot of stage g - 1, which both
+// groups have read), B computes stage g - 1; slot 2g + 1: A computes stage
+// g, B reads stage g.  A waits for its copies of stage g + 1 at the end of
+// slot 2g + 1, before the barrier after which both groups may read it.
+template <class C>
+__device__ __forceinline__ void pp_read(const char *ws, int wn0, int wm0,
+                                        int r32, int h, Frag<C> (&f)[C::KS],
+                                        v4i (&raw)[2][C::FN]) {
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s)
+    fetch<C>(ws, ws + C::WBYTES, s, wn0, wm0, r32, h, f[s], raw);
+}
+
+template <class C>
+__device__ __forceinline__ void pp_compute(const Frag<C> (&f)[C::KS],
+                                           const v4i (&raw)[2][C::FN],
+                                           v16i (&acc)[C::FN][C::FM]) {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) mma<C>(f[s], s, raw, acc);
+}
+
+template <class C, bool RAW>
+__global__ void __launch_bounds__(C::NT)
+gemm_pingpong_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  static_assert(C::NWAVES == 8 && C::NWN == 4 && C::NWM == 2, "ping-pong");
+  using A = PAux<C>;
+  __shared__ __attribute__((aligned(1024))) char lds[A::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+  const bool grp_a = wave < 4;
+  const int wn0 = (wave % C::NWN) * C::WN, wm0 = (wave / C::NWN) * C::WM;
+  char *aux = lds + C::S * C::STAGE;
+
+  const int G = (int)gridDim.x;
+  const int ntiles = tiles_m * tiles_n;
+  const int slot = xcd_remap(blockIdx.x, G);
+  const int mine = (ntiles - slot + G - 1) / G;
+  const int KT = p.K / C::KPS;
+  const int total = mine * KT;
+  const int ldw = C::W4 ? p.K / 2 : p.K;
+  const char *W = static_cast<const char *>(p.qw);
+  const char *X = reinterpret_cast<const char *>(p.qx);
+
+  // group A issues every copy of a stage: its own share and that of the
+  // group-B wave on the same SIMD
+  auto issue = [&](int g) {
+    const int i = g / KT, kt = g - i * KT;
+    int tm, tn;
+    persist_tile(slot + i * G, tiles_m, tm, tn);
+    char *dst = lds + (g % C::S) * C::STAGE;
+    if constexpr (!RAW)
+      if (kt == 0) {
+        persist_aux_copy<C>(p, aux + (i & 1) * A::BYTES, tn * C::BN, tm * C::BM,
+                            wave, lane);
+        persist_aux_copy<C>(p, aux + (i & 1) * A::BYTES, tn * C::BN, tm * C::BM,
+                            wave + 4, lane);
+      }
+    issue_stage<C>(p, W, X, ldw, tn * C::BN, tm * C::BM, kt, dst, wave, lane);
+    issue_stage<C>(p, W, X, ldw, tn * C::BN, tm * C::BM, kt, dst, wave + 4,
+                   lane);
+  };
+  constexpr int P2 = 2 * (C::IW + C::IX);  // operand copies per A wave per stage
+
+  v16i acc[C::FN][C::FM];
+  Frag<C> f[C::KS];
+  v4i raw[2][C::FN];
+  auto zero = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) acc[i][j] = v16i{};
+  };
+  auto epilogue = [&](int itile) {
+    int tm, tn;
+    persist_tile(slot + itile * G, tiles_m, tm, tn);
+    persist_epilogue<C, RAW>(p, aux + (itile & 1) * A::BYTES, acc, tn * C::BN,
+                             tm * C::BM, wn0, wm0, r32, h);
+  };
+
+  if (grp_a) {
+    const int npro = total < C::S - 1 ? total : C::S - 1;
+    for (int g = 0; g < npro; ++g) issue(g);
+    // stage 0 landed: at most the later prologue stages outstanding
+    if (npro >= 3) wait_vmcnt<2 * P2>();
+    else if (npro == 2) wait_vmcnt<P2>();
+    else wait_vmcnt<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+
+  if (grp_a) {
+    int g = 0;
+    auto stage = [&](bool last, int itile) {
+      // slot 2g: read stage g, issue stage g + S - 1
+      pp_read<C>(lds + (g % C::S) * C::STAGE, wn0, wm0, r32, h, f, raw);
+      if (g + C::S - 1 < total) issue(g + C::S - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // slot 2g + 1: compute stage g; stage g + 1 must land before the
+      // barrier (outstanding: the stages after it, S - 2 of them at most)
+      pp_compute<C>(f, raw, acc);
+      if (last) epilogue(itile);
+      const int later = min(C::S - 2, total - 2 - g);
+      if (later >= 2) wait_vmcnt<2 * P2>();
+      else if (later == 1) wait_vmcnt<P2>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      ++g;
+    };
+    for (int itile = 0; itile < mine; ++itile) {
+      zero();
+      for (int kt = 0; kt < KT - 1; ++kt) stage(false, itile);
+      stage(true, itile);
+    }
+  } else {
+    int g = 0;
+    auto read = [&]() {
+      // slot 2g + 1: read stage g; the reads complete before the barrier,
+      // after which group A may issue copies into this slot
+      pp_read<C>(lds + (g % C::S) * C::STAGE, wn0, wm0, r32, h, f, raw);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      ++g;
+    };
+    for (int itile = 0; itile < mine; ++itile) {
+      // slot 2g of the tile's first stage: finish the previous tile
+      if (itile > 0) {
+        pp_compute<C>(f, raw, acc);
+        epilogue(itile - 1);
+      }
+      zero();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read();
+      for (int kt = 1; kt < KT; ++kt) {
+        // slot 2g: compute stage g - 1
+        pp_compute<C>(f, raw, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read();
+      }
+    }
+    if (mine > 0) {
+      pp_compute<C>(f, raw, acc);
+      epilogue(mine - 1);
+    }
+  }
+}
+
 // ================================================================= skinny
 // Decode-sized M (<= 64; chosen for odd N, where the streaming rings do not
 // apply, or when forced): the weights are streamed from HBM once, straight
@@ -1566,6 +1850,26 @@ static hipError_t run_tiled(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The ping-pong kernel takes whole tiles: N a multiple of BN, K a multiple
+// of the stage width with at least S stages, and (fused epilogue) group
+// scales constant over each 32-column fragment and a 4-byte-aligned bias
+// (both gathered as words).  Other problems run the same tile shape in
+// gemm_tiled_kernel; the results are the same either way.
+template <class C, bool RAW>
+static hipError_t run_pingpong(const GemmArgs &a, hipStream_t s) {
+  const bool fits = a.N % C::BN == 0 && a.K % C::KPS == 0 &&
+                    a.K / C::KPS >= C::S &&
+                    (RAW || (a.G % 32 == 0 &&
+                             (!a.bias || ((uintptr_t)a.bias & 3) == 0)));
+  if (!fits) return run_tiled<C, RAW>(a, s);
+  const int tiles_m = (a.M + C::BM - 1) / C::BM, tiles_n = a.N / C::BN;
+  const int nt = tiles_m * tiles_n;
+  const int grid = nt < device_cus() ? nt : device_cus();
+  hipLaunchKernelGGL((gemm_pingpong_kernel<C, RAW>), dim3(grid), dim3(C::NT),
+                     0, s, a, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 template <class C, bool RAW>
 static hipError_t run_skinny(const GemmArgs &a, hipStream_t s) {
   const int blocks = (a.N + C::BN - 1) / C::BN;
@@ -1577,6 +1881,8 @@ static hipError_t run_skinny(const GemmArgs &a, hipStream_t s) {
 // Tiled configurations: {BN, BM, WN, WM, stages, stage k-bytes}.
 struct TileCfg {
   int bn, bm, wn, wm, s, kb;
+  int persist;  // 1: gemm_pingpong_kernel (whole tiles only, else
+                // gemm_tiled_kernel with the same tile; see run_pingpong)
 };
 static const TileCfg kTileCfgs[] = {
     {128, 128, 64, 64, 2, 128},    // 0: 4 waves
@@ -1607,6 +1913,9 @@ static const TileCfg kTileCfgs[] = {
     {64, 64, 32, 32, 9, 128},    // 25: 4 waves
     {64, 32, 32, 32, 10, 128},   // 26: 2 waves
     {64, 64, 64, 32, 8, 128},    // 27: 2 waves
+    // persistent ping-pong (two wave groups alternating memory and
+    // compute), 8 waves of 64 outputs x 128 tokens, 3-stage ring: W4 only
+    {256, 256, 64, 128, 3, 128, 1},  // 28
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 
@@ -1640,7 +1949,7 @@ static hipError_t run_tile_cfg(int id, const GemmArgs &a, hipStream_t s) {
     case 25: return run_tiled<Tile<64, 64, 32, 32, 9, W4>, RAW>(a, s);
     case 26: return run_tiled<Tile<64, 32, 32, 32, 10, W4>, RAW>(a, s);
     case 27: return run_tiled<Tile<64, 64, 64, 32, 8, W4>, RAW>(a, s);
-    default: break;
+    case 28: if constexpr (W4) return run_pingpong<Tile<256, 256, 64, 128, 3, W4>, RAW>(a, s); break;
   }
   return run_tiled<Tile<256, 256, 64, 64, 2, W4>, RAW>(a, s);
 }
@@ -1668,6 +1977,7 @@ static int stream_mx(int M) {
 static bool w8_only(int cfg) {
   return (cfg >= 16 && cfg <= 20) || cfg == 23;
 }
+static bool w4_only(int cfg) { return cfg == 28; }
 
 // Whether a plan of this kind / tile applies to a problem.  The tiled
 // kernels take any M and N; the decode kernels have their own limits.
@@ -1677,7 +1987,9 @@ static bool plan_applies(PlanKind kind, int cfg, int M, int N, int K, int bits) 
     case kGemv: return M == 1 && ldw % 1024 == 0;
     case kStream: return M >= 1 && M <= 64 && (N & 1) == 0;
     case kSkinny: return M >= 1 && M <= 64;
-    case kTiled: return cfg >= 0 && cfg < kNumTileCfgs && !(bits == 4 && w8_only(cfg));
+    case kTiled:
+      return cfg >= 0 && cfg < kNumTileCfgs && !(bits == 4 && w8_only(cfg)) &&
+             !(bits == 8 && w4_only(cfg));
   }
   return false;
 }
@@ -1866,6 +2178,12 @@ static Plan choose(int M, int N, int K, int bits) {
     if (tiles <= cus) return Plan{kTiled, 0, c};
   }
   if (bits == 4 && K < 4096) return Plan{kTiled, 0, 0};
+  // packed W4 over wide N with long K (GPT-NeoX-20B FFN1, 2048 x 24576 x
+  // 6144): the persistent ping-pong kernel, 302 us against 311 us for
+  // 192x256 and 326 us for 256x256 tiles (interleaved repeats; NeoX FFN2,
+  // N = 6144, stays faster on 192x256 tiles: 289 against 311 us)
+  if (bits == 4 && N >= 16384 && N % 256 == 0 && K % 128 == 0)
+    return Plan{kTiled, 0, 28};
   return Plan{kTiled, 0, pick(kW8Candidates, M, N)};
 }
 
@@ -2436,10 +2754,18 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
     return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d%s",
                     pl.mf, pl.mf <= 2 ? 4 : 2, bits, (N + 15) / 16, src);
   const TileCfg &c = kTileCfgs[pl.cfg];
+  const int tiles = ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm);
+  const int kps = c.kb;  // k per stage (INT8 activations)
+  if (c.persist && N % c.bn == 0 && K % kps == 0 && K / kps >= c.s)
+    return snprintf(buf, len,
+                    "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d kb=%d W%d "
+                    "tiles=%d %s grid=%d%s",
+                    pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, c.kb, bits, tiles,
+                    "persistent ping-pong",
+                    tiles < device_cus() ? tiles : device_cus(), src);
   return snprintf(buf, len,
                   "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d kb=%d W%d tiles=%d%s",
-                  pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, c.kb, bits,
-                  ((N + c.bn - 1) / c.bn) * ((M + c.bm - 1) / c.bm), src);
+                  pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, c.kb, bits, tiles, src);
 }
 
 }  // namespace zq

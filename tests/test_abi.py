@@ -245,7 +245,8 @@ def test_sched_import_overlap_splits_ranges(empty_table):
     "8 3073 768 1 16 stream 0",     # stream: even N
     "8 3072 768 1 65 skinny 0",     # skinny: at most 64 tokens
     "4 3072 768 1 64 tiled 16",     # W8-only tile for W4
-    "8 3072 768 1 64 tiled 28",     # no such tile
+    "8 3072 768 1 64 tiled 29",     # no such tile
+    "8 3072 768 1 64 tiled 28",     # W4-only tile for W8
     "8 3072 768 0 64 tiled 0",      # M from 1
     "8 3072 768 9 8 tiled 0",       # empty range
     "8 3072 700 1 8 tiled 0",       # K % 64
@@ -415,9 +416,11 @@ def test_chain_ws_gemm_host_side():
     # larger problems: fill x quality among the big tiles
     ((4096, 3072, 768, 8), "tiled cfg=13 "),      # BERT-base FFN1
     ((4096, 2304, 768, 8), "tiled cfg=14 "),      # BERT-base QKV
-    # W4: two-block 128x128 below K = 4096, the W8 picker above
+    # W4: two-block 128x128 below K = 4096; the persistent ping-pong kernel
+    # over N >= 16384 (NeoX FFN1); otherwise the W8 picker (NeoX FFN2)
     ((8192, 4096, 1024, 4), "tiled cfg=0 "),
-    ((2048, 24576, 6144, 4), "tiled cfg=12 "),
+    ((2048, 24576, 6144, 4), "tiled cfg=28 "),
+    ((2048, 6144, 24576, 4), "tiled cfg=13 "),
     # decode-sized token counts
     ((64, 16384, 4096, 8), "tiled cfg=22 "),
     ((64, 4096, 4096, 8), "stream BN=16 MX=64 "),
