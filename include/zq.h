@@ -236,6 +236,33 @@ size_t zq_gemm_workspace_bytes(int M, int N, int K, int bits);
 zq_status zq_gemm_ws_plan(int M, int N, int K, int bits, char *buf, int buflen);
 
 /*
+ * zq_gemm_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): zq_gemm_w8a8_ws (bits = 8) or zq_gemm_w4a8_ws (bits = 4)
+ * with the split-K partial sums in a scratch array that the library holds
+ * in device memory, ZQ_NOALLOC_SCRATCH_BYTES per device, from the first
+ * call on that device until the process ends, instead of a caller
+ * workspace.  No allocation happens in the call.  y is bit-identical to the
+ * _ws call's.
+ *   Arguments as zq_gemm_w8a8 / zq_gemm_w4a8 (qw: int8 [N][K] or packed
+ *   uint8 [N][K/2]), plus bits.
+ * Every call on one GPU shares that GPU's scratch array: calls that overlap
+ * on one GPU (different streams, or threads without ordering) race, and the
+ * array keeps the last call's contents (nothing in it needs to start at
+ * zero: each split writes its whole partial plane before it is read).
+ * Errors: as zq_gemm_w8a8; ZQ_EINVAL (bits not 4 or 8); ZQ_EUNSUPPORTED if
+ * the split would need more than ZQ_NOALLOC_SCRATCH_BYTES (the built-in
+ * splits need at most that: 33..64 tokens over fewer than 128 64x64 tiles,
+ * SK slices x M x N x 4 bytes <= 4 MiB) or the device index is 64 or more;
+ * ZQ_EHIP if the scratch array has no device address.
+ */
+#define ZQ_NOALLOC_SCRATCH_BYTES (4u << 20)
+zq_status zq_gemm_noalloc(int bits, const int8_t *qx, const float *sx,
+                          const void *qw, const float *sw, int G,
+                          const void *bias_fp16, int act, int M, int N, int K,
+                          void *y_fp16, void *stream);
+
+/*
  * zq_calibrate_minmax / zq_quant_act_static -- static per-tensor activation
  * quantization, the prior-PTQ scheme that token-wise scales replace
  * (summary page Sec. 3.4 "Token-wise Activation Quantization"; paper

@@ -20,10 +20,12 @@ __all__ = ["ZQError", "library_path", "lib", "quantize_weights",
            "quant_act_static", "gemm_tune", "sched_export", "sched_import",
            "sched_clear", "sched_entries", "Chain", "gemm_w8a8_ws",
            "gemm_w4a8_ws", "gemm_workspace_bytes", "gemm_ws_plan",
+           "gemm_noalloc", "NOALLOC_SCRATCH_BYTES",
            "ACT_NONE", "ACT_GELU"]
 
 ACT_NONE = 0
 ACT_GELU = 1
+NOALLOC_SCRATCH_BYTES = 4 << 20   # ZQ_NOALLOC_SCRATCH_BYTES
 _STATUS = {0: "ZQ_OK", 1: "ZQ_EINVAL", 2: "ZQ_ESHAPE", 3: "ZQ_EHIP",
            4: "ZQ_EUNSUPPORTED"}
 
@@ -88,6 +90,7 @@ def lib():
             "zq_gemm_w4a8_ws": [P, P, P, P, I, P, I, I, I, I, P, P,
                                 ctypes.c_size_t, P],
             "zq_gemm_ws_plan": [I, I, I, I, ctypes.c_char_p, I],
+            "zq_gemm_noalloc": [I, P, P, P, P, I, P, I, I, I, I, P, P],
             "zq_chain_run_eager": [P, I, P],
         }
         for name, args in sigs.items():
@@ -602,3 +605,24 @@ def gemm_w4a8_ws(qx, sx, qw, sw, G, bias=None, act=ACT_NONE, y=None, ws=None,
                  stream=None):
     return _gemm_ws(lib().zq_gemm_w4a8_ws, 4, qx, sx, qw, sw, G, bias, act, y,
                     ws, stream)
+
+
+def gemm_noalloc(bits, qx, sx, qw, sw, G, bias=None, act=ACT_NONE, y=None,
+                 stream=None):
+    """zq_gemm_noalloc: gemm_w8a8_ws / gemm_w4a8_ws with the library's own
+    per-device scratch array instead of a workspace (the call allocates
+    nothing on the device; y is allocated here when not given)."""
+    _need(qx, "qx", torch.int8, dim=2)
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = torch.empty(M, N, dtype=torch.float16, device=qx.device) if y is None else y
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, qx.device, 2)
+    _need(sx, "sx", torch.float32, qx.device)
+    _need(sw, "sw", torch.float32, qx.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, qx.device)
+    _need(y, "y", torch.float16, qx.device)
+    _check(lib().zq_gemm_noalloc(int(bits), _p(qx), _p(sx), _p(qw), _p(sw), G,
+                                 _p(bias), int(act), M, N, K, _p(y),
+                                 _stream(qx, stream)))
+    return y

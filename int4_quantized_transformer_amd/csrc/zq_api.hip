@@ -3,6 +3,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "zq_internal.h"
 
 namespace zq {
@@ -208,6 +210,37 @@ zq_status row_quant(const void *x, const void *gamma, const void *beta,
                     fn);
 }
 
+// ------------------------------------------------- device-resident scratch
+// The split-K workspace of zq_gemm_noalloc: one array per device, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address; its device address is looked up once per device (with
+// that device current) and only that address is passed to kernels.
+static __device__ __align__(256) char scratch[ZQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices] = {};
+
+static zq_status scratch_for_current_device(void **out, const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ZQ_EUNSUPPORTED, "%s: device %d beyond the %d supported", fn,
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ZQ_EHIP, "%s: no device address for the scratch array: %s",
+                  fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,6 +333,52 @@ zq_status zq_gemm_w4a8_ws(const int8_t *qx, const float *sx, const uint8_t *qw4,
                           size_t ws_bytes, void *stream) {
   return gemm_with_ws(qx, sx, qw4, sw, G, bias_fp16, act, M, N, K, y_fp16, ws,
                       ws_bytes, stream, 4, "zq_gemm_w4a8_ws");
+}
+
+zq_status zq_gemm_noalloc(int bits, const int8_t *qx, const float *sx,
+                          const void *qw, const float *sw, int G,
+                          const void *bias_fp16, int act, int M, int N, int K,
+                          void *y_fp16, void *stream) {
+  const char *fn = "zq_gemm_noalloc";
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (!sw || ((!sx || !y_fp16) && M != 0))
+    return fail(ZQ_EINVAL, "%s: null sx/sw/y", fn);
+  if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(y_fp16, 8) ||
+      (bias_fp16 && !aligned(bias_fp16, 2)))
+    return fail(ZQ_EINVAL, "%s: misaligned sx/sw/y/bias", fn);
+  if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+    return fail(ZQ_EINVAL, "%s: act=%d", fn, act);
+  if (G <= 0 || N % G != 0)
+    return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  if (M == 0) return ok();
+  const size_t need = zq::gemm_ws_bytes(M, N, K, bits);
+  if (need > ZQ_NOALLOC_SCRATCH_BYTES)
+    return fail(ZQ_EUNSUPPORTED,
+                "%s: the split needs %zu bytes of scratch, more than the %u "
+                "the library holds per device",
+                fn, need, (unsigned)ZQ_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_current_device(&ws, fn);
+    if (st != ZQ_OK) return st;
+  }
+  zq::GemmArgs a{};
+  a.qx = qx;
+  a.sx = sx;
+  a.qw = qw;
+  a.sw = sw;
+  a.bias = static_cast<const zq::half_t *>(bias_fp16);
+  a.out = y_fp16;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.act = act;
+  a.bits = bits;
+  a.raw_i32 = false;
+  return hip_status(zq::launch_gemm_ws(a, ws, (hipStream_t)stream), fn);
 }
 
 size_t zq_gemm_workspace_bytes(int M, int N, int K, int bits) {
