@@ -357,11 +357,16 @@ def grid_threads(name, L, M, G, zq):
     """Launch grid (threads) of the kernel behind a step entry, as the
     kernel trace reports it (used to find that launch in rocprofv3 output)."""
     plan = zq.gemm_plan(M, L.N, L.K, L.bits) if ".gemm" in name else ""
+    if plan.startswith("gemv") or plan.startswith("stream"):
+        return int(plan.split("grid=")[1].split()[0]) * 64 * \
+            int(plan.split("NW=")[1].split()[0])
     if plan.startswith("tiled"):
-        tiles = int(plan.split("tiles=")[1].split()[0])
+        # workgroups: one per tile, or (persistent kernel) the grid it reports
+        wgs = int(plan.split("grid=")[1].split()[0]) if "grid=" in plan else \
+            int(plan.split("tiles=")[1].split()[0])
         nt = 64 * (int(plan.split("BN=")[1].split()[0]) // int(plan.split("WN=")[1].split()[0])) \
             * (int(plan.split("BM=")[1].split()[0]) // int(plan.split("WM=")[1].split()[0]))
-        return tiles * nt
+        return wgs * nt
     return None
 
 
@@ -377,17 +382,17 @@ def source_shas():
     return out
 
 
-def traffic_for(path, entry, grid):
-    """HBM bytes per launch of one step entry from committed rocprofv3
-    counter runs, or None if absent, taken on other kernel sources, or on
-    another launch grid."""
+def traffic_for(path, step, entry, grid):
+    """HBM bytes per launch of one step entry ("<workload> M=<tokens>",
+    entry name) from committed rocprofv3 counter runs, or None if absent,
+    taken on other kernel sources, or on another launch grid."""
     try:
         with open(path) as f:
             t = json.load(f)
         shas = source_shas()
     except (OSError, ValueError):
         return None
-    e = t.get("entries", {}).get(entry)
+    e = t.get("steps", {}).get(step, {}).get(entry)
     if not e or t.get("sources") != shas or e.get("grid") != grid:
         return None
     return e.get("hbm_bytes_per_launch")
@@ -406,6 +411,8 @@ def step_entries(zq, wl, M):
         kern = {"tiled": "gemm_tiled_kernel", "stream": "gemm_stream_kernel",
                 "gemv": "gemm_gemv_kernel", "skinny": "gemm_skinny_kernel"}[
                     plan.split()[0]]
+        if "ping-pong" in plan:
+            kern = "gemm_pingpong_kernel"
         out.append({"name": gn, "kernel": kern,
                     "grid": grid_threads(gn, L, M, wl.G, zq),
                     "ops": 2 * M * L.N * L.K,
@@ -832,7 +839,8 @@ def _read_csv(path):
 
 def _short(name):
     for key in ("gemm_tiled_kernel", "gemm_skinny_kernel", "gemm_stream_kernel",
-                "gemm_gemv_kernel", "row_quant_kernel", "weight_quant_kernel"):
+                "gemm_gemv_kernel", "gemm_pingpong_kernel", "row_quant_kernel",
+                "weight_quant_kernel", "splitk_reduce_kernel"):
         if key in name:
             return key
     if "neg_kernel" in name:
@@ -961,19 +969,78 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
                     lines.append(f"| {name} | {cname} | {len(vv)} | {med:.0f} |"
                                  f" {scaled:.0f} | {alg} |")
                     traffic.setdefault(name, {"grid": g})[cname] = scaled
+    mfma_lines(d, gemm_e, lines)
     print("\n".join(lines))
     if traffic_out and traffic:
-        out = {"sources": source_shas(), "workload": wl.name, "tokens": M,
-               "entries": {}}
+        # one file for every profiled step; entries of other steps are kept
+        # when they were taken on the same kernel sources
+        out = {"sources": source_shas(), "steps": {}}
+        try:
+            with open(traffic_out) as f:
+                old = json.load(f)
+            if old.get("sources") == out["sources"]:
+                out["steps"] = old.get("steps", {})
+        except (OSError, ValueError):
+            pass
+        step = out["steps"][f"{wl.name} M={M}"] = {}
         for name, v in traffic.items():
             if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
-                out["entries"][name] = {
+                step[name] = {
                     "grid": v["grid"],
                     "hbm_bytes_per_launch": round(v["FETCH_SIZE"] + v["WRITE_SIZE"]),
                     "fetch_bytes": round(v["FETCH_SIZE"]),
                     "write_bytes": round(v["WRITE_SIZE"])}
         with open(traffic_out, "w") as f:
             json.dump(out, f, indent=1)
+
+
+def mfma_lines(d, gemm_e, lines):
+    """Clock and MFMA utilisation per GEMM entry from a --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE: GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs (clock = GRBM / 8 / kernel duration); the MFMA busy
+    cycles are summed over the 1024 SIMDs (busy = MFMA / 1024 / (GRBM / 8)),
+    i.e. the achieved INT8 rate as a fraction of the peak at the measured
+    clock."""
+    import glob
+    import statistics as st
+    per = {}
+    for cc in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                               recursive=True)):
+        for r in _read_csv(cc):
+            if r["Counter_Name"] not in ("SQ_VALU_MFMA_BUSY_CYCLES",
+                                         "GRBM_GUI_ACTIVE"):
+                continue
+            k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            dd = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+            dd[r["Counter_Name"]] = dd.get(r["Counter_Name"], 0.0) + \
+                float(r["Counter_Value"])
+            dd["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    if not per:
+        return
+    lines.append("")
+    lines.append("MFMA utilisation (per dispatch of a GEMM entry; the dispatches "
+                 "of one kernel and grid split equally by sorted MFMA busy "
+                 "cycles, matched to the entries' ops)")
+    lines.append("| entry | dispatches | median us (under counters) | clock GHz "
+                 "| MFMA busy | INT8 POP/s |")
+    lines.append("|---|---|---|---|---|---|")
+    for (k, g), dd in sorted(per.items()):
+        es = [e for e in gemm_e if e["kernel"] == k and e["grid"] == g]
+        rows = [v for v in dd.values() if "SQ_VALU_MFMA_BUSY_CYCLES" in v
+                and "GRBM_GUI_ACTIVE" in v]
+        if not es or not rows:
+            continue
+        sp = _split([r["SQ_VALU_MFMA_BUSY_CYCLES"] for r in rows], es, "ops")
+        for name, vv in (sp or {}).items():
+            sel = [r for r in rows if r["SQ_VALU_MFMA_BUSY_CYCLES"] in vv]
+            ops = [e["ops"] for e in es if e["name"] == name][0]
+            us = st.median(r["us"] for r in sel)
+            clk = st.median(r["GRBM_GUI_ACTIVE"] / 8 / (r["us"] * 1e3)
+                            for r in sel)
+            busy = st.median(r["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 /
+                             (r["GRBM_GUI_ACTIVE"] / 8) for r in sel)
+            lines.append(f"| {name} | {len(sel)} | {us:.1f} | {clk:.2f} | "
+                         f"{busy:.3f} | {ops / us / 1e9:.2f} |")
 
 
 def copy_calibration(torch, dev):
@@ -1098,7 +1165,8 @@ def main():
     roof["avg_launch_us"] = round(bd[dom] * 1e3, 2)
     roof["algorithmic"] = {"ops": ops, "bytes": nbytes}
     roof["grid_threads"] = grid_threads(dom, Ld, M, wl.G, zq)
-    roof["traffic"] = traffic_for(args.traffic, dom, roof["grid_threads"])
+    roof["traffic"] = traffic_for(args.traffic, f"{wl.name} M={M}", dom,
+                                  roof["grid_threads"])
     roof["timing"] = ("per-launch average from a HIP graph of this launch "
                       "over the rotating sets, events around the replays")
 
@@ -1185,17 +1253,17 @@ def decode_roofline(dec, traffic_path):
     name, e = max(case["per_linear"].items(), key=lambda kv: kv[1]["us"])
     t = e["us"] * 1e-6
     achieved = e["bytes"] / t / 1e9
-    try:
-        with open(traffic_path) as f:
-            tr = json.load(f).get("decode", {}).get(f"neox-20b M=1 {name}")
-        if tr and tr.get("sources") != source_shas():
-            tr = None
-    except (OSError, ValueError):
-        tr = None
+    import int4_quantized_transformer_amd as zq
+    from int4_quantized_transformer_amd import workloads as W
+    wl = W.workload("neox-20b")
+    lin = {L.name: L for L in wl.linears}[name.split()[0]]
+    entry = f"{lin.name}.gemm_w{lin.bits}a8"
+    tr = traffic_for(traffic_path, "neox-20b M=1", entry,
+                     grid_threads(entry, lin, 1, wl.G, zq))
     return {"bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": tr.get("hbm_bytes_per_launch") if tr else None,
+            "traffic": tr,
             "kernel": f"neox-20b M=1 {name} ({e['plan']})",
             "avg_launch_us": e["us"], "algorithmic": {"bytes": e["bytes"]},
             "layer_GB_per_s": case["GB_per_s"],

@@ -2740,15 +2740,24 @@ int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len) {
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
   const Plan pl = choose(M, N, K, bits);
   const char *src = pl.tuned ? " [table]" : "";
-  if (pl.kind == kGemv)
-    return snprintf(buf, len, "gemv NW=4 U=6 W%d rows=%d x_in_lds=%d%s", bits,
-                    N, K <= 32768 ? 1 : 0, src);
+  if (pl.kind == kGemv) {
+    // the launch grid of run_gemv with two blocks per CU
+    int grid = 2 * device_cus();
+    if (grid > N) grid = N;
+    int rpb = (N + grid - 1) / grid;
+    if (rpb > 1024) rpb = 1024;
+    grid = (N + rpb - 1) / rpb;
+    return snprintf(buf, len, "gemv NW=4 U=6 W%d rows=%d x_in_lds=%d grid=%d%s",
+                    bits, N, K <= 32768 ? 1 : 0, grid, src);
+  }
   if (pl.kind == kStream) {
     const int bn = pl.mf > 16 ? ((N + 15) / 16 <= device_cus() ? 16 : 32)
                    : (pl.mf > 1 && forced_stream() == 0 &&
                       (bits == 4 || stream_w8_wide(N))) ? 32 : 16;
-    return snprintf(buf, len, "stream BN=%d MX=%d NW=4 W%d row_blocks=%d%s", bn,
-                    pl.mf, bits, (N + bn - 1) / bn, src);
+    const int nrb = (N + bn - 1) / bn;
+    return snprintf(buf, len, "stream BN=%d MX=%d NW=4 W%d row_blocks=%d grid=%d%s",
+                    bn, pl.mf, bits, nrb, nrb < device_cus() ? nrb : device_cus(),
+                    src);
   }
   if (pl.kind == kSkinny)
     return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d%s",
