@@ -370,7 +370,7 @@ def grid_threads(name, L, M, G, zq):
     return None
 
 
-KERNEL_SOURCES = ("zq_gemm.hip", "zq_quant.hip")
+KERNEL_SOURCES = ("zq_gemm.hip", "zq_quant.hip", "zq_index.h", "zq_internal.h")
 
 
 def source_shas():

@@ -185,58 +185,9 @@ __device__ __forceinline__ void store_quad(const GemmArgs &p, int t, int nb,
 // consecutive rows (one LDS cycle) hit 8 different bank groups:
 //   128-byte rows: slot = chunk ^ ((row >> 1) & 7)
 //    64-byte rows: slot = chunk ^ ((row >> 2) & 3)
-template <int BN_, int BM_, int WN_, int WM_, int S_, bool W4_, int KB_ = 128,
-          bool A16_ = false>
-struct Tile {
-  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, S = S_;
-  static constexpr bool W4 = W4_;
-  // A16: fp16 activations (2 bytes per k) with INT8 weights, on the fp16
-  // MFMA (32x32x16): a stage holds 64 k, rows of 128 activation bytes and 64
-  // weight bytes, and k advances 16 per MFMA k-step
-  static constexpr bool A16 = A16_;
-  static constexpr int KB = KB_, KS = KB_ / 32;     // MFMA k-steps per stage
-  static constexpr int KPS = A16 ? KB / 2 : KB;     // k values per stage
-  static_assert(KB == 128 || (KB == 64 && !W4 && !A16), "stage width");
-  static_assert(!(A16 && W4), "W4 with fp16 activations");
-  static constexpr int NWN = BN / WN, NWM = BM / WM;
-  static constexpr int NWAVES = NWN * NWM, NT = NWAVES * kWave;
-  static constexpr int FN = WN / 32, FM = WM / 32;
-  static constexpr int XROW = KB;                   // activation bytes/row/stage
-  static constexpr int WROW = (W4 || A16) ? KB / 2 : KB;  // weight bytes/row/stage
-  static constexpr int WCPR = WROW / 16, XCPR = XROW / 16;  // chunks per row
-  static constexpr int WRPI = 64 / WCPR, XRPI = 64 / XCPR;  // rows per wave copy
-  static constexpr int WINS = BN / WRPI, XINS = BM / XRPI;  // wave copies/stage
-  // copies per wave (the same for every wave, so that every vmcnt wait is a
-  // constant); when the waves do not divide the copies evenly the last ones
-  // are padding that land in the padded tail of their region, never read
-  static constexpr int IW = (WINS + NWAVES - 1) / NWAVES;
-  static constexpr int IX = (XINS + NWAVES - 1) / NWAVES;
-  static constexpr int WBYTES = IW * NWAVES * 1024;  // weight region (padded)
-  static constexpr int XBYTES = IX * NWAVES * 1024;  // activation region
-  static constexpr int STAGE = WBYTES + XBYTES;
-  // epilogue operands copied into LDS with stage 0: bias of the tile's BN
-  // columns and scales of its BM tokens, each padded to whole 256-byte wave
-  // copies (64 lanes x 4 bytes)
-  static constexpr int AUX_BIAS = ((BN * 2 + 255) / 256) * 256;
-  static constexpr int AUX_SX = ((BM * 4 + 255) / 256) * 256;
-  static constexpr int LDS = S * STAGE + AUX_BIAS + AUX_SX;
-  static_assert(BN % WRPI == 0 && BM % XRPI == 0, "copy split");
-  static_assert(WN % 32 == 0 && WM % 32 == 0 && S >= 2, "tile");
-  static_assert((IW + IX) * (S - 2) < 64, "vmcnt range");
-  static_assert(LDS <= 160 * 1024, "LDS");
-};
 
 __device__ __forceinline__ v16i mfma32_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int sw128(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int sw64(int row) { return (row >> 2) & 3; }
-
-template <int BYTES>
-__device__ __forceinline__ int wswz(int chunk, int row) {
-  if constexpr (BYTES == 128) return chunk ^ sw128(row);
-  else return chunk ^ sw64(row);
 }
 
 template <class C>
@@ -246,29 +197,15 @@ __device__ __forceinline__ void issue_stage(const GemmArgs &p, const char *W,
                                             int wave, int lane) {
 #pragma unroll
   for (int j = 0; j < C::IW; ++j) {
-    const int q = wave * C::IW + j;
-    const int row = q * C::WRPI + lane / C::WCPR;  // >= BN: padding copy
-    const int chunk = wswz<C::WROW>(lane % C::WCPR, row);
-    int n = n0 + (row < C::BN ? row : C::BN - 1);
-    n = n < p.N ? n : p.N - 1;                 // rows past N: never stored
-    int kb = kt * C::WROW + chunk * 16;
-    if (kb >= ldw) kb -= C::WROW / 2;          // K % 128 == 64: unused half
-    __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + (size_t)n * ldw + kb),
-                                     ZQ_LPTR(stage + q * 1024), 16, 0, 0);
+    const CopyAddr c = tile_w_copy<C>(wave * C::IW + j, lane, n0, kt, p.N, ldw);
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + c.goff), ZQ_LPTR(stage + c.lds),
+                                     16, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < C::IX; ++j) {
-    const int q = wave * C::IX + j;
-    const int row = q * C::XRPI + lane / C::XCPR;  // >= BM: padding copy
-    const int chunk = wswz<C::XROW>(lane % C::XCPR, row);
-    int t = m0 + (row < C::BM ? row : C::BM - 1);
-    t = t < p.M ? t : p.M - 1;
-    constexpr int XB = C::A16 ? 2 : 1;         // activation bytes per k
-    int kb = kt * C::XROW + chunk * 16;
-    if (kb >= p.K * XB) kb -= C::XROW / 2;
-    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * p.K * XB + kb),
-                                     ZQ_LPTR(stage + C::WBYTES + q * 1024), 16,
-                                     0, 0);
+    const CopyAddr c = tile_x_copy<C>(wave * C::IX + j, lane, m0, kt, p.M, p.K);
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + c.goff), ZQ_LPTR(stage + c.lds),
+                                     16, 0, 0);
   }
 }
 
@@ -765,25 +702,7 @@ gemm_tiled_kernel(GemmArgs p) {
 // wait for that stage covers them); the fp16 (or int32) results are stored
 // straight from registers, each lane writing 4 consecutive outputs of one
 // token.
-template <class C>
-struct PAux {
-  static constexpr int BIAS = C::BN * 2;
-  static constexpr int SX = C::BM * 4;
-  static constexpr int SW = (C::BN / 32) * 4;
-  static constexpr int DW = (BIAS + SX + SW) / 4;          // dwords per tile
-  static constexpr int NCOPY = (DW + 63) / 64;              // wave copies
-  static constexpr int BYTES = NCOPY * 256;
-  static constexpr int LDS = C::S * C::STAGE + 2 * BYTES;
-  static_assert(C::BN % 32 == 0 && LDS <= 160 * 1024, "persistent LDS");
-};
 
-// Tile of logical index L: token tiles vary fastest, so the workgroups of
-// one XCD (contiguous logical slots, see xcd_remap) share weight tiles.
-__device__ __forceinline__ void persist_tile(int L, int tiles_m, int &tm,
-                                             int &tn) {
-  tm = L % tiles_m;
-  tn = L / tiles_m;
-}
 
 template <class C>
 __device__ __forceinline__ void persist_aux_copy(const GemmArgs &p, char *ab,
@@ -791,20 +710,15 @@ __device__ __forceinline__ void persist_aux_copy(const GemmArgs &p, char *ab,
                                                  int lane) {
   using A = PAux<C>;
   for (int c = wave; c < A::NCOPY; c += C::NWAVES) {
-    const int e = c * 64 + lane;
+    const AuxElem a = persist_aux_elem<C>(c * 64 + lane, n0, m0, p.M, p.G);
     const void *src = p.qw;                    // padding lanes: any dword
-    if (e < A::BIAS / 4) {
-      src = reinterpret_cast<const int *>(p.bias ? (const void *)p.bias
-                                                 : (const void *)p.sx) +
-            (p.bias ? n0 / 2 + e : 0);
-    } else if (e < (A::BIAS + A::SX) / 4) {
-      int t = m0 + e - A::BIAS / 4;
-      t = t < p.M ? t : p.M - 1;
-      src = p.sx + t;
-    } else if (e < A::DW) {
-      const int n = n0 + 32 * (e - (A::BIAS + A::SX) / 4);
-      src = p.sw + n / p.G;
-    }
+    if (a.src == kAuxBias)                     // without a bias: unused
+      src = p.bias ? (const void *)(reinterpret_cast<const int *>(p.bias) + a.index)
+                   : (const void *)p.sx;
+    else if (a.src == kAuxSx)
+      src = p.sx + a.index;
+    else if (a.src == kAuxSw)
+      src = p.sw + a.index;
     __builtin_amdgcn_global_load_lds(ZQ_GPTR(src), ZQ_LPTR(ab + c * 256), 4,
                                      0, 0);
   }
@@ -1213,31 +1127,6 @@ gemm_skinny_kernel(GemmArgs p) {
 // order-free, so each wave writes its own partial fragments and the
 // finishing wave adds them in wave order: the result does not depend on
 // timing.
-template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_, bool A16_ = false>
-struct Stream {
-  static constexpr int FN = FN_, MX = MX_, NW = NW_, CK = CK_, D = D_;
-  static constexpr bool W4 = W4_, A16 = A16_;
-  static_assert(!(W4 && A16), "A16 takes INT8 weights");
-  static constexpr int BN = 16 * FN;
-  static constexpr int MF = (MX + 15) / 16;
-  static constexpr int NT = NW * kWave;
-  static constexpr int XCK = (W4 || A16) ? 2 * CK : CK;
-  static constexpr int SPC = CK / 64;                // k-steps per chunk
-  static constexpr int IW = BN * CK / 1024;          // weight copies
-  static constexpr int IX = (MX * XCK + 1023) / 1024;  // activation copies
-  static constexpr int NAUX = MX + BN + BN / 2;      // aux dwords
-  static constexpr int IA = (NAUX + 63) / 64;        // aux copies
-  static constexpr int P = IW + IX + IA;             // copies per chunk
-  static constexpr int XOFF = IW * 1024, AOFF = (IW + IX) * 1024;
-  static constexpr int SLOT = AOFF + IA * 256;
-  static constexpr int RED = (A16 ? NW : 1) * FN * MF * 1024;  // one half
-  static constexpr int LDS = NW * D * SLOT + 2 * RED;
-  static constexpr int WSW = (CK / 16 < 16 ? CK / 16 : 16) - 1;
-  static constexpr int XSW = (XCK / 16 < 16 ? XCK / 16 : 16) - 1;
-  static_assert(CK % 64 == 0 && (BN * CK) % 1024 == 0, "chunk");
-  static_assert(D >= 2 && (D - 1) * P < 64, "vmcnt range");
-  static_assert(LDS <= 160 * 1024, "LDS");
-};
 
 // Workgroup barrier over LDS traffic that leaves the global->LDS copies in
 // flight: it waits for this wave's DS operations only (a release fence would
@@ -1299,45 +1188,27 @@ __device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
   const int n0 = rb * C::BN;
 #pragma unroll
   for (int q = 0; q < C::IW; ++q) {
-    const int o = q * 1024 + lane * 16;
-    const int row = o / C::CK;
-    const int col = ((o % C::CK) >> 4) ^ (row & C::WSW);
-    int n = n0 + row;
-    n = n < p.N ? n : p.N - 1;
-    int kb = c * C::CK + col * 16;
-    kb = kb < ldw ? kb : ldw - 16;
-    __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + (size_t)n * ldw + kb),
-                                     ZQ_LPTR(slot + q * 1024), 16, 0, 0);
+    const CopyAddr a = stream_w_copy<C>(q, lane, n0, c, p.N, ldw);
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + a.goff), ZQ_LPTR(slot + a.lds),
+                                     16, 0, 0);
   }
   const int xrow = C::A16 ? 2 * p.K : p.K;     // activation row bytes
 #pragma unroll
   for (int q = 0; q < C::IX; ++q) {
-    const int o = q * 1024 + lane * 16;
-    int row = o / C::XCK;
-    row = row < C::MX ? row : C::MX - 1;       // padding lanes: duplicates
-    const int col = ((o % C::XCK) >> 4) ^ (row & C::XSW);
-    const int t = row < p.M ? row : p.M - 1;
-    int kb = c * C::XCK + col * 16;
-    kb = kb < xrow ? kb : xrow - 16;
-    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + (size_t)t * xrow + kb),
-                                     ZQ_LPTR(slot + C::XOFF + q * 1024), 16,
-                                     0, 0);
+    const CopyAddr a = stream_x_copy<C>(q, lane, c, p.M, xrow);
+    __builtin_amdgcn_global_load_lds(ZQ_GPTR(X + a.goff), ZQ_LPTR(slot + a.lds),
+                                     16, 0, 0);
   }
 #pragma unroll
   for (int q = 0; q < C::IA; ++q) {
-    const int e = q * 64 + lane;
-    const void *src = p.qw;                    // any valid dword
-    if (e < C::MX) {
-      if (p.sx) src = p.sx + (e < p.M ? e : p.M - 1);
-    } else if (e < C::MX + C::BN) {
-      int n = n0 + e - C::MX;
-      n = n < p.N ? n : p.N - 1;
-      if (p.sw) src = p.sw + n / p.G;
-    } else if (e < C::NAUX) {
-      int d = n0 / 2 + (e - C::MX - C::BN);    // bias dword: columns 2d, 2d+1
-      const int last = p.N / 2 - 1;            // N is even here
-      d = d < last ? d : last;
-      if (p.bias) src = reinterpret_cast<const int *>(p.bias) + d;
+    const AuxElem a = stream_aux_elem<C>(q * 64 + lane, n0, p.M, p.N, p.G);
+    const void *src = p.qw;                    // padding lanes: any dword
+    if (a.src == kAuxSx) {
+      if (p.sx) src = p.sx + a.index;
+    } else if (a.src == kAuxSw) {
+      if (p.sw) src = p.sw + a.index;
+    } else if (a.src == kAuxBias) {
+      if (p.bias) src = reinterpret_cast<const int *>(p.bias) + a.index;
     }
     __builtin_amdgcn_global_load_lds(ZQ_GPTR(src),
                                      ZQ_LPTR(slot + C::AOFF + q * 256), 4, 0,

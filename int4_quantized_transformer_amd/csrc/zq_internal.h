@@ -8,6 +8,9 @@
 
 #include "zq.h"
 
+#define ZQ_HD __host__ __device__
+#include "zq_index.h"
+
 namespace zq {
 
 typedef _Float16 half_t;
@@ -16,8 +19,6 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-
-constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- reductions
 // Wave-wide all-reduce with DPP lane permutes inside each row of 16 lanes
@@ -203,16 +204,6 @@ __device__ __forceinline__ half_t gelu_half(float a, float s, half_t b) {
   return (half_t)g;
 }
 
-// ------------------------------------------------------------ XCD mapping
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Remap the hardware order so that each XCD receives a contiguous
-// range of logical tile ids; the map is a bijection on [0, total).
-__device__ __forceinline__ int xcd_remap(int pid, int total) {
-  constexpr int X = 8;
-  const int q = total / X, r = total % X;
-  const int x = pid % X, i = pid / X;
-  return (x < r) ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
-}
 
 // Launchers (defined in the .hip files); they return hipSuccess or the
 // error of the launch.  Arguments are already validated.
