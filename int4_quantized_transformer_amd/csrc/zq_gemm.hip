@@ -1181,16 +1181,21 @@ __device__ __forceinline__ void wait_chunks(int later) {
   wait_vmcnt<0>();
 }
 
+// Cache policy of a global -> LDS copy: non-temporal (nt), for bytes read
+// once per launch.
+constexpr int kCopyNT = 2;
+
 template <class C>
 __device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
                                              const char *X, int ldw, int rb,
                                              int c, char *slot, int lane) {
   const int n0 = rb * C::BN;
+  // every weight byte is copied once per launch: non-temporal
 #pragma unroll
   for (int q = 0; q < C::IW; ++q) {
     const CopyAddr a = stream_w_copy<C>(q, lane, n0, c, p.N, ldw);
     __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + a.goff), ZQ_LPTR(slot + a.lds),
-                                     16, 0, 0);
+                                     16, 0, kCopyNT);
   }
   const int xrow = C::A16 ? 2 * p.K : p.K;     // activation row bytes
 #pragma unroll
@@ -1216,9 +1221,12 @@ __device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
   }
 }
 
+// slot: the ring slot of chunk c (weights); xs: the chunk's activation
+// image (in the slot, or resident).
 template <class C>
 __device__ __forceinline__ void stream_compute(const GemmArgs &p,
-                                               const char *slot, int c,
+                                               const char *slot,
+                                               const char *xs, int c,
                                                int r16, int g,
                                                v4i (&acc)[C::FN][C::MF]) {
   const v4i zero = {0, 0, 0, 0};
@@ -1245,7 +1253,7 @@ __device__ __forceinline__ void stream_compute(const GemmArgs &p,
       for (int fm = 0; fm < C::MF; ++fm) {
         int row = fm * 16 + r16;
         row = row < p.M ? row : p.M - 1;
-        const char *xr = slot + C::XOFF + row * C::XCK;
+        const char *xr = xs + row * C::XCK;
         const int cx = 8 * s + 2 * g;
         v4i b0 = ld16(xr + ((cx ^ (row & C::XSW)) << 4));
         v4i b1 = ld16(xr + (((cx + 1) ^ (row & C::XSW)) << 4));
@@ -1269,7 +1277,7 @@ __device__ __forceinline__ void stream_compute(const GemmArgs &p,
       for (int fm = 0; fm < C::MF; ++fm) {
         int row = fm * 16 + r16;
         row = row < p.M ? row : p.M - 1;
-        v4i b = ld16(slot + C::XOFF + row * C::XCK +
+        v4i b = ld16(xs + row * C::XCK +
                      (((4 * s + g) ^ (row & C::XSW)) << 4));
         b = kok ? b : zero;
 #pragma unroll
@@ -1282,7 +1290,7 @@ __device__ __forceinline__ void stream_compute(const GemmArgs &p,
       for (int fm = 0; fm < C::MF; ++fm) {
         int row = fm * 16 + r16;
         row = row < p.M ? row : p.M - 1;
-        const char *xr = slot + C::XOFF + row * C::XCK;
+        const char *xr = xs + row * C::XCK;
         const int cx = 8 * s + 2 * g;
         v4i b0 = ld16(xr + ((cx ^ (row & C::XSW)) << 4));
         v4i b1 = ld16(xr + (((cx + 1) ^ (row & C::XSW)) << 4));
@@ -1309,7 +1317,8 @@ gemm_stream_kernel(GemmArgs p) {
   const char *W = static_cast<const char *>(p.qw);
   const char *X = reinterpret_cast<const char *>(p.qx);
   char *ring = lds + wave * (C::D * C::SLOT);
-  int *red = reinterpret_cast<int *>(lds + C::NW * C::D * C::SLOT);
+  char *xres = lds + C::NW * C::D * C::SLOT + wave * C::XRES;
+  int *red = reinterpret_cast<int *>(lds + C::NW * (C::D * C::SLOT + C::XRES));
 
   const int NRB = (p.N + C::BN - 1) / C::BN;
   const int NC = (ldw + C::CK - 1) / C::CK;            // chunks per row
@@ -1320,6 +1329,24 @@ gemm_stream_kernel(GemmArgs p) {
 
   for (int i = threadIdx.x; i < 2 * C::RED / 4; i += C::NT) red[i] = 0;
   lds_barrier();  // red[] cleared before any copy is issued
+
+  if constexpr (C::XR > 0) {
+    // this wave's activation chunks, once (the launcher guarantees
+    // ncw <= XR); issued before the ring, so the first chunk wait covers
+    // them, and read only by this wave
+    const int xrow = p.K;
+#pragma unroll
+    for (int ic = 0; ic < C::XR; ++ic)
+      if (ic < ncw) {
+#pragma unroll
+        for (int q = 0; q < C::IXC; ++q) {
+          const CopyAddr a = stream_x_copy<C>(q, lane, wave + ic * C::NW, p.M, xrow);
+          __builtin_amdgcn_global_load_lds(
+              ZQ_GPTR(X + a.goff),
+              ZQ_LPTR(xres + ic * C::XCH + (a.lds - C::XOFF)), 16, 0, 0);
+        }
+      }
+  }
 
   // copy cursor: chunk j_issue = (row block index ir, chunk index ic)
   int j_issue = 0, ir = 0, ic = 0;
@@ -1347,7 +1374,9 @@ gemm_stream_kernel(GemmArgs p) {
       if (j_issue < total) issue_next();
       wait_chunks<C>(j_issue - 1 - j);
       __builtin_amdgcn_sched_barrier(0);
-      stream_compute<C>(p, ring + ((unsigned)j % C::D) * C::SLOT,
+      const char *slot = ring + ((unsigned)j % C::D) * C::SLOT;
+      stream_compute<C>(p, slot,
+                        C::XR > 0 ? xres + ci * C::XCH : slot + C::XOFF,
                         wave + ci * C::NW, r16, g, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1845,6 +1874,34 @@ static int stream_mx(int M) {
   return M == 1 ? 1 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
 }
 
+static int forced_xres() {
+  static int v = [] {
+    const char *e = getenv("ZQ_XRES");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
+// Rings of 2 .. 16 token rows with resident activations (XR > 0): chosen
+// when every workgroup takes at least two row blocks (the activations are
+// then copied once instead of once per row block) and a wave's chunks fit
+// the resident region (four waves; row blocks of 16 rows for W8, 32 for
+// W4).  Returns XR, or 0 for the plain ring:
+//   2: K <= 4096, chunks of 512 weight bytes (W4: 256), two ring slots;
+//   6: K <= 6144, chunks of 256 weight bytes (W4: 128), three ring slots.
+// Longer chunks make each copy instruction read longer runs of a weight row
+// (GPT-J-6B FFN1, 16 x 16384 x 4096: 16.7 -> 15.9 us); the deeper ring of
+// the 256-byte chunks gained nothing (5 slots against 3: 13.2 / 13.1 us
+// for 16 x 12288 x 4096).  (ZQ_XRES=0 turns it off, 1 forces it wherever a
+// wave's chunks fit: tuning aids.)
+static int stream_resident(int M, int N, int K, int bits) {
+  if (M < 2 || M > 16 || (N & 1) || forced_xres() == 0 || K > 6144) return 0;
+  const int bn = bits == 4 ? 32 : 16;
+  const int nrb = (N + bn - 1) / bn;
+  if (forced_xres() < 1 && nrb < 2 * device_cus()) return 0;
+  return K <= 4096 ? 2 : 6;
+}
+
 static bool w8_only(int cfg) {
   return (cfg >= 16 && cfg <= 20) || cfg == 23;
 }
@@ -2132,6 +2189,17 @@ static hipError_t run(const Plan &pl, const GemmArgs &a, hipStream_t s) {
         return fn1 ? run_stream<Stream<1, 64, 4, 128, 3, W4>, RAW>(a, s)
                    : run_stream<Stream<2, 64, 4, 64, 3, W4>, RAW>(a, s);
       }
+    }
+    if (forced_stream() == 0) {
+      // resident activations (see stream_resident): the ring holds weights
+      // only, so it runs deeper with the smaller resident region
+      const int xr = stream_resident(a.M, a.N, a.K, a.bits);
+      if (xr == 2)
+        return run_stream<Stream<W4 ? 2 : 1, 16, 4, W4 ? 256 : 512, 2, W4, false, 2>,
+                          RAW>(a, s);
+      if (xr == 6)
+        return run_stream<Stream<W4 ? 2 : 1, 16, 4, W4 ? 128 : 256, 3, W4, false, 6>,
+                          RAW>(a, s);
     }
     // {FN, MX, NW, CK, D}; ZQ_STREAM=<index> picks another ring shape
     // (tuning aid)
@@ -2622,13 +2690,17 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
                     bits, N, K <= 32768 ? 1 : 0, grid, src);
   }
   if (pl.kind == kStream) {
-    const int bn = pl.mf > 16 ? ((N + 15) / 16 <= device_cus() ? 16 : 32)
+    const int xr = pl.mf == 16 && forced_stream() == 0
+                       ? stream_resident(M, N, K, bits) : 0;
+    const int bn = xr ? (bits == 4 ? 32 : 16)
+                   : pl.mf > 16 ? ((N + 15) / 16 <= device_cus() ? 16 : 32)
                    : (pl.mf > 1 && forced_stream() == 0 &&
                       (bits == 4 || stream_w8_wide(N))) ? 32 : 16;
     const int nrb = (N + bn - 1) / bn;
-    return snprintf(buf, len, "stream BN=%d MX=%d NW=4 W%d row_blocks=%d grid=%d%s",
-                    bn, pl.mf, bits, nrb, nrb < device_cus() ? nrb : device_cus(),
-                    src);
+    return snprintf(buf, len,
+                    "stream BN=%d MX=%d NW=4 W%d%s row_blocks=%d grid=%d%s", bn,
+                    pl.mf, bits, xr ? (xr == 2 ? " xres=2" : " xres=6") : "",
+                    nrb, nrb < device_cus() ? nrb : device_cus(), src);
   }
   if (pl.kind == kSkinny)
     return snprintf(buf, len, "skinny BN=16 MF=%d NW=8 U=%d W%d blocks=%d%s",

@@ -191,41 +191,56 @@ ZQ_HD inline void persist_tile(int L, int tiles_m, int &tm, int &tn) {
 // weight rows; each wave streams chunks of CK bytes of every row of a block
 // (and the matching activation bytes of MX token rows) through its own ring
 // of D LDS slots.
-template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_, bool A16_ = false>
+//
+// XR > 0 (resident activations): a wave always takes the same chunks of K
+// (c = wave, wave + NW, ...), so it copies the activation bytes of at most
+// XR such chunks once, into an LDS region of its own, and its ring carries
+// only the weights and the epilogue operands of each row block.
+template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_, bool A16_ = false,
+          int XR_ = 0>
 struct StreamGeom {
   static constexpr int FN = FN_, MX = MX_, NW = NW_, CK = CK_, D = D_;
   static constexpr bool W4 = W4_, A16 = A16_;
+  static constexpr int XR = XR_;
   static constexpr int BN = 16 * FN;
   static constexpr int MF = (MX + 15) / 16;
   static constexpr int NT = NW * kWave;
   static constexpr int XCK = (W4 || A16) ? 2 * CK : CK;
   static constexpr int SPC = CK / 64;                // k-steps per chunk
   static constexpr int IW = BN * CK / 1024;          // weight copies
-  static constexpr int IX = (MX * XCK + 1023) / 1024;  // activation copies
+  static constexpr int IXC = (MX * XCK + 1023) / 1024;  // copies per chunk's activations
+  static constexpr int IX = XR > 0 ? 0 : IXC;        // activation copies per ring slot
   static constexpr int NAUX = MX + BN + BN / 2;      // aux dwords
   static constexpr int IA = (NAUX + 63) / 64;        // aux copies
   static constexpr int P = IW + IX + IA;             // copies per chunk
   static constexpr int XOFF = IW * 1024, AOFF = (IW + IX) * 1024;
   static constexpr int SLOT = AOFF + IA * 256;
+  static constexpr int XCH = IXC * 1024;             // a chunk's activation image
+  static constexpr int XRES = XR * XCH;              // resident region per wave
   static constexpr int RED = (A16 ? NW : 1) * FN * MF * 1024;  // one half
-  static constexpr int LDS = NW * D * SLOT + 2 * RED;
+  static constexpr int LDS = NW * (D * SLOT + XRES) + 2 * RED;
   static constexpr int WSW = (CK / 16 < 16 ? CK / 16 : 16) - 1;
   static constexpr int XSW = (XCK / 16 < 16 ? XCK / 16 : 16) - 1;
   static constexpr bool ok_a16 = !(W4 && A16);
   static constexpr bool ok_chunk = CK % 64 == 0 && (BN * CK) % 1024 == 0;
-  static constexpr bool ok_vmcnt = D >= 2 && (D - 1) * P < 64;
+  // the resident copies are issued before the ring's first chunks (older,
+  // so complete once the first chunk is) and stay below the counter range
+  static constexpr bool ok_vmcnt = D >= 2 && XR * IXC + (D - 1) * P < 64;
   static constexpr bool ok_lds = LDS <= 160 * 1024;
+  static constexpr bool ok_xr = XR == 0 || (!A16 && MX <= 16);
   // whether the configuration is a valid kernel instance (Stream asserts it)
-  static constexpr bool ok = ok_a16 && ok_chunk && ok_vmcnt && ok_lds;
+  static constexpr bool ok = ok_a16 && ok_chunk && ok_vmcnt && ok_lds && ok_xr;
 };
 
-template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_, bool A16_ = false>
-struct Stream : StreamGeom<FN_, MX_, NW_, CK_, D_, W4_, A16_> {
-  using G = StreamGeom<FN_, MX_, NW_, CK_, D_, W4_, A16_>;
+template <int FN_, int MX_, int NW_, int CK_, int D_, bool W4_, bool A16_ = false,
+          int XR_ = 0>
+struct Stream : StreamGeom<FN_, MX_, NW_, CK_, D_, W4_, A16_, XR_> {
+  using G = StreamGeom<FN_, MX_, NW_, CK_, D_, W4_, A16_, XR_>;
   static_assert(G::ok_a16, "A16 takes INT8 weights");
   static_assert(G::ok_chunk, "chunk");
   static_assert(G::ok_vmcnt, "vmcnt range");
   static_assert(G::ok_lds, "LDS");
+  static_assert(G::ok_xr, "resident activations: INT8, at most 16 tokens");
 };
 
 // Weight copy q (of IW per chunk) of chunk c of the row block starting at
@@ -244,8 +259,10 @@ ZQ_HD inline CopyAddr stream_w_copy(int q, int lane, int n0, int c, int N,
   return CopyAddr{(int64_t)n * ldw + kb, q * 1024};
 }
 
-// Activation copy q (of IX per chunk) of chunk c: token rows past MX (the
-// padding of the last copy) and past M re-read a valid row.
+// Activation copy q (of IXC per chunk) of chunk c: token rows past MX (the
+// padding of the last copy) and past M re-read a valid row.  The LDS offset
+// is that of the ring slot; a resident chunk image (XR > 0) places the same
+// bytes at lds - XOFF from its own base.
 template <class C>
 ZQ_HD inline CopyAddr stream_x_copy(int q, int lane, int c, int M, int xrow) {
   const int o = q * 1024 + lane * 16;

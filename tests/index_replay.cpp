@@ -167,6 +167,8 @@ static void check_stream(const char *name, const Shape &sh) {
   const int64_t wbytes = (int64_t)sh.N * ldw, xbytes = (int64_t)sh.M * xrow;
   const int NRB = (sh.N + C::BN - 1) / C::BN;
   const int NC = (ldw + C::CK - 1) / C::CK;
+  // resident activations: launched only when a wave's chunks fit
+  if (C::XR > 0 && (NC + C::NW - 1) / C::NW > C::XR) return;
   for (int rb : sample(NRB))
     for (int c : sample(NC)) {
       const int n0 = rb * C::BN;
@@ -181,16 +183,26 @@ static void check_stream(const char *name, const Shape &sh) {
           img.put(a.lds + 16 * lane, a.goff);
           ++g_checked;
         }
-      for (int q = 0; q < C::IX; ++q)
+      // activations: in the ring slot (XR == 0), or in the chunk's
+      // resident image, copied once per launch (XR > 0), whose slots are
+      // checked here shifted by XOFF so that one image serves both
+      Image ximg(C::XOFF + C::XCH);
+      for (int q = 0; q < C::IXC; ++q)
         for (int lane = 0; lane < kWave; ++lane) {
           const CopyAddr a = stream_x_copy<C>(q, lane, c, sh.M, xrow);
           REQUIRE(a.goff >= 0 && a.goff + 16 <= xbytes && a.goff % 16 == 0,
                   "%s X copy %lld of %lld (M%d N%d K%d c %d)", name,
                   (long long)a.goff, (long long)xbytes, sh.M, sh.N, sh.K, c);
-          REQUIRE(a.lds >= C::XOFF && a.lds + 1024 <= C::AOFF, "%s X lds", name);
-          img.put(a.lds + 16 * lane, a.goff);
+          if (C::XR == 0) {
+            REQUIRE(a.lds >= C::XOFF && a.lds + 1024 <= C::AOFF, "%s X lds", name);
+          } else {
+            REQUIRE(a.lds >= C::XOFF && a.lds - C::XOFF + 1024 <= C::XCH,
+                    "%s resident X lds", name);
+          }
+          ximg.put(a.lds + 16 * lane, a.goff);
           ++g_checked;
         }
+
       // chunks read: weight row r, 16-byte column j of the chunk (inside
       // the row), activation row t < M, column j of its XCK bytes
       for (int r = 0; r < C::BN && n0 + r < sh.N; ++r)
@@ -203,7 +215,7 @@ static void check_stream(const char *name, const Shape &sh) {
         for (int j = 0; j < C::XCK / 16 && c * C::XCK + 16 * j < xrow; ++j) {
           const int slot = C::XOFF / 16 + (t * C::XCK) / 16 + (j ^ (t & C::XSW));
           const int64_t want = (int64_t)t * xrow + c * C::XCK + 16 * j;
-          REQUIRE(img.src[slot] == want, "%s X image t %d j %d c %d", name, t, j, c);
+          REQUIRE(ximg.src[slot] == want, "%s X image t %d j %d c %d", name, t, j, c);
         }
       for (int G : {1, 2, 32, 64, 128}) {
         if (sh.N % G) continue;
@@ -228,10 +240,11 @@ static void try_tile(const char *name, const Shape &sh) {
     check_tile<Tile<BN, BM, WN, WM, S, W4, KB, A16>, PP>(name, sh);
 }
 
-template <int FN, int MX, int NW, int CK, int D, bool W4, bool A16 = false>
+template <int FN, int MX, int NW, int CK, int D, bool W4, bool A16 = false,
+          int XR = 0>
 static void try_stream(const char *name, const Shape &sh) {
-  if constexpr (StreamGeom<FN, MX, NW, CK, D, W4, A16>::ok)
-    check_stream<Stream<FN, MX, NW, CK, D, W4, A16>>(name, sh);
+  if constexpr (StreamGeom<FN, MX, NW, CK, D, W4, A16, XR>::ok)
+    check_stream<Stream<FN, MX, NW, CK, D, W4, A16, XR>>(name, sh);
 }
 
 #include "index_configs.h"

@@ -46,7 +46,9 @@ def _shapes():
                     (65, 320, 576), (9, 8190, 1088), (64, 4098, 640),
                     (20, 6144, 1088), (48, 200, 4160), (1, 3000, 8192),
                     (33, 4096, 2048), (257, 200, 64), (1000, 4096, 768),
-                    (300, 33280, 384), (7, 64, 24576), (16, 24, 2048)]:
+                    (300, 33280, 384), (7, 64, 24576), (16, 24, 2048),
+                    (9, 8200, 4160), (5, 8194, 64), (7, 16400, 1088),
+                    (12, 16416, 4096), (16, 16384, 256)]:
         for bits in (8, 4):
             shapes.add((M, N, K, bits))
     return sorted(shapes)

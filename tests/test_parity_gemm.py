@@ -312,3 +312,57 @@ def empty_table():
     zq.sched_clear()
     yield
     zq.sched_clear()
+
+
+# Rings of 2 .. 16 token rows with resident activations: every workgroup
+# takes at least two row blocks, so each wave copies the activations of its
+# K-chunks once.  Shapes: both resident variants (2 chunks of 512 weight
+# bytes per wave, 6 of 256), a partial last chunk (K % 512 or K % 256 != 0
+# for W8, half chunks for W4), waves without chunks (K of one or two
+# chunks), ragged last row block, M < 16.
+RESIDENT = [  # (M, N, K, bits, chunks per wave held)
+    (16, 8192, 4096, 8, 2), (9, 8200, 4160, 8, 6), (2, 12288, 6144, 8, 6),
+    (16, 8192, 512, 8, 2), (5, 8194, 64, 8, 2), (3, 8192, 1600, 8, 2),
+    (16, 16384, 6144, 4, 6), (7, 16400, 1088, 4, 2), (16, 16384, 256, 4, 2),
+    (12, 16416, 4096, 4, 2), (8, 16384, 4224, 4, 6)]
+
+
+@pytest.mark.parametrize("M,N,K,bits,xr", RESIDENT)
+def test_resident_ring_i32_bit_exact(M, N, K, bits, xr):
+    plan = zq.gemm_plan(M, N, K, bits)
+    assert plan.startswith("stream") and f"xres={xr}" in plan, plan
+    qx = _codes((M, K), -127, 127, M * 3 + K + bits)
+    if bits == 8:
+        q = _codes((N, K), -127, 127, N + 5 * K)
+        qw = q
+        fn = zq.gemm_w8a8_i32
+    else:
+        q = _codes((N, K), -8, 7, N + 9 * K)
+        qw = oracle.pack_w4(q)
+        fn = zq.gemm_w4a8_i32
+    acc = fn(torch.from_numpy(qx).to(dev()), torch.from_numpy(qw).to(dev()))
+    ref = oracle.gemm_i32(qx, q)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(acc), ref), plan
+
+
+@pytest.mark.parametrize("M,N,K,bits", [(16, 8192, 4160, 8), (11, 16384, 2048, 4)])
+@pytest.mark.parametrize("act", [0, 1])
+def test_resident_ring_fused_vs_oracle_and_tiles(M, N, K, bits, act, empty_table):
+    # the fused epilogue of the resident ring against the oracle, and bit
+    # for bit the rows the tiled kernel gives (forced through the table)
+    G = 128
+    qx, sx, q, qw, sw, b = _fused_inputs(M, N, K, G, bits, 31 * M + K + act)
+    assert "xres=" in zq.gemm_plan(M, N, K, bits)
+    d = dev()
+    fn = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    args = (torch.from_numpy(qx).to(d), torch.from_numpy(sx).to(d),
+            torch.from_numpy(qw).to(d), torch.from_numpy(sw).to(d), G,
+            b[:N].to(d), act)
+    y = to_np(fn(*args))
+    z, _ = oracle.epilogue(oracle.gemm_i32(qx, q), sx, sw, G, b[:N].numpy(), act)
+    assert_fp16_close_to_oracle(y, z, zq.gemm_plan(M, N, K, bits))
+    zq.sched_import(f"{bits} {N} {K} 1 64 tiled 22\n")
+    assert zq.gemm_plan(M, N, K, bits).startswith("tiled cfg=22")
+    y_t = to_np(fn(*args))
+    assert np.array_equal(y.view(np.uint16), y_t.view(np.uint16))
