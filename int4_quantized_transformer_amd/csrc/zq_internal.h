@@ -143,6 +143,49 @@ __device__ __forceinline__ v2i quant8_pack(const float (&v)[8],
   return r;
 }
 
+// quant8_pack for values whose scale comes from their own row: amax is the
+// max |v| over a set of values that includes these eight.  Same codes as
+// quant8_pack, with fewer instructions:
+//  * no clamp: |v| <= amax gives |v * r| <= 127 (1 + 2^-24)^2 < 127.5 (S
+//    and r each round with relative error <= 2^-24), and likewise
+//    |fl(v / S)| < 127.5, so every code is in [-127, 127] already;
+//  * one rounding step: t = fma(v, r, 1.5 * 2^23) is 1.5 * 2^23 + RNE(v r)
+//    of the exact product v r (|v r| < 2^22, so t's unit is 1), its low
+//    byte is that integer in two's complement, and f = t - 1.5 * 2^23 is
+//    the integer exactly.  RNE(v r) and quant8_pack's rint(fl(v r)) can
+//    differ only if v r lies within |v r| 2^-24 <= 7.6e-6 of a
+//    half-integer; then d = fma(v, r, -f) (v r - f, rounded once) has
+//    |d| > 0.5 - 2^-15 and the eight values are redone with the IEEE
+//    division, the same test and fallback as quant8_pack's (whose own
+//    margin, 2.3e-5, the same threshold covers).
+__device__ __forceinline__ v2i quant8_pack_rowmax(const float (&v)[8],
+                                                  const Quantizer &z) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  float t[8];
+  float dm = 0.0f;  // max |d| of the eight (one compare instead of eight)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    t[i] = __builtin_fmaf(v[i], z.r, kMagic);  // S == 0: r == 0, code 0
+    const float d = __builtin_fmaf(v[i], z.r, -(t[i] - kMagic));
+    dm = fmaxf(dm, fabsf(d));
+  }
+  if (dm >= 0.499969482421875f) {  // 0.5 - 2^-15
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = __builtin_rintf(v[i] / z.s) + kMagic;
+  }
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_bit_cast(uint32_t, t[i]);
+  v2i r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = __builtin_amdgcn_perm(c[4 * h + 1], c[4 * h], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(c[4 * h + 3], c[4 * h + 2], 0x0c0c0400u);
+    r[h] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  return r;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) |
          ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);
@@ -186,6 +229,19 @@ __device__ __forceinline__ uint32_t fma_half2(float a0, float a1, float s,
       "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
       : "=&v"(r)
       : "v"(a0), "v"(a1), "v"(s), "v"(bb));
+  return r;
+}
+
+// LayerNorm's affine step for two values: fp16(a_i * g_i + b_i) rounded
+// once from the exact value, with g and b read as fp16 pairs (low: value 0,
+// high: value 1) straight from their registers.
+__device__ __forceinline__ uint32_t fma_half2_h(float a0, float a1, uint32_t gg,
+                                                uint32_t bb) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+      : "=&v"(r)
+      : "v"(a0), "v"(a1), "v"(gg), "v"(bb));
   return r;
 }
 

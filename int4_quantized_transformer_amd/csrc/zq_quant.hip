@@ -70,65 +70,22 @@ __device__ __forceinline__ float team_max(float v, float *lds) {
   return v;
 }
 
-template <int TPR, int NCH, bool LN, bool VEC>
-__global__ void __launch_bounds__(RowTeam<TPR>::kBlock)
-row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
-                 const half_t *__restrict__ beta, float eps, int M, int K,
-                 int8_t *__restrict__ qx, float *__restrict__ sx,
-                 half_t *__restrict__ ln_out) {
-  using T = RowTeam<TPR>;
-  __shared__ float red[TPR > kWave ? TPR / kWave : 1];
-  const int team = threadIdx.x / TPR;
-  const int tl = threadIdx.x % TPR;
-  const int row = blockIdx.x * T::kRows + team;
-  // A row past the end retires its whole team (16 or 32 lanes of a wave, a
-  // wave, or with TPR > 64 the entire block), so every cross-lane step of
-  // a live team reads live lanes only.
-  if (row >= M) return;
-
-  const half_t *xr = x + (size_t)row * K;
-  float v[NCH][8];
-  // VEC: chunk j of this lane is either wholly inside the row or wholly
-  // past its end (K % 8 == 0); such chunks hold zeros
-  bool ok[NCH];
-
-  // every chunk is loaded (past the row end: the row's last chunk) so that
-  // all loads are in flight together, then masked
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = tl + j * TPR;
-    ok[j] = c * 8 < K;
-    if constexpr (VEC) {
-      const int cc = ok[j] ? c : K / 8 - 1;
-      const half8 h = *reinterpret_cast<const half8 *>(xr + cc * 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = ok[j] ? (float)h[i] : 0.0f;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = c * 8 + i;
-        v[j][i] = (k < K) ? (float)xr[k] : 0.0f;
-      }
-    }
-  }
-
-  // LayerNorm weight and bias chunks: requested with the row, so that their
-  // latency overlaps the row's instead of following the two reductions
-  half8 hg[LN && VEC ? NCH : 1], hb[LN && VEC ? NCH : 1];
-  if constexpr (LN && VEC) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tl + j * TPR;
-      const int cc = ok[j] ? c : K / 8 - 1;
-      hg[j] = gamma ? *reinterpret_cast<const half8 *>(gamma + cc * 8)
-                    : half8{1, 1, 1, 1, 1, 1, 1, 1};
-      hb[j] = beta ? *reinterpret_cast<const half8 *>(beta + cc * 8)
-                   : half8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
+// LayerNorm (optional) and the token-wise quantizer of one row held in
+// registers (v, with ok[j] telling which chunks lie inside the row), then
+// the stores: codes, the scale and, when asked, the fp16 LayerNorm output.
+// hg / hb: this lane's gamma / beta chunks (VEC).  FULL: every chunk of
+// every lane lies inside the row (K = 8 NCH TPR), so no chunk is masked.
+template <int TPR, int NCH, bool LN, bool VEC, bool FULL = false>
+__device__ __forceinline__ void row_finish(
+    float (&v)[NCH][8], const bool (&ok)[NCH],
+    const half8 (&hg)[LN && VEC ? NCH : 1], const half8 (&hb)[LN && VEC ? NCH : 1],
+    const half_t *__restrict__ gamma, const half_t *__restrict__ beta,
+    float eps, int K, int tl, int row, float *red, int8_t *__restrict__ qx,
+    float *__restrict__ sx, half_t *__restrict__ ln_out) {
+  static_assert(VEC || !FULL, "FULL rows take the vector path");
   if constexpr (LN) {
-    // mean and biased variance (two passes over the registers, fp32)
+    // mean and biased variance (two passes over the registers, fp32); the
+    // centred values v - mean replace v
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -142,51 +99,54 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
       if constexpr (VEC) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float d = v[j][i] - mean;
-          cs = fmaf(d, d, cs);
+          v[j][i] -= mean;
+          cs = fmaf(v[j][i], v[j][i], cs);
         }
-        ss += ok[j] ? cs : 0.0f;
+        ss += (FULL || ok[j]) ? cs : 0.0f;
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int k = (tl + j * TPR) * 8 + i;
-          const float d = v[j][i] - mean;
-          cs += (k < K) ? d * d : 0.0f;
+          v[j][i] -= mean;
+          cs += (k < K) ? v[j][i] * v[j][i] : 0.0f;
         }
         ss += cs;
       }
     }
     const float var = team_sum<TPR>(ss, red) / (float)K;
     const float rstd = 1.0f / sqrtf(var + eps);
+    // y = (x - mean) rstd gamma + beta, rounded once to the fp16 value the
+    // LayerNorm emits (the quantizer takes that value)
+    half8 hy[VEC ? NCH : 1];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = tl + j * TPR;
-      if (!ok[j]) {
+      if (!FULL && !ok[j]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[j][i] = 0.0f;
         continue;
       }
-      float g[8], b[8];
       if constexpr (VEC) {
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        const u4 gw = __builtin_bit_cast(u4, hg[j]);
+        const u4 bw = __builtin_bit_cast(u4, hb[j]);
+        u4 yw;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          g[i] = (float)hg[j][i];
-          b[i] = (float)hb[j][i];
-        }
+        for (int q = 0; q < 4; ++q)
+          yw[q] = fma_half2_h(v[j][2 * q] * rstd, v[j][2 * q + 1] * rstd, gw[q],
+                              bw[q]);
+        hy[j] = __builtin_bit_cast(half8, yw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][i] = (float)hy[j][i];
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int k = c * 8 + i;
-          g[i] = (gamma && k < K) ? (float)gamma[k] : 1.0f;
-          b[i] = (beta && k < K) ? (float)beta[k] : 0.0f;
+          const float g = (gamma && k < K) ? (float)gamma[k] : 1.0f;
+          const float b = (beta && k < K) ? (float)beta[k] : 0.0f;
+          const float h = (float)(half_t)fmaf(v[j][i] * rstd, g, b);
+          v[j][i] = k < K ? h : 0.0f;
         }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = c * 8 + i;
-        // round to the fp16 value that the unfused LayerNorm would emit
-        const float h = (float)(half_t)((v[j][i] - mean) * rstd * g[i] + b[i]);
-        v[j][i] = (VEC || k < K) ? h : 0.0f;
       }
     }
     if (ln_out) {
@@ -195,12 +155,7 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
       for (int j = 0; j < NCH; ++j) {
         const int c = tl + j * TPR;
         if constexpr (VEC) {
-          if (ok[j]) {
-            half8 h;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = (half_t)v[j][i];
-            *reinterpret_cast<half8 *>(lr + c * 8) = h;
-          }
+          if (FULL || ok[j]) *reinterpret_cast<half8 *>(lr + c * 8) = hy[j];
         } else {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
@@ -225,14 +180,88 @@ row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
   for (int j = 0; j < NCH; ++j) {
     const int c = tl + j * TPR;
     if constexpr (VEC) {
-      const v2i p = quant8_pack(v[j], qz);
-      if (ok[j]) *reinterpret_cast<v2i *>(qr + c * 8) = p;
+      // amax is the max |v| of this row: the codes need no clamp
+      const v2i p = quant8_pack_rowmax(v[j], qz);
+      if (FULL || ok[j]) *reinterpret_cast<v2i *>(qr + c * 8) = p;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (c * 8 + i < K) qr[c * 8 + i] = (int8_t)quant_code(v[j][i], qz);
     }
   }
+}
+
+// Load one row (chunk j of this lane: k = 8 (tl + j TPR) .. + 7) into v.
+template <int TPR, int NCH, bool VEC, bool FULL>
+__device__ __forceinline__ void row_load(const half_t *__restrict__ x, int K,
+                                         int tl, int row, float (&v)[NCH][8],
+                                         bool (&ok)[NCH]) {
+  const half_t *xr = x + (size_t)row * K;
+  // VEC: chunk j of this lane is either wholly inside the row or wholly
+  // past its end (K % 8 == 0); such chunks hold zeros
+  // every chunk is loaded (past the row end: the row's last chunk) so that
+  // all loads are in flight together, then masked
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tl + j * TPR;
+    ok[j] = FULL || c * 8 < K;
+    if constexpr (VEC) {
+      const int cc = ok[j] ? c : K / 8 - 1;
+      const half8 h = *reinterpret_cast<const half8 *>(xr + cc * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] = ok[j] ? (float)h[i] : 0.0f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = c * 8 + i;
+        v[j][i] = (k < K) ? (float)xr[k] : 0.0f;
+      }
+    }
+  }
+}
+
+// gamma / beta chunks of this lane
+template <int TPR, int NCH>
+__device__ __forceinline__ void row_affine(const half_t *__restrict__ gamma,
+                                           const half_t *__restrict__ beta,
+                                           int K, int tl, half8 (&hg)[NCH],
+                                           half8 (&hb)[NCH]) {
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tl + j * TPR;
+    const int cc = c * 8 < K ? c : K / 8 - 1;
+    hg[j] = gamma ? *reinterpret_cast<const half8 *>(gamma + cc * 8)
+                  : half8{1, 1, 1, 1, 1, 1, 1, 1};
+    hb[j] = beta ? *reinterpret_cast<const half8 *>(beta + cc * 8)
+                 : half8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+template <int TPR, int NCH, bool LN, bool VEC, bool FULL>
+__global__ void __launch_bounds__(RowTeam<TPR>::kBlock)
+row_quant_kernel(const half_t *__restrict__ x, const half_t *__restrict__ gamma,
+                 const half_t *__restrict__ beta, float eps, int M, int K,
+                 int8_t *__restrict__ qx, float *__restrict__ sx,
+                 half_t *__restrict__ ln_out) {
+  using T = RowTeam<TPR>;
+  __shared__ float red[TPR > kWave ? TPR / kWave : 1];
+  const int team = threadIdx.x / TPR;
+  const int tl = threadIdx.x % TPR;
+  const int row = blockIdx.x * T::kRows + team;
+  // A row past the end retires its whole team (16 or 32 lanes of a wave, a
+  // wave, or with TPR > 64 the entire block), so every cross-lane step of
+  // a live team reads live lanes only.
+  if (row >= M) return;
+
+  float v[NCH][8];
+  bool ok[NCH];
+  row_load<TPR, NCH, VEC, FULL>(x, K, tl, row, v, ok);
+  // LayerNorm weight and bias chunks: requested with the row, so that their
+  // latency overlaps the row's instead of following the two reductions
+  half8 hg[LN && VEC ? NCH : 1], hb[LN && VEC ? NCH : 1];
+  if constexpr (LN && VEC) row_affine<TPR, NCH>(gamma, beta, K, tl, hg, hb);
+  row_finish<TPR, NCH, LN, VEC, FULL>(v, ok, hg, hb, gamma, beta, eps, K, tl,
+                                      row, red, qx, sx, ln_out);
 }
 
 template <int TPR, int NCH, bool LN, bool VEC>
@@ -242,9 +271,16 @@ static hipError_t launch_rows(const half_t *x, const half_t *g,
                               hipStream_t s) {
   using T = RowTeam<TPR>;
   const int grid = (M + T::kRows - 1) / T::kRows;
-  hipLaunchKernelGGL((row_quant_kernel<TPR, NCH, LN, VEC>), dim3(grid),
-                     dim3(T::kBlock), 0, s, x, g, b, eps, M, K, qx, sx,
-                     ln_out);
+  // rows that fill every lane's chunks exactly (768 with 16 lanes, 4096 or
+  // 6144 with 256 threads, ...) skip the chunk masks
+  if (VEC && K == 8 * NCH * TPR)
+    hipLaunchKernelGGL((row_quant_kernel<TPR, NCH, LN, VEC, VEC>), dim3(grid),
+                       dim3(T::kBlock), 0, s, x, g, b, eps, M, K, qx, sx,
+                       ln_out);
+  else
+    hipLaunchKernelGGL((row_quant_kernel<TPR, NCH, LN, VEC, false>), dim3(grid),
+                       dim3(T::kBlock), 0, s, x, g, b, eps, M, K, qx, sx,
+                       ln_out);
   return hipGetLastError();
 }
 
