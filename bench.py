@@ -413,12 +413,17 @@ def step_entries(zq, wl, M):
                     plan.split()[0]]
         if "ping-pong" in plan:
             kern = "gemm_pingpong_kernel"
+        ops = 2 * M * L.N * L.K
+        nbytes = gemm_bytes(M, L.N, L.K, L.bits, wl.G)
         out.append({"name": gn, "kernel": kern,
                     "grid": grid_threads(gn, L, M, wl.G, zq),
-                    "ops": 2 * M * L.N * L.K,
-                    "bytes": gemm_bytes(M, L.N, L.K, L.bits, wl.G),
-                    "read_bytes": gemm_bytes(M, L.N, L.K, L.bits, wl.G)
-                    - 2 * M * L.N})
+                    "ops": ops, "bytes": nbytes,
+                    "read_bytes": nbytes - 2 * M * L.N,
+                    # roofline time: what orders the durations of launches
+                    # that share a kernel and grid (ops at prefill, bytes at
+                    # decode)
+                    "roof_s": max(ops / (INT8_PEAK_TOPS * 1e12),
+                                  nbytes / (HBM_PEAK_GBS * 1e9))})
     return out
 
 
@@ -903,12 +908,13 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
         lines.append("")
         lines.append("GEMM step entries (dispatches of one kernel and grid "
                      "split equally by sorted duration, matched to the "
-                     "entries' ops)")
+                     "entries' roofline times max(ops / INT8 peak, bytes / HBM "
+                     "peak))")
         lines.append("| entry | kernel@grid | calls | avg us | median us |")
         lines.append("|---|---|---|---|---|")
         for (k, g, w), v in sorted(groups.items()):
             es = [e for e in gemm_e if e["kernel"] == k and e["grid"] == g]
-            sp = _split(v, es, "ops") if es else None
+            sp = _split(v, es, "roof_s") if es else None
             for name, vv in (sp or {}).items():
                 lines.append(f"| {name} | {k}@{g} | {len(vv)} | "
                              f"{st.mean(vv) / 1e3:.2f} | "
