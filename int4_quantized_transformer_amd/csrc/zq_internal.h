@@ -245,6 +245,17 @@ __device__ __forceinline__ uint32_t fma_half2_h(float a0, float a1, uint32_t gg,
   return r;
 }
 
+// The same for one value: fp16(a * g + b), g and b fp16, rounded once.
+__device__ __forceinline__ half_t fma_half_h(float a, half_t g, half_t b) {
+  const uint32_t gg = __builtin_bit_cast(uint16_t, g);
+  const uint32_t bb = __builtin_bit_cast(uint16_t, b);
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,1,1]"
+      : "=v"(r)
+      : "v"(a), "v"(gg), "v"(bb));
+  return __builtin_bit_cast(half_t, (uint16_t)r);
+}
+
 __device__ __forceinline__ half_t fma_half(float a, float s, half_t b) {
   const uint32_t bb = __builtin_bit_cast(uint16_t, b);
   uint32_t r;

@@ -104,11 +104,13 @@ __device__ __forceinline__ void row_finish(
         }
         ss += (FULL || ok[j]) ? cs : 0.0f;
       } else {
+        // the vector path's arithmetic, element by element (the same bits
+        // whenever K % 8 == 0)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int k = (tl + j * TPR) * 8 + i;
           v[j][i] -= mean;
-          cs += (k < K) ? v[j][i] * v[j][i] : 0.0f;
+          cs = (k < K) ? fmaf(v[j][i], v[j][i], cs) : cs;
         }
         ss += cs;
       }
@@ -142,9 +144,9 @@ __device__ __forceinline__ void row_finish(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int k = c * 8 + i;
-          const float g = (gamma && k < K) ? (float)gamma[k] : 1.0f;
-          const float b = (beta && k < K) ? (float)beta[k] : 0.0f;
-          const float h = (float)(half_t)fmaf(v[j][i] * rstd, g, b);
+          const half_t g = (gamma && k < K) ? gamma[k] : (half_t)1.0f;
+          const half_t b = (beta && k < K) ? beta[k] : (half_t)0.0f;
+          const float h = (float)fma_half_h(v[j][i] * rstd, g, b);
           v[j][i] = k < K ? h : 0.0f;
         }
       }
@@ -289,6 +291,10 @@ static hipError_t dispatch_nch(int nch, const half_t *x, const half_t *g,
                                const half_t *b, float eps, int M, int K,
                                int8_t *qx, float *sx, half_t *ln_out,
                                hipStream_t s) {
+  if constexpr (TPR == 64) {  // one wave per row of up to 6144 elements
+    if (nch > 8)
+      return launch_rows<TPR, 12, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
+  }
   switch (nch) {
     case 1: return launch_rows<TPR, 1, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
     case 2: return launch_rows<TPR, 2, LN, VEC>(x, g, b, eps, M, K, qx, sx, ln_out, s);
@@ -326,8 +332,18 @@ static hipError_t dispatch_tpr(const half_t *x, const half_t *g,
     tpr = next(tpr);
   while (tpr < 1024 && (long)M * tpr < 1024L * 64 && chunks >= 2 * next(tpr))
     tpr = next(tpr);
+  // ZQ_ROW_TPR=<16|32|64|256|1024> forces the team size where the row fits
+  // (tuning aid)
+  static const int forced = [] {
+    const char *e = getenv("ZQ_ROW_TPR");
+    return e ? atoi(e) : 0;
+  }();
+  if ((forced == 16 || forced == 32 || forced == 64 || forced == 256 ||
+       forced == 1024) &&
+      (chunks + forced - 1) / forced <= (forced == 64 ? 12 : 8))
+    tpr = forced;
   const int per = (chunks + tpr - 1) / tpr;
-  const int nch = per <= 4 ? per : (per <= 6 ? 6 : 8);
+  const int nch = per <= 4 ? per : (per <= 6 ? 6 : (per <= 8 ? 8 : 12));
   if (tpr == 16) return dispatch_nch<16, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
   if (tpr == 32) return dispatch_nch<32, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
   if (tpr == 64) return dispatch_nch<64, LN, VEC>(nch, x, g, b, eps, M, K, qx, sx, ln_out, s);
