@@ -146,6 +146,25 @@ def build_sets(wl, M, dev, rotate_bytes):
     return base, sets, R, per_set
 
 
+def clone_set(lins, M):
+    """Another rotating set: copies of a set's inputs, weights and scales,
+    and outputs of its own."""
+    import torch
+    out = []
+    for d in lins:
+        s = LinearSet()
+        s.L = d.L
+        s.x, s.qw, s.sw, s.b = d.x.clone(), d.qw.clone(), d.sw.clone(), d.b.clone()
+        s.qx = torch.empty_like(d.qx)
+        s.sx = torch.empty_like(d.sx)
+        s.y = torch.empty_like(d.y)
+        out.append(s)
+    return out
+
+
+ENTRY_MIN_SETS = 8
+
+
 def make_step(zq, lins, wl, M, stream_ptr):
     """Pre-marshalled launches of one step: a list of (name, fn, args)."""
     import ctypes
@@ -331,9 +350,16 @@ def entry_timings(torch, zq, sets, wl, M, steps):
     """Average duration of each step entry's launch: one HIP graph per entry
     holding that launch for every rotating set (so its inputs come from HBM
     as in the step), replayed `steps` times and timed with events around
-    the replays.  Graph launches carry no host gaps, so this is the kernel's
-    own duration plus the small inter-kernel gap of a graph.  Also returns
-    p10 / p50 / p90 of the per-launch time over separately timed replays."""
+    the replays.  The sets are topped up with copies to ENTRY_MIN_SETS, so
+    that a replay's own launch cost is spread over that many launches (with
+    one launch per graph it added about 5 us to each, a third of a
+    quantizer launch); graph launches carry no host gaps, so this is the
+    kernel's own duration plus the small inter-kernel gap of a graph.  Also
+    returns p10 / p50 / p90 of the per-launch time over separately timed
+    replays."""
+    sets = list(sets)
+    while len(sets) < ENTRY_MIN_SETS:
+        sets.append(clone_set(sets[0], M))
     names = [c[0] for c in make_step(zq, sets[0], wl, M, 0)]
     out, pct = {}, {}
     for j, name in enumerate(names):
@@ -1174,7 +1200,8 @@ def main():
     roof["traffic"] = traffic_for(args.traffic, f"{wl.name} M={M}", dom,
                                   roof["grid_threads"])
     roof["timing"] = ("per-launch average from a HIP graph of this launch "
-                      "over the rotating sets, events around the replays")
+                      f"over {max(R, ENTRY_MIN_SETS)} rotating sets, events "
+                      "around the replays")
 
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS",
