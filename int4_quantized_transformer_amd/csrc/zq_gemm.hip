@@ -501,17 +501,15 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs &p, char *lds,
   x.r32 = r32;
   x.h = h;
 
-  // tile order: XCD-contiguous ranges, then groups of 8 token tiles that
-  // share one weight tile
+  // tile order: XCD-contiguous ranges, then groups of 4 token tiles that
+  // share one weight tile (an XCD's 32 concurrent tiles: 8 weight tiles x 4
+  // token tiles, fewer operand bytes into its L2 than 4 x 8 at the prefill
+  // shapes)
   const int tiles_n = (p.N + C::BN - 1) / C::BN;
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
   const int pid = xcd_remap(blockIdx.x, tiles_n * tiles_m);
-  constexpr int GM = 8;
-  const int per_group = GM * tiles_n;
-  const int first_m = (pid / per_group) * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int tm = first_m + (pid % per_group) % gsz;
-  const int tn = (pid % per_group) / gsz;
+  int tm, tn;
+  grouped_tile<kTileGroup>(pid, tiles_m, tiles_n, tm, tn);
   const int n0 = tn * C::BN, m0 = tm * C::BM;
   const int wn0 = (wave % C::NWN) * C::WN, wm0 = (wave / C::NWN) * C::WM;
   x.n0 = n0;
@@ -842,7 +840,7 @@ gemm_pingpong_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   auto issue = [&](int g) {
     const int i = g / KT, kt = g - i * KT;
     int tm, tn;
-    persist_tile(slot + i * G, tiles_m, tm, tn);
+    persist_tile(slot + i * G, tiles_m, tiles_n, tm, tn);
     char *dst = lds + (g % C::S) * C::STAGE;
     if constexpr (!RAW)
       if (kt == 0) {
@@ -868,7 +866,7 @@ gemm_pingpong_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   };
   auto epilogue = [&](int itile) {
     int tm, tn;
-    persist_tile(slot + itile * G, tiles_m, tm, tn);
+    persist_tile(slot + itile * G, tiles_m, tiles_n, tm, tn);
     persist_epilogue<C, RAW>(p, aux + (itile & 1) * A::BYTES, acc, tn * C::BN,
                              tm * C::BM, wn0, wm0, r32, h);
   };

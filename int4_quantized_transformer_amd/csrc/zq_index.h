@@ -178,12 +178,37 @@ ZQ_HD inline AuxElem persist_aux_elem(int e, int n0, int m0, int M, int G) {
   return AuxElem{kAuxPad, 0};
 }
 
-// Tile of logical index L of the persistent kernel: token tiles vary
-// fastest, so the workgroups of one XCD (contiguous logical slots, see
-// xcd_remap) share weight tiles.
-ZQ_HD inline void persist_tile(int L, int tiles_m, int &tm, int &tn) {
-  tm = L % tiles_m;
-  tn = L / tiles_m;
+// Tile of workgroup pid (after xcd_remap) of the tiled kernel: groups of
+// GM token tiles that share one weight tile, token tiles fastest (the last
+// group may be short).
+constexpr int kTileGroup = 4;  // GM of the tiled kernel
+
+template <int GM>
+ZQ_HD inline void grouped_tile(int pid, int tiles_m, int tiles_n, int &tm,
+                               int &tn) {
+  const int per_group = GM * tiles_n;
+  const int first_m = (pid / per_group) * GM;
+  const int gsz = tiles_m - first_m < GM ? tiles_m - first_m : GM;
+  tm = first_m + (pid % per_group) % gsz;
+  tn = (pid % per_group) / gsz;
+}
+
+// Tile of logical index L of the persistent kernel: groups of (at most) 4
+// token tiles, token tiles fastest within a group, then the weight tiles,
+// then the next group.  The 32 workgroups of one XCD (contiguous logical
+// slots, see xcd_remap) then hold 8 weight tiles x 4 token tiles at a time,
+// which is the split of 32 that fetches the fewest operand bytes into the
+// XCD's L2 at the prefill shapes (8 token tiles x 4 weight tiles, the order
+// without groups, re-fetches every activation row in every round).
+ZQ_HD inline void persist_tile(int L, int tiles_m, int tiles_n, int &tm,
+                               int &tn) {
+  constexpr int TG = 4;
+  const int gsize = TG * tiles_n;
+  const int grp = L / gsize, r = L - grp * gsize;
+  const int first = grp * TG;
+  const int gs = tiles_m - first < TG ? tiles_m - first : TG;
+  tm = first + r % gs;
+  tn = r / gs;
 }
 
 // =================================================================== rings

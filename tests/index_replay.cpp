@@ -11,7 +11,9 @@
 //     (rows inside the tile and inside M / N, k inside K) is present in the
 //     LDS stage image, in the swizzled slot that the fragment reads use;
 //   * the epilogue-operand gathers (ring and persistent aux dwords) index
-//     inside sx [M], sw [N / G] and the bias dwords [N / 2].
+//     inside sx [M], sw [N / G] and the bias dwords [N / 2];
+//   * the tiled and persistent kernels' workgroup -> tile maps cover every
+//     tile exactly once.
 // Prints one line per (kernel, configuration) with the copies checked and
 // exits non-zero on the first violation.
 #include <stdint.h>
@@ -125,6 +127,19 @@ static void check_tile(const char *name, const Shape &sh) {
                     c, kt);
           }
       }
+  if (!PINGPONG) {
+    // the tiled kernel's workgroup -> tile map: every tile exactly once
+    const int total = tiles_m * tiles_n;
+    std::vector<int> seen(total, 0);
+    for (int b = 0; b < total; ++b) {
+      int tm, tn;
+      grouped_tile<kTileGroup>(xcd_remap(b, total), tiles_m, tiles_n, tm, tn);
+      REQUIRE(tm >= 0 && tm < tiles_m && tn >= 0 && tn < tiles_n, "%s tile", name);
+      ++seen[tn * tiles_m + tm];
+    }
+    for (int i = 0; i < total; ++i)
+      REQUIRE(seen[i] == 1, "%s tile %d run %d times", name, i, seen[i]);
+  }
   if (PINGPONG) {
     // the persistent aux gathers and the logical tile map (every tile once)
     for (int G : {32, 64, 128}) {
@@ -148,7 +163,7 @@ static void check_tile(const char *name, const Shape &sh) {
       const int slot = xcd_remap(b, grid);
       for (int L = slot; L < total; L += grid) {
         int tm, tn;
-        persist_tile(L, tiles_m, tm, tn);
+        persist_tile(L, tiles_m, tiles_n, tm, tn);
         REQUIRE(tm >= 0 && tm < tiles_m && tn >= 0 && tn < tiles_n, "%s tile", name);
         ++seen[tn * tiles_m + tm];
       }
