@@ -118,7 +118,8 @@ def test_quantize_weights_bit_exact(N, K, G, bits):
         assert np.array_equal(to_np(qw), oracle.pack_w4(q_ref))
 
 
-@pytest.mark.parametrize("M,K", [(40, 768), (3, 4096), (17, 1024)])
+@pytest.mark.parametrize("M,K", [(40, 768), (3, 4096), (17, 1024), (512, 768),
+                                 (256, 4096), (96, 6144)])
 def test_ln_quant_act_with_offset_gamma_beta(M, K):
     # gamma / beta views that start 2 bytes into their allocations: the
     # vector path reads them as 16-byte chunks, so such views take the
