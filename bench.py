@@ -61,6 +61,8 @@ def parse():
                     help="skip the W8A16 (fp16 activation) figure")
     ap.add_argument("--no-static", action="store_true",
                     help="skip the static per-tensor quantization comparator")
+    ap.add_argument("--no-xq", action="store_true",
+                    help="skip the one-token quantize-on-load figure")
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the layer-chain graph / schedule-table figure")
     ap.add_argument("--no-prefill", action="store_true",
@@ -595,6 +597,65 @@ def decode_figure(torch, zq, dev, steps=100, with_fp16=True):
             out[f"{name} M={M}"] = decode_case(torch, zq, dev, name, M, steps,
                                                with_fp16)
             torch.cuda.empty_cache()
+    return out
+
+
+def xq_figure(torch, zq, dev, steps=20):
+    """The linears whose input is not LayerNorm'd (attn-out, FFN2) at one
+    token: the quantizer launch followed by the GEMM against the
+    quantize-on-load call (one kernel: the GEMV quantizes the fp16 row as it
+    stages it), both in one HIP graph over rotating weight sets, the same
+    fp16 input, bias, y, codes and scales."""
+    from int4_quantized_transformer_amd import workloads as W
+    out = {"workload": "GPT-J-6B and GPT-NeoX-20B attn-out and FFN2 at one "
+                       "token; input = the linear's fp16 activation"}
+    stream = torch.cuda.current_stream()
+    saved = 0.0
+    for name in ("gptj-6b", "neox-20b"):
+        wl = W.workload(name)
+        for li, L in enumerate(wl.linears):
+            if L.name not in ("attn_out", "ffn2"):
+                continue
+            w, b = W.gen_weights(wl, li)
+            qw, sw = zq.quantize_weights(w.to(dev), wl.G, L.bits)
+            del w
+            x = W.gen_activations(wl, li, m_index=list(wl.M).index(1)).to(dev)
+            qx, sx = zq.quant_act(x)
+            R = max(2, -(-ROTATE_BYTES // qw.numel()))
+            qws = [qw] + [qw.clone() for _ in range(R - 1)]
+            y = torch.empty(1, L.N, dtype=torch.float16, device=dev)
+            bd = b.to(dev)
+            g8 = zq.gemm_w8a8 if L.bits == 8 else zq.gemm_w4a8
+            gx = zq.gemm_w8a8_xq if L.bits == 8 else zq.gemm_w4a8_xq
+
+            def two():
+                for w_ in qws:
+                    zq.quant_act(x, qx=qx, sx=sx)
+                    g8(qx, sx, w_, sw, wl.G, bd, 0, y=y)
+
+            def one():
+                for w_ in qws:
+                    gx(x, w_, sw, wl.G, bd, 0, y=y, qx=qx, sx=sx)
+
+            us = {}
+            for key, fn in (("quant_then_gemm", two), ("quantize_on_load", one)):
+                fn()
+                torch.cuda.synchronize()
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    fn()
+                ms, _ = timed_graphs(torch, [gr], steps, stream)
+                us[key] = round(ms * 1e3 / R, 2)
+                del gr
+            b_ = gemm_bytes(1, L.N, L.K, L.bits, wl.G)
+            us["GB_per_s_quantize_on_load"] = round(
+                b_ / (us["quantize_on_load"] * 1e-6) / 1e9, 1)
+            us["plan"] = zq.gemm_xq_plan(1, L.N, L.K, L.bits).split(" NW")[0]
+            out[f"{name} {L.name} W{L.bits}"] = us
+            saved += us["quant_then_gemm"] - us["quantize_on_load"]
+            del qws
+            torch.cuda.empty_cache()
+    out["us_saved_total"] = round(saved, 2)
     return out
 
 
@@ -1246,6 +1307,8 @@ def main():
         extras["w8a16"] = w8a16_figure(torch, zq, dev)
     if not args.no_static:
         extras["static_vs_tokenwise"] = static_figure(torch, zq, dev)
+    if not args.no_xq:
+        extras["quant_on_load"] = xq_figure(torch, zq, dev)
     if not args.no_chain:
         extras["layer_chain"] = chain_figure(torch, zq, dev)
     out["extras"] = extras

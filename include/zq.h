@@ -202,6 +202,42 @@ zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
 size_t zq_gemm_quant_workspace_bytes(int M, int N);
 
 /*
+ * zq_gemm_w8a8_xq / zq_gemm_w4a8_xq -- the linear of an fp16 activation
+ * with its token-wise quantization done by the consuming GEMM (the fused
+ * quantization in front of attn-out and FFN2 of Sec. 3.4
+ * "Quantization-Optimized Transformer Kernels", paper App. D, Fig. 2,
+ * taken on the consumer's side).  The result is bit for bit that of
+ * zq_quant_act(x) -> (qx, sx) followed by zq_gemm_w8a8 / _w4a8 on
+ * (qx, sx):
+ *   x   fp16 [M][K] (device, 16-byte aligned): e.g. the fp16 y of the
+ *       previous linear's zq_gemm_w8a8 with its bias and GeLU
+ *   qx  int8 [M][K], sx fp32 [M] (device, caller-owned, 16- and 4-byte
+ *       aligned): receive the codes and scales
+ *   y   fp16 [M][N]; qw/qw4, sw, G, bias, act, M, N, K as zq_gemm_w8a8.
+ * One token (M == 1) where zq_gemm_plan is the GEMV with the activation
+ * row in LDS (K <= 32768): one kernel.  Every block loads the whole fp16
+ * row, takes its max |x| and quantizes it into LDS, so no block needs
+ * another's result, and the quantizer launch with its fp16 read and code
+ * write disappear (block 0 writes qx and sx for the caller).  Elsewhere
+ * the row quantizer runs first and the plan's kernel reads qx and sx: at
+ * many tokens each workgroup of the consumer would have to quantize the
+ * activation tiles it shares with the others again, which costs more than
+ * the launch it saves.  zq_gemm_xq_plan says which form runs.
+ * Errors: as zq_gemm_w8a8, ZQ_EINVAL for a null or misaligned x/qx/sx, and
+ * ZQ_EUNSUPPORTED for K > ZQ_MAX_ROW_K.
+ */
+zq_status zq_gemm_w8a8_xq(const void *x_fp16, const int8_t *qw, const float *sw,
+                          int G, const void *bias_fp16, int act, int M, int N,
+                          int K, void *y_fp16, int8_t *qx, float *sx,
+                          void *stream);
+zq_status zq_gemm_w4a8_xq(const void *x_fp16, const uint8_t *qw4,
+                          const float *sw, int G, const void *bias_fp16,
+                          int act, int M, int N, int K, void *y_fp16,
+                          int8_t *qx, float *sx, void *stream);
+zq_status zq_gemm_xq_plan(int M, int N, int K, int bits, char *buf,
+                          int buflen);
+
+/*
  * zq_gemm_w8a8_ws / zq_gemm_w4a8_ws -- zq_gemm_w8a8 / zq_gemm_w4a8 with a
  * caller workspace, for decode-sized token counts over few weight tiles
  * (the small-batch schedules of the summary page's Sec. 3.4
@@ -440,7 +476,7 @@ const char *zq_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int zq_version(void);
-#define ZQ_VERSION 105
+#define ZQ_VERSION 106
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ or PyTorch implementation: if the library is missing, every call raises.
 __all__ = ["quantize_weights", "ln_quant_act", "quant_act", "gemm_w8a8",
            "gemm_w4a8", "gemm_w8a8_i32", "gemm_w4a8_i32", "gemm_w8a8_quant",
            "gemm_w4a8_quant", "gemm_quant_workspace_bytes", "gemm_plan",
-           "gemm_w8a16", "gemm_w8a16_plan", "calibrate_minmax",
+           "gemm_w8a16", "gemm_w8a16_plan", "gemm_w8a8_xq", "gemm_w4a8_xq",
+           "gemm_xq_plan", "calibrate_minmax",
            "quant_act_static", "gemm_tune", "sched_export", "sched_import",
            "sched_clear", "sched_entries", "Chain", "gemm_w8a8_ws",
            "gemm_w4a8_ws", "gemm_workspace_bytes", "gemm_ws_plan",

@@ -69,6 +69,9 @@ def lib():
                                    ctypes.c_size_t, P],
             "zq_gemm_plan": [I, I, I, I, ctypes.c_char_p, I],
             "zq_gemm_w8a16": [P, P, P, I, P, I, I, I, I, P, P],
+            "zq_gemm_w8a8_xq": [P, P, P, I, P, I, I, I, I, P, P, P, P],
+            "zq_gemm_w4a8_xq": [P, P, P, I, P, I, I, I, I, P, P, P, P],
+            "zq_gemm_xq_plan": [I, I, I, I, ctypes.c_char_p, I],
             "zq_gemm_w8a16_plan": [I, I, I, ctypes.c_char_p, I],
             "zq_calibrate_minmax": [P, I, I, F, I, P, P],
             "zq_quant_act_static": [P, I, I, P, P, P, P],
@@ -297,6 +300,49 @@ def gemm_w8a8_i32(qx, qw, acc=None, stream=None):
 
 def gemm_w4a8_i32(qx, qw4, acc=None, stream=None):
     return _gemm_i32(lib().zq_gemm_w4a8_i32, 4, qx, qw4, acc, stream)
+
+
+def _gemm_xq(fn, bits, x, qw, sw, G, bias, act, y, qx, sx, stream):
+    _need(x, "x", torch.float16, dim=2)
+    M, K = x.shape
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, x.device, 2)
+    N = qw.shape[0]
+    if qw.shape[1] != (K if bits == 8 else K // 2):
+        raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+    _need(sw, "sw", torch.float32, x.device)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, x.device)
+    y = torch.empty(M, N, dtype=torch.float16, device=x.device) if y is None else y
+    qx = torch.empty(M, K, dtype=torch.int8, device=x.device) if qx is None else qx
+    sx = torch.empty(M, dtype=torch.float32, device=x.device) if sx is None else sx
+    _need(y, "y", torch.float16, x.device)
+    _need(qx, "qx", torch.int8, x.device)
+    _need(sx, "sx", torch.float32, x.device)
+    _check(fn(_p(x), _p(qw), _p(sw), G, _p(bias), int(act), M, N, K, _p(y),
+              _p(qx), _p(sx), _stream(x, stream)))
+    return y, qx, sx
+
+
+def gemm_w8a8_xq(x, qw, sw, G, bias=None, act=ACT_NONE, y=None, qx=None,
+                 sx=None, stream=None):
+    """The linear of an fp16 activation x [M,K]: token-wise codes and scales
+    (returned, equal to quant_act(x)) and y = gemm_w8a8 of them, with the
+    quantization done inside the GEMV for one token.  Returns (y, qx, sx)."""
+    return _gemm_xq(lib().zq_gemm_w8a8_xq, 8, x, qw, sw, G, bias, act, y, qx,
+                    sx, stream)
+
+
+def gemm_w4a8_xq(x, qw4, sw, G, bias=None, act=ACT_NONE, y=None, qx=None,
+                 sx=None, stream=None):
+    """As gemm_w8a8_xq with packed INT4 weights qw4 [N,K/2]."""
+    return _gemm_xq(lib().zq_gemm_w4a8_xq, 4, x, qw4, sw, G, bias, act, y, qx,
+                    sx, stream)
+
+
+def gemm_xq_plan(M, N, K, bits) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().zq_gemm_xq_plan(M, N, K, bits, buf, 256))
+    return buf.value.decode()
 
 
 def gemm_w8a16(x, qw, sw, G, bias=None, act=ACT_NONE, y=None, stream=None):

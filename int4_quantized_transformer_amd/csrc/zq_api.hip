@@ -170,6 +170,41 @@ zq_status gemm_quant_out(const int8_t *qx, const float *sx, const void *qw,
                     fn);
 }
 
+zq_status gemm_xq(const void *x, const void *qw, const float *sw, int G,
+                  const void *bias, int act, int M, int N, int K, void *y,
+                  int8_t *qx, float *sx, void *stream, int bits,
+                  const char *fn) {
+  zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (!sw || ((!x || !sx || !y) && M != 0))
+    return fail(ZQ_EINVAL, "%s: null x/sx/sw/y", fn);
+  if (!aligned(x, 16) || !aligned(sx, 4) || !aligned(sw, 4) ||
+      !aligned(y, 8) || (bias && !aligned(bias, 2)))
+    return fail(ZQ_EINVAL, "%s: misaligned x/sx/sw/y/bias", fn);
+  if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+    return fail(ZQ_EINVAL, "%s: act=%d", fn, act);
+  if (G <= 0 || N % G != 0)
+    return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  if (K > ZQ_MAX_ROW_K)
+    return fail(ZQ_EUNSUPPORTED, "%s: K=%d exceeds %d", fn, K, ZQ_MAX_ROW_K);
+  if (M == 0) return ok();
+  zq::GemmArgs a{};
+  a.qx = static_cast<const int8_t *>(x);  // fp16 bytes
+  a.sx = nullptr;
+  a.qw = qw;
+  a.sw = sw;
+  a.bias = static_cast<const zq::half_t *>(bias);
+  a.out = y;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.act = act;
+  a.bits = bits;
+  a.raw_i32 = false;
+  return hip_status(zq::launch_gemm_xq(a, qx, sx, (hipStream_t)stream), fn);
+}
+
 zq_status gemm_raw(const int8_t *qx, const void *qw, int M, int N, int K,
                    int32_t *acc, void *stream, int bits, const char *fn) {
   zq_status st = check_gemm(qx, qw, M, N, K, bits, fn);
@@ -317,6 +352,33 @@ zq_status zq_gemm_w4a8_quant(const int8_t *qx, const float *sx,
                              size_t ws_bytes, void *stream) {
   return gemm_quant_out(qx, sx, qw4, sw, G, bias_fp16, act, M, N, K, qy, sy,
                         ws, ws_bytes, stream, 4, "zq_gemm_w4a8_quant");
+}
+
+zq_status zq_gemm_w8a8_xq(const void *x_fp16, const int8_t *qw, const float *sw,
+                          int G, const void *bias_fp16, int act, int M, int N,
+                          int K, void *y_fp16, int8_t *qx, float *sx,
+                          void *stream) {
+  return gemm_xq(x_fp16, qw, sw, G, bias_fp16, act, M, N, K, y_fp16, qx, sx,
+                 stream, 8, "zq_gemm_w8a8_xq");
+}
+
+zq_status zq_gemm_w4a8_xq(const void *x_fp16, const uint8_t *qw4,
+                          const float *sw, int G, const void *bias_fp16,
+                          int act, int M, int N, int K, void *y_fp16,
+                          int8_t *qx, float *sx, void *stream) {
+  return gemm_xq(x_fp16, qw4, sw, G, bias_fp16, act, M, N, K, y_fp16, qx, sx,
+                 stream, 4, "zq_gemm_w4a8_xq");
+}
+
+zq_status zq_gemm_xq_plan(int M, int N, int K, int bits, char *buf,
+                          int buflen) {
+  const char *fn = "zq_gemm_xq_plan";
+  if (!buf || buflen <= 0) return fail(ZQ_EINVAL, "%s: null buffer", fn);
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape M=%d N=%d K=%d", fn, M, N, K);
+  zq::describe_gemm_xq_plan(M, N, K, bits, buf, buflen);
+  return ok();
 }
 
 zq_status zq_gemm_w8a8_ws(const int8_t *qx, const float *sx, const int8_t *qw,

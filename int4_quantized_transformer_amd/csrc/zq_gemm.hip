@@ -1488,13 +1488,23 @@ static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
 // (even k / odd k), the activation bytes permuted to match, and the row sum
 // shifted right by 4 at the end.  Rows must be a whole number of 1 KB pieces
 // (K % 1024 == 0 for W8, K % 2048 == 0 for W4).
-template <int NW_, int U_, bool W4_, int XR_, bool A16_ = false>
+//
+// XQ: the activation arrives as the fp16 row the previous linear wrote, and
+// each block token-quantizes it while staging it into LDS: the block's
+// maximum of |x| over the whole row (every block loads the whole row, so no
+// other block's result is needed), S = amax / 127, and the codes from the
+// same exact quantizer helper as the row-quantizer kernel, so codes, S and
+// y equal those of the separate quantizer launch followed by this GEMM.
+// Block 0 also writes the codes and S out.
+template <int NW_, int U_, bool W4_, int XR_, bool A16_ = false,
+          bool XQ_ = false>
 struct Gemv {
   static constexpr int NW = NW_, U = U_;
   static constexpr bool W4 = W4_;
   // A16: fp16 activation row (2 bytes per k, held in LDS), INT8 weights;
   // fp32 row sums from v_dot2_f32_f16 on the widened codes
   static constexpr bool A16 = A16_;
+  static constexpr bool XQ = XQ_;
   static constexpr int NT = NW * kWave;
   static constexpr int RMAX = 1024;   // rows per block
   // XR > 0: the activation row (at most XMAX bytes) is held in LDS, loaded
@@ -1505,6 +1515,7 @@ struct Gemv {
   static constexpr int L = XL ? 1 : (W4 ? 3 : 2);  // loads per piece
   static_assert(U * L < 64, "vmcnt range");
   static_assert(!A16 || (XL && !W4), "fp16 activations: W8, row in LDS");
+  static_assert(!XQ || (XL && !A16), "quantized on load: codes in LDS");
 };
 
 template <int CTRL>
@@ -1549,9 +1560,11 @@ __device__ __forceinline__ float fdot8(v4i w, v4i x, float acc) {
 
 template <class C, bool RAW>
 __global__ void __launch_bounds__(C::NT)
-gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
+gemm_gemv_kernel(GemmArgs p, int rpb, int interleave, int8_t *xq_codes,
+                 float *xq_scale) {
   __shared__ int rowsum[C::RMAX];
   __shared__ __attribute__((aligned(1024))) char xs[C::XL ? C::XMAX : 16];
+  __shared__ float xq_red[C::NW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ldw = C::W4 ? p.K / 2 : p.K;
@@ -1584,7 +1597,7 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
   uint16_t ebits[E];
   float esx = 0.0f;
   if constexpr (!RAW) {
-    esx = C::A16 ? 1.0f : p.sx[0];
+    esx = C::A16 || C::XQ ? 1.0f : p.sx[0];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       int n = r0 + (int)threadIdx.x + e * C::NT;
@@ -1596,14 +1609,26 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
   }
 
   // activation row: loaded now (clamped, unconditional), stored into LDS
-  // after the first weight loads are in flight
+  // after the first weight loads are in flight.  Piece e of a thread holds
+  // the 16 codes at k = off .. off + 15; XQ loads their 32 fp16 bytes.
   constexpr int XR = C::XL ? C::XR : 1;
-  v4i xr[XR];
+  constexpr int XH = C::XQ ? 2 : 1;
+  v4i xr[XR][XH];
   if constexpr (C::XL) {
 #pragma unroll
     for (int e = 0; e < XR; ++e) {
       const int off = (e * C::NT + (int)threadIdx.x) * 16;
-      xr[e] = ld16(X + (off < xbytes ? off : xbytes - 16));
+      if constexpr (C::XQ) {
+        // only pieces inside the row (whole waves, K % 1024 == 0): the
+        // 32-byte fp16 pieces past its end would be re-read by every block
+        xr[e][0] = xr[e][1] = v4i{0, 0, 0, 0};
+        if (off < p.K) {
+          xr[e][0] = ld16(X + 2 * off);
+          xr[e][1] = ld16(X + 2 * off + 16);
+        }
+      } else {
+        xr[e][0] = ld16(X + (off < xbytes ? off : xbytes - 16));
+      }
     }
   }
 
@@ -1646,11 +1671,57 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
   };
 #pragma unroll
   for (int u = 0; u < C::U; ++u) load(u);
-  if constexpr (C::XL) {
+  if constexpr (C::XQ) {
+    // token-wise quantization of the row (K % 1024 == 0, so a wave's pieces
+    // are all inside the row or all past its end)
+    float m = 0.0f;
 #pragma unroll
     for (int e = 0; e < XR; ++e) {
       const int off = (e * C::NT + (int)threadIdx.x) * 16;
-      if (off < xbytes) *reinterpret_cast<v4i *>(xs + off) = xr[e];
+      if (off < p.K) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const half8 x8 = __builtin_bit_cast(half8, xr[e][h]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf((float)x8[i]));
+        }
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) xq_red[wave] = m;
+    lds_barrier();
+    float amax = 0.0f;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) amax = fmaxf(amax, xq_red[w]);
+    const Quantizer qz = make_quantizer(amax, 127.0f);
+    esx = qz.s;
+    const bool out = blockIdx.x == 0 && xq_codes != nullptr;
+#pragma unroll
+    for (int e = 0; e < XR; ++e) {
+      const int off = (e * C::NT + (int)threadIdx.x) * 16;
+      if (off < p.K) {
+        float v[2][8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const half8 x8 = __builtin_bit_cast(half8, xr[e][h]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[h][i] = (float)x8[i];
+        }
+        // amax is the max |x| of the row: the codes need no clamp
+        const v2i lo = quant8_pack_rowmax(v[0], qz);
+        const v2i hi = quant8_pack_rowmax(v[1], qz);
+        const v4i c = {lo[0], lo[1], hi[0], hi[1]};
+        *reinterpret_cast<v4i *>(xs + off) = c;
+        if (out) *reinterpret_cast<v4i *>(xq_codes + off) = c;
+      }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && xq_scale != nullptr)
+      xq_scale[0] = qz.s;
+  } else if constexpr (C::XL) {
+#pragma unroll
+    for (int e = 0; e < XR; ++e) {
+      const int off = (e * C::NT + (int)threadIdx.x) * 16;
+      if (off < xbytes) *reinterpret_cast<v4i *>(xs + off) = xr[e][0];
     }
   }
   lds_barrier();  // activation row and cleared row sums visible
@@ -1731,7 +1802,8 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave) {
 
 template <class C, bool RAW>
 static hipError_t run_gemv(const GemmArgs &a, hipStream_t s, int bpc,
-                           int interleave) {
+                           int interleave, int8_t *xq_codes = nullptr,
+                           float *xq_scale = nullptr) {
   const int cus = device_cus();
   int grid = bpc * cus;
   if (grid > a.N) grid = a.N;
@@ -1739,7 +1811,7 @@ static hipError_t run_gemv(const GemmArgs &a, hipStream_t s, int bpc,
   if (rpb > C::RMAX) rpb = C::RMAX;
   grid = (a.N + rpb - 1) / rpb;
   hipLaunchKernelGGL((gemm_gemv_kernel<C, RAW>), dim3(grid), dim3(C::NT), 0,
-                     s, a, rpb, interleave);
+                     s, a, rpb, interleave, xq_codes, xq_scale);
   return hipGetLastError();
 }
 
@@ -2254,6 +2326,76 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
   return run_plan(choose(a.M, a.N, a.K, a.bits), a, s);
 }
 
+// ---------------------------------------------- token quantization on load
+// The linear of an fp16 activation x (a.qx holds its bytes): the codes and
+// scale of the token-wise quantizer, then the GEMM with its epilogue.  Where
+// the plan is the one-token GEMV with the row in LDS, one kernel does both
+// (Gemv XQ) and writes the codes and scale for the caller; otherwise the
+// row quantizer writes them and the plan's kernel reads them.  Returns the
+// activation-row class of the one-kernel form (1: up to 8192 k, 2: up to
+// 32768 k), 0 where the two launches run.
+static int xq_one_kernel(int M, int N, int K, int bits) {
+  if (M != 1 || choose(M, N, K, bits).kind != kGemv) return 0;
+  const int f = forced_gemv() >= 0 ? forced_gemv() : 6;
+  if (!((f >> 1) & 1)) return 0;  // row not held in LDS
+  return K <= 8192 ? 1 : (K <= 32768 ? 2 : 0);
+}
+
+// Every block of the one-kernel form quantizes the whole row, so two 4-wave
+// blocks per compute unit do that work twice per unit, one 8-wave block once
+// (the same waves per SIMD).  One 8-wave block per unit for W4 (whose inner
+// loop is heavier in VALU work) and for rows of up to 8192 k: GPT-NeoX-20B
+// FFN2 (W4, 6144 x 24576) 16.8 -> 15.9 us, GPT-J attn-out (4096 x 4096)
+// 5.8 -> 5.65 us; two 4-wave blocks for longer W8 rows (GPT-J FFN2,
+// 4096 x 16384: 13.8 against 14.0 us).  Tuning aid: ZQ_XQ_NW=4 or 8.
+static int forced_xq_nw() {
+  static int v = [] {
+    const char *e = getenv("ZQ_XQ_NW");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
+static int xq_waves(int bits, int xc) {
+  const int f = forced_xq_nw();
+  if (f == 4 || f == 8) return f;
+  return bits == 4 || xc == 1 ? 8 : 4;
+}
+
+hipError_t launch_gemm_xq(const GemmArgs &a, int8_t *qx, float *sx,
+                          hipStream_t s) {
+  const int xc = xq_one_kernel(a.M, a.N, a.K, a.bits);
+  if (xc) {
+    const int f = forced_gemv() >= 0 ? forced_gemv() : 6;
+    const int il = f & 1;
+    if (xq_waves(a.bits, xc) == 8) {
+      if (a.bits == 4) {
+        if (xc == 1)
+          return run_gemv<Gemv<8, 6, true, 1, false, true>, false>(a, s, 1, il, qx, sx);
+        return run_gemv<Gemv<8, 6, true, 4, false, true>, false>(a, s, 1, il, qx, sx);
+      }
+      if (xc == 1)
+        return run_gemv<Gemv<8, 6, false, 1, false, true>, false>(a, s, 1, il, qx, sx);
+      return run_gemv<Gemv<8, 6, false, 4, false, true>, false>(a, s, 1, il, qx, sx);
+    }
+    if (a.bits == 4) {
+      if (xc == 1)
+        return run_gemv<Gemv<4, 6, true, 2, false, true>, false>(a, s, 2, il, qx, sx);
+      return run_gemv<Gemv<4, 6, true, 8, false, true>, false>(a, s, 2, il, qx, sx);
+    }
+    if (xc == 1)
+      return run_gemv<Gemv<4, 6, false, 2, false, true>, false>(a, s, 2, il, qx, sx);
+    return run_gemv<Gemv<4, 6, false, 8, false, true>, false>(a, s, 2, il, qx, sx);
+  }
+  const hipError_t e = launch_row_quant(a.qx, nullptr, nullptr, 0.0f, a.M,
+                                        a.K, false, qx, sx, nullptr, s);
+  if (e != hipSuccess) return e;
+  GemmArgs b = a;
+  b.qx = qx;
+  b.sx = sx;
+  return launch_gemm(b, s);
+}
+
 // ------------------------------------------------------------- split K
 // 17 .. 64 tokens over few weight tiles (N up to about 8K): 64x64 tiles
 // leave most compute units idle, and the skinny kernel moves four
@@ -2720,6 +2862,23 @@ int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len) {
   return snprintf(buf, len,
                   "tiled cfg=%d BN=%d BM=%d WN=%d WM=%d stages=%d kb=%d W%d tiles=%d%s",
                   pl.cfg, c.bn, c.bm, c.wn, c.wm, c.s, c.kb, bits, tiles, src);
+}
+
+int describe_gemm_xq_plan(int M, int N, int K, int bits, char *buf, int len) {
+  if (const int xc = xq_one_kernel(M, N, K, bits)) {
+    // the launch grid of run_gemv: one 8-wave or two 4-wave blocks per CU
+    const int nw = xq_waves(bits, xc);
+    int grid = (nw == 8 ? 1 : 2) * device_cus();
+    if (grid > N) grid = N;
+    int rpb = (N + grid - 1) / grid;
+    if (rpb > 1024) rpb = 1024;
+    grid = (N + rpb - 1) / rpb;
+    return snprintf(buf, len,
+                    "quantize-on-load gemv NW=%d U=6 W%d rows=%d x_in_lds=1 "
+                    "grid=%d", nw, bits, N, grid);
+  }
+  const int w = snprintf(buf, len, "row-quant + ");
+  return w + describe_gemm_plan(M, N, K, bits, buf + w, len - w);
 }
 
 }  // namespace zq

@@ -296,6 +296,13 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+// The linear of an fp16 activation (a.qx holds fp16 [M][K], a.sx unused):
+// token-wise codes qx [M][K] and scales sx [M] written for the caller, and
+// y = the GEMM of those codes (one kernel for one token where the plan is
+// the GEMV, else the row quantizer and the plan's kernel).
+hipError_t launch_gemm_xq(const GemmArgs &a, int8_t *qx, float *sx,
+                          hipStream_t s);
+int describe_gemm_xq_plan(int M, int N, int K, int bits, char *buf, int len);
 // The GEMM's fp16 output quantized token-wise (codes qy [M][N], scales sy
 // [M]) for the next linear; ws: caller workspace of gemm_quant_ws_bytes.
 hipError_t launch_gemm_quant(const GemmArgs &a, int8_t *qy, float *sy,

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert "zq_gemm_w8a8" in names and "zq_ln_quant_act" in names
     for n in names:
         assert hasattr(L, n), f"{n} declared in zq.h but not exported"
-    assert L.zq_version() == 105
+    assert L.zq_version() == 106
 
 
 def test_last_error_starts_empty_and_is_set_on_failure():
@@ -433,3 +433,30 @@ def test_chain_ws_gemm_host_side():
 def test_tile_rule_regression(empty_table, shape, plan):
     # the plans the schedule tuner measured best for these shapes
     assert Z.gemm_plan(*shape).startswith(plan), Z.gemm_plan(*shape)
+
+
+@pytest.mark.parametrize("fn", ["zq_gemm_w8a8_xq", "zq_gemm_w4a8_xq"])
+def test_gemm_xq_argument_checks(fn):
+    f = getattr(Z.lib(), fn)
+    # (x, qw, sw, G, bias, act, M, N, K, y, qx, sx, stream)
+    assert f(A, B, C, 64, None, 0, 1, 256, 100, D, E, A, None) == EUNSUP  # K % 64
+    assert f(A, B, C, 64, None, 0, 1, 96, 256, D, E, A, None) == ESHAPE   # N % G
+    assert f(A, B, C, 64, None, 2, 1, 256, 256, D, E, A, None) == EINVAL  # act
+    assert f(None, B, C, 64, None, 0, 1, 256, 256, D, E, A, None) == EINVAL
+    assert f(A, B, C, 64, None, 0, 1, 256, 256, D, None, A, None) == EINVAL  # qx
+    assert f(A, B, C, 64, None, 0, 1, 256, 256, D, E, None, None) == EINVAL  # sx
+    assert f(A, B, C, 64, None, 0, 1, 256, 256, None, E, A, None) == EINVAL  # y
+    assert f(ctypes.c_void_p(0x10008), B, C, 64, None, 0, 1, 256, 256, D, E, A,
+             None) == EINVAL                                              # x align
+    assert f(A, B, C, 64, None, 0, 1, 256, 65600, D, E, A, None) == EUNSUP  # row K
+    assert f(None, B, C, 64, None, 0, 0, 256, 256, None, None, None,
+             None) == OK                                                  # empty
+
+
+def test_gemm_xq_plan_names_the_form():
+    assert Z.gemm_xq_plan(1, 4096, 16384, 8).startswith("quantize-on-load gemv")
+    assert Z.gemm_xq_plan(1, 6144, 24576, 4).startswith("quantize-on-load gemv")
+    # past 32768 k the GEMV re-reads the row from the caches: two launches
+    assert Z.gemm_xq_plan(1, 4096, 65536, 8).startswith("row-quant + gemv")
+    assert Z.gemm_xq_plan(16, 4096, 16384, 8).startswith("row-quant + stream")
+    assert Z.gemm_xq_plan(2048, 6144, 24576, 4).startswith("row-quant + tiled")
