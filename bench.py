@@ -860,7 +860,9 @@ def chain_figure(torch, zq, dev, steps=50, reps=20):
     HIP graph per token count, and replayed again after tuning the schedule
     table at those token counts: a 12-layer BERT-base stack at seq 128 with
     batch 1, 16 and 128 (the pages' Table 6 shapes), one BERT-base layer,
-    and a 4-layer GPT-J decode stack.  Times are per stack, from events
+    and a 4-layer GPT-J decode stack, also with attn-out and FFN2 as
+    quantize-on-load calls (six launches per layer; one kernel each at one
+    token).  Times are per stack, from events
     around `steps` back-to-back runs (so launch gaps count), with the host
     time per run beside them."""
     from int4_quantized_transformer_amd import workloads as W
@@ -882,12 +884,14 @@ def chain_figure(torch, zq, dev, steps=50, reps=20):
 
     out = {"note": "layers of a stack share one layer's weights and buffers "
                    "(cache-resident across runs): a launch-overhead figure"}
-    for name, layers, ms in (("bert-base", 12, (128, 2048, 16384)),
-                             ("bert-base", 1, (128,)),
-                             ("gptj-6b", 4, (1, 16, 64))):
+    for name, layers, ms, xq in (("bert-base", 12, (128, 2048, 16384), False),
+                                 ("bert-base", 1, (128,), False),
+                                 ("gptj-6b", 4, (1, 16, 64), False),
+                                 ("gptj-6b", 4, (1, 16, 64), True)):
         wl = W.workload(name)
         zq.sched_clear()
-        c, B = W.layer_chain(wl, max(ms), dev, seed=1, layers=layers)
+        c, B = W.layer_chain(wl, max(ms), dev, seed=1, layers=layers,
+                             quant_on_load=xq)
         c.run_eager(max(ms))
         res = {"launches": len(c)}
         for M in ms:
@@ -911,7 +915,7 @@ def chain_figure(torch, zq, dev, steps=50, reps=20):
             e["tuned_graph_us"] = round(gt, 2)
             e["tuned_plans"] = [zq.gemm_plan(M, L.N, L.K, L.bits).split(" W")[0]
                                 for L in wl.linears]
-        out[f"{name} x{layers}"] = res
+        out[f"{name} x{layers}" + (" quant-on-load" if xq else "")] = res
         zq.sched_clear()
         c.close()
         del B

@@ -416,7 +416,10 @@ int zq_sched_entries(void);
  * added, as the call itself checks them (with M = max_m; ws_bytes against
  * the largest workspace any token count up to max_m needs), and a failing
  * add appends nothing.  Host only: no GPU is touched.  zq_chain_add_gemm_ws
- * records zq_gemm_w8a8_ws (bits 8) or zq_gemm_w4a8_ws (bits 4).
+ * records zq_gemm_w8a8_ws (bits 8) or zq_gemm_w4a8_ws (bits 4), and
+ * zq_chain_add_gemm_xq zq_gemm_w8a8_xq or zq_gemm_w4a8_xq (the graph for
+ * one token holds its single kernel, the graphs for more tokens the
+ * quantizer and the GEMM).
  *
  * zq_chain_run(chain, M, stream): runs the sequence over the first M rows
  * of every buffer.  The first run with a given M (or the first after the
@@ -465,6 +468,10 @@ zq_status zq_chain_add_gemm_w8a16(zq_chain *c, const void *x_fp16,
                                   const int8_t *qw, const float *sw, int G,
                                   const void *bias_fp16, int act, int N, int K,
                                   void *y_fp16);
+zq_status zq_chain_add_gemm_xq(zq_chain *c, int bits, const void *x_fp16,
+                               const void *qw, const float *sw, int G,
+                               const void *bias_fp16, int act, int N, int K,
+                               void *y_fp16, int8_t *qx, float *sx);
 zq_status zq_chain_run(zq_chain *c, int M, void *stream);
 zq_status zq_chain_run_eager(zq_chain *c, int M, void *stream);
 int zq_chain_graphs(const zq_chain *c);

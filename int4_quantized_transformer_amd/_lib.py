@@ -85,6 +85,7 @@ def lib():
             "zq_chain_add_gemm_quant": [P, I, P, P, P, P, I, P, I, I, I, P, P,
                                         P, ctypes.c_size_t],
             "zq_chain_add_gemm_w8a16": [P, P, P, P, I, P, I, I, I, P],
+            "zq_chain_add_gemm_xq": [P, I, P, P, P, I, P, I, I, I, P, P, P],
             "zq_chain_add_gemm_ws": [P, I, P, P, P, P, I, P, I, I, I, P, P,
                                      ctypes.c_size_t],
             "zq_chain_run": [P, I, P],
@@ -567,6 +568,25 @@ class Chain:
         self._rows(y, "y", torch.float16, N)
         _check(lib().zq_chain_add_gemm_w8a16(self._h, _p(x), _p(qw), _p(sw), G,
                                              _p(bias), int(act), N, K, _p(y)))
+
+    def gemm_xq(self, x, qw, sw, G, y, qx, sx, bias=None, act=ACT_NONE):
+        """gemm_w8a8_xq / gemm_w4a8_xq: the fp16 activation x quantized by
+        the GEMM (codes and scales into qx, sx)."""
+        K = x.shape[1]
+        bits = 8 if qw.dtype == torch.int8 else 4
+        self._rows(x, "x", torch.float16, K)
+        self._rows(qx, "qx", torch.int8, K)
+        self._rows(sx, "sx", torch.float32)
+        self._dev(qw, "qw", torch.int8 if bits == 8 else torch.uint8)
+        self._dev(sw, "sw", torch.float32)
+        self._dev(bias, "bias", torch.float16)
+        if qw.shape[1] != (K if bits == 8 else K // 2):
+            raise ValueError(f"qw shape {tuple(qw.shape)} does not match K={K}")
+        N = qw.shape[0]
+        self._rows(y, "y", torch.float16, N)
+        _check(lib().zq_chain_add_gemm_xq(self._h, bits, _p(x), _p(qw), _p(sw),
+                                          G, _p(bias), int(act), N, K, _p(y),
+                                          _p(qx), _p(sx)))
 
     def _stream(self, stream):
         if stream is not None:

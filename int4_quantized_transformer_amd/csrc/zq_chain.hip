@@ -16,7 +16,7 @@
 
 namespace {
 
-enum OpKind { kLnQuant, kQuant, kGemm, kGemmQuant, kGemmA16, kGemmWs };
+enum OpKind { kLnQuant, kQuant, kGemm, kGemmQuant, kGemmA16, kGemmWs, kGemmXq };
 
 struct ChainOp {
   OpKind kind;
@@ -82,6 +82,14 @@ zq_status run_op(const ChainOp &o, int M, void *s) {
                  : zq_gemm_w4a8_ws(o.gqx, o.gsx, (const uint8_t *)o.qw, o.sw,
                                    o.G, o.bias, o.act, M, o.N, o.K, o.y, o.ws,
                                    o.ws_bytes, s);
+    case kGemmXq:
+      return o.bits == 8
+                 ? zq_gemm_w8a8_xq(o.x, (const int8_t *)o.qw, o.sw, o.G,
+                                   o.bias, o.act, M, o.N, o.K, o.y, o.qx,
+                                   o.sx, s)
+                 : zq_gemm_w4a8_xq(o.x, (const uint8_t *)o.qw, o.sw, o.G,
+                                   o.bias, o.act, M, o.N, o.K, o.y, o.qx,
+                                   o.sx, s);
   }
   return zq::fail(ZQ_EINVAL, "zq_chain: unknown call kind");
 }
@@ -323,6 +331,28 @@ zq_status zq_chain_add_gemm_w8a16(zq_chain *c, const void *x_fp16,
   o.K = K;
   o.y = y_fp16;
   return add(c, o, "zq_chain_add_gemm_w8a16", !x_fp16 || !y_fp16);
+}
+
+zq_status zq_chain_add_gemm_xq(zq_chain *c, int bits, const void *x_fp16,
+                               const void *qw, const float *sw, int G,
+                               const void *bias_fp16, int act, int N, int K,
+                               void *y_fp16, int8_t *qx, float *sx) {
+  if (bits != 8 && bits != 4)
+    return zq::fail(ZQ_EINVAL, "zq_chain_add_gemm_xq: bits=%d", bits);
+  ChainOp o{kGemmXq};
+  o.bits = bits;
+  o.x = x_fp16;
+  o.qw = qw;
+  o.sw = sw;
+  o.G = G;
+  o.bias = bias_fp16;
+  o.act = act;
+  o.N = N;
+  o.K = K;
+  o.y = y_fp16;
+  o.qx = qx;
+  o.sx = sx;
+  return add(c, o, "zq_chain_add_gemm_xq", !x_fp16 || !y_fp16 || !qx || !sx);
 }
 
 zq_status zq_chain_run_eager(zq_chain *c, int M, void *stream) {

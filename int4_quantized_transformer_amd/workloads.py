@@ -138,7 +138,7 @@ def randn_fp16(shape, seed: int, std: float = 1.0, mean: float = 0.0):
 
 
 def layer_chain(wl: Workload, max_m: int, device, seed: int = 0,
-                layers: int = 1):
+                layers: int = 1, quant_on_load: bool = False):
     """The four linears of one encoder layer of ``wl`` over ``max_m`` tokens,
     recorded as a zq Chain: LN + token quantization -> QKV; token
     quantization -> attention output; LN + token quantization -> FFN1 (GeLU,
@@ -148,7 +148,11 @@ def layer_chain(wl: Workload, max_m: int, device, seed: int = 0,
     workload's outlier channels, like the layer input).  Weights are the
     workload's, quantized on the device.  ``layers`` > 1 records the layer's
     calls that many times over the same weights and buffers (a stand-in for
-    a model's stack of layers when timing launches).  Returns (chain,
+    a model's stack of layers when timing launches).  ``quant_on_load``
+    records attn-out and FFN2 as quantize-on-load calls instead (FFN1 writes
+    its fp16 output to the start of ``ws``, where the quantized-output call
+    keeps it, and FFN2 quantizes it; the codes and scales land in the same
+    buffers): six calls per layer, the same results.  Returns (chain,
     buffers)."""
     from . import _lib as zq
     qkv, ao, f1, f2 = wl.linears
@@ -180,15 +184,28 @@ def layer_chain(wl: Workload, max_m: int, device, seed: int = 0,
     B["y_ao"] = empty(max_m, ao.N)
     B["y_out"] = empty(max_m, f2.N)
     B["ws"] = empty(zq.gemm_quant_workspace_bytes(max_m, f1.N), dtype=torch.uint8)
+    h2 = B["ws"].view(torch.float16)[: max_m * f1.N].view(max_m, f1.N)
+    act1 = zq.ACT_GELU if f1.gelu else zq.ACT_NONE
     c = zq.Chain(max_m)
     for _ in range(layers):
         c.ln_quant(B["x"], B["qx0"], B["sx0"], B["gamma"], B["beta"], wl.ln_eps)
         c.gemm(B["qx0"], B["sx0"], B["qw0"], B["sw0"], wl.G, B["y_qkv"], B["b0"])
-        c.quant(B["ctx"], B["qx1"], B["sx1"])
-        c.gemm(B["qx1"], B["sx1"], B["qw1"], B["sw1"], wl.G, B["y_ao"], B["b1"])
+        if quant_on_load:
+            c.gemm_xq(B["ctx"], B["qw1"], B["sw1"], wl.G, B["y_ao"], B["qx1"],
+                      B["sx1"], B["b1"])
+        else:
+            c.quant(B["ctx"], B["qx1"], B["sx1"])
+            c.gemm(B["qx1"], B["sx1"], B["qw1"], B["sw1"], wl.G, B["y_ao"],
+                   B["b1"])
         c.ln_quant(B["h1"], B["qx2"], B["sx2"], B["gamma"], B["beta"], wl.ln_eps)
-        c.gemm_quant(B["qx2"], B["sx2"], B["qw2"], B["sw2"], wl.G, B["qx3"],
-                     B["sx3"], B["ws"], B["b2"],
-                     zq.ACT_GELU if f1.gelu else zq.ACT_NONE)
-        c.gemm(B["qx3"], B["sx3"], B["qw3"], B["sw3"], wl.G, B["y_out"], B["b3"])
+        if quant_on_load:
+            c.gemm(B["qx2"], B["sx2"], B["qw2"], B["sw2"], wl.G, h2, B["b2"],
+                   act1)
+            c.gemm_xq(h2, B["qw3"], B["sw3"], wl.G, B["y_out"], B["qx3"],
+                      B["sx3"], B["b3"])
+        else:
+            c.gemm_quant(B["qx2"], B["sx2"], B["qw2"], B["sw2"], wl.G, B["qx3"],
+                         B["sx3"], B["ws"], B["b2"], act1)
+            c.gemm(B["qx3"], B["sx3"], B["qw3"], B["sw3"], wl.G, B["y_out"],
+                   B["b3"])
     return c, B

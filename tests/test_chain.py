@@ -14,6 +14,8 @@ with its tuner (zq_gemm_tune).
   to FFN1's own fp16 output.
 * Tuning changes plans, never results: the GEMM's bits are the same before
   and after, and chains re-capture their graphs once the table changes.
+* A chain with attn-out and FFN2 recorded as quantize-on-load calls gives
+  the classic chain's outputs bit for bit, eager and from graphs.
 """
 import numpy as np
 import pytest
@@ -375,6 +377,37 @@ def test_chain_eager_and_graph_outputs_vs_oracle(name, max_m, ms):
         c.run(M)             # a second replay of the held graph
         ref.check(snap(B, M), B, M, f"{name} graph replay")
     c.close()
+
+
+@pytest.mark.parametrize("name,max_m,ms", [
+    ("gptj-6b", 64, (1, 16, 64)),            # one-kernel form at one token
+    ("bert-large", 96, (1, 17, 96)),         # W4 FFN
+    ("bert-base", 320, (320, 1)),
+])
+def test_quant_on_load_chain_matches_classic_chain(name, max_m, ms):
+    """attn-out and FFN2 recorded as quantize-on-load calls: six calls, and
+    every output (and FFN1's fp16 output) bit-identical to the classic
+    chain's, eager and from graphs; checked against the oracle as well."""
+    wl = W.workload(name)
+    c1, B1 = W.layer_chain(wl, max_m, dev(), seed=31)
+    c2, B2 = W.layer_chain(wl, max_m, dev(), seed=31, quant_on_load=True)
+    assert len(c1) == 7 and len(c2) == 6
+    ref = OracleLayer(wl, B2)
+    N1 = wl.linears[2].N
+    for M in ms:
+        wipe(B1)
+        c1.run_eager(M)
+        classic = snap(B1, M)
+        h_classic = to_np(B1["ws"][: 2 * M * N1]).copy()
+        for run in (c2.run_eager, c2.run, c2.run):
+            wipe(B2)
+            run(M)
+            got = snap(B2, M)
+            same(got, classic, M)
+            assert np.array_equal(to_np(B2["ws"][: 2 * M * N1]), h_classic), M
+        ref.check(got, B2, M, f"{name} quant-on-load graph")
+    c1.close()
+    c2.close()
 
 
 @pytest.mark.parametrize("name,ms", [("bert-base", (16, 128, 320)),
