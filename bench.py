@@ -61,6 +61,10 @@ def parse():
                     help="skip the W8A16 (fp16 activation) figure")
     ap.add_argument("--no-static", action="store_true",
                     help="skip the static per-tensor quantization comparator")
+    ap.add_argument("--quant-on-load", action="store_true",
+                    help="step: attn-out and FFN2 as quantize-on-load calls "
+                         "(zq_gemm_*_xq) where they run as one kernel (one "
+                         "token); with --summarize, summarize such a run")
     ap.add_argument("--no-xq", action="store_true",
                     help="skip the one-token quantize-on-load figure")
     ap.add_argument("--no-chain", action="store_true",
@@ -90,6 +94,22 @@ class LinearSet:
 
 def gemm_bytes(M, N, K, bits, G):
     return M * K + N * K * bits // 8 + 4 * (N // G) + 4 * M + 2 * N + 2 * M * N
+
+
+def xq_bytes(M, N, K, bits, G):
+    """The quantize-on-load linear: reads the fp16 activation (2MK) instead of
+    codes and scales, and writes the codes (MK) and scales (4M) besides y."""
+    return gemm_bytes(M, N, K, bits, G) + 2 * M * K
+
+
+# the step's attn-out and FFN2 as quantize-on-load calls (--quant-on-load)
+STEP_XQ = False
+
+
+def step_xq(zq, L, M):
+    """Whether the step runs linear L as one quantize-on-load kernel."""
+    return STEP_XQ and not L.ln and zq.gemm_xq_plan(
+        M, L.N, L.K, L.bits).startswith("quantize-on-load")
 
 
 def quant_bytes(M, K, ln=False):
@@ -176,6 +196,14 @@ def make_step(zq, lins, wl, M, stream_ptr):
     calls = []
     for s in lins:
         L = s.L
+        if step_xq(zq, L, M):
+            fn = L_.zq_gemm_w8a8_xq if L.bits == 8 else L_.zq_gemm_w4a8_xq
+            calls.append((f"{L.name}.gemm_w{L.bits}a8_xq", fn,
+                          (P(s.x.data_ptr()), P(s.qw.data_ptr()),
+                           P(s.sw.data_ptr()), wl.G, P(s.b.data_ptr()),
+                           int(L.gelu), M, L.N, L.K, P(s.y.data_ptr()),
+                           P(s.qx.data_ptr()), P(s.sx.data_ptr()), st)))
+            continue
         if L.ln:
             calls.append((f"{L.name}.ln_quant", L_.zq_ln_quant_act,
                           (P(s.x.data_ptr()), None, None,
@@ -200,6 +228,9 @@ def make_chain(zq, lins, wl, M):
     c = zq.Chain(M)
     for s in lins:
         L = s.L
+        if step_xq(zq, L, M):
+            c.gemm_xq(s.x, s.qw, s.sw, wl.G, s.y, s.qx, s.sx, s.b, int(L.gelu))
+            continue
         if L.ln:
             c.ln_quant(s.x, s.qx, s.sx, None, None, wl.ln_eps)
         else:
@@ -233,6 +264,8 @@ def run_calls(calls):
 
 def kernel_work(name, L, M, G):
     """(ops, bytes, bound) of one launch."""
+    if name.endswith("_xq"):
+        return (2 * M * L.N * L.K, xq_bytes(M, L.N, L.K, L.bits, G), "mfma")
     if ".gemm" in name:
         return (2 * M * L.N * L.K, gemm_bytes(M, L.N, L.K, L.bits, G), "mfma")
     return (0, quant_bytes(M, L.K, L.ln), "hbm")
@@ -385,6 +418,9 @@ def grid_threads(name, L, M, G, zq):
     """Launch grid (threads) of the kernel behind a step entry, as the
     kernel trace reports it (used to find that launch in rocprofv3 output)."""
     plan = zq.gemm_plan(M, L.N, L.K, L.bits) if ".gemm" in name else ""
+    if name.endswith("_xq"):
+        plan = zq.gemm_xq_plan(M, L.N, L.K, L.bits).replace(
+            "quantize-on-load ", "")
     if plan.startswith("gemv") or plan.startswith("stream"):
         return int(plan.split("grid=")[1].split()[0]) * 64 * \
             int(plan.split("NW=")[1].split()[0])
@@ -431,6 +467,19 @@ def step_entries(zq, wl, M):
     only), algorithmic ops and bytes."""
     out = []
     for L in wl.linears:
+        if step_xq(zq, L, M):
+            gn = f"{L.name}.gemm_w{L.bits}a8_xq"
+            ops = 2 * M * L.N * L.K
+            nbytes = xq_bytes(M, L.N, L.K, L.bits, wl.G)
+            xplan = zq.gemm_xq_plan(M, L.N, L.K, L.bits)
+            out.append({"name": gn, "kernel": "gemm_gemv_kernel",
+                        "grid": grid_threads(gn, L, M, wl.G, zq),
+                        "block": 64 * int(xplan.split("NW=")[1].split()[0]),
+                        "ops": ops, "bytes": nbytes,
+                        "read_bytes": nbytes - 2 * M * L.N - M * L.K - 4 * M,
+                        "roof_s": max(ops / (INT8_PEAK_TOPS * 1e12),
+                                      nbytes / (HBM_PEAK_GBS * 1e9))})
+            continue
         qn = f"{L.name}.ln_quant" if L.ln else f"{L.name}.quant"
         out.append({"name": qn, "kernel": "row_quant_kernel", "grid": None,
                     "ops": 0, "bytes": quant_bytes(M, L.K, L.ln)})
@@ -445,6 +494,8 @@ def step_entries(zq, wl, M):
         nbytes = gemm_bytes(M, L.N, L.K, L.bits, wl.G)
         out.append({"name": gn, "kernel": kern,
                     "grid": grid_threads(gn, L, M, wl.G, zq),
+                    "block": 64 * int(plan.split("NW=")[1].split()[0])
+                    if plan.startswith("gemv") else None,
                     "ops": ops, "bytes": nbytes,
                     "read_bytes": nbytes - 2 * M * L.N,
                     # roofline time: what orders the durations of launches
@@ -1004,7 +1055,8 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
         lines.append("| entry | kernel@grid | calls | avg us | median us |")
         lines.append("|---|---|---|---|---|")
         for (k, g, w), v in sorted(groups.items()):
-            es = [e for e in gemm_e if e["kernel"] == k and e["grid"] == g]
+            es = [e for e in gemm_e if e["kernel"] == k and e["grid"] == g
+                  and e.get("block") in (None, w)]
             sp = _split(v, es, "roof_s") if es else None
             for name, vv in (sp or {}).items():
                 lines.append(f"| {name} | {k}@{g} | {len(vv)} | "
@@ -1017,7 +1069,8 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
             cname = r["Counter_Name"]
             if cname not in ("FETCH_SIZE", "WRITE_SIZE"):
                 continue
-            k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]),
+                 int(r["Workgroup_Size"]))
             pmc.setdefault(cname, {}).setdefault(k, {}).setdefault(
                 r["Dispatch_Id"], 0.0)
             pmc[cname][k][r["Dispatch_Id"]] += float(r["Counter_Value"])
@@ -1028,7 +1081,7 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
                      f"bytes of the {COPY_BYTES >> 20} MiB copy)")
         factors = {}
         for cname, per in pmc.items():
-            cp = [v for (k, g), dd in per.items() if k == "copy"
+            cp = [v for (k, g, w), dd in per.items() if k == "copy"
                   for v in dd.values()]
             if cp:
                 factors[cname] = st.median(cp) * 1024 / COPY_BYTES
@@ -1038,7 +1091,7 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
         lines.append("|---|---|---|---|---|---|")
         for cname, per in pmc.items():
             f = factors.get(cname)
-            for (k, g), dd in sorted(per.items()):
+            for (k, g, w), dd in sorted(per.items()):
                 med = st.median(dd.values())
                 scaled = med * 1024 / f if f else None
                 lines.append(f"| {cname} | {k} | {g} | {len(dd)} | {med:.0f} | "
@@ -1054,9 +1107,10 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
             f = factors.get(cname)
             if not f:
                 continue
-            for (k, g), dd in sorted(per.items()):
+            for (k, g, w), dd in sorted(per.items()):
                 es = [dict(e, write_bytes=e["bytes"] - e["read_bytes"])
-                      for e in gemm_e if e["kernel"] == k and e["grid"] == g]
+                      for e in gemm_e if e["kernel"] == k and e["grid"] == g
+                      and e.get("block") in (None, w)]
                 key = "read_bytes" if cname == "FETCH_SIZE" else "write_bytes"
                 sp = _split(list(dd.values()), es, key) if es else None
                 for name, vv in (sp or {}).items():
@@ -1079,7 +1133,7 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
                 out["steps"] = old.get("steps", {})
         except (OSError, ValueError):
             pass
-        step = out["steps"][f"{wl.name} M={M}"] = {}
+        step = out["steps"][step_key(wl, M)] = {}
         for name, v in traffic.items():
             if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
                 step[name] = {
@@ -1089,6 +1143,11 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
                     "write_bytes": round(v["WRITE_SIZE"])}
         with open(traffic_out, "w") as f:
             json.dump(out, f, indent=1)
+
+
+def step_key(wl, M):
+    """Name of a profiled step in the traffic file."""
+    return f"{wl.name} M={M}" + (" quant-on-load" if STEP_XQ else "")
 
 
 def mfma_lines(d, gemm_e, lines):
@@ -1107,7 +1166,8 @@ def mfma_lines(d, gemm_e, lines):
             if r["Counter_Name"] not in ("SQ_VALU_MFMA_BUSY_CYCLES",
                                          "GRBM_GUI_ACTIVE"):
                 continue
-            k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]),
+                 int(r["Workgroup_Size"]))
             dd = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
             dd[r["Counter_Name"]] = dd.get(r["Counter_Name"], 0.0) + \
                 float(r["Counter_Value"])
@@ -1121,8 +1181,9 @@ def mfma_lines(d, gemm_e, lines):
     lines.append("| entry | dispatches | median us (under counters) | clock GHz "
                  "| MFMA busy | INT8 POP/s |")
     lines.append("|---|---|---|---|---|---|")
-    for (k, g), dd in sorted(per.items()):
-        es = [e for e in gemm_e if e["kernel"] == k and e["grid"] == g]
+    for (k, g, w), dd in sorted(per.items()):
+        es = [e for e in gemm_e if e["kernel"] == k and e["grid"] == g
+              and e.get("block") in (None, w)]
         rows = [v for v in dd.values() if "SQ_VALU_MFMA_BUSY_CYCLES" in v
                 and "GRBM_GUI_ACTIVE" in v]
         if not es or not rows:
@@ -1152,7 +1213,9 @@ def copy_calibration(torch, dev):
 
 
 def main():
+    global STEP_XQ
     args = parse()
+    STEP_XQ = args.quant_on_load
     if args.summarize:
         summarize(args.summarize, args.write_traffic, args.workload,
                   args.m_index)
@@ -1262,7 +1325,7 @@ def main():
     roof["avg_launch_us"] = round(bd[dom] * 1e3, 2)
     roof["algorithmic"] = {"ops": ops, "bytes": nbytes}
     roof["grid_threads"] = grid_threads(dom, Ld, M, wl.G, zq)
-    roof["traffic"] = traffic_for(args.traffic, f"{wl.name} M={M}", dom,
+    roof["traffic"] = traffic_for(args.traffic, step_key(wl, M), dom,
                                   roof["grid_threads"])
     roof["timing"] = ("per-launch average from a HIP graph of this launch "
                       f"over {max(R, ENTRY_MIN_SETS)} rotating sets, events "
@@ -1274,9 +1337,12 @@ def main():
         "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} encoder linears"
-                   if wl.name.startswith("bert") else
-                   f"{wl.name} decoder linears (prefill)",
+        "config": {"workload": (f"{wl.name} encoder linears"
+                                if wl.name.startswith("bert") else
+                                f"{wl.name} decoder linears ("
+                                + ("prefill" if M > 64 else "decode") + ")")
+                   + ("; attn-out and FFN2 quantize-on-load" if STEP_XQ
+                      else ""),
                    "tokens": M, "hidden": wl.linears[0].K, "group_rows": wl.G,
                    "linears": {L.name: f"{L.N}x{L.K} W{L.bits}A8"
                                + (" +LN" if L.ln else "")
