@@ -330,7 +330,16 @@ def test_chain_host_side():
                                          D) == OK
         assert L.zq_chain_add_gemm_w8a16(h, A, B, C, 64, None, 0, 768, 3000,
                                          D) == EUNSUP
-        assert L.zq_chain_length(h) == 4
+        # (c, bits, x, qw, sw, G, bias, act, N, K, y, qx, sx)
+        assert L.zq_chain_add_gemm_xq(h, 8, A, B, C, 64, None, 0, 768, 3072,
+                                      D, E, A) == OK
+        assert L.zq_chain_add_gemm_xq(h, 4, A, B, C, 64, None, 0, 768, 3000,
+                                      D, E, A) == EUNSUP
+        assert L.zq_chain_add_gemm_xq(h, 8, A, B, C, 64, None, 0, 768, 3072,
+                                      D, None, A) == EINVAL
+        assert L.zq_chain_add_gemm_xq(h, 6, A, B, C, 64, None, 0, 768, 3072,
+                                      D, E, A) == EINVAL
+        assert L.zq_chain_length(h) == 5
         assert L.zq_chain_run(h, 129, None) == EINVAL
         assert L.zq_chain_run(h, -1, None) == EINVAL
         assert L.zq_chain_run_eager(h, 129, None) == EINVAL

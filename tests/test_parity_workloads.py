@@ -12,7 +12,11 @@ For every linear of every workload and every token count M:
   * GEMM: the fused call over the whole problem, with sampled token rows
     (all rows when M <= 64) compared with the oracle's int32 GEMM and fp64
     epilogue computed on the same quantized inputs (1 fp16 ulp + 1e-3), and
-    the raw int32 hook bit-exact on the same rows.
+    the raw int32 hook bit-exact on the same rows;
+  * the linears without LayerNorm (attn-out, FFN2) also through the
+    quantize-on-load call on the fp16 input: codes, scales and y
+    bit-identical to the quantizer followed by the fused GEMM (one kernel
+    at one token).
 """
 import functools
 
@@ -108,3 +112,15 @@ def test_workload_linear(wi, li, mi):
     assert_fp16_close_to_oracle(to_np(y[ridx]), z,
                                 f"{wl.name}.{L.name} M={M} "
                                 f"{zq.gemm_plan(M, L.N, L.K, L.bits)}")
+
+    # ---- the quantize-on-load call on the fp16 input (linears without
+    # LayerNorm): codes, scales and y bit-identical to the two calls above
+    if not L.ln:
+        xq = zq.gemm_w8a8_xq if L.bits == 8 else zq.gemm_w4a8_xq
+        yq, qxq, sxq = xq(xd, qw, sw, wl.G, b.to(d), int(L.gelu))
+        torch.cuda.synchronize()
+        plan = zq.gemm_xq_plan(M, L.N, L.K, L.bits)
+        assert np.array_equal(to_np(sxq), sx_np), plan
+        assert np.array_equal(to_np(qxq), qx_np), plan
+        assert np.array_equal(to_np(yq).view(np.uint16),
+                              to_np(y).view(np.uint16)), plan
