@@ -1485,8 +1485,9 @@ static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
 // operands loaded before the weight stream.
 //
 // W4: the packed bytes are split as in the MFMA kernels into 16*q words
-// (even k / odd k), the activation bytes permuted to match, and the row sum
-// shifted right by 4 at the end.  Rows must be a whole number of 1 KB pieces
+// (even k / odd k), the activation bytes permuted to match (once, when the
+// row is staged in LDS; per piece when it is read from the caches), and the
+// row sum shifted right by 4 at the end.  Rows must be a whole number of 1 KB pieces
 // (K % 1024 == 0 for W8, K % 2048 == 0 for W4).
 //
 // XQ: the activation arrives as the fp16 row the previous linear wrote, and
@@ -1711,7 +1712,7 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave, int8_t *xq_codes,
         const v2i lo = quant8_pack_rowmax(v[0], qz);
         const v2i hi = quant8_pack_rowmax(v[1], qz);
         const v4i c = {lo[0], lo[1], hi[0], hi[1]};
-        *reinterpret_cast<v4i *>(xs + off) = c;
+        *reinterpret_cast<v4i *>(xs + off) = C::W4 ? perm_even_odd(c) : c;
         if (out) *reinterpret_cast<v4i *>(xq_codes + off) = c;
       }
     }
@@ -1721,7 +1722,9 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave, int8_t *xq_codes,
 #pragma unroll
     for (int e = 0; e < XR; ++e) {
       const int off = (e * C::NT + (int)threadIdx.x) * 16;
-      if (off < xbytes) *reinterpret_cast<v4i *>(xs + off) = xr[e][0];
+      if (off < xbytes)
+        *reinterpret_cast<v4i *>(xs + off) =
+            C::W4 ? perm_even_odd(xr[e][0]) : xr[e][0];
     }
   }
   lds_barrier();  // activation row and cleared row sums visible
@@ -1748,8 +1751,11 @@ gemm_gemv_kernel(GemmArgs p, int rpb, int interleave, int8_t *xq_codes,
             x0 = xv[u][0];
             x1 = xv[u][1];
           }
-          acc = dot16(unpack_w4(wv[u][0], wv[u][1]), perm_even_odd(x0), acc);
-          acc = dot16(unpack_w4(wv[u][2], wv[u][3]), perm_even_odd(x1), acc);
+          // (the row in LDS is stored in that order already)
+          acc = dot16(unpack_w4(wv[u][0], wv[u][1]),
+                      C::XL ? x0 : perm_even_odd(x0), acc);
+          acc = dot16(unpack_w4(wv[u][2], wv[u][3]),
+                      C::XL ? x1 : perm_even_odd(x1), acc);
         } else {
           const v4i x0 = C::XL ? ld16(xs + kb + lane * 16) : xv[u][0];
           acc = dot16(wv[u], x0, acc);
