@@ -71,6 +71,8 @@ def parse():
                     help="skip the layer-chain graph / schedule-table figure")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill GEMM figure of the larger configs")
+    ap.add_argument("--no-quantizers", action="store_true",
+                    help="skip the row-quantizer figure of every workload")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "traffic.json"))
     ap.add_argument("--only", default=None,
@@ -709,6 +711,73 @@ def xq_figure(torch, zq, dev, steps=20):
             del qws
             torch.cuda.empty_cache()
     out["us_saved_total"] = round(saved, 2)
+    return out
+
+
+def quantizer_figure(torch, zq, dev, steps=20):
+    """The row quantizers at every workload's token counts: LayerNorm +
+    quantization (QKV / FFN1 inputs, affine gamma / beta) and quantization
+    alone (attn-out / FFN2 inputs), each from one HIP graph over rotating
+    inputs, against torch's fp16 -> int8 cast of the same tensor, which
+    reads and writes the same bytes (2MK, MK) with no arithmetic to speak
+    of: the cost of moving them with a library elementwise kernel."""
+    from int4_quantized_transformer_amd import workloads as W
+    out = {"note": "us per launch (graph over rotating inputs; decode-sized "
+                   "rows are launch-bound, at most 64 input copies); "
+                   "GB_per_s = algorithmic bytes (2MK read + MK + 4M "
+                   "written, + 4K gamma/beta with LN) / time; torch_cast = "
+                   "int8 tensor .copy_(fp16 tensor) of the same shape"}
+    stream = torch.cuda.current_stream()
+    for wl in W.WORKLOADS:
+        seen = set()
+        for mi, M in enumerate(wl.M):
+            for li, L in enumerate(wl.linears):
+                key = (M, L.K, L.ln)
+                if key in seen:
+                    continue
+                seen.add(key)
+                x = W.gen_activations(wl, li, m_index=mi).to(dev)
+                nb = quant_bytes(M, L.K, L.ln)
+                R = min(64, max(8, -(-ROTATE_BYTES // (3 * M * L.K))))
+                xs = [x] + [x.clone() for _ in range(R - 1)]
+                qx = torch.empty(M, L.K, dtype=torch.int8, device=dev)
+                sx = torch.empty(M, dtype=torch.float32, device=dev)
+                gam = torch.ones(L.K, dtype=torch.float16, device=dev)
+                bet = torch.zeros(L.K, dtype=torch.float16, device=dev)
+                qc = torch.empty(M, L.K, dtype=torch.int8, device=dev)
+
+                def zq_call():
+                    for x_ in xs:
+                        if L.ln:
+                            zq.ln_quant_act(x_, gam, bet, wl.ln_eps, qx=qx,
+                                            sx=sx)
+                        else:
+                            zq.quant_act(x_, qx=qx, sx=sx)
+
+                def cast():
+                    for x_ in xs:
+                        qc.copy_(x_)
+
+                us = {}
+                for name, fn in (("us", zq_call), ("torch_cast_us", cast)):
+                    fn()
+                    torch.cuda.synchronize()
+                    gr = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gr):
+                        fn()
+                    ms, _ = timed_graphs(torch, [gr], steps, stream)
+                    us[name] = round(ms * 1e3 / R, 2)
+                    del gr
+                kind = "ln_quant" if L.ln else "quant"
+                out[f"{wl.name} {kind} {M}x{L.K}"] = {
+                    "us": us["us"],
+                    "GB_per_s": round(nb / (us["us"] * 1e-6) / 1e9, 1),
+                    "pct_hbm_peak": pct_attainable(0, nb, us["us"] * 1e-6),
+                    "torch_cast_us": us["torch_cast_us"],
+                    "vs_torch_cast": round(us["torch_cast_us"] / us["us"], 2),
+                }
+                del xs, x
+                torch.cuda.empty_cache()
     return out
 
 
@@ -1383,6 +1452,8 @@ def main():
         out["roofline_decode"] = decode_roofline(extras["decode"], args.traffic)
     if not args.no_prefill:
         extras["prefill"] = prefill_figure(torch, zq, dev)
+    if not args.no_quantizers:
+        extras["quantizers"] = quantizer_figure(torch, zq, dev)
     if not args.no_w8a16:
         extras["w8a16"] = w8a16_figure(torch, zq, dev)
     if not args.no_static:
