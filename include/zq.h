@@ -343,6 +343,56 @@ zq_status zq_gemm_w8a16(const void *x_fp16, const int8_t *qw, const float *sw,
 zq_status zq_gemm_w8a16_plan(int M, int N, int K, char *buf, int buflen);
 
 /*
+ * Chunk-contiguous weights for decode -- the codes of zq_quantize_weights in
+ * another order, for the weight-streaming GEMM at 1 .. 16 tokens, where the
+ * linear is bound by reading its weights from HBM (the small-batch
+ * schedules of the summary page's Sec. 3.4 "Quantization-Optimized
+ * Transformer Kernels", paper App. D).  Values and scales are unchanged;
+ * the bytes of each chunk of BN rows x CK row bytes are stored as one
+ * contiguous range, chunks in order along the row and row blocks in order
+ * along N:
+ *     qd[((rb * (R / CK) + c) * BN + r) * CK + b] = qw[(rb * BN + r) * R + c * CK + b]
+ * with R = K (W8) or K / 2 (W4, the packed bytes as they are), so the
+ * kernel's copies read 1 KB of consecutive bytes where the row-major layout
+ * gives 1024 / CK rows at a row stride.  BN and CK are fixed per shape
+ * (zq_chunked_layout; the same on every device).  The buffer has the size
+ * of the row-major one.
+ *
+ * zq_chunked_layout: the rows per block (16 or 32) and chunk bytes (128,
+ *   256 or 512) of the shape.
+ * zq_pack_chunked: row-major codes qw (int8 [N][K], or packed uint8
+ *   [N][K/2]) -> qd.  An offline step, asynchronous on stream; qw and qd
+ *   must not overlap.
+ * zq_gemm_w8a8_chunked / zq_gemm_w4a8_chunked: zq_gemm_w8a8 / zq_gemm_w4a8
+ *   with the weights in this layout, for 1 <= M <= 16 tokens; y is
+ *   bit-identical to those calls on the row-major codes.  The bias, when
+ *   given, must be 4-byte aligned.
+ * zq_gemm_chunked_i32: the raw int32 accumulator (test hook), bits 8 or 4.
+ * zq_gemm_chunked_plan: the kernel configuration for the shape.
+ * Errors: ZQ_EINVAL (null/misaligned pointer as for zq_gemm_w8a8, a bias
+ * not 4-byte aligned, bits not 4 or 8, overlapping qw / qd), ZQ_ESHAPE
+ * (M < 0, N or K <= 0, G <= 0, N % G != 0), ZQ_EUNSUPPORTED (K % 64 != 0,
+ * N not a multiple of BN or the row bytes not a multiple of CK, K above
+ * ZQ_MAX_GEMM_K_W8 / _W4, M > 16).
+ */
+zq_status zq_chunked_layout(int N, int K, int bits, int *rows,
+                            int *chunk_bytes);
+zq_status zq_pack_chunked(const void *qw, int N, int K, int bits, void *qd,
+                          void *stream);
+zq_status zq_gemm_w8a8_chunked(const int8_t *qx, const float *sx,
+                               const int8_t *qd, const float *sw, int G,
+                               const void *bias_fp16, int act, int M, int N,
+                               int K, void *y_fp16, void *stream);
+zq_status zq_gemm_w4a8_chunked(const int8_t *qx, const float *sx,
+                               const uint8_t *qd4, const float *sw, int G,
+                               const void *bias_fp16, int act, int M, int N,
+                               int K, void *y_fp16, void *stream);
+zq_status zq_gemm_chunked_i32(int bits, const int8_t *qx, const void *qd,
+                              int M, int N, int K, int32_t *acc, void *stream);
+zq_status zq_gemm_chunked_plan(int M, int N, int K, int bits, char *buf,
+                               int buflen);
+
+/*
  * zq_gemm_plan -- which kernel and tile shape the GEMM calls pick for a
  * problem (the schedule chosen by token count, paper App. D), written as a
  * NUL-terminated string into buf (at most buflen bytes).  No launch.

@@ -13,7 +13,9 @@ __all__ = ["quantize_weights", "ln_quant_act", "quant_act", "gemm_w8a8",
            "quant_act_static", "gemm_tune", "sched_export", "sched_import",
            "sched_clear", "sched_entries", "Chain", "gemm_w8a8_ws",
            "gemm_w4a8_ws", "gemm_workspace_bytes", "gemm_ws_plan",
-           "gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "lib",
+           "gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "chunked_layout",
+           "pack_chunked", "gemm_w8a8_chunked", "gemm_w4a8_chunked",
+           "gemm_chunked_i32", "gemm_chunked_plan", "lib",
            "ZQError", "library_path", "ACT_NONE", "ACT_GELU"]
 
 

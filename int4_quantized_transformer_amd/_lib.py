@@ -20,7 +20,9 @@ __all__ = ["ZQError", "library_path", "lib", "quantize_weights",
            "quant_act_static", "gemm_tune", "sched_export", "sched_import",
            "sched_clear", "sched_entries", "Chain", "gemm_w8a8_ws",
            "gemm_w4a8_ws", "gemm_workspace_bytes", "gemm_ws_plan",
-           "gemm_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "chunked_layout",
+           "pack_chunked", "gemm_w8a8_chunked", "gemm_w4a8_chunked",
+           "gemm_chunked_i32", "gemm_chunked_plan",
            "ACT_NONE", "ACT_GELU"]
 
 ACT_NONE = 0
@@ -96,6 +98,12 @@ def lib():
             "zq_gemm_ws_plan": [I, I, I, I, ctypes.c_char_p, I],
             "zq_gemm_noalloc": [I, P, P, P, P, I, P, I, I, I, I, P, P],
             "zq_chain_run_eager": [P, I, P],
+            "zq_chunked_layout": [I, I, I, P, P],
+            "zq_pack_chunked": [P, I, I, I, P, P],
+            "zq_gemm_w8a8_chunked": [P, P, P, P, I, P, I, I, I, I, P, P],
+            "zq_gemm_w4a8_chunked": [P, P, P, P, I, P, I, I, I, I, P, P],
+            "zq_gemm_chunked_i32": [I, P, P, I, I, I, P, P],
+            "zq_gemm_chunked_plan": [I, I, I, I, ctypes.c_char_p, I],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -301,6 +309,58 @@ def gemm_w8a8_i32(qx, qw, acc=None, stream=None):
 
 def gemm_w4a8_i32(qx, qw4, acc=None, stream=None):
     return _gemm_i32(lib().zq_gemm_w4a8_i32, 4, qx, qw4, acc, stream)
+
+
+def chunked_layout(N, K, bits):
+    """(rows per block, chunk bytes) of the chunk-contiguous decode layout
+    for the shape."""
+    r, c = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().zq_chunked_layout(N, K, bits, ctypes.byref(r),
+                                   ctypes.byref(c)))
+    return r.value, c.value
+
+
+def pack_chunked(qw, bits, qd=None, stream=None):
+    """Row-major codes (int8 [N,K] for W8, packed uint8 [N,K/2] for W4) in
+    the chunk-contiguous decode layout (same dtype and shape)."""
+    _need(qw, "qw", torch.int8 if bits == 8 else torch.uint8, dim=2)
+    N, kb = qw.shape
+    K = kb if bits == 8 else 2 * kb
+    qd = torch.empty_like(qw) if qd is None else qd
+    _need(qd, "qd", qw.dtype, qw.device, 2)
+    if qd.shape != qw.shape:
+        raise ValueError(f"qd shape {tuple(qd.shape)} != {tuple(qw.shape)}")
+    _check(lib().zq_pack_chunked(_p(qw), N, K, bits, _p(qd),
+                                 _stream(qw, stream)))
+    return qd
+
+
+def gemm_w8a8_chunked(qx, sx, qd, sw, G, bias=None, act=ACT_NONE, y=None,
+                      stream=None):
+    """gemm_w8a8 over weights in the chunk-contiguous layout (pack_chunked),
+    1..16 tokens; y is bit-identical to gemm_w8a8 on the row-major codes."""
+    return _gemm(lib().zq_gemm_w8a8_chunked, 8, qx, sx, qd, sw, G, bias, act,
+                 y, stream)
+
+
+def gemm_w4a8_chunked(qx, sx, qd4, sw, G, bias=None, act=ACT_NONE, y=None,
+                      stream=None):
+    """As gemm_w8a8_chunked with packed W4 codes."""
+    return _gemm(lib().zq_gemm_w4a8_chunked, 4, qx, sx, qd4, sw, G, bias, act,
+                 y, stream)
+
+
+def gemm_chunked_i32(bits, qx, qd, acc=None, stream=None):
+    """Raw int32 accumulator of the chunk-layout GEMM."""
+    fn = lib().zq_gemm_chunked_i32
+    return _gemm_i32(lambda *a: fn(bits, *a), bits, qx, qd, acc, stream)
+
+
+def gemm_chunked_plan(M, N, K, bits):
+    """The kernel configuration of the chunk-layout GEMM for the shape."""
+    buf = ctypes.create_string_buffer(160)
+    _check(lib().zq_gemm_chunked_plan(M, N, K, bits, buf, 160))
+    return buf.value.decode()
 
 
 def _gemm_xq(fn, bits, x, qw, sw, G, bias, act, y, qx, sx, stream):

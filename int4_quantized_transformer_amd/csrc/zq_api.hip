@@ -245,6 +245,66 @@ zq_status row_quant(const void *x, const void *gamma, const void *beta,
                     fn);
 }
 
+// Shapes of the chunk-contiguous weight layout: the 16-token ring's row
+// blocks and chunks must tile the matrix.
+zq_status check_chunked_shape(int N, int K, int bits, const char *fn) {
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  if (N <= 0 || K <= 0)
+    return fail(ZQ_ESHAPE, "%s: bad shape N=%d K=%d", fn, N, K);
+  if (K % 64 != 0)
+    return fail(ZQ_EUNSUPPORTED, "%s: K=%d is not a multiple of 64", fn, K);
+  int bn = 0, ck = 0;
+  if (!zq::chunked_layout(N, K, bits, &bn, &ck, nullptr))
+    return fail(ZQ_EUNSUPPORTED,
+                "%s: N=%d K=%d W%d does not tile into %d-row blocks of "
+                "%d-byte chunks", fn, N, K, bits, bn, ck);
+  return ZQ_OK;
+}
+
+zq_status gemm_chunked(const int8_t *qx, const float *sx, const void *qd,
+                       const float *sw, int G, const void *bias, int act,
+                       int M, int N, int K, void *out, bool raw, void *stream,
+                       int bits, const char *fn) {
+  zq_status st = check_chunked_shape(N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  st = check_gemm(qx, qd, M, N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (M > 16)
+    return fail(ZQ_EUNSUPPORTED, "%s: M=%d exceeds 16 tokens", fn, M);
+  if (!out && M != 0) return fail(ZQ_EINVAL, "%s: null output", fn);
+  if (raw) {
+    if (!aligned(out, 16))
+      return fail(ZQ_EINVAL, "%s: acc must be 16-byte aligned", fn);
+  } else {
+    if (!sw || (!sx && M != 0)) return fail(ZQ_EINVAL, "%s: null sx/sw", fn);
+    // the ring gathers the bias as pairs of columns (4-byte words)
+    if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(out, 8) ||
+        (bias && !aligned(bias, 4)))
+      return fail(ZQ_EINVAL, "%s: misaligned sx/sw/y/bias (bias: 4 bytes)",
+                  fn);
+    if (act != ZQ_ACT_NONE && act != ZQ_ACT_GELU)
+      return fail(ZQ_EINVAL, "%s: act=%d", fn, act);
+    if (G <= 0 || N % G != 0)
+      return fail(ZQ_ESHAPE, "%s: N=%d is not a multiple of G=%d", fn, N, G);
+  }
+  if (M == 0) return ok();
+  zq::GemmArgs a{};
+  a.qx = qx;
+  a.sx = raw ? nullptr : sx;
+  a.qw = qd;
+  a.sw = raw ? nullptr : sw;
+  a.bias = raw ? nullptr : static_cast<const zq::half_t *>(bias);
+  a.out = out;
+  a.G = raw ? 1 : G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.act = raw ? 0 : act;
+  a.bits = bits;
+  a.raw_i32 = raw;
+  return hip_status(zq::launch_gemm_chunked(a, (hipStream_t)stream), fn);
+}
+
 // ------------------------------------------------- device-resident scratch
 // The split-K workspace of zq_gemm_noalloc: one array per device, held until
 // the process ends.  In host code `scratch` names a host-side stand-in, not a
@@ -530,6 +590,69 @@ zq_status zq_gemm_w8a16(const void *x_fp16, const int8_t *qw, const float *sw,
   a.bits = 8;
   a.raw_i32 = false;
   return hip_status(zq::launch_gemm_w8a16(a, (hipStream_t)stream), fn);
+}
+
+zq_status zq_chunked_layout(int N, int K, int bits, int *rows,
+                            int *chunk_bytes) {
+  const char *fn = "zq_chunked_layout";
+  zq_status st = check_chunked_shape(N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  zq::chunked_layout(N, K, bits, rows, chunk_bytes, nullptr);
+  return ok();
+}
+
+zq_status zq_pack_chunked(const void *qw, int N, int K, int bits, void *qd,
+                          void *stream) {
+  const char *fn = "zq_pack_chunked";
+  zq_status st = check_chunked_shape(N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (!qw || !qd) return fail(ZQ_EINVAL, "%s: null qw/qd", fn);
+  if (!aligned(qw, 16) || !aligned(qd, 16))
+    return fail(ZQ_EINVAL, "%s: qw/qd must be 16-byte aligned", fn);
+  const size_t bytes = (size_t)N * K * bits / 8;
+  const char *a = static_cast<const char *>(qw);
+  const char *b = static_cast<const char *>(qd);
+  if (a < b + bytes && b < a + bytes)
+    return fail(ZQ_EINVAL, "%s: qw and qd overlap", fn);
+  return hip_status(
+      zq::launch_pack_chunked(qw, N, K, bits, qd, (hipStream_t)stream), fn);
+}
+
+zq_status zq_gemm_w8a8_chunked(const int8_t *qx, const float *sx,
+                               const int8_t *qd, const float *sw, int G,
+                               const void *bias_fp16, int act, int M, int N,
+                               int K, void *y_fp16, void *stream) {
+  return gemm_chunked(qx, sx, qd, sw, G, bias_fp16, act, M, N, K, y_fp16,
+                      false, stream, 8, "zq_gemm_w8a8_chunked");
+}
+
+zq_status zq_gemm_w4a8_chunked(const int8_t *qx, const float *sx,
+                               const uint8_t *qd4, const float *sw, int G,
+                               const void *bias_fp16, int act, int M, int N,
+                               int K, void *y_fp16, void *stream) {
+  return gemm_chunked(qx, sx, qd4, sw, G, bias_fp16, act, M, N, K, y_fp16,
+                      false, stream, 4, "zq_gemm_w4a8_chunked");
+}
+
+zq_status zq_gemm_chunked_i32(int bits, const int8_t *qx, const void *qd,
+                              int M, int N, int K, int32_t *acc,
+                              void *stream) {
+  const char *fn = "zq_gemm_chunked_i32";
+  if (bits != 8 && bits != 4) return fail(ZQ_EINVAL, "%s: bits=%d", fn, bits);
+  return gemm_chunked(qx, nullptr, qd, nullptr, 1, nullptr, 0, M, N, K, acc,
+                      true, stream, bits, fn);
+}
+
+zq_status zq_gemm_chunked_plan(int M, int N, int K, int bits, char *buf,
+                               int buflen) {
+  const char *fn = "zq_gemm_chunked_plan";
+  if (!buf || buflen <= 0) return fail(ZQ_EINVAL, "%s: null buffer", fn);
+  zq_status st = check_chunked_shape(N, K, bits, fn);
+  if (st != ZQ_OK) return st;
+  if (M < 0 || M > 16)
+    return fail(ZQ_ESHAPE, "%s: M=%d outside 0..16", fn, M);
+  zq::describe_gemm_chunked_plan(M, N, K, bits, buf, buflen);
+  return ok();
 }
 
 zq_status zq_gemm_w8a16_plan(int M, int N, int K, char *buf, int buflen) {

@@ -1183,7 +1183,7 @@ __device__ __forceinline__ void wait_chunks(int later) {
 // once per launch.
 constexpr int kCopyNT = 2;
 
-template <class C>
+template <class C, bool CHK>
 __device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
                                              const char *X, int ldw, int rb,
                                              int c, char *slot, int lane) {
@@ -1195,7 +1195,8 @@ __device__ __forceinline__ void stream_issue(const GemmArgs &p, const char *W,
   constexpr int wpol = C::MX <= 16 ? kCopyNT : 0;
 #pragma unroll
   for (int q = 0; q < C::IW; ++q) {
-    const CopyAddr a = stream_w_copy<C>(q, lane, n0, c, p.N, ldw);
+    const CopyAddr a = CHK ? stream_w_copy_chunked<C>(q, lane, rb, c, ldw)
+                           : stream_w_copy<C>(q, lane, n0, c, p.N, ldw);
     __builtin_amdgcn_global_load_lds(ZQ_GPTR(W + a.goff), ZQ_LPTR(slot + a.lds),
                                      16, 0, wpol);
   }
@@ -1308,7 +1309,8 @@ __device__ __forceinline__ void stream_compute(const GemmArgs &p,
   }
 }
 
-template <class C, bool RAW>
+// CHK: the weights are in the chunk-contiguous layout (stream_w_copy_chunked)
+template <class C, bool RAW, bool CHK = false>
 __global__ void __launch_bounds__(C::NT)
 gemm_stream_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
@@ -1353,7 +1355,7 @@ gemm_stream_kernel(GemmArgs p) {
   // copy cursor: chunk j_issue = (row block index ir, chunk index ic)
   int j_issue = 0, ir = 0, ic = 0;
   auto issue_next = [&]() {
-    stream_issue<C>(p, W, X, ldw, (int)blockIdx.x + ir * (int)gridDim.x,
+    stream_issue<C, CHK>(p, W, X, ldw, (int)blockIdx.x + ir * (int)gridDim.x,
                     wave + ic * C::NW,
                     ring + ((unsigned)j_issue % C::D) * C::SLOT, lane);
     ++j_issue;
@@ -1459,13 +1461,13 @@ static int device_cus() {
   return v;
 }
 
-template <class C, bool RAW>
+template <class C, bool RAW, bool CHK = false>
 static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
   const int nrb = (a.N + C::BN - 1) / C::BN;
   const int cus = device_cus();
   const int grid = nrb < cus ? nrb : cus;
-  hipLaunchKernelGGL((gemm_stream_kernel<C, RAW>), dim3(grid), dim3(C::NT), 0,
-                     s, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<C, RAW, CHK>), dim3(grid), dim3(C::NT),
+                     0, s, a);
   return hipGetLastError();
 }
 
@@ -1819,6 +1821,123 @@ static hipError_t run_gemv(const GemmArgs &a, hipStream_t s, int bpc,
   hipLaunchKernelGGL((gemm_gemv_kernel<C, RAW>), dim3(grid), dim3(C::NT), 0,
                      s, a, rpb, interleave, xq_codes, xq_scale);
   return hipGetLastError();
+}
+
+// ========================================================= chunked layout
+// Weights repacked for the rings of up to 16 token rows: [row block][chunk]
+// [BN rows][CK bytes], so that every copy instruction of the ring reads
+// 1 KB of consecutive bytes instead of 1024 / CK rows at a row stride (the
+// row-major weights).  BN and CK are those of the 16-token ring for the
+// shape, fixed here independently of the device (the rules of choose() /
+// stream_resident at 256 compute units), so that a packed buffer stays
+// valid everywhere; every token count from 1 to 16 runs that ring.
+//   W8: resident activations when K <= 6144 and N / 16 >= 512 (BN 16; CK 512
+//       for K <= 4096, else 256); else BN 32 when 256 < N / 16 and
+//       N / 32 <= 256, else BN 16; CK 256.
+//   W4: BN 32; resident activations when K <= 6144 and N / 32 >= 512 (CK 256
+//       packed bytes for K <= 4096, else 128); else CK 128.
+// Returns false when the shape does not tile (N % BN, row bytes % CK).
+bool chunked_layout(int N, int K, int bits, int *bn, int *ck, int *xr) {
+  const bool w4 = bits == 4;
+  const int ldw = w4 ? K / 2 : K;
+  int b, c, x = 0;
+  if (!w4) {
+    if (K <= 6144 && N / 16 >= 512) {
+      b = 16;
+      x = K <= 4096 ? 2 : 6;
+      c = K <= 4096 ? 512 : 256;
+    } else {
+      b = (N / 16 > 256 && N / 32 <= 256) ? 32 : 16;
+      c = 256;
+    }
+  } else {
+    b = 32;
+    if (K <= 6144 && N / 32 >= 512) {
+      x = K <= 4096 ? 2 : 6;
+      c = K <= 4096 ? 256 : 128;
+    } else {
+      c = 128;
+    }
+  }
+  if (bn) *bn = b;
+  if (ck) *ck = c;
+  if (xr) *xr = x;
+  return N > 0 && K > 0 && N % b == 0 && ldw % c == 0;
+}
+
+// Row-major codes -> chunked layout, one thread per 16-byte unit of the
+// output: unit u = ((rb * NC + c) * BN + r) * (CK / 16) + j holds bytes
+// c * CK + 16 j .. + 15 of row rb * BN + r.
+__global__ void __launch_bounds__(256)
+chunk_pack_kernel(const char *__restrict__ qw, int ldw, int bn, int ck,
+                  size_t units, char *__restrict__ out) {
+  const size_t u = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int jn = ck / 16;
+  const int j = (int)(u % jn);
+  const size_t rc = u / jn;  // (rb * NC + c) * BN + r
+  const int r = (int)(rc % bn);
+  const size_t chunk = rc / bn;
+  const int nc = ldw / ck;
+  const size_t rb = chunk / nc;
+  const int c = (int)(chunk % nc);
+  const size_t src = (rb * bn + r) * (size_t)ldw + (size_t)c * ck + 16 * j;
+  *reinterpret_cast<v4i *>(out + u * 16) =
+      *reinterpret_cast<const v4i *>(qw + src);
+}
+
+hipError_t launch_pack_chunked(const void *qw, int N, int K, int bits,
+                               void *out, hipStream_t s) {
+  int bn, ck;
+  chunked_layout(N, K, bits, &bn, &ck, nullptr);
+  const int ldw = bits == 4 ? K / 2 : K;
+  const size_t units = (size_t)N * ldw / 16;
+  const size_t grid = (units + 255) / 256;
+  hipLaunchKernelGGL(chunk_pack_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     static_cast<const char *>(qw), ldw, bn, ck, units,
+                     static_cast<char *>(out));
+  return hipGetLastError();
+}
+
+template <bool W4, bool RAW>
+static hipError_t run_chunked(const GemmArgs &a, hipStream_t s) {
+  int bn, ck, xr;
+  chunked_layout(a.N, a.K, a.bits, &bn, &ck, &xr);
+  if constexpr (W4) {
+    if (xr == 2)
+      return run_stream<Stream<2, 16, 4, 256, 2, true, false, 2>, RAW, true>(a, s);
+    if (xr == 6)
+      return run_stream<Stream<2, 16, 4, 128, 3, true, false, 6>, RAW, true>(a, s);
+    return run_stream<Stream<2, 16, 4, 128, 4, true>, RAW, true>(a, s);
+  } else {
+    if (xr == 2)
+      return run_stream<Stream<1, 16, 4, 512, 2, false, false, 2>, RAW, true>(a, s);
+    if (xr == 6)
+      return run_stream<Stream<1, 16, 4, 256, 3, false, false, 6>, RAW, true>(a, s);
+    if (bn == 32)
+      return run_stream<Stream<2, 16, 4, 256, 3, false>, RAW, true>(a, s);
+    return run_stream<Stream<1, 16, 4, 256, 4, false>, RAW, true>(a, s);
+  }
+}
+
+hipError_t launch_gemm_chunked(const GemmArgs &a, hipStream_t s) {
+  if (a.bits == 4)
+    return a.raw_i32 ? run_chunked<true, true>(a, s)
+                     : run_chunked<true, false>(a, s);
+  return a.raw_i32 ? run_chunked<false, true>(a, s)
+                   : run_chunked<false, false>(a, s);
+}
+
+int describe_gemm_chunked_plan(int M, int N, int K, int bits, char *buf,
+                               int len) {
+  int bn, ck, xr;
+  chunked_layout(N, K, bits, &bn, &ck, &xr);
+  const int nrb = N / bn;
+  return snprintf(buf, len,
+                  "chunked stream BN=%d CK=%d MX=16 NW=4 W%d%s M=%d "
+                  "row_blocks=%d grid=%d",
+                  bn, ck, bits, xr ? (xr == 2 ? " xres=2" : " xres=6") : "", M,
+                  nrb, nrb < device_cus() ? nrb : device_cus());
 }
 
 // ================================================================ dispatch

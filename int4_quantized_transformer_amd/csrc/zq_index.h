@@ -284,6 +284,22 @@ ZQ_HD inline CopyAddr stream_w_copy(int q, int lane, int n0, int c, int N,
   return CopyAddr{(int64_t)n * ldw + kb, q * 1024};
 }
 
+// The same copy from weights in the chunk-contiguous layout
+// [row block][chunk][BN rows][CK bytes] (N % BN == 0, ldw % CK == 0): the
+// BN x CK bytes of a chunk are one contiguous range, so the 1024 / CK rows
+// of one copy instruction are 1 KB of consecutive bytes (their 16-byte
+// columns permuted by the same swizzle).  The LDS image is the row-major
+// layout's.
+template <class C>
+ZQ_HD inline CopyAddr stream_w_copy_chunked(int q, int lane, int rb, int c,
+                                            int ldw) {
+  const int o = q * 1024 + lane * 16;
+  const int row = o / C::CK;
+  const int col = ((o % C::CK) >> 4) ^ (row & C::WSW);
+  const int64_t chunk = (int64_t)rb * (ldw / C::CK) + c;
+  return CopyAddr{(chunk * C::BN + row) * C::CK + col * 16, q * 1024};
+}
+
 // Activation copy q (of IXC per chunk) of chunk c: token rows past MX (the
 // padding of the last copy) and past M re-read a valid row.  The LDS offset
 // is that of the ring slot; a resident chunk image (XR > 0) places the same

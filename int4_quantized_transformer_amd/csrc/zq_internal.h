@@ -316,6 +316,15 @@ hipError_t launch_static_quant(const void *x, size_t n, const float *state,
                                int8_t *q, float *s_out, hipStream_t s);
 // INT8 weights with fp16 activations (a.qx holds fp16 [M][K], a.sx unused).
 hipError_t launch_gemm_w8a16(const GemmArgs &a, hipStream_t s);
+// Chunk-contiguous weight layout of the rings of up to 16 token rows:
+// its row-block and chunk sizes for the shape (false: the shape does not
+// tile), the repack, and the GEMM over it (1 <= M <= 16).
+bool chunked_layout(int N, int K, int bits, int *bn, int *ck, int *xr);
+hipError_t launch_pack_chunked(const void *qw, int N, int K, int bits,
+                               void *out, hipStream_t s);
+hipError_t launch_gemm_chunked(const GemmArgs &a, hipStream_t s);
+int describe_gemm_chunked_plan(int M, int N, int K, int bits, char *buf,
+                               int len);
 int describe_gemm_w8a16_plan(int M, int N, int K, char *buf, int len);
 // Human-readable schedule for (M, N, K, bits); returns chars written.
 int describe_gemm_plan(int M, int N, int K, int bits, char *buf, int len);

@@ -226,6 +226,37 @@ static void check_stream(const char *name, const Shape &sh) {
           const int64_t want = (int64_t)(n0 + r) * ldw + c * C::CK + 16 * j;
           REQUIRE(img.src[slot] == want, "%s W image r %d j %d c %d", name, r, j, c);
         }
+      // the chunk-contiguous weight layout (where the shape tiles into it):
+      // the same LDS image from one contiguous range per chunk, and every
+      // copy instruction reads 1 KB of consecutive bytes
+      if (sh.N % C::BN == 0 && ldw % C::CK == 0) {
+        Image cimg(C::SLOT);
+        for (int q = 0; q < C::IW; ++q) {
+          int64_t lo = INT64_MAX, hi = -1;
+          for (int lane = 0; lane < kWave; ++lane) {
+            const CopyAddr a = stream_w_copy_chunked<C>(q, lane, rb, c, ldw);
+            REQUIRE(a.goff >= 0 && a.goff + 16 <= wbytes && a.goff % 16 == 0,
+                    "%s chunked W copy %lld of %lld (N%d K%d rb %d c %d)",
+                    name, (long long)a.goff, (long long)wbytes, sh.N, sh.K,
+                    rb, c);
+            REQUIRE(a.lds == q * 1024, "%s chunked W lds", name);
+            cimg.put(a.lds + 16 * lane, a.goff);
+            lo = a.goff < lo ? a.goff : lo;
+            hi = a.goff > hi ? a.goff : hi;
+            ++g_checked;
+          }
+          REQUIRE(hi - lo == 1024 - 16 && lo % 1024 == 0,
+                  "%s chunked copy %d not one 1 KB run", name, q);
+        }
+        for (int r = 0; r < C::BN; ++r)
+          for (int j = 0; j < C::CK / 16; ++j) {
+            const int slot = (r * C::CK) / 16 + (j ^ (r & C::WSW));
+            const int64_t want =
+                (((int64_t)rb * (ldw / C::CK) + c) * C::BN + r) * C::CK + 16 * j;
+            REQUIRE(cimg.src[slot] == want, "%s chunked W image r %d j %d c %d",
+                    name, r, j, c);
+          }
+      }
       for (int t = 0; t < sh.M; ++t)
         for (int j = 0; j < C::XCK / 16 && c * C::XCK + 16 * j < xrow; ++j) {
           const int slot = C::XOFF / 16 + (t * C::XCK) / 16 + (j ^ (t & C::XSW));

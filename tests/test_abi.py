@@ -469,3 +469,40 @@ def test_gemm_xq_plan_names_the_form():
     assert Z.gemm_xq_plan(1, 4096, 65536, 8).startswith("row-quant + gemv")
     assert Z.gemm_xq_plan(16, 4096, 16384, 8).startswith("row-quant + stream")
     assert Z.gemm_xq_plan(2048, 6144, 24576, 4).startswith("row-quant + tiled")
+
+
+@pytest.mark.parametrize("N,K,bits,rows,chunk", [
+    (12288, 4096, 8, 16, 512), (4096, 4096, 8, 16, 256),
+    (16384, 4096, 8, 16, 512), (4096, 16384, 8, 16, 256),
+    (18432, 6144, 8, 16, 256), (6144, 6144, 8, 32, 256),
+    (24576, 6144, 4, 32, 128), (6144, 24576, 4, 32, 128),
+    (16384, 1024, 4, 32, 256)])
+def test_chunked_layout_of_the_decode_shapes(N, K, bits, rows, chunk):
+    # the 16-token ring each decode linear of GPT-J-6B / GPT-NeoX-20B runs
+    L = Z.lib()
+    r, c = ctypes.c_int(0), ctypes.c_int(0)
+    assert L.zq_chunked_layout(N, K, bits, ctypes.byref(r), ctypes.byref(c)) == OK
+    assert (r.value, c.value) == (rows, chunk)
+
+
+def test_chunked_argument_checks():
+    L = Z.lib()
+    r, c = ctypes.c_int(0), ctypes.c_int(0)
+    assert L.zq_chunked_layout(40, 256, 8, ctypes.byref(r), ctypes.byref(c)) == EUNSUP
+    assert L.zq_chunked_layout(256, 320, 8, ctypes.byref(r), ctypes.byref(c)) == EUNSUP
+    assert L.zq_chunked_layout(256, 256, 5, ctypes.byref(r), ctypes.byref(c)) == EINVAL
+    # pack: null / overlapping buffers
+    assert L.zq_pack_chunked(None, 256, 256, 8, B, None) == EINVAL
+    assert L.zq_pack_chunked(A, 256, 256, 8, ctypes.c_void_p(0x10000 + 4096),
+                             None) == EINVAL
+    # (qx, sx, qd, sw, G, bias, act, M, N, K, y, stream)
+    f = L.zq_gemm_w8a8_chunked
+    assert f(A, B, C, D, 64, None, 0, 17, 256, 256, E, None) == EUNSUP   # M > 16
+    assert f(A, B, C, D, 64, None, 0, 4, 40, 256, E, None) == EUNSUP     # N % BN
+    assert f(A, B, C, D, 64, ctypes.c_void_p(0x60002), 0, 4, 256, 256, E,
+             None) == EINVAL                                             # bias
+    assert f(A, B, C, D, 64, None, 0, 0, 256, 256, E, None) == OK        # empty
+    assert L.zq_gemm_chunked_i32(5, A, B, 4, 256, 256, C, None) == EINVAL
+    buf = ctypes.create_string_buffer(160)
+    assert L.zq_gemm_chunked_plan(16, 6144, 24576, 4, buf, 160) == OK
+    assert buf.value.startswith(b"chunked stream BN=32 CK=128")
