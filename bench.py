@@ -545,10 +545,13 @@ def fp16_linear_us(torch, dev, wl, li, M, steps=20):
 
 
 # ------------------------------------------------------------------ decode --
-def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True):
+def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True,
+                chunked=False):
     """One decoder layer's four linears at decode-sized M: GEMM GB/s against
     HBM for the layer (graph replay of the four launches over rotating
-    weight sets larger than the Infinity Cache) and per linear."""
+    weight sets larger than the Infinity Cache) and per linear.  chunked:
+    the weights repacked into the chunk-contiguous decode layout and the
+    _chunked calls (graph only; no fp16 comparator)."""
     from int4_quantized_transformer_amd import workloads as W
     wl = W.workload(name)
     mi = list(wl.M).index(M)
@@ -557,6 +560,8 @@ def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True):
         w, b = W.gen_weights(wl, li)
         x = W.gen_activations(wl, li, m_index=mi)
         qw, sw = zq.quantize_weights(w.to(dev), wl.G, L.bits)
+        if chunked:
+            qw = zq.pack_chunked(qw, L.bits)
         qx, sx = zq.quant_act(x.to(dev))
         lin.append((L, qx, sx, qw, sw, b.to(dev)))
         del w
@@ -577,6 +582,10 @@ def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True):
 
     def call(entry, y):
         L, qx, sx, qw, sw, b = entry
+        if chunked:
+            g = zq.gemm_w8a8_chunked if L.bits == 8 else zq.gemm_w4a8_chunked
+            g(qx, sx, qw, sw, wl.G, b, int(L.gelu), y=y)
+            return
         g = zq.gemm_w8a8_ws if L.bits == 8 else zq.gemm_w4a8_ws
         g(qx, sx, qw, sw, wl.G, b, int(L.gelu), y=y, ws=wss[wsidx[id(y)]])
 
@@ -598,16 +607,19 @@ def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True):
     ms_g /= R
     # the same launches from native code (the library's chain executor)
     chains = []
-    for s_ in sets:
-        c = zq.Chain(M)
-        for (L, qx, sx, qw, sw, b), y, ws in zip(s_, ys, wss):
-            c.gemm_ws(qx, sx, qw, sw, wl.G, y, ws, b, int(L.gelu))
-        chains.append(c)
-    for c in chains:
-        c.run_eager(M, stream=stream.cuda_stream)
-    ms_n, _ = timed_native(torch, chains, M, steps * R, stream)
-    by_launch = {"graph": round(ms_g * 1e3, 2), "native_eager": round(ms_n * 1e3, 2)}
-    ms = min(ms_g, ms_n)
+    by_launch = {"graph": round(ms_g * 1e3, 2)}
+    ms = ms_g
+    if not chunked:
+        for s_ in sets:
+            c = zq.Chain(M)
+            for (L, qx, sx, qw, sw, b), y, ws in zip(s_, ys, wss):
+                c.gemm_ws(qx, sx, qw, sw, wl.G, y, ws, b, int(L.gelu))
+            chains.append(c)
+        for c in chains:
+            c.run_eager(M, stream=stream.cuda_stream)
+        ms_n, _ = timed_native(torch, chains, M, steps * R, stream)
+        by_launch["native_eager"] = round(ms_n * 1e3, 2)
+        ms = min(ms_g, ms_n)
     nbytes = sum(gemm_bytes(M, L.N, L.K, L.bits, wl.G) for (L, *_r) in lin)
     gbs = nbytes / (ms * 1e-3) / 1e9
     per = {}
@@ -619,12 +631,13 @@ def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True):
             "us": round(mi_ * 1e3, 2),
             "GB_per_s": round(b_ / (mi_ * 1e-3) / 1e9, 1),
             "pct_attainable": pct_attainable(2 * M * L.N * L.K, b_, mi_ * 1e-3),
-            "plan": zq.gemm_ws_plan(M, L.N, L.K, L.bits).split(" W")[0],
+            "plan": (zq.gemm_chunked_plan(M, L.N, L.K, L.bits) if chunked
+                     else zq.gemm_ws_plan(M, L.N, L.K, L.bits)).split(" W")[0],
             "bytes": b_}
     del sets, chains
     torch.cuda.empty_cache()
     fp16 = {}
-    if with_fp16:
+    if with_fp16 and not chunked:
         for i, (L, *_r) in enumerate(lin):
             fp16[f"{L.name}"] = round(fp16_linear_us(torch, dev, wl, i, M,
                                                      steps // 4 or 1), 2)
@@ -651,6 +664,13 @@ def decode_figure(torch, zq, dev, steps=100, with_fp16=True):
         for M in ms:
             out[f"{name} M={M}"] = decode_case(torch, zq, dev, name, M, steps,
                                                with_fp16)
+            torch.cuda.empty_cache()
+    # the same layers with the weights in the chunk-contiguous decode layout
+    # (zq_pack_chunked): the rings at 16 tokens, the chunked GEMV at one
+    for name in ("gptj-6b", "neox-20b"):
+        for M in (1, 16):
+            out[f"{name} M={M} chunked"] = decode_case(
+                torch, zq, dev, name, M, steps, False, chunked=True)
             torch.cuda.empty_cache()
     return out
 

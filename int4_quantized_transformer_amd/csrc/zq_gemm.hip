@@ -1920,7 +1920,219 @@ static hipError_t run_chunked(const GemmArgs &a, hipStream_t s) {
   }
 }
 
+// One token over the chunked layout.  A row block (BN rows, all K) is one
+// contiguous range of BN * R bytes (R = row bytes), cut into 1 KB pieces of
+// 1024 / CK rows x CK bytes.  Workgroup b owns rbpb consecutive row blocks
+// (one, as launched); wave w of its NW waves reads pieces w, w + NW, ... of
+// that range (one contiguous window per workgroup), 16 bytes per lane, U
+// pieces in flight (non-temporal: read once).  The pieces per chunk (PPC)
+// are a multiple of NW, so a wave meets the same piece positions in every
+// chunk and each lane always sees the same weight rows (RS = PPC / NW of
+// them, one accumulator each).  The lanes of a row (CK / 16 consecutive
+// lanes) add their partial dot products with DPP at the end of the row
+// block; the epilogue runs once per workgroup, with its operands loaded
+// before the weight stream.  The activation row is staged in LDS once (W4:
+// each 16-byte group in the unpacked nibble order).
+template <int BN_, int CK_, int NW_, bool W4_>
+struct ChunkGemv {
+  static constexpr int BN = BN_, CK = CK_, NW = NW_, U = 8;
+  static constexpr bool W4 = W4_;
+  static constexpr int NT = NW * kWave;
+  static constexpr int PPC = BN * CK / 1024;  // pieces per chunk
+  static constexpr int RPP = 1024 / CK;       // rows per piece
+  static constexpr int LPR = CK / 16;         // lanes per row
+  static constexpr int RS = PPC / NW;
+  static constexpr int RMAX = 1024;           // rows per block
+  static constexpr int XMAX = 32768;          // activation bytes in LDS
+  static constexpr int XR = XMAX / (NT * 16);
+  // every piece position of a chunk belongs to exactly one wave, so each
+  // row's sum is written by one wave
+  static_assert(PPC % NW == 0, "pieces per chunk vs waves");
+  static_assert(U % RS == 0, "accumulator of a piece known at compile time");
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row lanes");
+};
+
+template <class C>
+__device__ __forceinline__ int row_lanes_sum(int v) {
+  v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_i<0x141>(v);   // row_half_mirror: 8-lane sums
+  if constexpr (C::LPR >= 16) v += dpp_i<0x140>(v);  // row_mirror: 16 lanes
+  if constexpr (C::LPR == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+template <class C, bool RAW>
+__global__ void __launch_bounds__(C::NT)
+gemm_chunk_gemv_kernel(GemmArgs p, int rbpb) {
+  __shared__ int rowsum[C::RMAX];
+  __shared__ __attribute__((aligned(1024))) char xs[C::XMAX];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ldw = C::W4 ? p.K / 2 : p.K;
+  const int NC = ldw / C::CK;                 // chunks per row block
+  const int NRB = p.N / C::BN;
+  const int rb0 = (int)blockIdx.x * rbpb;
+  const int rb1 = rb0 + rbpb < NRB ? rb0 + rbpb : NRB;
+  const int nrows = (rb1 - rb0) * C::BN;
+  const int per_rb = NC * C::PPC;             // pieces per row block
+  const int tot = (rb1 - rb0) * per_rb;       // pieces of the block
+  // pieces of this wave: wave, wave + NW, ... (per_rb % NW == 0)
+  const int npieces = tot > wave ? (tot - wave + C::NW - 1) / C::NW : 0;
+  const char *W = static_cast<const char *>(p.qw) +
+                  (size_t)rb0 * per_rb * 1024 + lane * 16;
+  const char *X = reinterpret_cast<const char *>(p.qx);
+
+  // epilogue operands of the rows this thread finishes (i = tid + e*NT)
+  constexpr int E = C::RMAX / C::NT;
+  float esw[E];
+  uint16_t ebits[E];
+  float esx = 0.0f;
+  if constexpr (!RAW) {
+    esx = p.sx[0];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      int n = rb0 * C::BN + (int)threadIdx.x + e * C::NT;
+      n = n < rb1 * C::BN ? n : rb1 * C::BN - 1;
+      esw[e] = p.sw[n / p.G];
+      ebits[e] = *(p.bias ? reinterpret_cast<const uint16_t *>(p.bias) + n
+                          : reinterpret_cast<const uint16_t *>(p.sw));
+    }
+  }
+  // the activation row (K bytes), loaded now, stored after the first
+  // weight loads are in flight
+  v4i xr[C::XR];
+#pragma unroll
+  for (int e = 0; e < C::XR; ++e) {
+    const int off = (e * C::NT + (int)threadIdx.x) * 16;
+    xr[e] = ld16(X + (off < p.K ? off : p.K - 16));
+  }
+
+  // load cursor: piece g = wave + NW * li of the block's range, its chunk c
+  // within the row block (clamped to the last piece once there)
+  const int q0 = wave < tot ? wave : tot - 1;
+  int li = 0, lq = q0;
+  v4i wv[C::U];
+  auto load = [&](int u) {
+    wv[u] = __builtin_nontemporal_load(
+        reinterpret_cast<const v4i *>(W + (size_t)lq * 1024));
+    lq = li < npieces - 1 ? lq + C::NW : lq;
+    ++li;
+  };
+#pragma unroll
+  for (int u = 0; u < C::U; ++u) load(u);
+#pragma unroll
+  for (int e = 0; e < C::XR; ++e) {
+    const int off = (e * C::NT + (int)threadIdx.x) * 16;
+    if (off < p.K)
+      *reinterpret_cast<v4i *>(xs + off) = C::W4 ? perm_even_odd(xr[e]) : xr[e];
+  }
+  lds_barrier();  // activation row visible
+
+  // this lane's rows (within a row block) and 16-byte column of a chunk
+  const int p0 = wave % C::PPC;
+  const int jcol = lane % C::LPR;
+  int acc[C::RS];
+#pragma unroll
+  for (int i = 0; i < C::RS; ++i) acc[i] = 0;
+  // consume cursor: piece index within the row block (wi) and row block
+  int ci = 0, wi = q0 % per_rb, rbl = q0 / per_rb;
+  for (int c0 = 0; c0 < npieces; c0 += C::U) {
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      if (c0 + u < npieces) {
+        const int i = u % C::RS;  // (unrolled: a constant)
+        const int c = wi / C::PPC;                       // chunk
+        const int kb = c * C::CK + 16 * jcol;            // weight byte in row
+        if constexpr (C::W4) {
+          const v4i x0 = ld16(xs + 2 * kb);
+          const v4i x1 = ld16(xs + 2 * kb + 16);
+          acc[i] = dot16(unpack_w4(wv[u][0], wv[u][1]), x0, acc[i]);
+          acc[i] = dot16(unpack_w4(wv[u][2], wv[u][3]), x1, acc[i]);
+        } else {
+          acc[i] = dot16(wv[u], ld16(xs + kb), acc[i]);
+        }
+        int nw = wi + C::NW;
+        const bool wrap = nw >= per_rb;
+        if (wrap || ci == npieces - 1) {
+          // end of this wave's share of the row block: row sums
+#pragma unroll
+          for (int r = 0; r < C::RS; ++r) {
+            const int sum = row_lanes_sum<C>(acc[r]);
+            if (jcol == 0) {
+              const int row = (p0 + C::NW * r) * C::RPP + lane / C::LPR;
+              rowsum[rbl * C::BN + row] = C::W4 ? (sum >> 4) : sum;
+            }
+            acc[r] = 0;
+          }
+        }
+        wi = wrap ? nw - per_rb : nw;
+        rbl = wrap ? rbl + 1 : rbl;
+        ++ci;
+      }
+      load(u);
+    }
+  }
+  lds_barrier();  // row sums complete (the trailing re-reads stay in flight)
+
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = (int)threadIdx.x + e * C::NT;
+    if (i < nrows) {
+      const int n = rb0 * C::BN + i;
+      const int a = rowsum[i];
+      if constexpr (RAW) {
+        static_cast<int32_t *>(p.out)[n] = a;
+      } else {
+        const half_t b =
+            p.bias ? __builtin_bit_cast(half_t, ebits[e]) : (half_t)0.0f;
+        const float sc = esx * esw[e];
+        static_cast<half_t *>(p.out)[n] =
+            p.act == ZQ_ACT_GELU ? gelu_half((float)a, sc, b)
+                                 : fma_half((float)a, sc, b);
+      }
+    }
+  }
+}
+
+template <class C, bool RAW>
+static hipError_t run_chunk_gemv(const GemmArgs &a, hipStream_t s) {
+  // one row block per workgroup (against up to two workgroups per CU with
+  // several row blocks each: the eight GPT-J / NeoX one-token linears 114.3
+  // -> 112.4 us; 16 pieces in flight instead of 8: 123.1 / 126.5 us)
+  const int nrb = a.N / C::BN;
+  hipLaunchKernelGGL((gemm_chunk_gemv_kernel<C, RAW>), dim3(nrb), dim3(C::NT),
+                     0, s, a, 1);
+  return hipGetLastError();
+}
+
+// the one-token kernel over the chunked layout applies while the activation
+// row fits its LDS image
+static bool chunk_gemv_ok(int M, int K) { return M == 1 && K <= 32768; }
+
+template <bool W4, bool RAW>
+static hipError_t run_chunked_gemv(const GemmArgs &a, hipStream_t s) {
+  int bn, ck, xr;
+  chunked_layout(a.N, a.K, a.bits, &bn, &ck, &xr);
+  (void)xr;
+  if constexpr (W4) {
+    if (ck == 256) return run_chunk_gemv<ChunkGemv<32, 256, 4, true>, RAW>(a, s);
+    return run_chunk_gemv<ChunkGemv<32, 128, 4, true>, RAW>(a, s);
+  } else {
+    if (ck == 512) return run_chunk_gemv<ChunkGemv<16, 512, 4, false>, RAW>(a, s);
+    if (bn == 32) return run_chunk_gemv<ChunkGemv<32, 256, 4, false>, RAW>(a, s);
+    return run_chunk_gemv<ChunkGemv<16, 256, 4, false>, RAW>(a, s);
+  }
+}
+
 hipError_t launch_gemm_chunked(const GemmArgs &a, hipStream_t s) {
+  if (chunk_gemv_ok(a.M, a.K)) {
+    if (a.bits == 4)
+      return a.raw_i32 ? run_chunked_gemv<true, true>(a, s)
+                       : run_chunked_gemv<true, false>(a, s);
+    return a.raw_i32 ? run_chunked_gemv<false, true>(a, s)
+                     : run_chunked_gemv<false, false>(a, s);
+  }
   if (a.bits == 4)
     return a.raw_i32 ? run_chunked<true, true>(a, s)
                      : run_chunked<true, false>(a, s);
@@ -1933,6 +2145,10 @@ int describe_gemm_chunked_plan(int M, int N, int K, int bits, char *buf,
   int bn, ck, xr;
   chunked_layout(N, K, bits, &bn, &ck, &xr);
   const int nrb = N / bn;
+  if (chunk_gemv_ok(M, K))
+    return snprintf(buf, len,
+                    "chunked gemv BN=%d CK=%d NW=4 U=8 W%d row_blocks=%d "
+                    "grid=%d", bn, ck, bits, nrb, nrb);
   return snprintf(buf, len,
                   "chunked stream BN=%d CK=%d MX=16 NW=4 W%d%s M=%d "
                   "row_blocks=%d grid=%d",

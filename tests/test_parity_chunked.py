@@ -4,7 +4,8 @@
   (a permutation of the row-major bytes: qd[((rb*NC + c)*BN + r)*CK + b] =
   qw[(rb*BN + r)*R + c*CK + b]).
 * zq_gemm_chunked_i32 on the packed oracle codes: int32 accumulators
-  bit-exact against oracle.gemm_i32 on the row-major codes, 1..16 tokens,
+  bit-exact against oracle.gemm_i32 on the row-major codes, 1..16 tokens
+  (one token: the chunked GEMV, or the ring for K > 32768),
   every ring the layout selects (W8 16- and 32-row blocks, W4, resident
   activations with 512- / 256-byte and 256- / 128-byte chunks), the full
   code range.
@@ -61,6 +62,9 @@ LAYOUT_SHAPES = [
     (8, 8192, 1024), (8, 8192, 4608), (8, 6144, 768), (8, 256, 512),
     (8, 1024, 8192), (4, 16384, 1024), (4, 16384, 5120), (4, 64, 256),
     (4, 2048, 9216),
+    # K > 32768: one token runs the ring (the activation row exceeds the
+    # one-token kernel's LDS image)
+    (8, 64, 33024), (4, 64, 33024),
 ]
 
 
