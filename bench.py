@@ -65,6 +65,11 @@ def parse():
                     help="step: attn-out and FFN2 as quantize-on-load calls "
                          "(zq_gemm_*_xq) where they run as one kernel (one "
                          "token); with --summarize, summarize such a run")
+    ap.add_argument("--chunked", action="store_true",
+                    help="step (at most 16 tokens): the GEMMs on weights in "
+                         "the chunk-contiguous decode layout (zq_pack_chunked, "
+                         "zq_gemm_*_chunked); graph launches only; with "
+                         "--summarize, summarize such a run")
     ap.add_argument("--no-xq", action="store_true",
                     help="skip the one-token quantize-on-load figure")
     ap.add_argument("--no-chain", action="store_true",
@@ -108,6 +113,15 @@ def xq_bytes(M, N, K, bits, G):
 STEP_XQ = False
 
 
+# the step's GEMMs on the chunk-contiguous decode layout (--chunked)
+STEP_CHUNKED = False
+
+
+def step_chunked(M):
+    """Whether the step runs its GEMMs on the chunked decode layout."""
+    return STEP_CHUNKED and M <= 16
+
+
 def step_xq(zq, L, M):
     """Whether the step runs linear L as one quantize-on-load kernel."""
     return STEP_XQ and not L.ln and zq.gemm_xq_plan(
@@ -142,6 +156,8 @@ def build_sets(wl, M, dev, rotate_bytes):
         wd = w.to(dev)
         qw, sw = zq.quantize_weights(wd, wl.G, L.bits)
         del wd
+        if step_chunked(M):
+            qw = zq.pack_chunked(qw, L.bits)
         base.append(dict(L=L, x=x.to(dev), qw=qw, sw=sw, b=b.to(dev),
                          w_cpu=w, b_cpu=b, x_cpu=x))
     per_set = 0
@@ -215,7 +231,11 @@ def make_step(zq, lins, wl, M, stream_ptr):
             calls.append((f"{L.name}.quant", L_.zq_quant_act,
                           (P(s.x.data_ptr()), M, L.K, P(s.qx.data_ptr()),
                            P(s.sx.data_ptr()), st)))
-        fn = L_.zq_gemm_w8a8 if L.bits == 8 else L_.zq_gemm_w4a8
+        if step_chunked(M):
+            fn = (L_.zq_gemm_w8a8_chunked if L.bits == 8
+                  else L_.zq_gemm_w4a8_chunked)
+        else:
+            fn = L_.zq_gemm_w8a8 if L.bits == 8 else L_.zq_gemm_w4a8
         calls.append((f"{L.name}.gemm_w{L.bits}a8", fn,
                       (P(s.qx.data_ptr()), P(s.sx.data_ptr()),
                        P(s.qw.data_ptr()), P(s.sw.data_ptr()), wl.G,
@@ -420,6 +440,8 @@ def grid_threads(name, L, M, G, zq):
     """Launch grid (threads) of the kernel behind a step entry, as the
     kernel trace reports it (used to find that launch in rocprofv3 output)."""
     plan = zq.gemm_plan(M, L.N, L.K, L.bits) if ".gemm" in name else ""
+    if ".gemm" in name and step_chunked(M):
+        plan = zq.gemm_chunked_plan(M, L.N, L.K, L.bits).replace("chunked ", "")
     if name.endswith("_xq"):
         plan = zq.gemm_xq_plan(M, L.N, L.K, L.bits).replace(
             "quantize-on-load ", "")
@@ -487,9 +509,14 @@ def step_entries(zq, wl, M):
                     "ops": 0, "bytes": quant_bytes(M, L.K, L.ln)})
         gn = f"{L.name}.gemm_w{L.bits}a8"
         plan = zq.gemm_plan(M, L.N, L.K, L.bits)
+        if step_chunked(M):
+            plan = zq.gemm_chunked_plan(M, L.N, L.K, L.bits).replace(
+                "chunked ", "")
         kern = {"tiled": "gemm_tiled_kernel", "stream": "gemm_stream_kernel",
                 "gemv": "gemm_gemv_kernel", "skinny": "gemm_skinny_kernel"}[
                     plan.split()[0]]
+        if step_chunked(M) and plan.startswith("gemv"):
+            kern = "gemm_chunk_gemv_kernel"
         if "ping-pong" in plan:
             kern = "gemm_pingpong_kernel"
         ops = 2 * M * L.N * L.K
@@ -1246,7 +1273,8 @@ def summarize(d, traffic_out=None, workload="neox-20b", m_index=None):
 
 def step_key(wl, M):
     """Name of a profiled step in the traffic file."""
-    return f"{wl.name} M={M}" + (" quant-on-load" if STEP_XQ else "")
+    return (f"{wl.name} M={M}" + (" quant-on-load" if STEP_XQ else "")
+            + (" chunked" if step_chunked(M) else ""))
 
 
 def mfma_lines(d, gemm_e, lines):
@@ -1312,9 +1340,10 @@ def copy_calibration(torch, dev):
 
 
 def main():
-    global STEP_XQ
+    global STEP_XQ, STEP_CHUNKED
     args = parse()
     STEP_XQ = args.quant_on_load
+    STEP_CHUNKED = args.chunked
     if args.summarize:
         summarize(args.summarize, args.write_traffic, args.workload,
                   args.m_index)
@@ -1378,11 +1407,14 @@ def main():
     # executor; the step is timed both ways and `value` takes the faster
     # (on this runtime a graph node costs more than a native launch once
     # the host keeps ahead of the GPU)
-    chains = [make_chain(zq, sets[r], wl, M) for r in range(R)]
-    for i in range(args.warmup):
-        chains[i % R].run_eager(M, stream=stream.cuda_stream)
-    ms_n, wall_n = timed_native(torch, chains, M, args.steps, stream)
-    by_launch = {"native_eager": round(ms_n, 5)}
+    # (the chain executor has no chunked-layout call: graph only there)
+    by_launch = {}
+    if not step_chunked(M):
+        chains = [make_chain(zq, sets[r], wl, M) for r in range(R)]
+        for i in range(args.warmup):
+            chains[i % R].run_eager(M, stream=stream.cuda_stream)
+        ms_n, wall_n = timed_native(torch, chains, M, args.steps, stream)
+        by_launch["native_eager"] = round(ms_n, 5)
     if not args.no_graph:
         by_launch["graph"] = round(ms_g, 5)
     launch = min(by_launch, key=by_launch.get)
