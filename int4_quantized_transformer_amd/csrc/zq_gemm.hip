@@ -1830,7 +1830,8 @@ static hipError_t run_gemv(const GemmArgs &a, hipStream_t s, int bpc,
 // row-major weights).  BN and CK are those of the 16-token ring for the
 // shape, fixed here independently of the device (the rules of choose() /
 // stream_resident at 256 compute units), so that a packed buffer stays
-// valid everywhere; every token count from 1 to 16 runs that ring.
+// valid everywhere.  2 to 16 tokens run that ring; one token runs
+// gemm_chunk_gemv_kernel (the ring where its activation row would not fit).
 //   W8: resident activations when K <= 6144 and N / 16 >= 512 (BN 16; CK 512
 //       for K <= 4096, else 256); else BN 32 when 256 < N / 16 and
 //       N / 32 <= 256, else BN 16; CK 256.
