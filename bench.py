@@ -68,8 +68,8 @@ def parse():
     ap.add_argument("--chunked", action="store_true",
                     help="step (at most 16 tokens): the GEMMs on weights in "
                          "the chunk-contiguous decode layout (zq_pack_chunked, "
-                         "zq_gemm_*_chunked); graph launches only; with "
-                         "--summarize, summarize such a run")
+                         "zq_gemm_*_chunked); with --summarize, summarize "
+                         "such a run")
     ap.add_argument("--no-xq", action="store_true",
                     help="skip the one-token quantize-on-load figure")
     ap.add_argument("--no-chain", action="store_true",
@@ -257,7 +257,10 @@ def make_chain(zq, lins, wl, M):
             c.ln_quant(s.x, s.qx, s.sx, None, None, wl.ln_eps)
         else:
             c.quant(s.x, s.qx, s.sx)
-        c.gemm(s.qx, s.sx, s.qw, s.sw, wl.G, s.y, s.b, int(L.gelu))
+        if step_chunked(M):
+            c.gemm_chunked(s.qx, s.sx, s.qw, s.sw, wl.G, s.y, s.b, int(L.gelu))
+        else:
+            c.gemm(s.qx, s.sx, s.qw, s.sw, wl.G, s.y, s.b, int(L.gelu))
     return c
 
 
@@ -578,7 +581,7 @@ def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True,
     HBM for the layer (graph replay of the four launches over rotating
     weight sets larger than the Infinity Cache) and per linear.  chunked:
     the weights repacked into the chunk-contiguous decode layout and the
-    _chunked calls (graph only; no fp16 comparator)."""
+    _chunked calls (no fp16 comparator)."""
     from int4_quantized_transformer_amd import workloads as W
     wl = W.workload(name)
     mi = list(wl.M).index(M)
@@ -634,19 +637,20 @@ def decode_case(torch, zq, dev, name, M, steps=100, with_fp16=True,
     ms_g /= R
     # the same launches from native code (the library's chain executor)
     chains = []
-    by_launch = {"graph": round(ms_g * 1e3, 2)}
-    ms = ms_g
-    if not chunked:
-        for s_ in sets:
-            c = zq.Chain(M)
-            for (L, qx, sx, qw, sw, b), y, ws in zip(s_, ys, wss):
+    for s_ in sets:
+        c = zq.Chain(M)
+        for (L, qx, sx, qw, sw, b), y, ws in zip(s_, ys, wss):
+            if chunked:
+                c.gemm_chunked(qx, sx, qw, sw, wl.G, y, b, int(L.gelu))
+            else:
                 c.gemm_ws(qx, sx, qw, sw, wl.G, y, ws, b, int(L.gelu))
-            chains.append(c)
-        for c in chains:
-            c.run_eager(M, stream=stream.cuda_stream)
-        ms_n, _ = timed_native(torch, chains, M, steps * R, stream)
-        by_launch["native_eager"] = round(ms_n * 1e3, 2)
-        ms = min(ms_g, ms_n)
+        chains.append(c)
+    for c in chains:
+        c.run_eager(M, stream=stream.cuda_stream)
+    ms_n, _ = timed_native(torch, chains, M, steps * R, stream)
+    by_launch = {"graph": round(ms_g * 1e3, 2),
+                 "native_eager": round(ms_n * 1e3, 2)}
+    ms = min(ms_g, ms_n)
     nbytes = sum(gemm_bytes(M, L.N, L.K, L.bits, wl.G) for (L, *_r) in lin)
     gbs = nbytes / (ms * 1e-3) / 1e9
     per = {}
@@ -1407,14 +1411,11 @@ def main():
     # executor; the step is timed both ways and `value` takes the faster
     # (on this runtime a graph node costs more than a native launch once
     # the host keeps ahead of the GPU)
-    # (the chain executor has no chunked-layout call: graph only there)
-    by_launch = {}
-    if not step_chunked(M):
-        chains = [make_chain(zq, sets[r], wl, M) for r in range(R)]
-        for i in range(args.warmup):
-            chains[i % R].run_eager(M, stream=stream.cuda_stream)
-        ms_n, wall_n = timed_native(torch, chains, M, args.steps, stream)
-        by_launch["native_eager"] = round(ms_n, 5)
+    chains = [make_chain(zq, sets[r], wl, M) for r in range(R)]
+    for i in range(args.warmup):
+        chains[i % R].run_eager(M, stream=stream.cuda_stream)
+    ms_n, wall_n = timed_native(torch, chains, M, args.steps, stream)
+    by_launch = {"native_eager": round(ms_n, 5)}
     if not args.no_graph:
         by_launch["graph"] = round(ms_g, 5)
     launch = min(by_launch, key=by_launch.get)

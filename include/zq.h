@@ -469,7 +469,10 @@ int zq_sched_entries(void);
  * records zq_gemm_w8a8_ws (bits 8) or zq_gemm_w4a8_ws (bits 4), and
  * zq_chain_add_gemm_xq zq_gemm_w8a8_xq or zq_gemm_w4a8_xq (the graph for
  * one token holds its single kernel, the graphs for more tokens the
- * quantizer and the GEMM).
+ * quantizer and the GEMM).  zq_chain_add_gemm_chunked records
+ * zq_gemm_w8a8_chunked or zq_gemm_w4a8_chunked (weights in the chunked
+ * decode layout; the chain's max_m must be at most 16, else
+ * ZQ_EUNSUPPORTED).
  *
  * zq_chain_run(chain, M, stream): runs the sequence over the first M rows
  * of every buffer.  The first run with a given M (or the first after the
@@ -518,6 +521,11 @@ zq_status zq_chain_add_gemm_w8a16(zq_chain *c, const void *x_fp16,
                                   const int8_t *qw, const float *sw, int G,
                                   const void *bias_fp16, int act, int N, int K,
                                   void *y_fp16);
+zq_status zq_chain_add_gemm_chunked(zq_chain *c, int bits, const int8_t *qx,
+                                    const float *sx, const void *qd,
+                                    const float *sw, int G,
+                                    const void *bias_fp16, int act, int N,
+                                    int K, void *y_fp16);
 zq_status zq_chain_add_gemm_xq(zq_chain *c, int bits, const void *x_fp16,
                                const void *qw, const float *sw, int G,
                                const void *bias_fp16, int act, int N, int K,

@@ -98,6 +98,7 @@ def lib():
             "zq_gemm_ws_plan": [I, I, I, I, ctypes.c_char_p, I],
             "zq_gemm_noalloc": [I, P, P, P, P, I, P, I, I, I, I, P, P],
             "zq_chain_run_eager": [P, I, P],
+            "zq_chain_add_gemm_chunked": [P, I, P, P, P, P, I, P, I, I, I, P],
             "zq_chunked_layout": [I, I, I, P, P],
             "zq_pack_chunked": [P, I, I, I, P, P],
             "zq_gemm_w8a8_chunked": [P, P, P, P, I, P, I, I, I, I, P, P],
@@ -617,6 +618,15 @@ class Chain:
                                           _p(sw), G, _p(bias), int(act), N, K,
                                           _p(y), _p(ws),
                                           0 if ws is None else ws.numel()))
+
+    def gemm_chunked(self, qx, sx, qd, sw, G, y, bias=None, act=ACT_NONE):
+        """gemm_w8a8_chunked / gemm_w4a8_chunked (weights from pack_chunked;
+        the chain's max_m must be at most 16)."""
+        bits, N, K = self._gemm_common(qx, sx, qd, sw, bias)
+        self._rows(y, "y", torch.float16, N)
+        _check(lib().zq_chain_add_gemm_chunked(self._h, bits, _p(qx), _p(sx),
+                                               _p(qd), _p(sw), G, _p(bias),
+                                               int(act), N, K, _p(y)))
 
     def gemm_w8a16(self, x, qw, sw, G, y, bias=None, act=ACT_NONE):
         K = x.shape[1]

@@ -16,7 +16,9 @@
 
 namespace {
 
-enum OpKind { kLnQuant, kQuant, kGemm, kGemmQuant, kGemmA16, kGemmWs, kGemmXq };
+enum OpKind {
+  kLnQuant, kQuant, kGemm, kGemmQuant, kGemmA16, kGemmWs, kGemmXq, kGemmChunked
+};
 
 struct ChainOp {
   OpKind kind;
@@ -90,6 +92,14 @@ zq_status run_op(const ChainOp &o, int M, void *s) {
                  : zq_gemm_w4a8_xq(o.x, (const uint8_t *)o.qw, o.sw, o.G,
                                    o.bias, o.act, M, o.N, o.K, o.y, o.qx,
                                    o.sx, s);
+    case kGemmChunked:
+      return o.bits == 8
+                 ? zq_gemm_w8a8_chunked(o.gqx, o.gsx, (const int8_t *)o.qw,
+                                        o.sw, o.G, o.bias, o.act, M, o.N, o.K,
+                                        o.y, s)
+                 : zq_gemm_w4a8_chunked(o.gqx, o.gsx, (const uint8_t *)o.qw,
+                                        o.sw, o.G, o.bias, o.act, M, o.N, o.K,
+                                        o.y, s);
   }
   return zq::fail(ZQ_EINVAL, "zq_chain: unknown call kind");
 }
@@ -131,6 +141,10 @@ zq_status add(zq_chain *c, const ChainOp &op, const char *fn,
     return zq::fail(ZQ_EINVAL, "%s: null buffer sized by M", fn);
   zq_status st = run_op(op, 0, nullptr);
   if (st != ZQ_OK) return st;
+  if (op.kind == kGemmChunked && c->max_m > 16)
+    return zq::fail(ZQ_EUNSUPPORTED,
+                    "%s: the chunked layout serves at most 16 tokens (max_m=%d)",
+                    fn, c->max_m);
   if (op.kind == kGemmQuant &&
       op.ws_bytes < zq_gemm_quant_workspace_bytes(c->max_m, op.N))
     return zq::fail(ZQ_EINVAL, "%s: workspace of %zu bytes, %zu needed for %d rows",
@@ -291,6 +305,28 @@ zq_status zq_chain_add_gemm_quant(zq_chain *c, int bits, const int8_t *qx,
   o.ws = ws;
   o.ws_bytes = ws_bytes;
   return add(c, o, "zq_chain_add_gemm_quant", !qx || !sx || !qy || !sy || !ws);
+}
+
+zq_status zq_chain_add_gemm_chunked(zq_chain *c, int bits, const int8_t *qx,
+                                    const float *sx, const void *qd,
+                                    const float *sw, int G,
+                                    const void *bias_fp16, int act, int N,
+                                    int K, void *y_fp16) {
+  if (bits != 8 && bits != 4)
+    return zq::fail(ZQ_EINVAL, "zq_chain_add_gemm_chunked: bits=%d", bits);
+  ChainOp o{kGemmChunked};
+  o.bits = bits;
+  o.gqx = qx;
+  o.gsx = sx;
+  o.qw = qd;
+  o.sw = sw;
+  o.G = G;
+  o.bias = bias_fp16;
+  o.act = act;
+  o.N = N;
+  o.K = K;
+  o.y = y_fp16;
+  return add(c, o, "zq_chain_add_gemm_chunked", !qx || !sx || !y_fp16);
 }
 
 zq_status zq_chain_add_gemm_ws(zq_chain *c, int bits, const int8_t *qx,

@@ -506,3 +506,19 @@ def test_chunked_argument_checks():
     buf = ctypes.create_string_buffer(160)
     assert L.zq_gemm_chunked_plan(16, 6144, 24576, 4, buf, 160) == OK
     assert buf.value.startswith(b"chunked stream BN=32 CK=128")
+
+
+def test_chain_chunked_gemm_host_side():
+    L = Z.lib()
+    for max_m, want in ((16, OK), (17, EUNSUP)):
+        h = ctypes.c_void_p()
+        assert L.zq_chain_create(max_m, ctypes.byref(h)) == OK
+        # (chain, bits, qx, sx, qd, sw, G, bias, act, N, K, y)
+        assert L.zq_chain_add_gemm_chunked(h, 8, A, B, C, D, 128, None, 0,
+                                           8192, 1024, E) == want
+        assert L.zq_chain_add_gemm_chunked(h, 8, A, B, C, D, 128, None, 0,
+                                           40, 1024, E) == EUNSUP  # N % BN
+        assert L.zq_chain_add_gemm_chunked(h, 5, A, B, C, D, 128, None, 0,
+                                           8192, 1024, E) == EINVAL
+        assert L.zq_chain_length(h) == (1 if want == OK else 0)
+        L.zq_chain_destroy(h)

@@ -187,3 +187,41 @@ def test_chunked_decode_linears_full_size(wl, li, M):
     what = f"{wl} linear {li} " + zq.gemm_chunked_plan(M, N, K, bits)
     assert np.array_equal(yn.view(np.uint16), to_np(y_rm).view(np.uint16)), what
     assert_fp16_close_to_oracle(yn[:, cols], z, what)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_chunked_chain_graph_and_eager_vs_oracle(M):
+    """Two chunked-layout GEMMs (W8 with resident activations, then W4)
+    recorded in a chain of 16 rows: the HIP graph and the native eager run
+    over the first M rows give the same bits, within the oracle tolerance,
+    and leave the rows past M untouched."""
+    d = dev()
+    G = 128
+    lins = [(8, 8192, 1024, 0), (4, 2048, 2048, 1)]
+    ch = zq.Chain(16)
+    ref, outs = [], []
+    for li, (bits, N, K, act) in enumerate(lins):
+        x = W.randn_fp16((16, K), seed=70 + li, std=1.0)
+        w = W.randn_fp16((N, K), seed=80 + li, std=0.02)
+        b = W.randn_fp16((N,), seed=90 + li, std=0.5)
+        qx, sx = oracle.quant_tokens(x.numpy())
+        q, sw = oracle.quantize_weights(w.numpy(), G, bits)
+        y = torch.full((16, N), 7.0, dtype=torch.float16, device=d)
+        ch.gemm_chunked(_to_dev(qx), _to_dev(sx), _pack(q, bits), _to_dev(sw),
+                        G, y, b.to(d), act)
+        acc = oracle.gemm_i32(qx[:M], q)
+        z, _ = oracle.epilogue(acc, sx[:M], sw, G, b.numpy(), act)
+        ref.append(z)
+        outs.append(y)
+    ch.run(M)
+    torch.cuda.synchronize()
+    graph = [to_np(y).copy() for y in outs]
+    for y in outs:
+        y.fill_(7.0)
+    ch.run_eager(M)
+    torch.cuda.synchronize()
+    for li, (y, g, z) in enumerate(zip(outs, graph, ref)):
+        e = to_np(y)
+        assert np.array_equal(e.view(np.uint16), g.view(np.uint16)), li
+        assert_fp16_close_to_oracle(g[:M], z, f"chain linear {li}")
+        assert (g[M:] == 7.0).all(), li
