@@ -1942,13 +1942,17 @@ struct ChunkGemv {
   static constexpr int PPC = BN * CK / 1024;  // pieces per chunk
   static constexpr int RPP = 1024 / CK;       // rows per piece
   static constexpr int LPR = CK / 16;         // lanes per row
-  static constexpr int RS = PPC / NW;
+  // NW <= PPC: each wave owns RS = PPC / NW piece positions of every chunk;
+  // NW > PPC: WPP = NW / PPC waves share a position, each taking every WPP-th
+  // chunk, and their row sums meet in LDS by atomic adds
+  static constexpr int RS = NW <= PPC ? PPC / NW : 1;
+  static constexpr int WPP = NW <= PPC ? 1 : NW / PPC;
   static constexpr int RMAX = 1024;           // rows per block
   static constexpr int XMAX = 32768;          // activation bytes in LDS
   static constexpr int XR = XMAX / (NT * 16);
   // every piece position of a chunk belongs to exactly one wave, so each
   // row's sum is written by one wave
-  static_assert(PPC % NW == 0, "pieces per chunk vs waves");
+  static_assert(PPC % NW == 0 || NW % PPC == 0, "pieces per chunk vs waves");
   static_assert(U % RS == 0, "accumulator of a piece known at compile time");
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row lanes");
 };
@@ -1983,6 +1987,10 @@ gemm_chunk_gemv_kernel(GemmArgs p, int rbpb) {
   const char *W = static_cast<const char *>(p.qw) +
                   (size_t)rb0 * per_rb * 1024 + lane * 16;
   const char *X = reinterpret_cast<const char *>(p.qx);
+  if constexpr (C::WPP > 1) {
+    // shared positions add their partial row sums: start from zero
+    for (int i = threadIdx.x; i < nrows; i += C::NT) rowsum[i] = 0;
+  }
 
   // epilogue operands of the rows this thread finishes (i = tid + e*NT)
   constexpr int E = C::RMAX / C::NT;
@@ -2062,7 +2070,11 @@ gemm_chunk_gemv_kernel(GemmArgs p, int rbpb) {
             const int sum = row_lanes_sum<C>(acc[r]);
             if (jcol == 0) {
               const int row = (p0 + C::NW * r) * C::RPP + lane / C::LPR;
-              rowsum[rbl * C::BN + row] = C::W4 ? (sum >> 4) : sum;
+              const int v = C::W4 ? (sum >> 4) : sum;
+              if constexpr (C::WPP > 1)
+                ds_add1(lds_addr(&rowsum[rbl * C::BN + row]), v);
+              else
+                rowsum[rbl * C::BN + row] = v;
             }
             acc[r] = 0;
           }
@@ -2111,19 +2123,49 @@ static hipError_t run_chunk_gemv(const GemmArgs &a, hipStream_t s) {
 // row fits its LDS image
 static bool chunk_gemv_ok(int M, int K) { return M == 1 && K <= 32768; }
 
+// Waves per workgroup of the one-token kernel: 8 (more bytes in flight per
+// workgroup) where the row blocks number fewer than the CUs, or fewer than
+// two per CU and hold at most 64 KB each; else 4.  Measured, 4 -> 8 waves
+// (us): NeoX FFN2 19.5 -> 16.9, attention output 9.8 -> 9.5, GPT-J
+// attention output 5.88 -> 5.51, but GPT-J FFN2 (256 KB row blocks)
+// 13.9 -> 15.8.  ZQ_CGEMV_NW=<4|8> forces one where it applies (tuning aid).
+static int chunk_gemv_waves(int N, int K, int bits) {
+  int bn, ck;
+  chunked_layout(N, K, bits, &bn, &ck, nullptr);
+  const int nc = (bits == 4 ? K / 2 : K) / ck;
+  const int ppc = bn * ck / 1024;
+  const bool ok8 = ppc == 8 || nc % 2 == 0;  // per-row-block pieces % 8
+  static const int forced = [] {
+    const char *e = getenv("ZQ_CGEMV_NW");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced == 4) return 4;
+  if (forced == 8) return ok8 ? 8 : 4;
+  const int nrb = N / bn, cus = device_cus();
+  const long rb_bytes = (long)bn * (bits == 4 ? K / 2 : K);
+  return ok8 && (nrb < cus || (nrb < 2 * cus && rb_bytes <= 65536)) ? 8 : 4;
+}
+
+template <int NW, bool W4, bool RAW>
+static hipError_t run_chunked_gemv_nw(const GemmArgs &a, int bn, int ck,
+                                      hipStream_t s) {
+  if constexpr (W4) {
+    if (ck == 256) return run_chunk_gemv<ChunkGemv<32, 256, NW, true>, RAW>(a, s);
+    return run_chunk_gemv<ChunkGemv<32, 128, NW, true>, RAW>(a, s);
+  } else {
+    if (ck == 512) return run_chunk_gemv<ChunkGemv<16, 512, NW, false>, RAW>(a, s);
+    if (bn == 32) return run_chunk_gemv<ChunkGemv<32, 256, NW, false>, RAW>(a, s);
+    return run_chunk_gemv<ChunkGemv<16, 256, NW, false>, RAW>(a, s);
+  }
+}
+
 template <bool W4, bool RAW>
 static hipError_t run_chunked_gemv(const GemmArgs &a, hipStream_t s) {
-  int bn, ck, xr;
-  chunked_layout(a.N, a.K, a.bits, &bn, &ck, &xr);
-  (void)xr;
-  if constexpr (W4) {
-    if (ck == 256) return run_chunk_gemv<ChunkGemv<32, 256, 4, true>, RAW>(a, s);
-    return run_chunk_gemv<ChunkGemv<32, 128, 4, true>, RAW>(a, s);
-  } else {
-    if (ck == 512) return run_chunk_gemv<ChunkGemv<16, 512, 4, false>, RAW>(a, s);
-    if (bn == 32) return run_chunk_gemv<ChunkGemv<32, 256, 4, false>, RAW>(a, s);
-    return run_chunk_gemv<ChunkGemv<16, 256, 4, false>, RAW>(a, s);
-  }
+  int bn, ck;
+  chunked_layout(a.N, a.K, a.bits, &bn, &ck, nullptr);
+  if (chunk_gemv_waves(a.N, a.K, a.bits) == 8)
+    return run_chunked_gemv_nw<8, W4, RAW>(a, bn, ck, s);
+  return run_chunked_gemv_nw<4, W4, RAW>(a, bn, ck, s);
 }
 
 hipError_t launch_gemm_chunked(const GemmArgs &a, hipStream_t s) {
@@ -2148,8 +2190,9 @@ int describe_gemm_chunked_plan(int M, int N, int K, int bits, char *buf,
   const int nrb = N / bn;
   if (chunk_gemv_ok(M, K))
     return snprintf(buf, len,
-                    "chunked gemv BN=%d CK=%d NW=4 U=8 W%d row_blocks=%d "
-                    "grid=%d", bn, ck, bits, nrb, nrb);
+                    "chunked gemv BN=%d CK=%d NW=%d U=8 W%d row_blocks=%d "
+                    "grid=%d", bn, ck, chunk_gemv_waves(N, K, bits), bits,
+                    nrb, nrb);
   return snprintf(buf, len,
                   "chunked stream BN=%d CK=%d MX=16 NW=4 W%d%s M=%d "
                   "row_blocks=%d grid=%d",
