@@ -57,6 +57,47 @@ MUTANTS = {
     # first batch not used to initialize
     "static_first_ignored": ("    if (first) {\n        state[0] = mn;",
                              "    if (0) {\n        state[0] = mn;"),
+    # static range: the minimum updated with the batch maximum
+    "static_min_from_max": ("b0 = w * mn;", "b0 = w * mx;"),
+    # static quantization without the clamp to the calibrated range
+    "static_no_clamp": ("        if (x > (float)qmax)\n            x = (float)qmax;\n"
+                        "        if (x < -(float)qmax)\n            x = -(float)qmax;\n",
+                        ""),
+    # LayerNorm variance about zero instead of about the mean
+    "ln_var_not_centred": ("double d = zqo_half_to_double(row[k]) - mean;",
+                           "double d = zqo_half_to_double(row[k]);"),
+    # LayerNorm output not centred
+    "ln_out_not_centred": ("(zqo_half_to_double(row[k]) - mean) / denom",
+                           "zqo_half_to_double(row[k]) / denom"),
+    # LayerNorm weight and bias swapped
+    "ln_gamma_beta_swapped": ("/ denom * g + b;", "/ denom * b + g;"),
+    # scale from the signed maximum instead of max |x|
+    "scale_signed_max": ("float a = fabsf((float)zqo_half_to_double(v[i]));",
+                         "float a = (float)zqo_half_to_double(v[i]);"),
+    # W4 code range [-8, 8] read as qmax = 8
+    "w4_qmax_8": ("        qmax = 7;", "        qmax = 8;"),
+    # weight group of one row instead of G rows (scale of the first row only)
+    "weight_group_one_row": ("quantize_unit(w + off, (size_t)G * K, qmax, q + off)",
+                             "quantize_unit(w + off, (size_t)K, qmax, q + off);"
+                             " quantize_with_scale(w + off, (size_t)G * K, sw[g],"
+                             " qmax, q + off)"),
+    # int8 codes read as unsigned in the GEMM
+    "gemm_unsigned_codes": ("s += (int64_t)a[k] * (int64_t)b[k];",
+                            "s += (int64_t)(uint8_t)a[k] * (int64_t)b[k];"),
+    # token scale not applied in the epilogue
+    "epilogue_no_token_scale": ("(double)acc[idx] * (double)sx[t] * (double)sw[n / G]",
+                                "(double)acc[idx] * (double)sw[n / G]"),
+    # GeLU applied before the bias is added
+    "epilogue_gelu_before_bias": (
+        "        if (bias)\n            v += zqo_half_to_double(bias[n]);\n"
+        "        if (act == 1)\n            v = 0.5 * v * (1.0 + erf(v / sqrt(2.0)));\n",
+        "        if (act == 1)\n            v = 0.5 * v * (1.0 + erf(v / sqrt(2.0)));\n"
+        "        if (bias)\n            v += zqo_half_to_double(bias[n]);\n"),
+    # binary16 subnormals with quantum 2^-25
+    "half_subnormal_quantum": ("v = ldexp((double)m, -24);",
+                               "v = ldexp((double)m, -25);"),
+    # binary16 overflow one binade late
+    "half_overflow_late": ("if (ex > 15)", "if (ex > 16)"),
 }
 
 
