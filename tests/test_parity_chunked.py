@@ -225,3 +225,21 @@ def test_chunked_chain_graph_and_eager_vs_oracle(M):
         assert np.array_equal(e.view(np.uint16), g.view(np.uint16)), li
         assert_fp16_close_to_oracle(g[:M], z, f"chain linear {li}")
         assert (g[M:] == 7.0).all(), li
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_chunked_empty_m_is_a_no_op(bits):
+    """No tokens: the calls succeed and write nothing."""
+    d = dev()
+    N, K, G = 256, 512, 64
+    qd = _pack(np.zeros((N, K), np.int8), bits)
+    qx = torch.empty(0, K, dtype=torch.int8, device=d)
+    sx = torch.empty(0, dtype=torch.float32, device=d)
+    sw = torch.ones(N // G, dtype=torch.float32, device=d)
+    y = torch.full((1, N), 7.0, dtype=torch.float16, device=d)
+    fc = zq.gemm_w8a8_chunked if bits == 8 else zq.gemm_w4a8_chunked
+    fc(qx, sx, qd, sw, G, None, 0, y[:0])
+    acc = zq.gemm_chunked_i32(bits, qx, qd)
+    torch.cuda.synchronize()
+    assert acc.shape == (0, N)
+    assert (to_np(y) == 7.0).all()

@@ -91,6 +91,14 @@ def test_ln_quant_act_without_ln_out_matches_with():
     assert torch.equal(qa, qb) and torch.equal(sa, sb)
 
 
+def test_row_quantizers_with_no_rows():
+    """No tokens: both quantizers succeed and return empty codes and scales."""
+    x = torch.empty(0, 768, dtype=torch.float16, device=dev())
+    for qx, sx in (zq.quant_act(x), zq.ln_quant_act(x)):
+        assert qx.shape == (0, 768) and sx.shape == (0,)
+    torch.cuda.synchronize()
+
+
 def test_ln_constant_rows():
     x = torch.full((4, 512), 3.0, dtype=torch.float16)
     qx, sx = zq.ln_quant_act(x.to(dev()))
