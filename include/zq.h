@@ -364,13 +364,15 @@ zq_status zq_gemm_w8a16_plan(int M, int N, int K, char *buf, int buflen);
  *   [N][K/2]) -> qd.  An offline step, asynchronous on stream; qw and qd
  *   must not overlap.
  * zq_gemm_w8a8_chunked / zq_gemm_w4a8_chunked: zq_gemm_w8a8 / zq_gemm_w4a8
- *   with the weights in this layout, for 1 <= M <= 16 tokens; y is
- *   bit-identical to those calls on the row-major codes.  The bias, when
- *   given, must be 4-byte aligned.
+ *   with the weights in this layout, for 0 <= M <= 16 tokens (M = 0
+ *   writes nothing); y is bit-identical to those calls on the row-major
+ *   codes.  The bias, when given, must be 4-byte aligned; act as for
+ *   zq_gemm_w8a8.
  * zq_gemm_chunked_i32: the raw int32 accumulator (test hook), bits 8 or 4.
  * zq_gemm_chunked_plan: the kernel configuration for the shape.
  * Errors: ZQ_EINVAL (null/misaligned pointer as for zq_gemm_w8a8, a bias
- * not 4-byte aligned, bits not 4 or 8, overlapping qw / qd), ZQ_ESHAPE
+ * not 4-byte aligned, act not 0 or 1, bits not 4 or 8, overlapping
+ * qw / qd), ZQ_ESHAPE
  * (M < 0, N or K <= 0, G <= 0, N % G != 0), ZQ_EUNSUPPORTED (K % 64 != 0,
  * N not a multiple of BN or the row bytes not a multiple of CK, K above
  * ZQ_MAX_GEMM_K_W8 / _W4, M > 16).
