@@ -502,6 +502,8 @@ def test_chunked_argument_checks():
     assert f(A, B, C, D, 64, ctypes.c_void_p(0x60002), 0, 4, 256, 256, E,
              None) == EINVAL                                             # bias
     assert f(A, B, C, D, 64, None, 0, 0, 256, 256, E, None) == OK        # empty
+    assert f(A, B, C, D, 64, None, 2, 4, 256, 256, E, None) == EINVAL    # act
+    assert f(A, B, C, D, 48, None, 0, 4, 256, 256, E, None) == ESHAPE    # N % G
     assert L.zq_gemm_chunked_i32(5, A, B, 4, 256, 256, C, None) == EINVAL
     buf = ctypes.create_string_buffer(160)
     assert L.zq_gemm_chunked_plan(16, 6144, 24576, 4, buf, 160) == OK
