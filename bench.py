@@ -10,8 +10,9 @@ GPT-NeoX-20B-shaped linears at 2048 tokens (prefill), hidden 6144, INT8
 attention weights (QKV 18432x6144, out 6144x6144) and nibble-packed INT4
 feed-forward weights (FFN1 24576x6144 with GeLU, FFN2 6144x24576), 128-row
 weight groups: the largest of the five workloads that fits one GPU.  Its
-activations follow the GPT-J recipe (0.5% outlier channels x30): "the same
-distributions as config 3" is read 0-indexed.
+activations follow the GPT-J recipe (0.5% outlier channels x30): its value
+recipe is borrowed from another workload, and that reference is read as
+counting workloads from zero.
 
 Memory: R rotating sets of weights, inputs, intermediates and outputs (each
 set one "layer") make the working set larger than twice the 256 MB Infinity
@@ -75,7 +76,7 @@ def parse():
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the layer-chain graph / schedule-table figure")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the prefill GEMM figure of the larger configs")
+                    help="skip the prefill GEMM figure of the larger workloads")
     ap.add_argument("--no-quantizers", action="store_true",
                     help="skip the row-quantizer figure of every workload")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
@@ -834,7 +835,7 @@ def quantizer_figure(torch, zq, dev, steps=20):
 
 def prefill_figure(torch, zq, dev, steps=20):
     """Fused W8A8 / W4A8 GEMMs at the prefill token counts of the other
-    large configs (BERT-large 8192 tokens with W4 FFN, GPT-J-6B 2048; the
+    large workloads (BERT-large 8192 tokens with W4 FFN, GPT-J-6B 2048; the
     GPT-NeoX-20B step is the headline): per linear, the average launch from
     a graph holding it for every rotating set, TOPS and % of the 5.0 POP/s
     INT8 peak, beside the torch fp16 matmul of the same shape."""
@@ -1355,8 +1356,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); the fused linear shards over tokens with "
-              "no communication, see the design notes", file=sys.stderr)
+              f"WORLD_SIZE={world}); the fused linear shards over tokens: each "
+              "GPU runs the same layer on its own token rows with the weights "
+              "replicated, and needs no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -1485,8 +1487,8 @@ def main():
                    "activations": (
                        f"N(0,1), {wl.n_outliers(wl.linears[0].K)} of "
                        f"{wl.linears[0].K} channels x{wl.outlier_factor:g}"
-                       + ("; the BASELINE distribution reference ('as in "
-                          "config 3' / 'config 1') read 0-indexed: GPT-J's "
+                       + ("; value recipe of another workload, its "
+                          "reference read as counting from zero: GPT-J's "
                           "recipe for NeoX, BERT-base's for BERT-large"
                           if wl.name in ("neox-20b", "bert-large") else ""))},
         "roofline": roof,
