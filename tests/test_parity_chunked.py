@@ -243,3 +243,35 @@ def test_chunked_empty_m_is_a_no_op(bits):
     torch.cuda.synchronize()
     assert acc.shape == (0, N)
     assert (to_np(y) == 7.0).all()
+
+
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("bits", [8, 4])
+def test_chunked_at_the_int32_bound(bits, M):
+    """The largest K below the accumulator bound that the layout tiles
+    (130816 = 511 chunks of 256 bytes; W4: 1022 chunks of 128), every code at
+    its two's-complement extreme: |acc| reaches 128 * 128 * K, within 0.2%
+    of 2^31 - 1, and must be exact."""
+    K, N, G = 130816, 64, 32
+    assert K <= 131008 and 128 * 128 * K <= 2 ** 31 - 1
+    lo, hi = (-128, 127) if bits == 8 else (-8, 7)
+    ts = np.where(np.arange(M) % 2 == 0, -128, 127).astype(np.int8)
+    rs = np.where((np.arange(N) // 3) % 2 == 0, lo, hi).astype(np.int8)
+    qx = np.repeat(ts[:, None], K, axis=1).astype(np.int8)
+    q = np.repeat(rs[:, None], K, axis=1).astype(np.int8)
+    sx = np.full(M, 1e-5, np.float32)
+    sw = np.full(N // G, 1e-4 if bits == 8 else 1e-3, np.float32)
+    tq, tsx, tsw = _to_dev(qx), _to_dev(sx), _to_dev(sw)
+    qd = _pack(q, bits)
+    acc = zq.gemm_chunked_i32(bits, tq, qd)
+    fc = zq.gemm_w8a8_chunked if bits == 8 else zq.gemm_w4a8_chunked
+    fr = zq.gemm_w8a8 if bits == 8 else zq.gemm_w4a8
+    y = fc(tq, tsx, qd, tsw, G, None, 0)
+    y_rm = fr(tq, tsx, _to_dev(_rowmajor(q, bits)), tsw, G, None, 0)
+    ref = oracle.gemm_i32(qx, q)
+    torch.cuda.synchronize()
+    what = zq.gemm_chunked_plan(M, N, K, bits)
+    assert np.abs(ref.astype(np.int64)).max() == 128 * (-lo) * K
+    assert np.array_equal(to_np(acc), ref), what
+    assert np.array_equal(to_np(y).view(np.uint16),
+                          to_np(y_rm).view(np.uint16)), what
